@@ -1,0 +1,52 @@
+"""Multi-head attention as EinSums, evaluated in float64 (TEST INFRASTRUCTURE).
+
+Page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法",
+section 2.1, the multi-head attention example:
+
+    Q_proj[s,h,d] = sum_a Q[s,a] W_Q[a,h,d]          (same for K and V)
+    Scores[h,s,t] = (1/sqrt(d_k)) sum_d Q_proj[s,h,d] K_proj[t,h,d]
+    Attn[h,s,t]   = softmax over t of Scores[h,s,t]
+    O[s,h,d]      = sum_t Attn[h,s,t] V_proj[t,h,d]
+    Output[s,a]   = sum_h sum_d O[s,h,d] W_O[a,h,d]
+
+(t is the page's primed s; d_k is the per-head width.)  Softmax is written as
+two EinSums: LSE[h,s] = logsumexp_t Scores[h,s,t] and
+Attn[h,s,t] = exp(Scores[h,s,t] - LSE[h,s]).
+
+Every contraction here is a library product (numpy tensordot / matmul in
+float64) used as one step of the definition; every intermediate stays in
+float64.  ``rows`` restricts the computation to a subset of query positions s
+(all of K_proj and V_proj are still formed), so large layers can be checked
+on a sample of rows.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import ref
+
+
+def mha(t: Dict[str, object], rows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    q, k, v = (ref._as_np(t[n]) for n in ("Q", "K", "V"))
+    wq, wk, wv, wo = (ref._as_np(t[n]) for n in ("W_Q", "W_K", "W_V", "W_O"))
+    a, h, dh = wq.shape
+    if rows is not None:
+        q = q[np.asarray(rows)]
+    # projections: contract a
+    qp = np.tensordot(q, wq, axes=([1], [0]))       # [s, h, d]
+    kp = np.tensordot(k, wk, axes=([1], [0]))       # [t, h, d]
+    vp = np.tensordot(v, wv, axes=([1], [0]))       # [t, h, d]
+    # scores: contract d per head
+    qh = np.transpose(qp, (1, 0, 2))                 # [h, s, d]
+    kh = np.transpose(kp, (1, 2, 0))                 # [h, d, t]
+    scores = np.matmul(qh, kh) / np.sqrt(dh)         # [h, s, t]
+    m = scores.max(axis=2, keepdims=True)
+    lse = m + np.log(np.exp(scores - m).sum(axis=2, keepdims=True))
+    attn = np.exp(scores - lse)                      # [h, s, t]
+    vh = np.transpose(vp, (1, 0, 2))                 # [h, t, d]
+    o = np.transpose(np.matmul(attn, vh), (1, 0, 2))  # [s, h, d]
+    out = np.tensordot(o, wo, axes=([1, 2], [1, 2]))  # [s, a]
+    return {"Q_proj": qp, "K_proj": kp, "V_proj": vp, "Scores": scores,
+            "LSE": lse[..., 0], "Attn": attn, "O": o, "Output": out}

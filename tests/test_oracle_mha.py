@@ -1,0 +1,59 @@
+"""Pins of the fp64 attention-graph oracle (CPU only).
+
+The library-product evaluation in oracle.mha is checked against the node-by-
+node nested-loop evaluation of the same EinSums, and against closed forms:
+softmax rows sum to one, and with K_proj == 0 every attention weight is 1/t
+so O is the mean of V_proj over t.
+"""
+import math
+
+import numpy as np
+import torch
+
+from oracle import mha, ref
+from tensor_relational_algebra_amd import workloads
+
+
+def _inputs(s, a, h, dh, seed=0):
+    case = workloads.MhaCase(s=s, a=a, h=h, dh=dh, wid=90 + seed)
+    return case.make_inputs()
+
+
+def test_graph_equals_node_by_node_loops():
+    t = _inputs(12, 16, 2, 4)
+    r = mha.mha(t)
+    qp = ref.einsum("sa,ahd->shd", t["Q"], t["W_Q"])
+    kp = ref.einsum("sa,ahd->shd", t["K"], t["W_K"])
+    vp = ref.einsum("sa,ahd->shd", t["V"], t["W_V"])
+    sc = ref.einsum("shd,thd->hst", qp, kp, post_scale=1 / math.sqrt(4))
+    lse = ref.einsum("hst->hs", sc, None, "ident", "lse")
+    at = ref.einsum("hst,hs->hst", sc, lse, "exp_sub", "none")
+    o = ref.einsum("hst,thd->shd", at, vp)
+    out = ref.einsum("shd,ahd->sa", o, t["W_O"])
+    for name, want in [("Q_proj", qp), ("K_proj", kp), ("V_proj", vp), ("Scores", sc),
+                       ("LSE", lse), ("Attn", at), ("O", o), ("Output", out)]:
+        np.testing.assert_allclose(r[name], want, rtol=1e-12, atol=1e-12, err_msg=name)
+
+
+def test_softmax_rows_sum_to_one():
+    r = mha.mha(_inputs(16, 32, 4, 8, seed=1))
+    np.testing.assert_allclose(r["Attn"].sum(axis=2), 1.0, rtol=0, atol=1e-12)
+
+
+def test_zero_keys_give_uniform_attention():
+    t = _inputs(8, 16, 2, 4, seed=2)
+    t["W_K"] = torch.zeros_like(t["W_K"])
+    r = mha.mha(t)
+    # exp(0 - log 8) is 1/8 up to the rounding of exp and log
+    np.testing.assert_allclose(r["Attn"], np.full(r["Attn"].shape, 1.0 / 8), rtol=1e-15, atol=0)
+    want_o = np.broadcast_to(r["V_proj"].mean(axis=0, keepdims=True), r["O"].shape)
+    np.testing.assert_allclose(r["O"], want_o, rtol=0, atol=1e-13)
+
+
+def test_row_sample_equals_full():
+    t = _inputs(16, 16, 2, 8, seed=3)
+    full = mha.mha(t)
+    rows = np.array([0, 5, 15])
+    part = mha.mha(t, rows=rows)
+    np.testing.assert_allclose(part["Output"], full["Output"][rows], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(part["Attn"], full["Attn"][:, rows], rtol=1e-13, atol=1e-13)

@@ -1,0 +1,68 @@
+"""The pins must catch plausible mistakes in the oracle (CPU only).
+
+Each case compiles a copy of oracle/einsum_ref.c with one planted mistake (a
+wrong sign, a dropped term, a transposed operand, a swapped aggregate, a
+missing scale) into a temporary library, points the oracle at it, and checks
+that at least one pin of test_oracle_definition fails.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle.ref as ref
+from tests import test_oracle_definition as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "einsum_ref.c")
+
+MUTATIONS = {
+    "sqdiff_sign": ("case OR_JOIN_SQDIFF: return (x - y) * (x - y);",
+                    "case OR_JOIN_SQDIFF: return (x + y) * (x + y);"),
+    "dropped_last_term": ("if (++idx[cl[p]] < bounds[cl[p]])",
+                          "if (++idx[cl[p]] < bounds[cl[p]] - 1)"),
+    "transposed_operand": ("for (int p = n - 1; p >= 0; --p) {\n        st[p] = s;",
+                           "for (int p = 0; p < n; ++p) {\n        st[p] = s;"),
+    "max_is_min": ("else if (agg == OR_AGG_MAX) acc = v > acc ? v : acc;\n                else acc = v < acc ? v : acc;\n            } while (next_tuple(nc, cl, bounds, idx));\n            r = acc;\n        }\n        z[o] = post_scale * r;",
+                   "else if (agg == OR_AGG_MAX) acc = v < acc ? v : acc;\n                else acc = v < acc ? v : acc;\n            } while (next_tuple(nc, cl, bounds, idx));\n            r = acc;\n        }\n        z[o] = post_scale * r;"),
+    "scale_dropped": ("z[o] = post_scale * r;", "z[o] = r;"),
+    "lse_without_max": ("r = m + log(s);", "r = log(s);"),
+    "int_add_is_sub": ("static int64_t join_i(int op, int64_t x, int64_t y)\n{\n    switch (op) {\n    case OR_JOIN_MUL: return x * y;\n    case OR_JOIN_SQDIFF: return (x - y) * (x - y);\n    case OR_JOIN_ADD: return x + y;",
+                       "static int64_t join_i(int op, int64_t x, int64_t y)\n{\n    switch (op) {\n    case OR_JOIN_MUL: return x * y;\n    case OR_JOIN_SQDIFF: return (x - y) * (x - y);\n    case OR_JOIN_ADD: return x - y;"),
+}
+
+PIN_FUNCS = [
+    pins.test_hand_cases,
+    pins.test_matmul_equals_library_product,
+    pins.test_four_index_contraction_equals_library,
+    pins.test_squared_distance_closed_form,
+    pins.test_max_plus_special_cases,
+    pins.test_logsumexp_closed_forms,
+    pins.test_batched_and_attention_specs_equal_library,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert old in src, f"mutation {name} no longer applies"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new, 1))
+    lib = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-fopenmp", "-o", str(lib), str(path), "-lm"], check=True)
+    ref._load()  # make sure the real library's signatures are set up first
+    mut = ctypes.CDLL(str(lib))
+    for fn in ("oracle_einsum_f64", "oracle_einsum_i64"):
+        getattr(mut, fn).argtypes = getattr(ref._lib, fn).argtypes
+        getattr(mut, fn).restype = ctypes.c_int
+    mut.oracle_max_threads.restype = ctypes.c_int
+    monkeypatch.setattr(ref, "_lib", mut)
+    caught = []
+    for f in PIN_FUNCS:
+        try:
+            f()
+        except AssertionError:
+            caught.append(f.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
