@@ -1,0 +1,243 @@
+/*
+ * tra.h -- C ABI of libtra: extended EinSum executed as tensor-relational
+ * algebra (TRA) join + aggregation on one AMD Instinct MI355X (gfx950).
+ *
+ * Method: page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法"
+ * (an EinDecomp summary).  Section 2.1 defines the extended EinSum (any
+ * associative-commutative aggregate, any binary scalar join); section 2.2
+ * defines tensor relations, the partition rule, and the three TRA operations
+ * (join, aggregation, repartition) and the mechanical EinSum -> TRA lowering
+ * under a partition vector d; sections 3.1-3.2 give the communication cost
+ * model and the dynamic programme that choose d; section 4.3 prunes d to
+ * powers of two and asks for task counts that are multiples of P.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every function returns a tra_status: 0 (TRA_OK) or a negative code.
+ *   tra_last_error() gives a thread-local text for the last failure.  No C++
+ *   exception crosses this boundary.
+ * - All validation happens on the host before anything is launched; an
+ *   error return means nothing was enqueued.
+ * - Device pointers are plain HIP device addresses owned by the caller
+ *   (libtra never allocates device memory).  Streams are hipStream_t passed
+ *   as void*; NULL means the legacy default stream.  Calls are asynchronous
+ *   with respect to the host: nothing synchronises.
+ * - A "relation" is a tensor stored in the relation layout: given the
+ *   tensor's labels l_1..l_n, extents B_l and part counts d_l (d_l | B_l,
+ *   block extent b_l = B_l / d_l), the element with global index g sits at
+ *       offset = rowmajor(k; d) * prod(b) + rowmajor(r; b),
+ *       k_l = g_l / b_l,  r_l = g_l % b_l,
+ *   i.e. the sub-tensors (section 2.2's partition rule) one after another in
+ *   row-major key order, each sub-tensor dense row-major.  With every d_l = 1
+ *   this is the ordinary dense row-major array.
+ * - Canonical label order: the output labels in output order, then the
+ *   contracted labels in order of first appearance (first operand, then the
+ *   second).  bounds[] and d[] arguments follow it.
+ * - Element counts of every tensor must stay below 2^31.
+ * - Integer arithmetic is 32-bit two's complement (wrap-around), so integer
+ *   results do not depend on the order of aggregation.
+ */
+#ifndef TRA_H
+#define TRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TRA_OK = 0,
+    TRA_E_NULL = -1,          /* a required pointer argument is NULL */
+    TRA_E_SPEC = -2,          /* spec string does not parse ("ab,bc->ac", "abc->ab") */
+    TRA_E_LABELS = -3,        /* output label in no operand, label repeated in one operand,
+                                 more than 24 labels, or rank above 12 */
+    TRA_E_INDIVISIBLE = -4,   /* an extent < 1, a part count < 1, or d_l does not divide B_l */
+    TRA_E_DLEN = -5,          /* n_labels differs from the spec's distinct label count, or a
+                                 per-operand d vector has the wrong length / unequal shared entries */
+    TRA_E_DTYPE = -6,         /* unknown dtype, or a dtype the op is not defined for
+                                 (lse / exp_sub on integers, integer output of a float op) */
+    TRA_E_OP = -7,            /* unknown join/aggregate, aggregate NONE with contracted labels,
+                                 a binary join with one operand, ident with two, post_scale != 1
+                                 on integers */
+    TRA_E_WORKSPACE = -8,     /* workspace smaller than tra_plan_info().workspace_bytes */
+    TRA_E_ALIGN = -9,         /* a device pointer is not 16-byte aligned */
+    TRA_E_HIP = -10,          /* the HIP runtime reported an error at launch */
+    TRA_E_NO_CANDIDATE = -11, /* the chooser found no admissible partition vector */
+    TRA_E_RANGE = -12,        /* a tensor has 2^31 or more elements */
+    TRA_E_GRAPH = -13,        /* malformed EinGraph description */
+    TRA_E_BUFFER = -14        /* caller's output buffer too small */
+} tra_status;
+
+typedef enum { TRA_F32 = 0, TRA_BF16 = 1, TRA_I32 = 2 } tra_dtype;
+
+/* Joins (section 2.1: any binary scalar function). */
+typedef enum {
+    TRA_JOIN_MUL = 0,     /* x * y */
+    TRA_JOIN_SQDIFF = 1,  /* (x - y)^2 */
+    TRA_JOIN_ADD = 2,     /* x + y */
+    TRA_JOIN_IDENT = 3,   /* x (one operand) */
+    TRA_JOIN_EXP_SUB = 4  /* exp(x - y) (float only) */
+} tra_join_op;
+
+/* Aggregates (section 2.1: any associative and commutative reduction). */
+typedef enum {
+    TRA_AGG_NONE = 0,     /* no contracted label: Z = JOIN(...) */
+    TRA_AGG_SUM = 1,
+    TRA_AGG_MAX = 2,
+    TRA_AGG_MIN = 3,
+    TRA_AGG_LSE = 4       /* log(sum(exp(v))) (float only) */
+} tra_agg_op;
+
+/* Kernel family a plan was lowered to (reported by tra_plan_info). */
+typedef enum {
+    TRA_KERNEL_GENERIC = 0,   /* one thread per output element, any spec / op / layout */
+    TRA_KERNEL_ELEMWISE = 1,  /* aggregate NONE, vectorised along the output's last label */
+    TRA_KERNEL_ROWREDUCE = 2, /* one wavefront per output element, contiguous contracted run */
+    TRA_KERNEL_VALU_TILE = 3, /* register-blocked output tiles on the vector ALUs */
+    TRA_KERNEL_MFMA_BF16 = 4  /* bf16 x bf16 -> fp32 matrix-core tiles (mul + sum only) */
+} tra_kernel_family;
+
+typedef struct tra_plan_s *tra_plan_t;
+
+typedef struct {
+    int64_t n_tasks;          /* N: join tasks = product of d over all labels */
+    int64_t n_groups;         /* G: aggregation groups = product of d over the output labels */
+    int64_t n_agg;            /* partials per group = product of d over contracted labels */
+    int64_t agg_split;        /* workgroups that share one output tile (1 = in-register fold) */
+    int64_t x_elems, y_elems, z_elems;
+    size_t x_bytes, y_bytes, z_bytes;
+    size_t workspace_bytes;   /* device scratch tra_execute needs (0 = none) */
+    int32_t kernel;           /* tra_kernel_family */
+    int32_t n_labels;
+    char labels[32];          /* canonical label order, NUL-terminated */
+} tra_plan_info_t;
+
+/*
+ * tra_plan -- lower one extended EinSum under a partition vector to a TRA
+ * plan (section 2.2, "EinSum to TRA": partition X and Y by d, join every
+ * key-matched sub-tensor pair, aggregate by the output part of the key;
+ * section 3.1: a task is the triple (bound, EinSum, inputs)).
+ *
+ *   spec       "xlabels,ylabels->zlabels" or "xlabels->zlabels"; labels are
+ *              single ASCII letters; at most 24 distinct labels, rank <= 12.
+ *   bounds     n_labels extents B_l in canonical label order.
+ *   d          n_labels part counts d_l in canonical order, d_l | B_l.  The
+ *              ≥P-tasks rule belongs to the chooser, not here: any d is run.
+ *   join_op    tra_join_op; agg_op: tra_agg_op.
+ *   in_dtype   dtype of both operands; out_dtype: dtype of Z.  Float
+ *              inputs accumulate in fp32, integers in int32.
+ *   post_scale multiplies the aggregated value (float only; 1 otherwise).
+ *   out_plan   receives a host-only handle (no device work, no HIP call).
+ * Errors: TRA_E_NULL, TRA_E_SPEC, TRA_E_LABELS, TRA_E_DLEN,
+ * TRA_E_INDIVISIBLE, TRA_E_DTYPE, TRA_E_OP, TRA_E_RANGE.
+ */
+int tra_plan(const char *spec, const int64_t *bounds, const int32_t *d, int n_labels,
+             int join_op, int agg_op, int in_dtype, int out_dtype, float post_scale,
+             tra_plan_t *out_plan);
+
+/* Sizes and the lowering decision of a plan.  Errors: TRA_E_NULL. */
+int tra_plan_info(tra_plan_t plan, tra_plan_info_t *info);
+
+/* Free a plan's host memory.  NULL is accepted. */
+int tra_plan_destroy(tra_plan_t plan);
+
+/*
+ * tra_execute -- run the plan's join + aggregation on the GPU
+ * (section 2.2: join of key-matched pairs, then GROUP BY the output key and
+ * reduce).  Each output sub-tensor's partials are folded in ascending order
+ * of the contracted part of the key; no atomics, so runs are bitwise
+ * reproducible.
+ *
+ *   x_rel, y_rel   operand relations under the plan's d (y_rel NULL for a
+ *                  one-operand spec), dtype in_dtype, 16-byte aligned.
+ *   z_rel          output relation under the plan's d restricted to the
+ *                  output labels; fully overwritten.  Must not alias inputs.
+ *   workspace      device scratch of at least info.workspace_bytes (may be
+ *                  NULL when that is 0); contents on entry are ignored.
+ *   hip_stream     hipStream_t the kernels are enqueued on.
+ * Errors: TRA_E_NULL, TRA_E_ALIGN, TRA_E_WORKSPACE, TRA_E_HIP.
+ */
+int tra_execute(tra_plan_t plan, const void *x_rel, const void *y_rel, void *z_rel,
+                void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * tra_repartition -- re-cut one tensor from partition vector d_from to d_to
+ * (section 2.2, repartition; the initial partition of section 4.1's runtime
+ * is the case d_from = all ones).  A pure permutation of elements: every
+ * element is read once and written once, bit-exact.
+ *
+ *   bounds   rank extents; d_from, d_to: rank part counts each.
+ *   dtype    tra_dtype (only its size matters).
+ *   src,dst  device relations, 16-byte aligned, non-overlapping.
+ * Errors: TRA_E_NULL, TRA_E_DLEN (rank < 1 or > 12), TRA_E_INDIVISIBLE,
+ * TRA_E_DTYPE, TRA_E_ALIGN, TRA_E_RANGE, TRA_E_HIP.
+ */
+int tra_repartition(const int64_t *bounds, int rank, const int32_t *d_from,
+                    const int32_t *d_to, int dtype, const void *src, void *dst,
+                    void *hip_stream);
+
+/*
+ * tra_canonical_labels -- write the canonical label order of a spec
+ * (output labels, then contracted labels by first appearance) into out
+ * (NUL-terminated).  Returns the label count (> 0) or a negative status
+ * (TRA_E_NULL, TRA_E_SPEC, TRA_E_LABELS, TRA_E_BUFFER).
+ */
+int tra_canonical_labels(const char *spec, char *out, int out_cap);
+
+/*
+ * tra_d_from_operand_form -- convert a per-operand partition vector (one
+ * entry per label occurrence, first operand's labels then the second's, as
+ * in section 2.2's matmul example [d_i, d_j, d_j, d_k]) to the canonical
+ * per-label vector.  Occurrences of one label must agree (section 2.2
+ * requires the two j entries to be equal).
+ *   d_ops   n_ops entries; d_out: receives n_labels entries.
+ * Errors: TRA_E_NULL, TRA_E_SPEC, TRA_E_LABELS, TRA_E_DLEN.
+ */
+int tra_d_from_operand_form(const char *spec, const int32_t *d_ops, int n_ops,
+                            int32_t *d_out, int d_out_cap);
+
+/*
+ * tra_cost -- the communication cost of one EinSum under d (section 3.1):
+ * N*(|X sub-tensor| + |Y sub-tensor|) + (N/n_agg)*(n_agg-1)*|Z sub-tensor|,
+ * in elements, N being the node's join-task count.
+ * Errors: as tra_plan's validation of spec/bounds/d.
+ */
+int tra_cost(const char *spec, const int64_t *bounds, const int32_t *d, int n_labels,
+             int64_t *cost_out);
+
+/*
+ * tra_choose -- pick a partition vector for every node of an EinGraph by
+ * the dynamic programme of section 3.2 over the cost model of section 3.1.
+ *
+ * graph_desc: one node per line, fields separated by blanks:
+ *     <name> <kind> <spec> <label=extent,...> <input,input>
+ *   kind is "einsum" or "softmax" (softmax: spec "hst->hst", the pair
+ *   LSE = lse over the last label and Attn = exp(S - LSE) under one d);
+ *   an input names an earlier node or, prefixed by '@', a graph input.
+ *   Blank lines and lines starting with '#' are ignored.
+ * P: required task multiple (a candidate needs N >= P and N % P == 0).
+ * Candidates: every d_l a power of two dividing B_l (section 4.3).
+ * Repartition term: 0 when the producer's part counts on its output labels
+ * equal the consumer's on the matching input labels, else the tensor size.
+ * Ties: lower cost, then fewer tasks, then the lexicographically smaller d.
+ *
+ *   d_out      receives, node after node in description order, each node's
+ *              d in its canonical label order (d_cap entries available).
+ *   cost_out   receives the total graph cost (may be NULL).
+ * Errors: TRA_E_NULL, TRA_E_GRAPH, TRA_E_SPEC, TRA_E_LABELS,
+ * TRA_E_NO_CANDIDATE, TRA_E_BUFFER.
+ */
+int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_cap, int64_t *cost_out);
+
+/* Text of a status code (static storage). */
+const char *tra_status_string(int status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char *tra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TRA_H */

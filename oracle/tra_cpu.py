@@ -150,3 +150,23 @@ def task_counts(spec: str, dmap: Dict[str, int]) -> Tuple[int, int, int]:
     n_agg = int(np.prod([dmap[c] for c in contracted], dtype=np.int64)) if contracted else 1
     g = int(np.prod([dmap[c] for c in out], dtype=np.int64)) if out else 1
     return g * n_agg, g, n_agg
+
+
+def buffer_offset(g: Sequence[int], shape: Sequence[int], d: Sequence[int]) -> int:
+    """Position of the element with global index g in the flat relation buffer:
+    its sub-tensor's key k = g // b comes first (row-major over d, times the
+    sub-tensor volume), then its place r = g % b inside the sub-tensor."""
+    _check(shape, d)
+    b = [s // k for s, k in zip(shape, d)]
+    key = [gi // bi for gi, bi in zip(g, b)]
+    r = [gi % bi for gi, bi in zip(g, b)]
+    vol = 1
+    for bi in b:
+        vol *= bi
+    kpos = 0
+    for ki, di in zip(key, d):
+        kpos = kpos * di + ki
+    rpos = 0
+    for ri, bi in zip(r, b):
+        rpos = rpos * bi + ri
+    return kpos * vol + rpos

@@ -1,1 +1,10 @@
-"""MI355X-native executor for extended EinSum as tensor-relational algebra."""
+"""MI355X-native executor for extended EinSum as tensor-relational algebra.
+
+The compute path is the C-ABI library libtra (include/tra.h: tra_plan,
+tra_execute, tra_repartition, tra_choose, ...) with hand-written gfx950 HIP
+kernels; this package is its thin Python binding (torch supplies device
+memory and streams) plus the seeded synthetic workloads.
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH, Plan, TraError, from_relation, lib, to_relation, tra_canonical_labels, tra_choose, tra_cost,
+    tra_d_from_operand_form, tra_execute, tra_plan, tra_repartition)

@@ -1,0 +1,231 @@
+"""ctypes binding of libtra (include/tra.h): argument marshalling only.
+
+Every function here converts Python / torch arguments to the C ABI, calls the
+library, and turns a negative status into ``TraError``.  All computation runs
+in the library's HIP kernels; there is no Python or CPU fallback, and a
+missing library raises at the first call.  torch supplies device memory and
+the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence, Tuple, Union
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_build", "libtra.so")
+
+DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
+TORCH_DTYPES = {0: torch.float32, 1: torch.bfloat16, 2: torch.int32}
+DTYPE_OF_TORCH = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2}
+JOINS = {"mul": 0, "sqdiff": 1, "add": 2, "ident": 3, "exp_sub": 4}
+AGGS = {"none": 0, "sum": 1, "max": 2, "min": 3, "lse": 4}
+KERNELS = {0: "generic", 1: "elemwise", 2: "rowreduce", 3: "valu_tile", 4: "mfma_bf16"}
+
+
+class TraError(RuntimeError):
+    def __init__(self, code: int, what: str, detail: str):
+        super().__init__(f"{what} (status {code}): {detail}")
+        self.code = code
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("n_tasks", ctypes.c_int64), ("n_groups", ctypes.c_int64), ("n_agg", ctypes.c_int64),
+                ("agg_split", ctypes.c_int64), ("x_elems", ctypes.c_int64), ("y_elems", ctypes.c_int64),
+                ("z_elems", ctypes.c_int64), ("x_bytes", ctypes.c_size_t), ("y_bytes", ctypes.c_size_t),
+                ("z_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int32),
+                ("n_labels", ctypes.c_int32), ("labels", ctypes.c_char * 32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtra.so (built in-tree by ``build()``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libtra is not built ({LIB_PATH} missing); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        sig = {
+            "tra_plan": ([ctypes.c_char_p, P, P, I, I, I, I, I, ctypes.c_float, P], I),
+            "tra_plan_info": ([P, P], I),
+            "tra_plan_destroy": ([P], I),
+            "tra_execute": ([P, P, P, P, P, ctypes.c_size_t, P], I),
+            "tra_repartition": ([P, I, P, P, I, P, P, P], I),
+            "tra_canonical_labels": ([ctypes.c_char_p, ctypes.c_char_p, I], I),
+            "tra_d_from_operand_form": ([ctypes.c_char_p, P, I, P, I], I),
+            "tra_cost": ([ctypes.c_char_p, P, P, I, P], I),
+            "tra_choose": ([ctypes.c_char_p, I, P, I, P], I),
+            "tra_status_string": ([I], ctypes.c_char_p),
+            "tra_last_error": ([], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        L = lib()
+        raise TraError(rc, L.tra_status_string(rc).decode(), L.tra_last_error().decode())
+    return rc
+
+
+def _i64(v: Sequence[int]):
+    return (ctypes.c_int64 * len(v))(*[int(a) for a in v])
+
+
+def _i32(v: Sequence[int]):
+    return (ctypes.c_int32 * len(v))(*[int(a) for a in v])
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def tra_canonical_labels(spec: str) -> str:
+    buf = ctypes.create_string_buffer(64)
+    _check(lib().tra_canonical_labels(spec.encode(), buf, 64))
+    return buf.value.decode()
+
+
+def _ordered(spec: str, v: Union[Dict[str, int], Sequence[int]]) -> List[int]:
+    if isinstance(v, dict):
+        return [int(v[c]) for c in tra_canonical_labels(spec)]
+    return [int(a) for a in v]
+
+
+def tra_d_from_operand_form(spec: str, d_ops: Sequence[int]) -> List[int]:
+    n = len(tra_canonical_labels(spec))
+    out = (ctypes.c_int32 * n)()
+    _check(lib().tra_d_from_operand_form(spec.encode(), _i32(d_ops), len(d_ops), out, n))
+    return list(out)
+
+
+def tra_cost(spec: str, bounds, d) -> int:
+    b, dd = _ordered(spec, bounds), _ordered(spec, d)
+    c = ctypes.c_int64()
+    _check(lib().tra_cost(spec.encode(), _i64(b), _i32(dd), len(b), ctypes.byref(c)))
+    return c.value
+
+
+class Plan:
+    """Owns a tra_plan_t handle and a copy of its tra_plan_info_t."""
+
+    def __init__(self, handle: int, spec: str, in_dtype: int, out_dtype: int):
+        self.handle = handle
+        self.spec = spec
+        self.in_dtype = in_dtype
+        self.out_dtype = out_dtype
+        info = PlanInfo()
+        _check(lib().tra_plan_info(handle, ctypes.byref(info)))
+        self.info = info
+
+    @property
+    def kernel(self) -> str:
+        return KERNELS[self.info.kernel]
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.tra_plan_destroy(self.handle)
+            self.handle = None
+
+    def workspace(self, device) -> Optional[torch.Tensor]:
+        n = self.info.workspace_bytes
+        return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def tra_plan(spec: str, bounds, d, join: str = "mul", agg: str = "sum", in_dtype: str = "f32",
+             out_dtype: str = "f32", post_scale: float = 1.0) -> Plan:
+    b, dd = _ordered(spec, bounds), _ordered(spec, d)
+    h = ctypes.c_void_p()
+    _check(lib().tra_plan(spec.encode(), _i64(b), _i32(dd), len(b), JOINS[join], AGGS[agg], DTYPES[in_dtype],
+                          DTYPES[out_dtype], float(post_scale), ctypes.byref(h)))
+    return Plan(h.value, spec, DTYPES[in_dtype], DTYPES[out_dtype])
+
+
+def _dev_ptr(t: Optional[torch.Tensor], what: str, numel: int, dtype: Optional[int]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{what} has {t.numel()} elements, the plan needs {numel}")
+    if dtype is not None and DTYPE_OF_TORCH.get(t.dtype) != dtype:
+        raise ValueError(f"{what} has dtype {t.dtype}, the plan needs {TORCH_DTYPES[dtype]}")
+    return t.data_ptr()
+
+
+def tra_execute(plan: Plan, x: torch.Tensor, y: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Run the plan on device relations x (and y); returns z (allocated if None)."""
+    inf = plan.info
+    px = _dev_ptr(x, "x", inf.x_elems, plan.in_dtype)
+    py = _dev_ptr(y, "y", inf.y_elems, plan.in_dtype) if inf.y_elems else None
+    if z is None:
+        z = torch.empty(inf.z_elems, dtype=TORCH_DTYPES[plan.out_dtype], device=x.device)
+    pz = _dev_ptr(z, "z", inf.z_elems, plan.out_dtype)
+    if workspace is None and inf.workspace_bytes:
+        workspace = plan.workspace(x.device)
+    pw = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().tra_execute(plan.handle, px, py, pz, pw, wb, _stream(stream)))
+    return z
+
+
+def tra_repartition(src: torch.Tensor, bounds: Sequence[int], d_from: Sequence[int], d_to: Sequence[int],
+                    dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Re-cut a device relation of the tensor `bounds` from d_from to d_to."""
+    n = 1
+    for b in bounds:
+        n *= int(b)
+    dt = DTYPE_OF_TORCH[src.dtype]
+    if dst is None:
+        dst = torch.empty(n, dtype=src.dtype, device=src.device)
+    ps = _dev_ptr(src, "src", n, dt)
+    pd = _dev_ptr(dst, "dst", n, dt)
+    r = len(bounds)
+    _check(lib().tra_repartition(_i64(bounds), r, _i32(d_from), _i32(d_to), dt, ps, pd, _stream(stream)))
+    return dst
+
+
+def to_relation(dense: torch.Tensor, d: Sequence[int], out: Optional[torch.Tensor] = None, stream=None):
+    """Dense row-major tensor -> relation under d (the initial partition)."""
+    return tra_repartition(dense.reshape(-1), list(dense.shape), [1] * dense.dim(), d, out, stream)
+
+
+def from_relation(rel: torch.Tensor, shape: Sequence[int], d: Sequence[int], out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Relation under d -> dense row-major tensor of `shape`."""
+    return tra_repartition(rel.reshape(-1), list(shape), d, [1] * len(shape), out, stream).reshape(shape)
+
+
+def tra_choose(graph_desc: str, p: int) -> Tuple[List[List[int]], int]:
+    """Partition vectors for every node of an EinGraph (see include/tra.h)."""
+    cap = 24 * max(1, graph_desc.count("\n") + 1)
+    out = (ctypes.c_int32 * cap)()
+    cost = ctypes.c_int64()
+    _check(lib().tra_choose(graph_desc.encode(), int(p), out, cap, ctypes.byref(cost)))
+    res, pos = [], 0
+    for line in graph_desc.splitlines():
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        spec = f[2]
+        n = len(spec.split("->")[1]) if f[1] == "softmax" else len(tra_canonical_labels(spec))
+        res.append(list(out[pos:pos + n]))
+        pos += n
+    return res, cost.value

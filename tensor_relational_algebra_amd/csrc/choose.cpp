@@ -1,0 +1,316 @@
+// choose.cpp -- partition-vector choice for an EinGraph.
+//
+// Page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法":
+//  * section 3.1: a node under d costs N*(|X sub|+|Y sub|) for its join
+//    inputs plus (N/n_agg)*(n_agg-1)*|Z sub| for its aggregation (numbers
+//    moved; N is the node's join-task count), and an edge costs a
+//    repartition when the producer's blocking differs from what the
+//    consumer needs;
+//  * section 3.2: candidates must give at least P tasks and divide the
+//    extents; DP[v][d_v] = Cost(v,d_v) + min over d_u of
+//    (DP[u][d_u] + Repartition(d_u, d_v)), read back from the output node;
+//  * section 4.3: part counts are powers of two, and the task count a
+//    multiple of P.
+// The repartition term is 0 when the producer's part counts on its output
+// labels equal the consumer's on the matching input labels, else the size of
+// the tensor.  The minimum over d_u therefore splits into "best producer
+// candidate with the consumer's blocking" and "best producer candidate
+// overall plus the tensor size", which keeps the DP linear in the number of
+// candidates per edge while giving the same minimum and the same tie-break.
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "plan.h"
+
+namespace {
+
+struct Cand {
+    std::vector<int32_t> d;  // canonical order
+    int64_t n_tasks;
+    int64_t cost;            // node cost
+    int64_t dp;              // accumulated
+    std::vector<int> pick;   // chosen producer candidate per input slot (-1 = graph input)
+};
+
+struct GNode {
+    std::string name, kind, spec;
+    std::vector<std::string> ops;
+    std::string out, canon, con;
+    int64_t B[128];
+    std::vector<std::string> inputs;
+    std::vector<int> src;    // producer node index per slot, -1 = graph input
+    std::vector<Cand> cands;
+};
+
+int fail(int code, const std::string &m)
+{
+    tra::set_error(m);
+    return code;
+}
+
+bool key_less(const Cand &a, int64_t ca, const Cand &b, int64_t cb)
+{
+    if (ca != cb) return ca < cb;
+    if (a.n_tasks != b.n_tasks) return a.n_tasks < b.n_tasks;
+    return a.d < b.d;
+}
+
+int64_t einsum_cost(const std::vector<std::string> &ops, const std::string &out, const std::string &con,
+                    const int64_t *B, const int32_t *D)
+{
+    std::string all;
+    for (auto &o : ops)
+        for (char c : o)
+            if (all.find(c) == std::string::npos) all.push_back(c);
+    int64_t n = 1, n_agg = 1;
+    for (char c : all) n *= D[(int)c];
+    for (char c : con) n_agg *= D[(int)c];
+    auto blk = [&](const std::string &t) {
+        int64_t v = 1;
+        for (char c : t) v *= B[(int)c] / D[(int)c];
+        return v;
+    };
+    int64_t in = 0;
+    for (auto &o : ops) in += blk(o);
+    return n * in + (n / n_agg) * (n_agg - 1) * blk(out);
+}
+
+int64_t node_cost(const GNode &g, const Cand &c)
+{
+    int32_t D[128];
+    for (int i = 0; i < 128; ++i) D[i] = 1;
+    for (size_t i = 0; i < g.canon.size(); ++i) D[(int)g.canon[i]] = c.d[i];
+    if (g.kind == "softmax") {
+        // LSE over the last label, then exp(S - LSE), under the same d
+        std::string hst = g.out, hs = g.out.substr(0, g.out.size() - 1), t = g.out.substr(g.out.size() - 1);
+        return einsum_cost({hst}, hs, t, g.B, D) + einsum_cost({hst, hs}, hst, "", g.B, D);
+    }
+    return einsum_cost(g.ops, g.out, g.con, g.B, D);
+}
+
+std::vector<std::string> split(const std::string &s, char sep)
+{
+    std::vector<std::string> v;
+    std::string cur;
+    for (char c : s) {
+        if (c == sep) {
+            v.push_back(cur);
+            cur.clear();
+        } else {
+            cur.push_back(c);
+        }
+    }
+    v.push_back(cur);
+    return v;
+}
+
+int parse_graph(const char *desc, std::vector<GNode> &nodes)
+{
+    std::istringstream in(desc);
+    std::string line;
+    while (std::getline(in, line)) {
+        std::istringstream ls(line);
+        std::vector<std::string> f;
+        std::string w;
+        while (ls >> w) f.push_back(w);
+        if (f.empty() || f[0][0] == '#') continue;
+        if (f.size() != 5) return fail(TRA_E_GRAPH, "a node line needs 5 fields: " + line);
+        GNode g;
+        g.name = f[0];
+        g.kind = f[1];
+        g.spec = f[2];
+        if (g.kind != "einsum" && g.kind != "softmax") return fail(TRA_E_GRAPH, "unknown node kind " + g.kind);
+        char canon[64];
+        int nl = tra_canonical_labels(g.spec.c_str(), canon, sizeof(canon));
+        if (nl < 0) return nl;
+        size_t arrow = g.spec.find("->");
+        g.ops = split(g.spec.substr(0, arrow), ',');
+        g.out = g.spec.substr(arrow + 2);
+        g.canon = canon;
+        g.con = g.canon.substr(g.out.size());
+        if (g.kind == "softmax" && (g.ops.size() != 1 || g.ops[0] != g.out || g.out.size() < 2))
+            return fail(TRA_E_GRAPH, "a softmax node is written like hst->hst");
+        for (int i = 0; i < 128; ++i) g.B[i] = 0;
+        for (auto &kv : split(f[3], ',')) {
+            if (kv.size() < 3 || kv[1] != '=') return fail(TRA_E_GRAPH, "bad extent entry " + kv);
+            long long v = std::atoll(kv.c_str() + 2);
+            if (v < 1) return fail(TRA_E_GRAPH, "extent < 1 in " + kv);
+            g.B[(int)kv[0]] = v;
+        }
+        for (char c : g.canon)
+            if (!g.B[(int)c]) return fail(TRA_E_GRAPH, std::string("no extent for label '") + c + "' in " + g.name);
+        g.inputs = split(f[4], ',');
+        if (g.inputs.size() != g.ops.size())
+            return fail(TRA_E_GRAPH, "node " + g.name + " lists " + std::to_string(g.inputs.size()) +
+                                         " inputs for " + std::to_string(g.ops.size()) + " operands");
+        for (size_t s = 0; s < g.inputs.size(); ++s) {
+            const std::string &src = g.inputs[s];
+            if (!src.empty() && src[0] == '@') {
+                g.src.push_back(-1);
+                continue;
+            }
+            int found = -1;
+            for (size_t j = 0; j < nodes.size(); ++j)
+                if (nodes[j].name == src) found = (int)j;
+            if (found < 0) return fail(TRA_E_GRAPH, "input " + src + " of " + g.name + " is not an earlier node");
+            if (nodes[found].out.size() != g.ops[s].size())
+                return fail(TRA_E_GRAPH, "rank of " + src + " does not match its use in " + g.name);
+            for (size_t p = 0; p < g.ops[s].size(); ++p)
+                if (nodes[found].B[(int)nodes[found].out[p]] != g.B[(int)g.ops[s][p]])
+                    return fail(TRA_E_GRAPH, "extents of " + src + " do not match its use in " + g.name);
+            g.src.push_back(found);
+        }
+        nodes.push_back(g);
+    }
+    if (nodes.empty()) return fail(TRA_E_GRAPH, "empty graph");
+    std::vector<int> uses(nodes.size(), 0);
+    for (auto &g : nodes)
+        for (int s : g.src)
+            if (s >= 0 && ++uses[s] > 1)
+                return fail(TRA_E_GRAPH, "node " + nodes[s].name + " feeds two consumers; the DP needs a tree");
+    int roots = 0;
+    for (size_t j = 0; j < nodes.size(); ++j) roots += uses[j] == 0;
+    if (roots != 1) return fail(TRA_E_GRAPH, "the graph must have exactly one output node");
+    return TRA_OK;
+}
+
+void make_candidates(GNode &g, int P)
+{
+    const size_t L = g.canon.size();
+    std::vector<std::vector<int32_t>> opts(L);
+    for (size_t i = 0; i < L; ++i)
+        for (int64_t k = 1; k <= g.B[(int)g.canon[i]]; k *= 2)
+            if (g.B[(int)g.canon[i]] % k == 0) opts[i].push_back((int32_t)k);
+    std::vector<size_t> idx(L, 0);
+    while (true) {
+        Cand c;
+        c.d.resize(L);
+        int64_t n = 1;
+        for (size_t i = 0; i < L; ++i) {
+            c.d[i] = opts[i][idx[i]];
+            n *= c.d[i];
+        }
+        if (n >= P && n % P == 0) {
+            c.n_tasks = n;
+            c.cost = node_cost(g, c);
+            g.cands.push_back(std::move(c));
+        }
+        size_t i = L;
+        while (i > 0) {
+            --i;
+            if (++idx[i] < opts[i].size()) break;
+            idx[i] = 0;
+            if (i == 0) return;
+        }
+        if (L == 0) return;
+    }
+}
+
+// part counts of candidate c on the labels `labels` of node g
+std::vector<int32_t> blocking(const GNode &g, const Cand &c, const std::string &labels)
+{
+    std::vector<int32_t> b;
+    for (char l : labels) b.push_back(c.d[g.canon.find(l)]);
+    return b;
+}
+
+}  // namespace
+
+extern "C" int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_cap, int64_t *cost_out)
+{
+    if (!graph_desc || !d_out) return fail(TRA_E_NULL, "graph_desc / d_out is NULL");
+    if (P < 1) return fail(TRA_E_GRAPH, "P must be >= 1");
+    std::vector<GNode> nodes;
+    int rc = parse_graph(graph_desc, nodes);
+    if (rc) return rc;
+    size_t need = 0;
+    for (auto &g : nodes) need += g.canon.size();
+    if ((size_t)d_cap < need) return fail(TRA_E_BUFFER, "d_out needs " + std::to_string(need) + " entries");
+    for (auto &g : nodes) {
+        make_candidates(g, P);
+        if (g.cands.empty()) return fail(TRA_E_NO_CANDIDATE, "no admissible partition vector for " + g.name);
+    }
+    for (size_t v = 0; v < nodes.size(); ++v) {
+        GNode &g = nodes[v];
+        // per input slot: producer's global best and best per output blocking
+        struct SlotInfo {
+            int u = -1;
+            int best = -1;
+            std::map<std::vector<int32_t>, int> by_block;
+            int64_t size = 0;
+        };
+        std::vector<SlotInfo> slots(g.src.size());
+        for (size_t s = 0; s < g.src.size(); ++s) {
+            int u = g.src[s];
+            slots[s].u = u;
+            if (u < 0) continue;
+            GNode &pu = nodes[u];
+            int64_t size = 1;
+            for (char c : pu.out) size *= pu.B[(int)c];
+            slots[s].size = size;
+            for (int i = 0; i < (int)pu.cands.size(); ++i) {
+                const Cand &c = pu.cands[i];
+                if (slots[s].best < 0 || key_less(c, c.dp, pu.cands[slots[s].best], pu.cands[slots[s].best].dp))
+                    slots[s].best = i;
+                auto blk = blocking(pu, c, pu.out);
+                auto it = slots[s].by_block.find(blk);
+                if (it == slots[s].by_block.end() ||
+                    key_less(c, c.dp, pu.cands[it->second], pu.cands[it->second].dp))
+                    slots[s].by_block[blk] = i;
+            }
+        }
+        for (Cand &c : g.cands) {
+            c.dp = c.cost;
+            c.pick.assign(g.src.size(), -1);
+            for (size_t s = 0; s < g.src.size(); ++s) {
+                if (slots[s].u < 0) continue;
+                GNode &pu = nodes[slots[s].u];
+                auto want = blocking(g, c, g.ops[s]);
+                const Cand &gb = pu.cands[slots[s].best];
+                int64_t gcost = gb.dp + (blocking(pu, gb, pu.out) == want ? 0 : slots[s].size);
+                int pick = slots[s].best;
+                int64_t pcost = gcost;
+                auto it = slots[s].by_block.find(want);
+                if (it != slots[s].by_block.end()) {
+                    const Cand &mb = pu.cands[it->second];
+                    if (key_less(mb, mb.dp, gb, gcost)) {
+                        pick = it->second;
+                        pcost = mb.dp;
+                    }
+                }
+                c.pick[s] = pick;
+                c.dp += pcost;
+            }
+        }
+    }
+    // the output node is the one nobody consumes (the last one in a valid tree)
+    std::vector<int> uses(nodes.size(), 0);
+    for (auto &g : nodes)
+        for (int s : g.src)
+            if (s >= 0) uses[s]++;
+    int root = -1;
+    for (size_t j = 0; j < nodes.size(); ++j)
+        if (!uses[j]) root = (int)j;
+    GNode &rg = nodes[root];
+    int ri = 0;
+    for (int i = 1; i < (int)rg.cands.size(); ++i)
+        if (key_less(rg.cands[i], rg.cands[i].dp, rg.cands[ri], rg.cands[ri].dp)) ri = i;
+    std::vector<int> chosen(nodes.size(), -1);
+    std::vector<std::pair<int, int>> stack{{root, ri}};
+    while (!stack.empty()) {
+        auto [v, i] = stack.back();
+        stack.pop_back();
+        chosen[v] = i;
+        for (size_t s = 0; s < nodes[v].src.size(); ++s)
+            if (nodes[v].src[s] >= 0) stack.push_back({nodes[v].src[s], nodes[v].cands[i].pick[s]});
+    }
+    size_t pos = 0;
+    for (size_t v = 0; v < nodes.size(); ++v)
+        for (int32_t x : nodes[v].cands[chosen[v]].d) d_out[pos++] = x;
+    if (cost_out) *cost_out = rg.cands[ri].dp;
+    return TRA_OK;
+}

@@ -1,0 +1,291 @@
+// k_simple.hip -- generic join+aggregate, elementwise, row-reduction,
+// split-fold and repartition kernels for gfx950.
+//
+// Page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法",
+// section 2.2: a join applies a kernel function to every key-matched pair of
+// sub-tensors; an aggregation groups the results by the output part of the
+// key and reduces each group; a repartition re-cuts a relation under another
+// partition vector.  Here every output element belongs to one group, and the
+// thread (or wavefront) that owns it walks the group's contracted partitions
+// in ascending key order and each partition's in-block range in row-major
+// order, folding the joined values as it goes; nothing is materialised.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "plan.h"
+
+namespace tra {
+
+// ---------------------------------------------------------------- generic
+// One thread per output element, any spec / join / aggregate / layout.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void k_generic(GenericDesc g, int join, int agg, int two,
+                                                 const TI *__restrict__ x, const TI *__restrict__ y,
+                                                 TO *__restrict__ z)
+{
+    using A = typename Scalar<TI>::acc;
+    const int last = g.con.n - 1;
+    const uint32_t E = last >= 0 ? g.con.ext[last] : 1;
+    const int64_t sxl = last >= 0 ? g.con.st[0][last] : 0, syl = last >= 0 ? g.con.st[1][last] : 0;
+    const int64_t n_outer = g.n_con / E;
+    for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < g.n_out;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        int64_t xo = 0, yo = 0;
+        radix_offsets(g.out, o, xo, yo);
+        Fold<A> f;
+        f.init(agg);
+        for (int64_t c = 0; c < n_outer; ++c) {
+            int64_t xc = xo, yc = yo;
+            int64_t idx = c;
+            for (int i = last - 1; i >= 0; --i) {
+                uint32_t e = g.con.ext[i];
+                int64_t q = idx / e;
+                int64_t dgt = idx - q * e;
+                idx = q;
+                xc += dgt * g.con.st[0][i];
+                yc += dgt * g.con.st[1][i];
+            }
+            for (uint32_t e = 0; e < E; ++e) {
+                A xv = Scalar<TI>::load(x, xc + e * sxl);
+                A yv = two ? Scalar<TI>::load(y, yc + e * syl) : A(0);
+                f.add(agg, join_any(join, xv, yv));
+            }
+        }
+        Scalar<TO>::store(z, o, (A)f.result(agg, g.post_scale));
+    }
+}
+
+// ---------------------------------------------------------------- elementwise
+// Aggregate NONE: z = join(x, y) (times post_scale); `vec` consecutive output
+// elements share one digit decomposition.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void k_elemwise(ElemDesc g, int join, int two, const TI *__restrict__ x,
+                                                  const TI *__restrict__ y, TO *__restrict__ z)
+{
+    using A = typename Scalar<TI>::acc;
+    const int vec = g.vec;
+    const int f = g.out.n - 1;
+    const int64_t sx = f >= 0 ? g.out.st[0][f] : 0, sy = f >= 0 ? g.out.st[1][f] : 0;
+    const int64_t n_vec = g.n_out / vec;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n_vec;
+         v += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t o = v * vec;
+        int64_t xo = 0, yo = 0;
+        radix_offsets(g.out, o, xo, yo);
+        for (int i = 0; i < vec; ++i) {
+            A xv = Scalar<TI>::load(x, xo + (vec > 1 ? i * sx : 0));
+            A yv = two ? Scalar<TI>::load(y, yo + (vec > 1 ? i * sy : 0)) : A(0);
+            A r = join_any(join, xv, yv);
+            if constexpr (sizeof(A) == 4 && !std::is_same<A, int32_t>::value) r *= g.post_scale;
+            Scalar<TO>::store(z, o + i, r);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- row reduce
+// One wavefront per output element.  Lanes stride over the contiguous last
+// contracted run (X stride 1); the outer contracted digits (the contracted
+// keys first, ascending) are walked in order; the 64 lane partials are then
+// combined by a butterfly.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void k_rowreduce(RowDesc g, int join, int agg, int two,
+                                                   const TI *__restrict__ x, const TI *__restrict__ y,
+                                                   TO *__restrict__ z)
+{
+    using A = typename Scalar<TI>::acc;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t o = wave; o < g.n_out; o += n_waves) {
+        int64_t xo = 0, yo = 0;
+        radix_offsets(g.out, o, xo, yo);
+        Fold<A> f;
+        f.init(agg);
+        for (int64_t c = 0; c < g.n_outer; ++c) {
+            int64_t xc = xo, yc = yo;
+            radix_offsets(g.outer, c, xc, yc);
+            for (int64_t e = lane; e < g.inner; e += 64) {
+                A xv = Scalar<TI>::load(x, xc + e);
+                A yv = two ? Scalar<TI>::load(y, yc + e * g.inner_sy) : A(0);
+                f.add(agg, join_any(join, xv, yv));
+            }
+        }
+        if constexpr (std::is_same<A, float>::value) {
+            for (int off = 32; off >= 1; off >>= 1) {
+                float om = __shfl_xor(f.m, off, 64);
+                float os = __shfl_xor(f.s, off, 64);
+                f.merge(agg, om, os);
+            }
+        } else {
+            for (int off = 32; off >= 1; off >>= 1) f.merge(agg, __shfl_xor(f.m, off, 64), 0);
+        }
+        if (lane == 0) Scalar<TO>::store(z, o, (A)f.result(agg, g.post_scale));
+    }
+}
+
+// ---------------------------------------------------------------- split fold
+// Deterministic cross-workgroup aggregation: partial s of output o sits at
+// ws[s * n + o]; fold s = 0..S-1 in order, then finish.
+template <typename A, typename TO>
+__global__ __launch_bounds__(256) void k_split_fold(const A *__restrict__ ws, int64_t n, int split, int agg,
+                                                    float scale, TO *__restrict__ z)
+{
+    for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n; o += (int64_t)gridDim.x * blockDim.x) {
+        Fold<A> f;
+        f.init(agg);
+        for (int s = 0; s < split; ++s) f.merge(agg, ws[(int64_t)s * n + o], A(1));
+        if constexpr (std::is_same<A, float>::value) {
+            Scalar<TO>::store(z, o, f.m * scale);
+        } else {
+            Scalar<TO>::store(z, o, f.m);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- repartition
+// Destination positions are enumerated in the destination's own layout, so
+// writes are sequential; each digit of the destination index maps to a
+// source stride.  U is the copy unit (vec elements).
+template <typename U>
+__global__ __launch_bounds__(256) void k_repartition(RepartDesc r, int vec, const U *__restrict__ src,
+                                                     U *__restrict__ dst)
+{
+    const int64_t n_units = r.n_elems / vec;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_units;
+         u += (int64_t)gridDim.x * blockDim.x) {
+        int64_t so = 0, unused = 0;
+        radix_offsets(r.dst, u * vec, so, unused);
+        dst[u] = src[so / vec];
+    }
+}
+
+// Power-of-two destination digits: 32-bit shifts and masks.
+template <typename U>
+__global__ __launch_bounds__(256) void k_repartition_p2(Pow2Group g, int lvec, uint32_t n_units,
+                                                        const U *__restrict__ src, U *__restrict__ dst)
+{
+    const uint32_t stride = gridDim.x * blockDim.x;
+    uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
+#pragma unroll 4
+    for (; u < n_units; u += stride) {
+        uint32_t e = u << lvec;
+        int32_t so = 0;
+        for (int i = 0; i < g.n; ++i) so += (int32_t)((e >> g.sh[i]) & g.mask[i]) * g.st[0][i];
+        dst[u] = src[so >> lvec];
+    }
+}
+
+static int grid_for(int64_t work, int per_block = 256)
+{
+    int64_t b = (work + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > 65536) b = 65536;
+    return (int)b;
+}
+
+#define TRA_DISPATCH_IO(IN, OUT, CALL)                                                      \
+    do {                                                                                    \
+        if (IN == D_F32 && OUT == D_F32) { using TI = float; using TO = float; CALL; }      \
+        else if (IN == D_F32 && OUT == D_BF16) { using TI = float; using TO = bf16_t; CALL; } \
+        else if (IN == D_BF16 && OUT == D_F32) { using TI = bf16_t; using TO = float; CALL; } \
+        else if (IN == D_BF16 && OUT == D_BF16) { using TI = bf16_t; using TO = bf16_t; CALL; } \
+        else { using TI = int32_t; using TO = int32_t; CALL; }                              \
+    } while (0)
+
+int launch_generic(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    int grid = grid_for(p.gen.n_out);
+    TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
+                    hipLaunchKernelGGL((k_generic<TI, TO>), dim3(grid), dim3(256), 0, s, p.gen, p.join, p.agg,
+                                       p.n_ops == 2 ? 1 : 0, (const TI *)x, (const TI *)y, (TO *)z));
+    return (int)hipGetLastError();
+}
+
+int launch_elemwise(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    int grid = grid_for(p.el.n_out / p.el.vec);
+    TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
+                    hipLaunchKernelGGL((k_elemwise<TI, TO>), dim3(grid), dim3(256), 0, s, p.el, p.join,
+                                       p.n_ops == 2 ? 1 : 0, (const TI *)x, (const TI *)y, (TO *)z));
+    return (int)hipGetLastError();
+}
+
+int launch_rowreduce(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    int grid = grid_for(p.row.n_out * 64);
+    TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
+                    hipLaunchKernelGGL((k_rowreduce<TI, TO>), dim3(grid), dim3(256), 0, s, p.row, p.join, p.agg,
+                                       p.n_ops == 2 ? 1 : 0, (const TI *)x, (const TI *)y, (TO *)z));
+    return (int)hipGetLastError();
+}
+
+int launch_split_fold(const tra_plan_s &p, const void *ws, void *z, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    int64_t n = p.info.z_elems;
+    int grid = grid_for(n);
+    int split = p.gv.split;
+    if (p.in_dtype == D_I32) {
+        hipLaunchKernelGGL((k_split_fold<int32_t, int32_t>), dim3(grid), dim3(256), 0, s, (const int32_t *)ws, n,
+                           split, p.agg, 1.0f, (int32_t *)z);
+    } else if (p.out_dtype == D_BF16) {
+        hipLaunchKernelGGL((k_split_fold<float, bf16_t>), dim3(grid), dim3(256), 0, s, (const float *)ws, n, split,
+                           p.agg, p.post_scale, (bf16_t *)z);
+    } else {
+        hipLaunchKernelGGL((k_split_fold<float, float>), dim3(grid), dim3(256), 0, s, (const float *)ws, n, split,
+                           p.agg, p.post_scale, (float *)z);
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_repartition(const RepartDesc &r, int esz, const void *src, void *dst, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    const int unit = r.vec * esz;
+    const int64_t n_units = r.n_elems / r.vec;
+    // power-of-two digits: shift/mask path
+    bool p2 = n_units < (1ll << 31);
+    Pow2Group g{};
+    g.n = r.dst.n;
+    int sh = 0;
+    for (int i = r.dst.n - 1; i >= 0 && p2; --i) {
+        uint32_t e = r.dst.ext[i];
+        if (e & (e - 1)) p2 = false;
+        g.sh[i] = (uint8_t)sh;
+        g.mask[i] = e - 1;
+        g.st[0][i] = (int32_t)r.dst.st[0][i];
+        while ((1u << sh) < ((1u << g.sh[i]) * e)) ++sh;
+    }
+    if (p2) {
+        int lvec = 0;
+        while ((1 << lvec) < r.vec) ++lvec;
+        int grid = grid_for(n_units / 4 + 1);
+#define TRA_REP_P2(U) hipLaunchKernelGGL((k_repartition_p2<U>), dim3(grid), dim3(256), 0, s, g, lvec, \
+                                          (uint32_t)n_units, (const U *)src, (U *)dst)
+        switch (unit) {
+        case 16: TRA_REP_P2(uint4); break;
+        case 8: TRA_REP_P2(uint2); break;
+        case 4: TRA_REP_P2(uint32_t); break;
+        default: TRA_REP_P2(uint16_t); break;
+        }
+#undef TRA_REP_P2
+        return (int)hipGetLastError();
+    }
+    int grid = grid_for(n_units);
+#define TRA_REP(U) hipLaunchKernelGGL((k_repartition<U>), dim3(grid), dim3(256), 0, s, r, r.vec, (const U *)src, (U *)dst)
+    switch (unit) {
+    case 16: TRA_REP(uint4); break;
+    case 8: TRA_REP(uint2); break;
+    case 4: TRA_REP(uint32_t); break;
+    default: TRA_REP(uint16_t); break;
+    }
+#undef TRA_REP
+    return (int)hipGetLastError();
+}
+
+const char *hip_error_text(int err) { return hipGetErrorString((hipError_t)err); }
+
+}  // namespace tra

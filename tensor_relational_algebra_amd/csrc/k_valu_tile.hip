@@ -1,0 +1,296 @@
+// k_valu_tile.hip -- register-blocked join + aggregation on the vector ALUs.
+//
+// Page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法",
+// section 2.1: the join may be any binary scalar function, e.g. (x-y)^2, and
+// the aggregate any associative-commutative reduction, e.g. max.  Such joins
+// are not products, so they do not map to the matrix cores: each thread owns
+// an 8x8 block of one output sub-tensor, keeps its 64 running aggregates in
+// registers, and walks the contracted range (contracted keys ascending, then
+// the in-block index) through an LDS-staged tile of both operands.
+//
+// Operands are addressed through the relation layout's per-sub-dimension
+// strides (power-of-two groups), so any partition vector d is read in place.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "plan.h"
+
+namespace tra {
+
+constexpr int VT_BM = 128, VT_BN = 128, VT_BK = 32, VT_PAD = 4, VT_THREADS = 256;
+
+TileShape valu_tile_shape(int variant)
+{
+    if (variant == 0) return {VT_BM, VT_BN, VT_BK};
+    return {0, 0, 0};
+}
+
+// Map the linear workgroup id to an output tile.  Consecutive ids land on
+// different XCDs (round-robin dispatch); regroup them so each XCD owns a
+// contiguous run of tiles, then sweep tile columns within groups of rows so
+// that neighbouring workgroups share operand panels in that XCD's L2.
+__device__ __forceinline__ void tile_of(uint32_t nb, uint32_t tiles_n, uint32_t &tm, uint32_t &tn)
+{
+    uint32_t b = blockIdx.x;
+    if (nb % 8 == 0) b = (b % 8) * (nb / 8) + b / 8;
+    const uint32_t G = 4;
+    uint32_t tiles_m = nb / tiles_n;
+    uint32_t per = G * tiles_n;
+    uint32_t g = b / per, first = g * G;
+    uint32_t gs = min(tiles_m - first, G);
+    uint32_t r = b % per;
+    tm = first + r % gs;
+    tn = r / gs;
+}
+
+template <int JOIN, typename A>
+__device__ __forceinline__ A vjoin(A a, A b)
+{
+    if constexpr (std::is_same<A, float>::value) {
+        if constexpr (JOIN == J_MUL) return a * b;
+        else if constexpr (JOIN == J_SQDIFF) { float t = a - b; return t * t; }
+        else return a + b;
+    } else {
+        if constexpr (JOIN == J_MUL) return wmul(a, b);
+        else if constexpr (JOIN == J_SQDIFF) { int32_t t = wsub(a, b); return wmul(t, t); }
+        else return wadd(a, b);
+    }
+}
+
+template <int AGG, typename A>
+__device__ __forceinline__ A vfold(A acc, A v)
+{
+    if constexpr (AGG == A_SUM) {
+        if constexpr (std::is_same<A, float>::value) return acc + v;
+        else return wadd(acc, v);
+    } else if constexpr (AGG == A_MAX) {
+        if constexpr (std::is_same<A, float>::value) return fmaxf(acc, v);
+        else return max(acc, v);
+    } else {
+        if constexpr (std::is_same<A, float>::value) return fminf(acc, v);
+        else return min(acc, v);
+    }
+}
+
+// Two contracted steps folded at once (lets max / min use a 3-input op).
+template <int JOIN, int AGG, typename A>
+__device__ __forceinline__ A vstep2(A acc, A a0, A b0, A a1, A b1)
+{
+    if constexpr (AGG == A_SUM && JOIN == J_SQDIFF && std::is_same<A, float>::value) {
+        float t0 = a0 - b0, t1 = a1 - b1;
+        return fmaf(t1, t1, fmaf(t0, t0, acc));
+    } else if constexpr (AGG == A_SUM && JOIN == J_MUL && std::is_same<A, float>::value) {
+        return fmaf(a1, b1, fmaf(a0, b0, acc));
+    } else if constexpr (AGG == A_SUM) {
+        return vfold<AGG>(vfold<AGG>(acc, vjoin<JOIN>(a0, b0)), vjoin<JOIN>(a1, b1));
+    } else {
+        return vfold<AGG>(acc, vfold<AGG>(vjoin<JOIN>(a0, b0), vjoin<JOIN>(a1, b1)));
+    }
+}
+
+template <int AGG, typename A>
+__device__ __forceinline__ A vinit()
+{
+    if constexpr (AGG == A_SUM) return A(0);
+    else if constexpr (AGG == A_MAX) {
+        if constexpr (std::is_same<A, float>::value) return -INFINITY;
+        else return INT32_MIN;
+    } else {
+        if constexpr (std::is_same<A, float>::value) return INFINITY;
+        else return INT32_MAX;
+    }
+}
+
+template <int JOIN, int AGG, typename T, typename TO, bool AK, bool BKM>
+__global__ __launch_bounds__(VT_THREADS) void k_valu_tile(GemmView v, const T *__restrict__ x,
+                                                         const T *__restrict__ y, TO *__restrict__ z,
+                                                         T *__restrict__ ws)
+{
+    using A = T;
+    constexpr int BM = VT_BM, BN = VT_BN, BK = VT_BK;
+    constexpr int LDA = BM + VT_PAD, LDB = BN + VT_PAD;
+    __shared__ __attribute__((aligned(16))) A As[BK * LDA];
+    __shared__ __attribute__((aligned(16))) A Bs[BK * LDB];
+
+    const int tid = threadIdx.x;
+    const uint32_t tiles_n = v.gn.total / BN;
+    const uint32_t nb = (v.gm.total / BM) * tiles_n;
+    uint32_t tm, tn;
+    tile_of(nb, tiles_n, tm, tn);
+    const uint32_t m0 = tm * BM, n0 = tn * BN;
+    const uint32_t bidx = blockIdx.y;
+    const int32_t bx = p2off<0>(v.gb, bidx), by = p2off<1>(v.gb, bidx), bz = p2off<2>(v.gb, bidx);
+    const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
+    const uint32_t kend = kbeg + (uint32_t)v.k_per_split;
+
+    // Loader assignment: 4 vectors of 4 elements per thread for each operand.
+    // K-major operand: vector along k; 8 vectors per row of BK.
+    // MN-major operand: vector along m/n; BM/4 vectors per k-row.
+    int32_t a_off[4], b_off[4];
+    int a_row[4], a_col[4], b_row[4], b_col[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        int q = tid + VT_THREADS * r;
+        if constexpr (AK) {
+            a_col[r] = (q % (BK / 4)) * 4;  // k
+            a_row[r] = q / (BK / 4);        // m
+            a_off[r] = p2off<0>(v.gm, m0 + a_row[r]) + bx;
+        } else {
+            a_row[r] = (q % (BM / 4)) * 4;  // m
+            a_col[r] = q / (BM / 4);        // k
+            a_off[r] = p2off<0>(v.gm, m0 + a_row[r]) + bx;
+        }
+        if constexpr (BKM) {
+            b_col[r] = (q % (BK / 4)) * 4;
+            b_row[r] = q / (BK / 4);
+            b_off[r] = p2off<0>(v.gn, n0 + b_row[r]) + by;
+        } else {
+            b_row[r] = (q % (BN / 4)) * 4;
+            b_col[r] = q / (BN / 4);
+            b_off[r] = p2off<0>(v.gn, n0 + b_row[r]) + by;
+        }
+    }
+
+    A acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = vinit<AGG, A>();
+
+    const int tx = tid % 16, ty = tid / 16;
+    using V4 = typename std::conditional<std::is_same<A, float>::value, float4, int4>::type;
+    V4 ra[4], rb[4];
+
+    auto gload = [&](uint32_t k0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (AK) ra[r] = *(const V4 *)(x + a_off[r] + p2off<0>(v.gk, k0 + a_col[r]));
+            else ra[r] = *(const V4 *)(x + a_off[r] + p2off<0>(v.gk, k0 + a_col[r]));
+            if constexpr (BKM) rb[r] = *(const V4 *)(y + b_off[r] + p2off<1>(v.gk, k0 + b_col[r]));
+            else rb[r] = *(const V4 *)(y + b_off[r] + p2off<1>(v.gk, k0 + b_col[r]));
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (AK) {
+                As[(a_col[r] + 0) * LDA + a_row[r]] = ra[r].x;
+                As[(a_col[r] + 1) * LDA + a_row[r]] = ra[r].y;
+                As[(a_col[r] + 2) * LDA + a_row[r]] = ra[r].z;
+                As[(a_col[r] + 3) * LDA + a_row[r]] = ra[r].w;
+            } else {
+                *(V4 *)&As[a_col[r] * LDA + a_row[r]] = ra[r];
+            }
+            if constexpr (BKM) {
+                Bs[(b_col[r] + 0) * LDB + b_row[r]] = rb[r].x;
+                Bs[(b_col[r] + 1) * LDB + b_row[r]] = rb[r].y;
+                Bs[(b_col[r] + 2) * LDB + b_row[r]] = rb[r].z;
+                Bs[(b_col[r] + 3) * LDB + b_row[r]] = rb[r].w;
+            } else {
+                *(V4 *)&Bs[b_col[r] * LDB + b_row[r]] = rb[r];
+            }
+        }
+    };
+
+    gload(kbeg);
+    for (uint32_t k0 = kbeg; k0 < kend; k0 += BK) {
+        __syncthreads();
+        lstore();
+        __syncthreads();
+        if (k0 + BK < kend) gload(k0 + BK);
+#pragma unroll 4
+        for (int kk = 0; kk < BK; kk += 2) {
+            V4 a0l = *(const V4 *)&As[kk * LDA + ty * 4], a0h = *(const V4 *)&As[kk * LDA + 64 + ty * 4];
+            V4 b0l = *(const V4 *)&Bs[kk * LDB + tx * 4], b0h = *(const V4 *)&Bs[kk * LDB + 64 + tx * 4];
+            V4 a1l = *(const V4 *)&As[(kk + 1) * LDA + ty * 4], a1h = *(const V4 *)&As[(kk + 1) * LDA + 64 + ty * 4];
+            V4 b1l = *(const V4 *)&Bs[(kk + 1) * LDB + tx * 4], b1h = *(const V4 *)&Bs[(kk + 1) * LDB + 64 + tx * 4];
+            A a0[8] = {a0l.x, a0l.y, a0l.z, a0l.w, a0h.x, a0h.y, a0h.z, a0h.w};
+            A b0[8] = {b0l.x, b0l.y, b0l.z, b0l.w, b0h.x, b0h.y, b0h.z, b0h.w};
+            A a1[8] = {a1l.x, a1l.y, a1l.z, a1l.w, a1h.x, a1h.y, a1h.z, a1h.w};
+            A b1[8] = {b1l.x, b1l.y, b1l.z, b1l.w, b1h.x, b1h.y, b1h.z, b1h.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = vstep2<JOIN, AGG>(acc[i][j], a0[i], b0[j], a1[i], b1[j]);
+        }
+    }
+
+    // Epilogue: rows ty*4+{0..3}, 64+ty*4+{0..3}; columns tx*4+{0..3}, 64+tx*4+{0..3}.
+    const bool split = v.split > 1;
+    T *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t m = m0 + (i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4));
+        const int32_t om = p2off<1>(v.gm, m) + bz;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t nbase = n0 + h * 64 + tx * 4;
+            int32_t on[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) on[j] = p2off<1>(v.gn, nbase + j);
+            const bool vec = on[1] == on[0] + 1 && on[2] == on[0] + 2 && on[3] == on[0] + 3 && ((om + on[0]) & 3) == 0;
+            A r4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r4[j] = acc[i][h * 4 + j];
+            if (split) {
+                if (vec) *(V4 *)&wsp[om + on[0]] = V4{r4[0], r4[1], r4[2], r4[3]};
+                else
+                    for (int j = 0; j < 4; ++j) wsp[om + on[j]] = r4[j];
+            } else {
+                if constexpr (std::is_same<A, float>::value) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) r4[j] *= v.post_scale;
+                }
+                if constexpr (std::is_same<TO, float>::value || std::is_same<TO, int32_t>::value) {
+                    if (vec) *(V4 *)&z[om + on[0]] = V4{r4[0], r4[1], r4[2], r4[3]};
+                    else
+                        for (int j = 0; j < 4; ++j) z[om + on[j]] = r4[j];
+                } else {
+                    for (int j = 0; j < 4; ++j) Scalar<TO>::store(z, om + on[j], (float)r4[j]);
+                }
+            }
+        }
+    }
+}
+
+int launch_split_fold(const tra_plan_s &p, const void *ws, void *z, void *stream);
+
+template <int JOIN, int AGG, typename T, typename TO>
+static int launch_vt(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    const GemmView &v = p.gv;
+    dim3 grid((v.gm.total / VT_BM) * (v.gn.total / VT_BN), v.gb.total, v.split);
+#define TRA_VT(AK, BKM)                                                                                  \
+    hipLaunchKernelGGL((k_valu_tile<JOIN, AGG, T, TO, AK, BKM>), grid, dim3(VT_THREADS), 0, s, v,       \
+                       (const T *)x, (const T *)y, (TO *)z, (T *)ws)
+    if (p.a_kmajor && p.b_kmajor) TRA_VT(true, true);
+    else if (p.a_kmajor) TRA_VT(true, false);
+    else if (p.b_kmajor) TRA_VT(false, true);
+    else TRA_VT(false, false);
+#undef TRA_VT
+    int err = (int)hipGetLastError();
+    if (err || v.split == 1) return err;
+    return launch_split_fold(p, ws, z, stream);
+}
+
+template <typename T, typename TO>
+static int launch_vt_ops(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream)
+{
+#define TRA_OPS(J, AG) if (p.join == J && p.agg == AG) return launch_vt<J, AG, T, TO>(p, x, y, z, ws, stream)
+    TRA_OPS(J_MUL, A_SUM);
+    TRA_OPS(J_SQDIFF, A_SUM);
+    TRA_OPS(J_ADD, A_MAX);
+    TRA_OPS(J_ADD, A_MIN);
+#undef TRA_OPS
+    return (int)hipErrorInvalidValue;
+}
+
+int launch_valu_tile(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream)
+{
+    if (p.in_dtype == D_I32) return launch_vt_ops<int32_t, int32_t>(p, x, y, z, ws, stream);
+    if (p.out_dtype == D_BF16) return launch_vt_ops<float, bf16_t>(p, x, y, z, ws, stream);
+    return launch_vt_ops<float, float>(p, x, y, z, ws, stream);
+}
+
+}  // namespace tra

@@ -1,0 +1,633 @@
+// plan.cpp -- spec parsing, validation and the EinSum -> TRA lowering
+// (page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法",
+// section 2.2 "from EinSum to TRA": partition the operands by d, join every
+// key-matched pair of sub-tensors, aggregate by the output part of the key).
+//
+// On one GPU the N = prod(d) join tasks are not shipped to devices; the
+// planner turns the relation layout into per-sub-dimension strides, so a
+// kernel can walk any sub-tensor pair directly in HBM, and picks the kernel
+// family that does the join and the aggregation of a group in registers.
+#include <algorithm>
+#include <initializer_list>
+#include <utility>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "plan.h"
+
+namespace tra {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string &msg) { g_last_error = msg; }
+
+static int fail(int code, const std::string &msg)
+{
+    set_error(msg);
+    return code;
+}
+
+static bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+static int ilog2(uint64_t v)
+{
+    int r = 0;
+    while ((1ull << r) < v) ++r;
+    return r;
+}
+
+static int dtype_size(int dt) { return dt == D_BF16 ? 2 : 4; }
+
+// Parse "ab,bc->ac" / "abc->ab".  On success fills ops / out and the
+// canonical label order (output labels, then contracted by first appearance).
+static int parse_spec(const char *spec, std::vector<std::string> &ops, std::string &out,
+                      std::string &canon, std::string &con)
+{
+    if (!spec) return fail(TRA_E_NULL, "spec is NULL");
+    std::string s;
+    for (const char *c = spec; *c; ++c)
+        if (*c != ' ') s.push_back(*c);
+    size_t arrow = s.find("->");
+    if (arrow == std::string::npos || s.find("->", arrow + 1) != std::string::npos)
+        return fail(TRA_E_SPEC, "spec needs exactly one '->': " + s);
+    std::string lhs = s.substr(0, arrow);
+    out = s.substr(arrow + 2);
+    ops.clear();
+    size_t start = 0;
+    while (true) {
+        size_t comma = lhs.find(',', start);
+        ops.push_back(lhs.substr(start, comma == std::string::npos ? std::string::npos : comma - start));
+        if (comma == std::string::npos) break;
+        start = comma + 1;
+    }
+    if (ops.size() < 1 || ops.size() > 2) return fail(TRA_E_SPEC, "one or two operands expected: " + s);
+    auto letters = [](const std::string &t) {
+        for (char c : t)
+            if (!((c >= 'a' && c <= 'z') || (c >= 'A' && c <= 'Z'))) return false;
+        return true;
+    };
+    for (auto &o : ops) {
+        if (o.empty()) return fail(TRA_E_SPEC, "an operand has no labels: " + s);
+        if (!letters(o)) return fail(TRA_E_SPEC, "labels must be letters: " + s);
+    }
+    if (!letters(out)) return fail(TRA_E_SPEC, "labels must be letters: " + s);
+    auto repeated = [](const std::string &t) {
+        for (size_t i = 0; i < t.size(); ++i)
+            if (t.find(t[i], i + 1) != std::string::npos) return true;
+        return false;
+    };
+    for (auto &o : ops)
+        if (repeated(o)) return fail(TRA_E_LABELS, "label repeated within an operand: " + s);
+    if (repeated(out)) return fail(TRA_E_LABELS, "label repeated in the output: " + s);
+    for (auto &o : ops)
+        if ((int)o.size() > kMaxRank) return fail(TRA_E_LABELS, "rank above 12: " + s);
+    if ((int)out.size() > kMaxRank) return fail(TRA_E_LABELS, "rank above 12: " + s);
+    std::string all = ops[0] + (ops.size() > 1 ? ops[1] : "");
+    for (char c : out)
+        if (all.find(c) == std::string::npos)
+            return fail(TRA_E_LABELS, std::string("output label '") + c + "' is in no operand");
+    con.clear();
+    for (char c : all)
+        if (out.find(c) == std::string::npos && con.find(c) == std::string::npos) con.push_back(c);
+    canon = out + con;
+    if ((int)canon.size() > kMaxLabels) return fail(TRA_E_LABELS, "more than 24 labels");
+    return TRA_OK;
+}
+
+// Relation-layout strides of a tensor with labels `t`: in-block stride of
+// each label (row-major over block extents) and key stride (row-major over
+// part counts, times the block volume).
+static void relation_strides(const std::string &t, const int64_t *B, const int32_t *d,
+                             int64_t *bs, int64_t *ks)
+{
+    int64_t vol = 1;
+    for (char c : t) vol *= B[(int)c] / d[(int)c];
+    int64_t sb = 1, sk = vol;
+    for (int p = (int)t.size() - 1; p >= 0; --p) {
+        int c = t[p];
+        bs[p] = sb;
+        ks[p] = sk;
+        sb *= B[c] / d[c];
+        sk *= d[c];
+    }
+}
+
+struct SubDim {
+    uint32_t ext;
+    int64_t st[3];
+};
+
+// Sub-dimensions of a label group: keys first (in group order), then the
+// in-block indices; `tens` are up to three tensors whose strides are recorded.
+static std::vector<SubDim> group_subdims(const std::string &group, const int64_t *B, const int32_t *d,
+                                         const std::string *tens[3])
+{
+    std::vector<SubDim> v;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (char c : group) {
+            int64_t ext = pass == 0 ? d[(int)c] : B[(int)c] / d[(int)c];
+            if (ext == 1) continue;
+            SubDim s{(uint32_t)ext, {0, 0, 0}};
+            for (int t = 0; t < 3; ++t) {
+                if (!tens[t]) continue;
+                size_t p = tens[t]->find(c);
+                if (p == std::string::npos) continue;
+                int64_t bs[kMaxRank], ks[kMaxRank];
+                relation_strides(*tens[t], B, d, bs, ks);
+                s.st[t] = pass == 0 ? ks[p] : bs[p];
+            }
+            v.push_back(s);
+        }
+    }
+    return v;
+}
+
+static Radix to_radix(const std::vector<SubDim> &v)
+{
+    Radix r{};
+    r.n = (int32_t)v.size();
+    for (size_t i = 0; i < v.size(); ++i) {
+        r.ext[i] = v[i].ext;
+        for (int t = 0; t < 3; ++t) r.st[t][i] = v[i].st[t];
+    }
+    return r;
+}
+
+static bool to_pow2(const std::vector<SubDim> &v, Pow2Group &g)
+{
+    g = Pow2Group{};
+    g.n = (int32_t)v.size();
+    int sh = 0;
+    uint64_t total = 1;
+    for (int i = (int)v.size() - 1; i >= 0; --i) {
+        if (!is_pow2(v[i].ext)) return false;
+        g.sh[i] = (uint8_t)sh;
+        g.mask[i] = v[i].ext - 1;
+        for (int t = 0; t < 3; ++t) g.st[t][i] = (int32_t)v[i].st[t];
+        sh += ilog2(v[i].ext);
+        total *= v[i].ext;
+    }
+    if (total > 0x7fffffffull) return false;
+    g.total = (uint32_t)total;
+    return true;
+}
+
+static int64_t elems_of(const std::string &t, const int64_t *B)
+{
+    int64_t n = 1;
+    for (char c : t) n *= B[(int)c];
+    return n;
+}
+
+// Last sub-dimension of a group has stride 1 in tensor t and a multiple of vec elements.
+static bool contiguous_last(const std::vector<SubDim> &v, int t, int vec)
+{
+    return !v.empty() && v.back().st[t] == 1 && v.back().ext % vec == 0;
+}
+
+// Largest offset a list of sub-dimension groups can reach in tensor slot t of
+// each group (the kernels never index beyond it).  Checked against the
+// tensor's element count before any launch.
+static int64_t max_offset(std::initializer_list<std::pair<const std::vector<SubDim> *, int>> groups)
+{
+    int64_t m = 0;
+    for (auto &g : groups)
+        for (const SubDim &s : *g.first) m += (int64_t)(s.ext - 1) * s.st[g.second];
+    return m;
+}
+
+static void choose_split(tra_plan_s &p, int64_t tiles, int64_t k_steps, int bk)
+{
+    int split = 1;
+    if (tiles < 128) {
+        while (split * 2 <= k_steps && tiles * split < 256 && k_steps % (split * 2) == 0) split *= 2;
+    }
+    p.gv.split = split;
+    p.gv.k_per_split = (int32_t)(k_steps / split * bk);
+    p.info.agg_split = split;
+    p.info.workspace_bytes = split > 1 ? (size_t)split * (size_t)p.info.z_elems * 4 : 0;
+}
+
+// Try the tile kernels (GEMM view).  Returns true and fills p when eligible.
+static bool lower_tile(tra_plan_s &p)
+{
+    if (p.n_ops != 2) return false;
+    const std::string &X = p.xl, &Y = p.yl, &Z = p.zl;
+    std::string M, N, Bt, K;
+    for (char c : Z) {
+        bool inx = X.find(c) != std::string::npos, iny = Y.find(c) != std::string::npos;
+        if (inx && iny) Bt.push_back(c);
+        else if (inx) M.push_back(c);
+        else N.push_back(c);
+    }
+    for (char c : p.con) {
+        bool inx = X.find(c) != std::string::npos, iny = Y.find(c) != std::string::npos;
+        if (!(inx && iny)) return false;  // contracted label in one operand only
+        K.push_back(c);
+    }
+    if (M.empty() || N.empty() || K.empty()) return false;
+    const std::string *tm[3] = {&X, &Z, nullptr}, *tn[3] = {&Y, &Z, nullptr};
+    const std::string *tk[3] = {&X, &Y, nullptr}, *tb[3] = {&X, &Y, &Z};
+    auto sm = group_subdims(M, p.B, p.d, tm), sn = group_subdims(N, p.B, p.d, tn);
+    auto sk = group_subdims(K, p.B, p.d, tk), sb = group_subdims(Bt, p.B, p.d, tb);
+    GemmView gv{};
+    if (!to_pow2(sm, gv.gm) || !to_pow2(sn, gv.gn) || !to_pow2(sk, gv.gk) || !to_pow2(sb, gv.gb))
+        return false;
+    gv.post_scale = p.post_scale;
+    gv.z_elems = p.info.z_elems;
+    const bool mfma = p.join == J_MUL && p.agg == A_SUM && p.in_dtype == D_BF16;
+    // join / aggregate pairs the vector-ALU tile kernel is built for
+    const bool valu_op = (p.join == J_MUL && p.agg == A_SUM) || (p.join == J_SQDIFF && p.agg == A_SUM) ||
+                         (p.join == J_ADD && (p.agg == A_MAX || p.agg == A_MIN));
+    const bool valu = valu_op && (p.in_dtype == D_F32 || p.in_dtype == D_I32);
+    if (!mfma && !valu) return false;
+    if (max_offset({{&sm, 0}, {&sk, 0}, {&sb, 0}}) >= p.info.x_elems ||
+        max_offset({{&sn, 0}, {&sk, 1}, {&sb, 1}}) >= p.info.y_elems ||
+        max_offset({{&sm, 1}, {&sn, 1}, {&sb, 2}}) >= p.info.z_elems)
+        return false;  // never true for a valid relation layout
+    const int vec = mfma ? 8 : 4;
+    bool ak, bk;
+    if (contiguous_last(sk, 0, vec)) ak = true;
+    else if (!mfma && contiguous_last(sm, 0, vec)) ak = false;  // matrix cores: K-major X only
+    else return false;
+    if (contiguous_last(sk, 1, vec)) bk = true;
+    else if (contiguous_last(sn, 0, vec)) bk = false;
+    else return false;
+    // pick the largest tile variant that divides the problem
+    for (int variant = 0; variant < 4; ++variant) {
+        TileShape ts = mfma ? mfma_tile_shape(variant) : valu_tile_shape(variant);
+        if (ts.bm == 0) break;
+        if (gv.gm.total % ts.bm || gv.gn.total % ts.bn || gv.gk.total % ts.bk) continue;
+        p.gv = gv;
+        p.tile = variant;
+        p.a_kmajor = ak;
+        p.b_kmajor = bk;
+        p.kernel = mfma ? TRA_KERNEL_MFMA_BF16 : TRA_KERNEL_VALU_TILE;
+        int64_t tiles = (int64_t)(gv.gm.total / ts.bm) * (gv.gn.total / ts.bn) * gv.gb.total;
+        choose_split(p, tiles, gv.gk.total / ts.bk, ts.bk);
+        return true;
+    }
+    return false;
+}
+
+static bool lower_generic(tra_plan_s &p)
+{
+    const std::string *tz[3] = {&p.xl, p.n_ops == 2 ? &p.yl : nullptr, nullptr};
+    auto so = group_subdims(p.zl, p.B, p.d, tz);
+    auto sc = group_subdims(p.con, p.B, p.d, tz);
+    if (max_offset({{&so, 0}, {&sc, 0}}) >= p.info.x_elems ||
+        (p.n_ops == 2 && max_offset({{&so, 1}, {&sc, 1}}) >= p.info.y_elems))
+        return false;
+    p.gen.out = to_radix(so);
+    p.gen.con = to_radix(sc);
+    p.gen.n_out = p.info.z_elems;
+    int64_t nc = 1;
+    for (auto &s : sc) nc *= s.ext;
+    p.gen.n_con = nc;
+    p.gen.post_scale = p.post_scale;
+    p.kernel = TRA_KERNEL_GENERIC;
+
+    if (p.agg == A_NONE) {
+        p.el.out = p.gen.out;
+        p.el.n_out = p.gen.n_out;
+        p.el.post_scale = p.post_scale;
+        // vectorise along the fastest output sub-dimension when it is
+        // contiguous (stride 1) or broadcast (stride 0) in both operands
+        int vec = 1;
+        if (!so.empty()) {
+            const SubDim &f = so.back();
+            bool okx = f.st[0] == 1 || f.st[0] == 0;
+            bool oky = p.n_ops == 1 || f.st[1] == 1 || f.st[1] == 0;
+            if (okx && oky && f.ext % 4 == 0) vec = 4;
+        }
+        p.el.vec = vec;
+        p.kernel = TRA_KERNEL_ELEMWISE;
+        return true;
+    }
+    // one wavefront per output row when the last contracted run is contiguous in X
+    if (!sc.empty() && sc.back().st[0] == 1 && sc.back().ext >= 64) {
+        std::vector<SubDim> outer(sc.begin(), sc.end() - 1);
+        p.row.out = p.gen.out;
+        p.row.outer = to_radix(outer);
+        p.row.n_out = p.gen.n_out;
+        int64_t no = 1;
+        for (auto &s : outer) no *= s.ext;
+        p.row.n_outer = no;
+        p.row.inner = sc.back().ext;
+        p.row.inner_sy = sc.back().st[1];
+        p.row.post_scale = p.post_scale;
+        p.kernel = TRA_KERNEL_ROWREDUCE;
+    }
+    return true;
+}
+
+}  // namespace tra
+
+using namespace tra;
+
+extern "C" {
+
+const char *tra_last_error(void) { return g_last_error.c_str(); }
+
+const char *tra_status_string(int s)
+{
+    switch (s) {
+    case TRA_OK: return "ok";
+    case TRA_E_NULL: return "null pointer argument";
+    case TRA_E_SPEC: return "spec does not parse";
+    case TRA_E_LABELS: return "invalid labels";
+    case TRA_E_INDIVISIBLE: return "part count does not divide the extent";
+    case TRA_E_DLEN: return "wrong partition vector / label count";
+    case TRA_E_DTYPE: return "unsupported dtype";
+    case TRA_E_OP: return "invalid join / aggregate";
+    case TRA_E_WORKSPACE: return "workspace too small";
+    case TRA_E_ALIGN: return "device pointer not 16-byte aligned";
+    case TRA_E_HIP: return "HIP runtime error";
+    case TRA_E_NO_CANDIDATE: return "no admissible partition vector";
+    case TRA_E_RANGE: return "tensor too large";
+    case TRA_E_GRAPH: return "malformed graph description";
+    case TRA_E_BUFFER: return "output buffer too small";
+    }
+    return "unknown status";
+}
+
+int tra_canonical_labels(const char *spec, char *out, int out_cap)
+{
+    if (!out) return fail(TRA_E_NULL, "out is NULL");
+    std::vector<std::string> ops;
+    std::string zl, canon, con;
+    int rc = parse_spec(spec, ops, zl, canon, con);
+    if (rc) return rc;
+    if ((int)canon.size() + 1 > out_cap) return fail(TRA_E_BUFFER, "label buffer too small");
+    std::memcpy(out, canon.c_str(), canon.size() + 1);
+    return (int)canon.size();
+}
+
+int tra_d_from_operand_form(const char *spec, const int32_t *d_ops, int n_ops, int32_t *d_out, int d_out_cap)
+{
+    if (!d_ops || !d_out) return fail(TRA_E_NULL, "NULL vector");
+    std::vector<std::string> ops;
+    std::string zl, canon, con;
+    int rc = parse_spec(spec, ops, zl, canon, con);
+    if (rc) return rc;
+    int occ = 0;
+    for (auto &o : ops) occ += (int)o.size();
+    if (n_ops != occ) return fail(TRA_E_DLEN, "per-operand vector needs one entry per label occurrence");
+    if (d_out_cap < (int)canon.size()) return fail(TRA_E_BUFFER, "d_out too small");
+    int32_t seen[128];
+    for (int i = 0; i < 128; ++i) seen[i] = 0;
+    int pos = 0;
+    for (auto &o : ops)
+        for (char c : o) {
+            int32_t v = d_ops[pos++];
+            if (seen[(int)c] && seen[(int)c] != v)
+                return fail(TRA_E_DLEN, std::string("occurrences of label '") + c + "' are split differently");
+            seen[(int)c] = v;
+        }
+    for (size_t i = 0; i < canon.size(); ++i) d_out[i] = seen[(int)canon[i]];
+    return TRA_OK;
+}
+
+static int validate_bounds(const std::string &canon, const int64_t *bounds, const int32_t *d, int n_labels,
+                           int64_t *B, int32_t *D)
+{
+    if (!bounds || !d) return fail(TRA_E_NULL, "bounds / d is NULL");
+    if (n_labels != (int)canon.size())
+        return fail(TRA_E_DLEN, "expected " + std::to_string(canon.size()) + " labels (" + canon + "), got " +
+                                    std::to_string(n_labels));
+    for (int i = 0; i < n_labels; ++i) {
+        int c = canon[i];
+        if (bounds[i] < 1) return fail(TRA_E_INDIVISIBLE, std::string("extent of '") + (char)c + "' < 1");
+        if (d[i] < 1 || bounds[i] % d[i])
+            return fail(TRA_E_INDIVISIBLE, std::string("d of '") + (char)c + "' = " + std::to_string(d[i]) +
+                                               " does not divide " + std::to_string(bounds[i]));
+        B[c] = bounds[i];
+        D[c] = d[i];
+    }
+    return TRA_OK;
+}
+
+int tra_cost(const char *spec, const int64_t *bounds, const int32_t *d, int n_labels, int64_t *cost_out)
+{
+    if (!cost_out) return fail(TRA_E_NULL, "cost_out is NULL");
+    std::vector<std::string> ops;
+    std::string zl, canon, con;
+    int rc = parse_spec(spec, ops, zl, canon, con);
+    if (rc) return rc;
+    int64_t B[128] = {0};
+    int32_t D[128] = {0};
+    rc = validate_bounds(canon, bounds, d, n_labels, B, D);
+    if (rc) return rc;
+    int64_t n = 1, n_agg = 1;
+    for (char c : canon) n *= D[(int)c];
+    for (char c : con) n_agg *= D[(int)c];
+    auto blk = [&](const std::string &t) {
+        int64_t v = 1;
+        for (char c : t) v *= B[(int)c] / D[(int)c];
+        return v;
+    };
+    int64_t in = 0;
+    for (auto &o : ops) in += blk(o);
+    *cost_out = n * in + (n / n_agg) * (n_agg - 1) * blk(zl);
+    return TRA_OK;
+}
+
+int tra_plan(const char *spec, const int64_t *bounds, const int32_t *d, int n_labels, int join_op, int agg_op,
+             int in_dtype, int out_dtype, float post_scale, tra_plan_t *out_plan)
+{
+    if (!out_plan) return fail(TRA_E_NULL, "out_plan is NULL");
+    *out_plan = nullptr;
+    std::vector<std::string> ops;
+    std::string zl, canon, con;
+    int rc = parse_spec(spec, ops, zl, canon, con);
+    if (rc) return rc;
+    tra_plan_s *p = new (std::nothrow) tra_plan_s();
+    if (!p) return fail(TRA_E_RANGE, "out of host memory");
+    rc = validate_bounds(canon, bounds, d, n_labels, p->B, p->d);
+    if (rc) {
+        delete p;
+        return rc;
+    }
+    auto bad = [&](int code, const std::string &m) {
+        delete p;
+        return fail(code, m);
+    };
+    if (in_dtype < D_F32 || in_dtype > D_I32 || out_dtype < D_F32 || out_dtype > D_I32)
+        return bad(TRA_E_DTYPE, "unknown dtype");
+    if (join_op < J_MUL || join_op > J_EXP_SUB) return bad(TRA_E_OP, "unknown join");
+    if (agg_op < A_NONE || agg_op > A_LSE) return bad(TRA_E_OP, "unknown aggregate");
+    if (agg_op == A_NONE && !con.empty()) return bad(TRA_E_OP, "aggregate NONE with contracted labels " + con);
+    if (ops.size() == 1 && join_op != J_IDENT) return bad(TRA_E_OP, "a one-operand spec takes the ident join");
+    if (ops.size() == 2 && join_op == J_IDENT) return bad(TRA_E_OP, "ident takes one operand");
+    const bool is_int = in_dtype == D_I32;
+    if (is_int && (join_op == J_EXP_SUB || agg_op == A_LSE)) return bad(TRA_E_DTYPE, "exp / lse on integers");
+    if (is_int != (out_dtype == D_I32)) return bad(TRA_E_DTYPE, "integer inputs give integer outputs only");
+    if (is_int && post_scale != 1.0f) return bad(TRA_E_OP, "post_scale applies to floats only");
+
+    p->spec = spec;
+    p->n_ops = (int)ops.size();
+    p->xl = ops[0];
+    p->yl = ops.size() > 1 ? ops[1] : "";
+    p->zl = zl;
+    p->canon = canon;
+    p->con = con;
+    p->join = join_op;
+    p->agg = agg_op;
+    p->in_dtype = in_dtype;
+    p->out_dtype = out_dtype;
+    p->post_scale = post_scale;
+
+    tra_plan_info_t &in = p->info;
+    in.n_tasks = 1;
+    in.n_agg = 1;
+    for (char c : canon) in.n_tasks *= p->d[(int)c];
+    for (char c : con) in.n_agg *= p->d[(int)c];
+    in.n_groups = in.n_tasks / in.n_agg;
+    in.agg_split = 1;
+    in.x_elems = elems_of(p->xl, p->B);
+    in.y_elems = p->n_ops == 2 ? elems_of(p->yl, p->B) : 0;
+    in.z_elems = elems_of(zl, p->B);
+    for (int64_t e : {in.x_elems, in.y_elems, in.z_elems})
+        if (e >= (int64_t)1 << 31) return bad(TRA_E_RANGE, "a tensor has 2^31 or more elements");
+    in.x_bytes = (size_t)in.x_elems * dtype_size(in_dtype);
+    in.y_bytes = (size_t)in.y_elems * dtype_size(in_dtype);
+    in.z_bytes = (size_t)in.z_elems * dtype_size(out_dtype);
+    in.workspace_bytes = 0;
+    in.n_labels = (int32_t)canon.size();
+    std::memset(in.labels, 0, sizeof(in.labels));
+    std::memcpy(in.labels, canon.c_str(), canon.size());
+
+    if (!lower_tile(*p) && !lower_generic(*p)) return bad(TRA_E_RANGE, "internal: descriptor exceeds a tensor");
+    in.kernel = p->kernel;
+    *out_plan = p;
+    return TRA_OK;
+}
+
+int tra_plan_info(tra_plan_t plan, tra_plan_info_t *info)
+{
+    if (!plan || !info) return fail(TRA_E_NULL, "plan / info is NULL");
+    *info = plan->info;
+    return TRA_OK;
+}
+
+int tra_plan_destroy(tra_plan_t plan)
+{
+    delete plan;
+    return TRA_OK;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int tra_execute(tra_plan_t p, const void *x, const void *y, void *z, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!p) return fail(TRA_E_NULL, "plan is NULL");
+    if (!x || !z || (p->n_ops == 2 && !y)) return fail(TRA_E_NULL, "operand / output pointer is NULL");
+    if (!aligned16(x) || !aligned16(z) || (y && !aligned16(y)) || (ws && !aligned16(ws)))
+        return fail(TRA_E_ALIGN, "device pointers must be 16-byte aligned");
+    if (p->info.workspace_bytes > 0 && (!ws || ws_bytes < p->info.workspace_bytes))
+        return fail(TRA_E_WORKSPACE, "workspace of " + std::to_string(p->info.workspace_bytes) + " bytes needed");
+    int err = 0;
+    switch (p->kernel) {
+    case TRA_KERNEL_MFMA_BF16: err = launch_mfma_bf16(*p, x, y, z, ws, stream); break;
+    case TRA_KERNEL_VALU_TILE: err = launch_valu_tile(*p, x, y, z, ws, stream); break;
+    case TRA_KERNEL_ROWREDUCE: err = launch_rowreduce(*p, x, y, z, stream); break;
+    case TRA_KERNEL_ELEMWISE: err = launch_elemwise(*p, x, y, z, stream); break;
+    default: err = launch_generic(*p, x, y, z, stream); break;
+    }
+    if (err) return fail(TRA_E_HIP, std::string("kernel launch failed: ") + hip_error_text(err));
+    return TRA_OK;
+}
+
+int tra_repartition(const int64_t *bounds, int rank, const int32_t *d_from, const int32_t *d_to, int dtype,
+                    const void *src, void *dst, void *stream)
+{
+    if (!bounds || !d_from || !d_to || !src || !dst) return fail(TRA_E_NULL, "NULL argument");
+    if (rank < 1 || rank > kMaxRank) return fail(TRA_E_DLEN, "rank must be 1..12");
+    if (dtype < D_F32 || dtype > D_I32) return fail(TRA_E_DTYPE, "unknown dtype");
+    if (!aligned16(src) || !aligned16(dst)) return fail(TRA_E_ALIGN, "device pointers must be 16-byte aligned");
+    // label i of the tensor is the letter 'a' + i
+    int64_t B[128] = {0};
+    int32_t Du[128] = {0}, Dv[128] = {0};
+    std::string t;
+    int64_t n = 1;
+    for (int i = 0; i < rank; ++i) {
+        int c = 'a' + i;
+        t.push_back((char)c);
+        if (bounds[i] < 1) return fail(TRA_E_INDIVISIBLE, "extent < 1");
+        if (d_from[i] < 1 || d_to[i] < 1 || bounds[i] % d_from[i] || bounds[i] % d_to[i])
+            return fail(TRA_E_INDIVISIBLE, "part count does not divide extent of dim " + std::to_string(i));
+        B[c] = bounds[i];
+        Du[c] = d_from[i];
+        Dv[c] = d_to[i];
+        n *= bounds[i];
+    }
+    if (n >= (int64_t)1 << 31) return fail(TRA_E_RANGE, "tensor has 2^31 or more elements");
+    // The destination enumerates its own layout: key digits of every label,
+    // then in-block digits.  For each label the destination digits are
+    // refined so that every refined digit maps to the source affinely:
+    //  * b_u % b_v == 0 (destination block inside a source block, per = b_u/b_v):
+    //      k_v = q*per + p  ->  k_u = q, r_u = p*b_v + r_v
+    //  * b_v % b_u == 0 (source block inside a destination block, per = b_v/b_u):
+    //      r_v = p*b_u + s  ->  k_u = k_v*per + p, r_u = s
+    // The refined digits sit where the original digit sat, so the destination
+    // order is unchanged.  Part counts where neither block extent divides the
+    // other are rejected.
+    int64_t bsu[kMaxRank], ksu[kMaxRank];
+    relation_strides(t, B, Du, bsu, ksu);
+    std::vector<SubDim> keys, inner;
+    for (int i = 0; i < rank; ++i) {
+        int c = t[i];
+        int64_t bu = B[c] / Du[c], bv = B[c] / Dv[c];
+        if (bu % bv == 0) {
+            int64_t per = bu / bv;
+            if (Du[c] > 1) keys.push_back({(uint32_t)Du[c], {ksu[i], 0, 0}});
+            if (per > 1) keys.push_back({(uint32_t)per, {bv * bsu[i], 0, 0}});
+            if (bv > 1) inner.push_back({(uint32_t)bv, {bsu[i], 0, 0}});
+        } else if (bv % bu == 0) {
+            int64_t per = bv / bu;
+            if (Dv[c] > 1) keys.push_back({(uint32_t)Dv[c], {per * ksu[i], 0, 0}});
+            if (per > 1) inner.push_back({(uint32_t)per, {ksu[i], 0, 0}});
+            if (bu > 1) inner.push_back({(uint32_t)bu, {bsu[i], 0, 0}});
+        } else {
+            return fail(TRA_E_INDIVISIBLE, "in every dimension one block extent must divide the other");
+        }
+    }
+    std::vector<SubDim> subs(keys);
+    subs.insert(subs.end(), inner.begin(), inner.end());
+    // merge neighbours that are one affine run in the source
+    std::vector<SubDim> merged;
+    for (const SubDim &sd : subs) {
+        if (!merged.empty() && merged.back().st[0] == (int64_t)sd.ext * sd.st[0] &&
+            (uint64_t)merged.back().ext * sd.ext < (1ull << 31)) {
+            merged.back().ext *= sd.ext;
+            merged.back().st[0] = sd.st[0];
+        } else {
+            merged.push_back(sd);
+        }
+    }
+    if (max_offset({{&merged, 0}}) >= n) return fail(TRA_E_RANGE, "internal: descriptor exceeds the tensor");
+    RepartDesc r{};
+    r.dst = to_radix(merged);
+    r.n_elems = n;
+    int esz = dtype_size(dtype);
+    // `vec` consecutive destination elements are one aligned source vector when
+    // the fastest digit has source stride 1 and every stride keeps alignment
+    int vec = 16 / esz;
+    auto ok = [&](int v) {
+        if (merged.empty()) return n % v == 0;
+        if (merged.back().st[0] != 1 || merged.back().ext % v) return false;
+        for (const SubDim &sd : merged)
+            if (&sd != &merged.back() && sd.st[0] % v) return false;
+        return true;
+    };
+    while (vec > 1 && !ok(vec)) vec /= 2;
+    r.vec = vec;
+    int err = launch_repartition(r, esz, src, dst, stream);
+    if (err) return fail(TRA_E_HIP, std::string("kernel launch failed: ") + hip_error_text(err));
+    return TRA_OK;
+}
+
+}  // extern "C"

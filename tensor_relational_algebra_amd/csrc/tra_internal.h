@@ -1,0 +1,96 @@
+// tra_internal.h -- descriptors passed from the host planner to the kernels.
+//
+// A relation (page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法",
+// section 2.2) is addressed through "sub-dimensions": every label l with part
+// count d_l and block extent b_l contributes a key sub-dimension (extent d_l)
+// and an in-block sub-dimension (extent b_l); the element offset in a tensor
+// is the sum over its sub-dimensions of index * stride.  Sub-dimensions of
+// extent 1 are dropped.  A flattened index over a list of sub-dimensions is
+// mixed-radix with the last sub-dimension fastest.
+#pragma once
+#include <stdint.h>
+
+namespace tra {
+
+constexpr int kMaxLabels = 24;
+constexpr int kMaxRank = 12;
+constexpr int kMaxSub = 2 * kMaxRank;   // sub-dimensions of one index group
+
+// Mixed-radix index space with runtime extents; strides into up to three
+// tensors (0 = the tensor does not carry that sub-dimension).
+struct Radix {
+    int32_t n;
+    uint32_t ext[kMaxSub];
+    int64_t st[3][kMaxSub];
+};
+
+// Power-of-two index group: offset_t(idx) = sum_i ((idx >> sh_i) & mask_i) * st[t][i].
+struct Pow2Group {
+    int32_t n;
+    uint32_t total;
+    uint8_t sh[kMaxSub];
+    uint32_t mask[kMaxSub];
+    int32_t st[3][kMaxSub];
+};
+
+// Join / aggregate codes (mirror tra.h).
+enum Join : int32_t { J_MUL = 0, J_SQDIFF = 1, J_ADD = 2, J_IDENT = 3, J_EXP_SUB = 4 };
+enum Agg : int32_t { A_NONE = 0, A_SUM = 1, A_MAX = 2, A_MIN = 3, A_LSE = 4 };
+enum DType : int32_t { D_F32 = 0, D_BF16 = 1, D_I32 = 2 };
+
+// One-thread-per-output kernel: output positions enumerated in the output
+// relation's own layout (so thread o writes z[o]); `out` gives X/Y strides of
+// the output sub-dimensions (st[0] = X, st[1] = Y); `con` enumerates the
+// contracted sub-dimensions, keys first (ascending key order), then in-block.
+struct GenericDesc {
+    Radix out;
+    Radix con;
+    int64_t n_out;
+    int64_t n_con;
+    float post_scale;
+};
+
+// GEMM view of a two-operand EinSum: output labels only in X form M, only in
+// Y form N, in both form B (batch); contracted labels (in both) form K.
+// Group strides: gm {X, Z}, gn {Y, Z}, gk {X, Y}, gb {X, Y, Z}.
+struct GemmView {
+    Pow2Group gm, gn, gk, gb;
+    int32_t split;          // workgroups sharing one output tile along K
+    int32_t k_per_split;    // K extent each of them folds
+    int64_t z_elems;        // for the split workspace stride
+    float post_scale;
+};
+
+// Row reduction: one wavefront per output element; `out` as in GenericDesc;
+// `outer` = contracted sub-dims except the last, `inner` = extent and X/Y
+// strides of the last contracted sub-dim (X stride 1).
+struct RowDesc {
+    Radix out;
+    Radix outer;
+    int64_t n_out;
+    int64_t n_outer;
+    int64_t inner;
+    int64_t inner_sy;
+    float post_scale;
+};
+
+// Elementwise (aggregate NONE): `out` as in GenericDesc; vec elements of the
+// fastest output sub-dimension are handled together when its X/Y strides
+// allow (vx / vy: 1 = contiguous, 0 = broadcast, else scalar path).
+struct ElemDesc {
+    Radix out;
+    int64_t n_out;
+    int32_t vec;
+    float post_scale;
+};
+
+// Repartition: destination positions enumerated in the destination layout;
+// `dst` has, per destination sub-dimension, the source stride (st[0]).
+// Runs of `vec` consecutive elements are contiguous in both layouts.
+struct RepartDesc {
+    Radix dst;
+    int64_t n_elems;
+    int32_t vec;
+};
+
+}  // namespace tra

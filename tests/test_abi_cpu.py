@@ -1,0 +1,202 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every entry point
+include/tra.h declares, plans without a GPU, rejects every invalid argument
+with its documented status, and its chooser agrees with the oracle's cost
+model and dynamic programme.  No compute kernel is launched here.
+"""
+import json
+import os
+import re
+
+import pytest
+
+import tensor_relational_algebra_amd as tra
+from oracle import chooser
+from tensor_relational_algebra_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_binding.LIB_PATH), reason="libtra not built")
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "tra.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(tra_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert "tra_plan" in names and "tra_execute" in names and "tra_repartition" in names
+    L = tra.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in tra.h but not exported"
+
+
+def test_canonical_labels_and_operand_form():
+    assert tra.tra_canonical_labels("ij,jk->ik") == "ikj"
+    assert tra.tra_canonical_labels("abef,cfed->abcd") == "abcdef"
+    assert tra.tra_canonical_labels("shd,ahd->sa") == "sahd"
+    assert tra.tra_canonical_labels("hst->hs") == "hst"
+    # the page's per-operand matmul vector [d_i, d_j(X), d_j(Y), d_k]
+    assert tra.tra_d_from_operand_form("ij,jk->ik", [4, 1, 1, 4]) == [4, 4, 1]
+    assert tra.tra_d_from_operand_form("ij,jk->ik", [1, 4, 4, 1]) == [1, 1, 4]
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_d_from_operand_form("ij,jk->ik", [1, 2, 4, 1])
+    assert e.value.code == -5
+
+
+def test_plan_task_structure_matches_the_worked_examples():
+    g = json.load(open(os.path.join(GOLDEN, "matmul_partition_examples.json")))
+    for c in g["cases"]:
+        d = tra.tra_d_from_operand_form("ij,jk->ik", c["d4"])
+        p = tra.tra_plan("ij,jk->ik", [256, 256, 256], d, "mul", "sum", "i32", "i32")
+        assert (p.info.n_tasks, p.info.n_groups, p.info.n_agg) == (c["N"], c["G"], c["n_agg"])
+        assert p.info.z_elems == 65536
+
+
+def test_kernel_family_choice():
+    p = tra.tra_plan("ij,jk->ik", {"i": 16384, "j": 8192, "k": 8192}, {"i": 16, "j": 4, "k": 4},
+                     "mul", "sum", "bf16", "f32")
+    assert p.kernel == "mfma_bf16" and p.info.workspace_bytes == 0
+    p = tra.tra_plan("abef,cfed->abcd", dict(a=64, b=64, c=64, d=64, e=32, f=32),
+                     dict(a=2, b=2, c=2, d=2, e=4, f=4), "mul", "sum", "bf16", "f32")
+    assert p.kernel == "mfma_bf16" and p.info.n_tasks == 256 and p.info.n_agg == 16
+    p = tra.tra_plan("ij,jk->ik", {"i": 8192, "j": 256, "k": 8192}, {"i": 16, "j": 1, "k": 16},
+                     "sqdiff", "sum", "f32", "f32")
+    assert p.kernel == "valu_tile"
+    p = tra.tra_plan("ij,jk->ik", {"i": 8192, "j": 256, "k": 8192}, {"i": 16, "j": 1, "k": 16},
+                     "add", "max", "i32", "i32")
+    assert p.kernel == "valu_tile"
+    p = tra.tra_plan("hst->hs", {"h": 32, "s": 4096, "t": 4096}, {"h": 32, "s": 8, "t": 1},
+                     "ident", "lse", "f32", "f32")
+    assert p.kernel == "rowreduce"
+    p = tra.tra_plan("hst,hs->hst", {"h": 32, "s": 4096, "t": 4096}, {"h": 32, "s": 8, "t": 1},
+                     "exp_sub", "none", "f32", "bf16")
+    assert p.kernel == "elemwise"
+    # small partitioned matmul: one output tile per group, so the contracted
+    # range is split over workgroups with a workspace
+    p = tra.tra_plan("ij,jk->ik", [256, 256, 256], [1, 1, 4], "mul", "sum", "f32", "f32")
+    assert p.kernel == "valu_tile" and p.info.agg_split > 1
+    assert p.info.workspace_bytes == p.info.agg_split * 65536 * 4
+
+
+@pytest.mark.parametrize("args,code", [
+    (("ij,jk-ik", [2, 2, 2], [1, 1, 1]), -2),                      # no arrow
+    (("ij,jk,kl->il", [2, 2, 2, 2], [1, 1, 1, 1]), -2),            # three operands
+    (("i1,jk->ik", [2, 2, 2], [1, 1, 1]), -2),                     # non-letter label
+    (("ii,jk->ik", [2, 2, 2], [1, 1, 1]), -3),                     # repeated label
+    (("ij,jk->iq", [2, 2, 2], [1, 1, 1]), -3),                     # output label in no operand
+    (("ij,jk->ik", [2, 2], [1, 1]), -5),                           # wrong label count
+    (("ij,jk->ik", [4, 4, 4], [3, 1, 1]), -4),                     # d does not divide
+    (("ij,jk->ik", [4, 4, 4], [0, 1, 1]), -4),                     # d < 1
+    (("ij,jk->ik", [4, 0, 4], [1, 1, 1]), -4),                     # extent < 1
+])
+def test_plan_validation_errors(args, code):
+    spec, b, d = args
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_plan(spec, b, d)
+    assert e.value.code == code
+    assert tra.lib().tra_last_error().decode()
+
+
+def test_plan_op_and_dtype_errors():
+    b, d = [8, 8, 8], [1, 1, 1]
+    cases = [
+        (dict(join="mul", agg="none"), -7),                          # contracted labels, no aggregate
+        (dict(join="ident", agg="sum"), -7),                         # ident with two operands
+        (dict(join="exp_sub", agg="sum", in_dtype="i32", out_dtype="i32"), -6),
+        (dict(join="mul", agg="lse", in_dtype="i32", out_dtype="i32"), -6),
+        (dict(join="mul", agg="sum", in_dtype="i32", out_dtype="f32"), -6),
+        (dict(join="mul", agg="sum", in_dtype="i32", out_dtype="i32", post_scale=2.0), -7),
+    ]
+    for kw, code in cases:
+        with pytest.raises(tra.TraError) as e:
+            tra.tra_plan("ij,jk->ik", b, d, **kw)
+        assert e.value.code == code, kw
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_plan("ij->i", [4, 4], [1, 1], "mul", "sum")        # binary join, one operand
+    assert e.value.code == -7
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_plan("ij,jk->ik", [65536, 65536, 2], [1, 1, 1])    # 2^32 elements
+    assert e.value.code == -12
+
+
+def test_execute_and_repartition_host_errors():
+    import ctypes
+    L = tra.lib()
+    p = tra.tra_plan("ij,jk->ik", [256, 256, 256], [1, 1, 4], "mul", "sum", "f32", "f32")
+    assert L.tra_execute(None, 16, 16, 16, None, 0, None) == -1
+    assert L.tra_execute(p.handle, None, 16, 16, None, 0, None) == -1
+    assert L.tra_execute(p.handle, 17, 16, 16, None, 0, None) == -9           # misaligned
+    assert L.tra_execute(p.handle, 16, 16, 16, None, 0, None) == -8           # workspace missing
+    assert L.tra_execute(p.handle, 16, 16, 16, 16, 8, None) == -8             # workspace too small
+    I64, I32 = ctypes.c_int64, ctypes.c_int32
+    b = (I64 * 2)(8, 8)
+    d1 = (I32 * 2)(1, 1)
+    d3 = (I32 * 2)(3, 1)
+    assert L.tra_repartition(b, 2, d1, d3, 0, 16, 32, None) == -4            # 3 does not divide 8
+    assert L.tra_repartition(b, 0, d1, d1, 0, 16, 32, None) == -5            # rank 0
+    assert L.tra_repartition(b, 2, d1, d1, 7, 16, 32, None) == -6            # bad dtype
+    assert L.tra_repartition(b, 2, d1, d1, 0, 18, 32, None) == -9            # misaligned
+    assert L.tra_repartition(b, 2, None, d1, 0, 16, 32, None) == -1
+    b6 = (I64 * 1)(6)
+    d2 = (I32 * 1)(2)
+    d3b = (I32 * 1)(3)
+    assert L.tra_repartition(b6, 1, d2, d3b, 0, 16, 32, None) == -4          # blocks 3 and 2 do not nest
+
+
+def test_cost_matches_hand_worked_values():
+    g = json.load(open(os.path.join(GOLDEN, "chooser_costs.json")))
+    for c in g["cases"]:
+        assert tra.tra_cost(c["spec"], c["bounds"], c["d"]) == c["cost"], c["_work"]
+
+
+def _desc(nodes):
+    lines = []
+    for n in nodes:
+        b = ",".join(f"{k}={v}" for k, v in n.bounds.items())
+        lines.append(f"{n.name} {n.kind} {n.spec} {b} {','.join(n.inputs)}")
+    return "\n".join(lines)
+
+
+def _check_against_oracle(nodes, p):
+    want_cost, want = chooser.dp(nodes, p)
+    got, cost = tra.tra_choose(_desc(nodes), p)
+    assert cost == want_cost
+    for n, dv in zip(nodes, got):
+        assert dv == [want[n.name][c] for c in n.labels()], n.name
+    asg = {n.name: dict(zip(n.labels(), dv)) for n, dv in zip(nodes, got)}
+    assert chooser.graph_cost(nodes, asg) == cost
+
+
+def test_choose_equals_oracle_dp_small_graphs():
+    b = {"i": 8, "j": 8, "k": 8, "l": 8}
+    chain = [chooser.Node("A", "ij,jk->ik", b, ["@X", "@Y"]), chooser.Node("B", "ik,kl->il", b, ["A", "@W"])]
+    for p in (4, 16):
+        _check_against_oracle(chain, p)
+    _check_against_oracle(chooser.mha_graph(s=32, a=32, h=4, dh=8), 16)
+
+
+def test_choose_full_attention_graph():
+    nodes = chooser.mha_graph(s=4096, a=4096, h=32, dh=128)
+    got, cost = tra.tra_choose(_desc(nodes), 256)
+    asg = {n.name: dict(zip(n.labels(), dv)) for n, dv in zip(nodes, got)}
+    assert chooser.graph_cost(nodes, asg) == cost
+    for n in nodes:
+        t = chooser.n_tasks(n, asg[n.name])
+        assert t >= 256 and t % 256 == 0
+        for c, v in asg[n.name].items():
+            assert v & (v - 1) == 0 and n.bounds[c] % v == 0
+
+
+def test_choose_errors():
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_choose("A einsum ij,jk->ik i=2,j=2,k=2 @X,@Y", 64)
+    assert e.value.code == -11
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_choose("A einsum ij,jk->ik i=2,j=2 @X,@Y", 1)
+    assert e.value.code == -13
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_choose("A einsum ij,jk->ik i=2,j=2,k=2 @X,B", 1)
+    assert e.value.code == -13

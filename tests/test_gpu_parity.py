@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case draws its inputs from the seeded generators, runs dense ->
+relation -> join + aggregation -> dense on the GPU, and compares with the
+oracle: integers and max-plus bit-exact, fp32 to 1e-4 and bf16-in / fp32-acc
+to 2e-2 (max-norm relative error).  Reduced sizes are compared element by
+element (they span several tiles and partitions); the full workload sizes,
+in the launch configuration the bench uses, are compared on sampled outputs.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import tensor_relational_algebra_amd as tra
+from oracle import ref, tra_cpu
+from tensor_relational_algebra_amd import workloads as wl
+from tests.gpu_util import DEV, check, maxnorm_rel_err, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------ repartition
+
+REPART_CASES = [
+    ((16,), (1,), (4,)),
+    ((8, 12), (2, 3), (4, 1)),
+    ((64, 32), (1, 1), (4, 8)),
+    ((64, 32), (4, 8), (16, 2)),
+    ((6, 8, 10), (3, 2, 5), (1, 4, 1)),
+    ((32, 16, 8, 4), (2, 4, 2, 1), (8, 1, 4, 2)),
+    ((256, 96), (16, 3), (2, 12)),
+]
+
+
+@pytest.mark.parametrize("shape,du,dv", REPART_CASES)
+@pytest.mark.parametrize("dtype", [torch.int32, torch.float32, torch.bfloat16])
+def test_repartition_matches_the_partition_rule(shape, du, dv, dtype):
+    n = int(np.prod(shape))
+    dense = torch.arange(n, dtype=torch.int64).reshape(shape)
+    t = dense.to(dtype) if dtype != torch.bfloat16 else (dense % 256).to(dtype)
+    src = torch.from_numpy(tra_cpu.to_buffer(t.view(torch.int16).numpy() if dtype == torch.bfloat16 else t.numpy(), du))
+    if dtype == torch.bfloat16:
+        src = src.view(torch.bfloat16)
+    want = tra_cpu.to_buffer(t.view(torch.int16).numpy() if dtype == torch.bfloat16 else t.numpy(), dv)
+    got = tra.tra_repartition(src.to(DEV), list(shape), list(du), list(dv)).cpu()
+    got = got.view(torch.int16).numpy() if dtype == torch.bfloat16 else got.numpy()
+    np.testing.assert_array_equal(got, want)
+    # round trip and dense <-> relation
+    back = tra.tra_repartition(tra.tra_repartition(src.to(DEV), list(shape), list(du), list(dv)),
+                               list(shape), list(dv), list(du))
+    assert torch.equal(back.cpu(), src)
+    dn = tra.from_relation(src.to(DEV), list(shape), list(du)).cpu()
+    assert torch.equal(dn, t)
+
+
+def test_repartition_gemm_output_full_size():
+    """The blocked GEMM's output Y [16384, 8192] re-cut from [16, 4] to [4, 16]."""
+    shape = (16384, 8192)
+    n = shape[0] * shape[1]
+    iota = torch.arange(n, dtype=torch.int32, device=DEV)
+    rel = tra.tra_repartition(iota, list(shape), [1, 1], list(wl.GEMM25D_Y_FROM))
+    out = tra.tra_repartition(rel, list(shape), list(wl.GEMM25D_Y_FROM), list(wl.GEMM25D_Y_TO))
+    rng = np.random.default_rng(5)
+    gi = rng.integers(0, shape[0], 20000)
+    gj = rng.integers(0, shape[1], 20000)
+    pos_from = [tra_cpu.buffer_offset((a, b), shape, wl.GEMM25D_Y_FROM) for a, b in zip(gi, gj)]
+    pos_to = [tra_cpu.buffer_offset((a, b), shape, wl.GEMM25D_Y_TO) for a, b in zip(gi, gj)]
+    want = torch.from_numpy((gi * shape[1] + gj).astype(np.int32))
+    assert torch.equal(rel[torch.tensor(pos_from, device=DEV)].cpu(), want)
+    assert torch.equal(out[torch.tensor(pos_to, device=DEV)].cpu(), want)
+    back = tra.tra_repartition(out, list(shape), list(wl.GEMM25D_Y_TO), [1, 1])
+    assert torch.equal(back, iota)
+
+
+# ------------------------------------------------------------ partitioned matmul
+
+@pytest.mark.parametrize("d4", [[4, 1, 1, 4], [1, 4, 4, 1], [2, 2, 2, 2], [1, 1, 1, 1]])
+@pytest.mark.parametrize("base", [wl.MATMUL_F32, wl.MATMUL_I32], ids=["f32", "i32"])
+def test_partitioned_matmul_256(base, d4):
+    check(base.with_d(wl.matmul_d(d4)))
+
+
+# ------------------------------------------------------------ squared distance / max-plus
+
+SMALL_NL = {"i": 512, "j": 96, "k": 384}
+
+
+@pytest.mark.parametrize("d", [{"i": 1, "j": 1, "k": 1}, {"i": 2, "j": 1, "k": 3}, {"i": 4, "j": 3, "k": 2},
+                               {"i": 4, "j": 1, "k": 2}, {"i": 2, "j": 2, "k": 2}])
+@pytest.mark.parametrize("base", [wl.SQDIST, wl.MAXPLUS], ids=["sqdist", "maxplus"])
+def test_nonlinear_joins_small(base, d):
+    check(base.scaled(SMALL_NL, d))
+
+
+@pytest.mark.parametrize("d", [wl.matmul_d([16, 1, 1, 16]), wl.matmul_d([8, 1, 1, 32]), wl.matmul_d([16, 2, 2, 16])])
+@pytest.mark.parametrize("base", [wl.SQDIST, wl.MAXPLUS], ids=["sqdist", "maxplus"])
+def test_nonlinear_joins_full_size_sampled(base, d):
+    err, plan = check(base.with_d(d), sample=4096)
+    assert plan.kernel == "valu_tile"
+
+
+def test_min_plus_variant():
+    b = {"i": 256, "j": 64, "k": 256}
+    check(wl.EinsumCase("minplus", 77, "ij,jk->ik", b, {"i": 2, "j": 2, "k": 1}, "add", "min", "i32", "i32",
+                        (("int", {"lo": -50, "hi": 50}), ("int", {"lo": -50, "hi": 50}))))
+
+
+# ------------------------------------------------------------ four-index contraction
+
+C3_SMALL = {"a": 16, "b": 8, "c": 16, "d": 32, "e": 16, "f": 8}
+
+
+@pytest.mark.parametrize("d", [dict(a=1, b=1, c=1, d=1, e=1, f=1), dict(a=2, b=2, c=2, d=2, e=4, f=4),
+                               dict(a=4, b=1, c=2, d=1, e=2, f=1), dict(a=1, b=2, c=4, d=4, e=1, f=2)])
+def test_contract4_small(d):
+    check(wl.CONTRACT4.scaled(C3_SMALL, d))
+
+
+@pytest.mark.parametrize("d", [wl.CONTRACT4.d, dict(a=1, b=1, c=1, d=1, e=1, f=1),
+                               dict(a=4, b=4, c=4, d=4, e=1, f=1)])
+def test_contract4_full_size_sampled(d):
+    err, plan = check(wl.CONTRACT4.with_d(d), sample=4096, seed=3)
+    if d == wl.CONTRACT4.d:
+        assert plan.kernel == "mfma_bf16"
+
+
+# ------------------------------------------------------------ blocked GEMM
+
+@pytest.mark.parametrize("d", [{"i": 16, "j": 4, "k": 4}, {"i": 4, "j": 2, "k": 2}, {"i": 1, "j": 1, "k": 1}])
+def test_gemm25d_small(d):
+    check(wl.GEMM25D.scaled({"i": 2048, "j": 1024, "k": 512}, d))
+
+
+def test_gemm25d_full_size_sampled():
+    err, plan = check(wl.GEMM25D, sample=2048, seed=4)
+    assert plan.kernel == "mfma_bf16"
+
+
+def test_gemm_bf16_output_and_post_scale():
+    c = wl.EinsumCase("gemm_bf16out", 78, "ij,jk->ik", {"i": 512, "j": 256, "k": 256}, {"i": 2, "j": 2, "k": 2},
+                      "mul", "sum", "bf16", "bf16", (("normal", {"std": 1.0}), ("normal", {"std": 1.0})),
+                      post_scale=0.125)
+    check(c)
+
+
+# ------------------------------------------------------------ softmax as two EinSums
+
+@pytest.mark.parametrize("d", [dict(h=1, s=1, t=1), dict(h=2, s=4, t=1), dict(h=2, s=2, t=4)])
+def test_logsumexp_and_normalise(d):
+    b = {"h": 4, "s": 64, "t": 512}
+    s_case = wl.EinsumCase("lse", 79, "hst->hs", b, d, "ident", "lse", "f32", "f32",
+                           (("normal", {"std": 3.0}),))
+    (scores,) = s_case.make_inputs()
+    lse_gpu, plan = run_gpu(s_case, [scores])
+    want_lse = ref.einsum("hst->hs", scores, None, "ident", "lse")
+    assert maxnorm_rel_err(lse_gpu.double().numpy(), want_lse) <= 1e-4
+    n_case = wl.EinsumCase("norm", 80, "hst,hs->hst", b, d, "exp_sub", "none", "f32", "f32", ((), ()))
+    attn, plan2 = run_gpu(n_case, [scores, torch.from_numpy(want_lse.astype(np.float32))])
+    want = ref.einsum("hst,hs->hst", scores, want_lse.astype(np.float32), "exp_sub", "none")
+    assert maxnorm_rel_err(attn.double().numpy(), want) <= 1e-4
+    assert plan2.kernel == "elemwise"
+    np.testing.assert_allclose(attn.double().sum(-1).numpy(), 1.0, atol=1e-4)
+
+
+# ------------------------------------------------------------ generic path, property style
+
+GENERIC_SPECS = [
+    ("ij,jk->ik", {"i": 5, "j": 7, "k": 3}),
+    ("bij,bjk->bik", {"b": 3, "i": 4, "j": 6, "k": 5}),
+    ("ijk,jl->il", {"i": 6, "j": 4, "k": 3, "l": 5}),
+    ("ij,k->ijk", {"i": 4, "j": 3, "k": 6}),
+    ("ij,ji->", {"i": 6, "j": 8}),
+    ("hst->hs", {"h": 3, "s": 4, "t": 10}),
+    ("ij,jk->ki", {"i": 6, "j": 9, "k": 4}),
+    ("abef,cfed->abcd", {"a": 2, "b": 3, "c": 2, "d": 3, "e": 4, "f": 2}),
+]
+
+
+def _divisors(n):
+    return [k for k in range(1, n + 1) if n % k == 0]
+
+
+@pytest.mark.parametrize("spec,bounds", GENERIC_SPECS)
+def test_every_join_aggregate_dtype_on_small_shapes(spec, bounds):
+    ops, out, con = ref.parse(spec)
+    rng = np.random.default_rng(21)
+    labels = tra.tra_canonical_labels(spec)
+    for idt in ("i32", "f32", "bf16"):
+        joins = ["ident"] if len(ops) == 1 else (["mul", "sqdiff", "add"] if idt == "i32"
+                                                  else ["mul", "sqdiff", "add", "exp_sub"])
+        aggs = (["none"] if not con else []) + ["sum", "max", "min"] + ([] if idt == "i32" else ["lse"])
+        for join, agg in itertools.product(joins, aggs):
+            dmap = {c: int(rng.choice(_divisors(bounds[c]))) for c in labels}
+            dist = ("int", {"lo": -9, "hi": 9}) if idt == "i32" else ("uniform", {"lo": -1.0, "hi": 1.0})
+            odt = "i32" if idt == "i32" else "f32"
+            case = wl.EinsumCase(f"prop_{spec}_{join}_{agg}", 300, spec, bounds, dmap, join, agg, idt, odt,
+                                 tuple([dist] * len(ops)))
+            check(case)
+
+
+# ------------------------------------------------------------ determinism
+
+@pytest.mark.parametrize("case", [wl.CONTRACT4, wl.SQDIST.scaled({"i": 1024, "j": 256, "k": 1024}),
+                                  wl.MATMUL_F32.with_d(wl.matmul_d([1, 4, 4, 1]))], ids=["mfma", "valu", "split"])
+def test_bitwise_reproducible(case):
+    a, _ = run_gpu(case)
+    b, _ = run_gpu(case)
+    assert torch.equal(a, b)

@@ -59,6 +59,14 @@ def test_layout_closed_form_and_round_trips():
         tra_cpu.to_buffer(t, (4, 2, 4))
 
 
+def test_buffer_offset_agrees_with_the_partitioned_buffer():
+    for shape, d in [((6, 4, 8), (3, 2, 4)), ((4, 6), (2, 3)), ((16,), (4,)), ((2, 3, 4, 5), (1, 3, 2, 5))]:
+        t = np.arange(int(np.prod(shape))).reshape(shape)
+        buf = tra_cpu.to_buffer(t, d)
+        for g in itertools.product(*[range(s) for s in shape]):
+            assert buf[tra_cpu.buffer_offset(g, shape, d)] == t[g]
+
+
 CASES = [
     ("ij,jk->ik", {"i": 4, "j": 6, "k": 2}),
     ("abef,cfed->abcd", {"a": 2, "b": 2, "c": 2, "d": 2, "e": 4, "f": 2}),
