@@ -1,0 +1,257 @@
+"""Benchmark of the extended-EinSum / TRA hot path on one MI355X.
+
+Workload (one step): the pairwise squared distance D[i,k] = sum_j (X[i,j] -
+Y[j,k])^2 with i = k = 8192, j = 256 (fp32, N(0,1) inputs) and its max-plus
+variant Z[i,k] = max_j (X[i,j] + Y[j,k]) (int32, uniform [-1000, 1000]), both
+under the partition vector d = [16, 1, 1, 16]:
+  dense -> relation for X and Y (tra_repartition), join + aggregation
+  (tra_execute), relation -> dense for the output (tra_repartition).
+Plans are made once, before timing (host only).  Inputs are resident in HBM
+before the timed region.
+
+value = algorithmic operations of one step / step time, in GFLOP/s, counting
+3 per (x-y)^2 + sum term and 2 per x+y / max term.
+
+The JSON line also carries:
+  roofline      the dominant kernel (squared-distance join) against the
+                vector-ALU issue ceiling, timed with HIP events on its stream;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload;
+  extra         the other workloads measured in the same run (partitioned
+                matmul, four-index contraction, blocked GEMM and its output
+                repartition, attention EinGraph), each against its own roof.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks and the vector-ALU issue ceiling derived from unit counts.
+CU, CLK = 256, 2.4e9
+HBM_PEAK = 8.0e12                 # bytes/s
+BF16_MFMA_PEAK = 2.5166e15        # dense flop/s
+VALU_LANE_OPS = CU * 4 * 16 * CLK  # 4 SIMDs x 16 lanes per CU per clock = 39.3e12 lane-ops/s
+# one (x-y)^2 + sum term = v_sub_f32 + v_fmac_f32 (2 lane-ops, 3 flops); packed fp32 is not used
+SQDIST_FLOP_PER_TERM = 3
+SQDIST_OPS_PER_TERM = 2
+VALU_SQDIST_PEAK = VALU_LANE_OPS / SQDIST_OPS_PER_TERM * SQDIST_FLOP_PER_TERM  # flop/s
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of extra workloads to run")
+    return ap.parse_args()
+
+
+def _events_time(fn, reps: int, stream) -> float:
+    """Average milliseconds per call of fn(), HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import tensor_relational_algebra_amd as tra
+    from tensor_relational_algebra_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    sq, mp = wl.SQDIST, wl.MAXPLUS
+    B = sq.bounds
+    d = sq.d
+    xs_h, ys_h = sq.make_inputs()
+    xm_h, ym_h = mp.make_inputs()
+    xs, ys, xm, ym = (t.to(dev) for t in (xs_h, ys_h, xm_h, ym_h))
+    plan_sq = tra.tra_plan(sq.spec, B, d, sq.join, sq.agg, sq.in_dtype, sq.out_dtype)
+    plan_mp = tra.tra_plan(mp.spec, B, d, mp.join, mp.agg, mp.in_dtype, mp.out_dtype)
+    dx, dy, dz = [d["i"], d["j"]], [d["j"], d["k"]], [d["i"], d["k"]]
+    sx, sy, sz = [B["i"], B["j"]], [B["j"], B["k"]], [B["i"], B["k"]]
+    # resident buffers
+    xr_s = torch.empty_like(xs).reshape(-1)
+    yr_s = torch.empty_like(ys).reshape(-1)
+    xr_m = torch.empty_like(xm).reshape(-1)
+    yr_m = torch.empty_like(ym).reshape(-1)
+    zr_s = torch.empty(plan_sq.info.z_elems, dtype=torch.float32, device=dev)
+    zr_m = torch.empty(plan_mp.info.z_elems, dtype=torch.int32, device=dev)
+    zd_s = torch.empty(sz, dtype=torch.float32, device=dev)
+    zd_m = torch.empty(sz, dtype=torch.int32, device=dev)
+    sq_ms = []
+
+    def step(time_dominant: bool = False):
+        tra.to_relation(xs, dx, xr_s)
+        tra.to_relation(ys, dy, yr_s)
+        if time_dominant:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        tra.tra_execute(plan_sq, xr_s, yr_s, zr_s)
+        if time_dominant:
+            e1.record(stream)
+            sq_ms.append((e0, e1))
+        tra.from_relation(zr_s, sz, dz, zd_s)
+        tra.to_relation(xm, dx, xr_m)
+        tra.to_relation(ym, dy, yr_m)
+        tra.tra_execute(plan_mp, xr_m, yr_m, zr_m)
+        tra.from_relation(zr_m, sz, dz, zd_m)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(time_dominant=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    terms = B["i"] * B["j"] * B["k"]
+    step_ops = terms * SQDIST_FLOP_PER_TERM + terms * 2
+    value = step_ops / (ms_per_step * 1e-3) / 1e9
+    sq_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in sq_ms]))
+    achieved = terms * SQDIST_FLOP_PER_TERM / (sq_launch_ms * 1e-3)
+
+    out = {
+        "metric": "einsum GFLOP/s & % of MFMA peak; repartition GB/s & % HBM peak (1 GPU)",
+        "value": round(value, 2),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+i32",
+        "data": "synthetic",
+        "config": {"workload": "pairwise squared distance + max-plus, i=k=8192, j=256, d=[16,1,1,16] "
+                               "(dense->relation, join+aggregate, relation->dense)",
+                   "i": B["i"], "j": B["j"], "k": B["k"], "d": [d["i"], d["j"], d["j"], d["k"]],
+                   "kernel": plan_sq.kernel},
+        "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": round(VALU_SQDIST_PEAK / 1e12, 3),
+                     "unit": "TFLOP/s", "frac": round(achieved / VALU_SQDIST_PEAK, 4), "traffic": None,
+                     "kernel": "k_valu_tile<sqdiff,sum>", "launch_ms": round(sq_launch_ms, 4)},
+    }
+
+    # zero-copy check of the timed outputs on a few rows against the oracle
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(xs_h, ys_h, xm_h, ym_h, zd_s, zd_m)
+    if not args.no_extra:
+        only = set(filter(None, args.only.split(",")))
+        out["extra"] = _extra(tra, wl, dev, stream, only)
+    print(json.dumps(out), flush=True)
+
+
+def _cpu_baseline(xs_h, ys_h, xm_h, ym_h, zd_s, zd_m):
+    """The oracle (as it stands) on the first `rows` output rows of both joins."""
+    import numpy as np
+    from oracle import ref
+
+    rows = 2048
+    n_k = zd_s.shape[1]
+    idx = np.arange(rows * n_k, dtype=np.int64)
+    t = time.perf_counter()
+    ws = ref.einsum("ij,jk->ik", xs_h, ys_h, "sqdiff", "sum", out_index=idx)
+    wm = ref.einsum("ij,jk->ik", xm_h, ym_h, "add", "max", out_index=idx)
+    dt = time.perf_counter() - t
+    terms = rows * n_k * xs_h.shape[1]
+    # the sampled rows of the timed GPU outputs agree with the oracle
+    gs = zd_s[:rows].reshape(-1).cpu().double().numpy()
+    gm = zd_m[:rows].reshape(-1).cpu().numpy().astype(np.int64)
+    err = float(np.abs(gs - ws).max() / np.abs(ws).max())
+    assert err <= 1e-4, f"squared distance differs from the oracle: {err}"
+    assert np.array_equal(gm, wm), "max-plus differs from the oracle"
+    return {"value": round(terms * (SQDIST_FLOP_PER_TERM + 2) / dt / 1e9, 3), "unit": "GFLOP/s",
+            "cores": int(ref.max_threads()), "kind": "oracle",
+            "sample": f"first {rows} of 8192 output rows of both joins ({terms / 1e9:.2f} G terms each), "
+                      f"{dt:.1f} s; GPU rows checked: rel err {err:.2e}, max-plus exact"}
+
+
+def _extra(tra, wl, dev, stream, only):
+    import torch
+    res = {}
+
+    def want(name):
+        return not only or name in only
+
+    def timed_execute(plan, x, y, reps=10):
+        z = torch.empty(plan.info.z_elems, dtype=tra._binding.TORCH_DTYPES[plan.out_dtype], device=dev)
+        ws = plan.workspace(dev)
+        for _ in range(2):
+            tra.tra_execute(plan, x, y, z, ws)
+        return _events_time(lambda: tra.tra_execute(plan, x, y, z, ws), reps, stream), z
+
+    if want("matmul"):
+        for base in (wl.MATMUL_F32, wl.MATMUL_I32):
+            x, y = (t.to(dev) for t in base.make_inputs())
+            for d4 in wl.MATMUL_D4:
+                dm = wl.matmul_d(d4)
+                p = tra.tra_plan(base.spec, base.bounds, dm, base.join, base.agg, base.in_dtype, base.out_dtype)
+                xr = tra.to_relation(x, [dm["i"], dm["j"]])
+                yr = tra.to_relation(y, [dm["j"], dm["k"]])
+                ms, _ = timed_execute(p, xr, yr, reps=50)
+                res[f"matmul_{base.in_dtype}_{'x'.join(map(str, d4))}"] = {
+                    "us": round(ms * 1e3, 2), "GFLOP/s": round(2 * 256 ** 3 / ms / 1e6, 1), "kernel": p.kernel,
+                    "split": p.info.agg_split}
+
+    if want("contract4"):
+        c = wl.CONTRACT4
+        a, b = (t.to(dev) for t in c.make_inputs())
+        p = tra.tra_plan(c.spec, c.bounds, c.d, c.join, c.agg, c.in_dtype, c.out_dtype)
+        ar = tra.to_relation(a, [c.d[l] for l in "abef"])
+        br = tra.to_relation(b, [c.d[l] for l in "cfed"])
+        ms, _ = timed_execute(p, ar, br, reps=50)
+        fl = 2 * 64 ** 4 * 32 ** 2
+        res["contract4"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
+                            "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4), "kernel": p.kernel}
+
+    if want("gemm25d"):
+        g = wl.GEMM25D
+        x, a = (t.to(dev) for t in g.make_inputs())
+        p = tra.tra_plan(g.spec, g.bounds, g.d, g.join, g.agg, g.in_dtype, g.out_dtype)
+        xr = tra.to_relation(x, [g.d["i"], g.d["j"]])
+        ar = tra.to_relation(a, [g.d["j"], g.d["k"]])
+        del x, a
+        ms, yr = timed_execute(p, xr, ar, reps=10)
+        fl = 2 * 16384 * 8192 * 8192
+        res["gemm25d"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                          "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4), "kernel": p.kernel}
+        shape = [16384, 8192]
+        dst = torch.empty_like(yr)
+        f = lambda: tra.tra_repartition(yr, shape, list(wl.GEMM25D_Y_FROM), list(wl.GEMM25D_Y_TO), dst)
+        f()
+        ms = _events_time(f, 20, stream)
+        nbytes = 2 * yr.numel() * 4
+        res["gemm25d_repartition"] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / ms / 1e6, 1),
+                                      "frac_hbm_peak": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
+        del xr, ar, yr, dst
+    torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    main()
