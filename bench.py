@@ -36,11 +36,13 @@ if ROOT not in sys.path:
 CU, CLK = 256, 2.4e9
 HBM_PEAK = 8.0e12                 # bytes/s
 BF16_MFMA_PEAK = 2.5166e15        # dense flop/s
-VALU_LANE_OPS = CU * 4 * 16 * CLK  # 4 SIMDs x 16 lanes per CU per clock = 39.3e12 lane-ops/s
-# one (x-y)^2 + sum term = v_sub_f32 + v_fmac_f32 (2 lane-ops, 3 flops); packed fp32 is not used
+# fp32 vector 157.3 TFLOP/s = 256 CUs x 128 fp32 lanes/clock x 2 (FMA) x 2.4 GHz, i.e.
+# 78.6e12 single-instruction lane-ops per second (no packed math involved).
+VALU_LANE_OPS = CU * 128 * CLK
+# one (x-y)^2 + sum term = v_sub_f32 + v_fmac_f32: 2 lane-ops, counted as 3 flops
 SQDIST_FLOP_PER_TERM = 3
 SQDIST_OPS_PER_TERM = 2
-VALU_SQDIST_PEAK = VALU_LANE_OPS / SQDIST_OPS_PER_TERM * SQDIST_FLOP_PER_TERM  # flop/s
+VALU_SQDIST_PEAK = VALU_LANE_OPS / SQDIST_OPS_PER_TERM * SQDIST_FLOP_PER_TERM  # 117.96e12 flop/s
 
 
 def _parse():
@@ -171,7 +173,7 @@ def _cpu_baseline(xs_h, ys_h, xm_h, ym_h, zd_s, zd_m):
     import numpy as np
     from oracle import ref
 
-    rows = 2048
+    rows = 8192
     n_k = zd_s.shape[1]
     idx = np.arange(rows * n_k, dtype=np.int64)
     t = time.perf_counter()

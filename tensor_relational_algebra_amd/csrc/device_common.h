@@ -151,7 +151,8 @@ template <int T>
 __device__ __forceinline__ int32_t p2off(const Pow2Group &g, uint32_t idx)
 {
     int32_t o = 0;
-    for (int i = 0; i < g.n; ++i) o += (int32_t)((idx >> g.sh[i]) & g.mask[i]) * g.st[T][i];
+#pragma unroll
+    for (int i = 0; i < kP2Max; ++i) o += (int32_t)((idx >> g.sh[i]) & g.mask[i]) * g.st[T][i];
     return o;
 }
 

@@ -16,8 +16,8 @@
 // sub-dimension strides.  An operand stored contiguously along the
 // contracted labels ("K-major") is staged in LDS as [row][k] and fed to the
 // matrix cores with 16-byte LDS reads; one stored contiguously along its
-// output labels ("MN-major") is staged as [k][row] and gathered with 16-bit
-// LDS reads.
+// output labels ("MN-major") is staged as [k][row] exactly as it arrives and
+// transposed on the way to the matrix cores by gfx950's ds_read_b64_tr_b16.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -61,80 +61,99 @@ __device__ __forceinline__ void mfma_tile_of(uint32_t nb, uint32_t tiles_n, uint
     tn = r / gs;
 }
 
+// LDS staging.  K-major operand: [rows][BK + 8] (16-byte fragment reads,
+// conflict-free with the 144-byte row pitch).  MN-major operand: [BK][rows +
+// 32]: rows are written as they arrive from HBM and transposed on the way out
+// by ds_read_b64_tr_b16 (the 64-element pad spreads the four k-rows one read
+// touches over distinct banks).
 template <int V>
 constexpr int lds_elems(bool kmajor, bool is_a)
 {
     constexpr MfmaCfg c = mfma_cfg(V);
     int rows = is_a ? c.bm : c.bn;
-    return kmajor ? rows * (c.bk + 8) : c.bk * (rows + 8);
+    return kmajor ? rows * (c.bk + 8) : c.bk * (rows + 32);
 }
 
-template <int V, bool AK, bool BKM>
+template <int V, bool BKM>
 constexpr size_t mfma_lds_bytes()
 {
-    return 2 * (size_t)(lds_elems<V>(AK, true) + lds_elems<V>(BKM, false)) * 2;
+    return 2 * (size_t)(lds_elems<V>(true, true) + lds_elems<V>(BKM, false)) * 2;
 }
 
-// Loader for one operand tile (rows x BK) into LDS.
-//   KM: operand contiguous along k.  Vectors of 8 bf16 (16 bytes).
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+
+// Power-of-two digit layouts split cleanly at aligned boundaries: for r0 a
+// multiple of 2^b and d < 2^b, off(r0 + d) = off(r0) + off(d).  So every
+// per-thread offset below is computed once, and each k-tile only adds the
+// uniform term off(k0).
+
+// Loader for one operand tile (rows x BK) into LDS, 16-byte vectors.
+//   KM: operand contiguous along k -> LDS [row][k]; else along rows -> LDS [k][row].
 template <int ROWS, int BK, int NT, bool KM, int T>
 struct TileLoader {
     static constexpr int NV = ROWS * BK / 8 / NT;   // vectors per thread
-    static constexpr int LD = KM ? BK + 8 : ROWS + 8;
-    int32_t row_off[NV];  // KM: offset of each row; !KM: offset of the 8-row group
-    int col[NV];          // KM: k within tile; !KM: k row within tile
-    int row[NV];          // KM: row within tile; !KM: first row of the group
+    static constexpr int LD = KM ? BK + 8 : ROWS + 32;
+    int32_t off[NV];      // row part + in-tile k part of each vector's source offset
+    int32_t lds_off[NV];  // destination element offset in the stage
     uint4 reg[NV];
 
-    __device__ __forceinline__ void init(const Pow2Group &g_rows, uint32_t r0, int32_t base, int tid)
+    __device__ __forceinline__ void init(const Pow2Group &g_rows, const Pow2Group &gk, uint32_t r0, int32_t base,
+                                         int tid)
     {
+        const int32_t rbase = p2off<0>(g_rows, r0) + base;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             int q = tid + NT * i;
+            int row, col;
             if constexpr (KM) {
-                col[i] = (q % (BK / 8)) * 8;
-                row[i] = q / (BK / 8);
+                col = (q % (BK / 8)) * 8;
+                row = q / (BK / 8);
+                lds_off[i] = row * LD + col;
             } else {
-                row[i] = (q % (ROWS / 8)) * 8;
-                col[i] = q / (ROWS / 8);
+                row = (q % (ROWS / 8)) * 8;
+                col = q / (ROWS / 8);
+                lds_off[i] = col * LD + row;
             }
-            row_off[i] = p2off<0>(g_rows, r0 + row[i]) + base;
+            off[i] = rbase + p2off<0>(g_rows, row) + p2off<T>(gk, col);
         }
     }
-    __device__ __forceinline__ void load(const uint16_t *__restrict__ p, const Pow2Group &gk, uint32_t k0)
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ p, int32_t koff)
     {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            int32_t o = row_off[i] + p2off<T>(gk, k0 + col[i]);
-            reg[i] = *(const uint4 *)(p + o);
-        }
+        for (int i = 0; i < NV; ++i) reg[i] = *(const uint4 *)(p + off[i] + koff);
     }
     __device__ __forceinline__ void store(uint16_t *lds)
     {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            if constexpr (KM) *(uint4 *)&lds[row[i] * LD + col[i]] = reg[i];
-            else *(uint4 *)&lds[col[i] * LD + row[i]] = reg[i];
-        }
+        for (int i = 0; i < NV; ++i) *(uint4 *)&lds[lds_off[i]] = reg[i];
     }
 };
 
-// 8 consecutive k of one row r of a staged operand, as an MFMA operand.
-template <bool KM, int LD>
-__device__ __forceinline__ bf16x8_t frag(const uint16_t *lds, int r, int k)
+// A fragment (K-major staging): 8 consecutive k of row r.
+template <int LD>
+__device__ __forceinline__ bf16x8_t frag_k(const uint16_t *lds, int r, int k)
 {
-    if constexpr (KM) {
-        uint4 u = *(const uint4 *)&lds[r * LD + k];
-        return __builtin_bit_cast(bf16x8_t, u);
-    } else {
-        shortx8_t s;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] = (short)lds[(k + e) * LD + r];
-        return __builtin_bit_cast(bf16x8_t, s);
-    }
+    uint4 u = *(const uint4 *)&lds[r * LD + k];
+    return __builtin_bit_cast(bf16x8_t, u);
 }
 
-template <int V, bool AK, bool BKM, typename TO>
+// B fragment from [k][n] staging via two transposing reads.  Lane l (group
+// g = l/16, s = l%16) addresses row kb + s/4, columns nb + 4*(s%4)..+3 with
+// kb = k + 8*(g/2), nb = n + 16*(g%2); lane l then holds B[k + 8*(l/32) + e][n + l%32].
+template <int LD>
+__device__ __forceinline__ bf16x8_t frag_tr(const uint16_t *lds, int n, int k, int lane)
+{
+    const int g = lane >> 4, sl = lane & 15;
+    const int kb = k + 8 * (g >> 1) + (sl >> 2), nb = n + 16 * (g & 1) + 4 * (sl & 3);
+    typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
+    const uint16_t *p0 = lds + kb * LD + nb;
+    bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4 *)(p0));
+    bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4 *)(p0 + 4 * LD));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int V, bool BKM, typename TO>
 __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf16(
     GemmView v, const uint16_t *__restrict__ x, const uint16_t *__restrict__ y, TO *__restrict__ z,
     float *__restrict__ ws)
@@ -143,8 +162,9 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     constexpr int BM = C.bm, BN = C.bn, BK = C.bk, WM = C.wm, WN = C.wn;
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-    constexpr int A_EL = lds_elems<V>(AK, true), B_EL = lds_elems<V>(BKM, false);
-    constexpr int LDA = AK ? BK + 8 : BM + 8, LDB = BKM ? BK + 8 : BN + 8;
+    constexpr int A_EL = lds_elems<V>(true, true), B_EL = lds_elems<V>(BKM, false);
+    constexpr int LDA = BK + 8, LDB = BKM ? BK + 8 : BN + 32;
+    constexpr int STAGE = A_EL + B_EL;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -159,10 +179,10 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
     const uint32_t kend = kbeg + (uint32_t)v.k_per_split;
 
-    TileLoader<BM, BK, NT, AK, 0> la;
+    TileLoader<BM, BK, NT, true, 0> la;
     TileLoader<BN, BK, NT, BKM, 1> lb;
-    la.init(v.gm, m0, bx, tid);
-    lb.init(v.gn, n0, by, tid);
+    la.init(v.gm, v.gk, m0, bx, tid);
+    lb.init(v.gn, v.gk, n0, by, tid);
 
     floatx16_t acc[TM][TN];
 #pragma unroll
@@ -172,36 +192,48 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // stage s: A at s * (A_EL + B_EL), B right after it
-    constexpr int STAGE = A_EL + B_EL;
-
-    la.load(x, v.gk, kbeg);
-    lb.load(y, v.gk, kbeg);
+    la.load(x, p2off<0>(v.gk, kbeg));
+    lb.load(y, p2off<1>(v.gk, kbeg));
     la.store(smem);
     lb.store(smem + A_EL);
     __syncthreads();
 
     const int r_lane = lane & 31, k_lane = (lane >> 5) * 8;
+    const int a_row0 = wm * (BM / WM) + r_lane;
+    const int b_col0 = wn * (BN / WN);
     int stage = 0;
     for (uint32_t k0 = kbeg; k0 < kend; k0 += BK) {
         const bool more = k0 + BK < kend;
         if (more) {
-            la.load(x, v.gk, k0 + BK);
-            lb.load(y, v.gk, k0 + BK);
+            la.load(x, p2off<0>(v.gk, k0 + BK));
+            lb.load(y, p2off<1>(v.gk, k0 + BK));
         }
         const uint16_t *a_s = smem + stage * STAGE, *b_s = a_s + A_EL;
+        bf16x8_t af[2][TM], bf[2][TN];
 #pragma unroll
-        for (int ks = 0; ks < BK; ks += 16) {
-            bf16x8_t af[TM], bf[TN];
+        for (int i = 0; i < TM; ++i) af[0][i] = frag_k<LDA>(a_s, a_row0 + i * 32, k_lane);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = frag<AK, LDA>(a_s, wm * (BM / WM) + i * 32 + r_lane, ks + k_lane);
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (BKM) bf[0][j] = frag_k<LDB>(b_s, b_col0 + j * 32 + r_lane, k_lane);
+            else bf[0][j] = frag_tr<LDB>(b_s, b_col0 + j * 32, 0, lane);
+        }
 #pragma unroll
-            for (int j = 0; j < TN; ++j) bf[j] = frag<BKM, LDB>(b_s, wn * (BN / WN) + j * 32 + r_lane, ks + k_lane);
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int cur = ks & 1, nxt = cur ^ 1;
+            if (ks + 1 < BK / 16) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) af[nxt][i] = frag_k<LDA>(a_s, a_row0 + i * 32, (ks + 1) * 16 + k_lane);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (BKM) bf[nxt][j] = frag_k<LDB>(b_s, b_col0 + j * 32 + r_lane, (ks + 1) * 16 + k_lane);
+                    else bf[nxt][j] = frag_tr<LDB>(b_s, b_col0 + j * 32, (ks + 1) * 16, lane);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
         }
         if (more) {
             la.store(smem + (stage ^ 1) * STAGE);
@@ -215,18 +247,27 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     // 8*(e/4) + 4*(l/32) + e%4 and column l%32 of its 32x32 block.
     const bool split = v.split > 1;
     float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
+    // row = (wave row + 32 i + 8 (e/4)) + (4 (l/32) + e%4): a multiple of 8 plus
+    // a part below 8, so its offset splits into a wave-uniform and a lane part.
+    const int32_t zm0 = p2off<1>(v.gm, m0) + bz, zn0 = p2off<1>(v.gn, n0);
+    int32_t lo[4];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const uint32_t n = n0 + wn * (BN / WN) + j * 32 + r_lane;
-        const int32_t on = p2off<1>(v.gn, n) + bz;
+    for (int r = 0; r < 4; ++r) lo[r] = p2off<1>(v.gm, 4 * (lane >> 5) + r);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const uint32_t m = m0 + wm * (BM / WM) + i * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
-                const int32_t o = p2off<1>(v.gm, m) + on;
-                if (split) wsp[o] = acc[i][j][e];
-                else Scalar<TO>::store(z, o, acc[i][j][e] * v.post_scale);
+        for (int q = 0; q < 4; ++q) {
+            const int32_t hi = zm0 + p2off<1>(v.gm, wm * (BM / WM) + i * 32 + 8 * q);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int32_t on = zn0 + p2off<1>(v.gn, b_col0 + j * 32 + r_lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int32_t o = hi + lo[r] + on;
+                    const float val = acc[i][j][4 * q + r];
+                    if (split) wsp[o] = val;
+                    else Scalar<TO>::store(z, o, val * v.post_scale);
+                }
             }
         }
     }
@@ -234,21 +275,21 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
 
 int launch_split_fold(const tra_plan_s &p, const void *ws, void *z, void *stream);
 
-template <int V, bool AK, bool BKM, typename TO>
+template <int V, bool BKM, typename TO>
 static int launch_v(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, hipStream_t s)
 {
     constexpr MfmaCfg C = mfma_cfg(V);
-    constexpr size_t lds = mfma_lds_bytes<V, AK, BKM>();
+    constexpr size_t lds = mfma_lds_bytes<V, BKM>();
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_mfma_bf16<V, AK, BKM, TO>,
+        hipError_t e = hipFuncSetAttribute((const void *)k_mfma_bf16<V, BKM, TO>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return (int)e;
         attr_set = true;
     }
     const GemmView &v = p.gv;
     dim3 grid((v.gm.total / C.bm) * (v.gn.total / C.bn), v.gb.total, v.split);
-    hipLaunchKernelGGL((k_mfma_bf16<V, AK, BKM, TO>), grid, dim3(C.wm * C.wn * 64), lds, s, v,
+    hipLaunchKernelGGL((k_mfma_bf16<V, BKM, TO>), grid, dim3(C.wm * C.wn * 64), lds, s, v,
                        (const uint16_t *)x, (const uint16_t *)y, (TO *)z, (float *)ws);
     return (int)hipGetLastError();
 }
@@ -256,8 +297,8 @@ static int launch_v(const tra_plan_s &p, const void *x, const void *y, void *z, 
 template <int V, typename TO>
 static int launch_layout(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, hipStream_t s)
 {
-    if (p.b_kmajor) return launch_v<V, true, true, TO>(p, x, y, z, ws, s);
-    return launch_v<V, true, false, TO>(p, x, y, z, ws, s);
+    if (p.b_kmajor) return launch_v<V, true, TO>(p, x, y, z, ws, s);
+    return launch_v<V, false, TO>(p, x, y, z, ws, s);
 }
 
 template <typename TO>

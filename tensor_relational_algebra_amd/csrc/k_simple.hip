@@ -168,9 +168,7 @@ __global__ __launch_bounds__(256) void k_repartition_p2(Pow2Group g, int lvec, u
     uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
 #pragma unroll 4
     for (; u < n_units; u += stride) {
-        uint32_t e = u << lvec;
-        int32_t so = 0;
-        for (int i = 0; i < g.n; ++i) so += (int32_t)((e >> g.sh[i]) & g.mask[i]) * g.st[0][i];
+        const int32_t so = p2off<0>(g, u << lvec);
         dst[u] = src[so >> lvec];
     }
 }
@@ -246,18 +244,18 @@ int launch_repartition(const RepartDesc &r, int esz, const void *src, void *dst,
     hipStream_t s = (hipStream_t)stream;
     const int unit = r.vec * esz;
     const int64_t n_units = r.n_elems / r.vec;
-    // power-of-two digits: shift/mask path
-    bool p2 = n_units < (1ll << 31);
+    // power-of-two digits (at most kP2Max of them): shift/mask path
+    bool p2 = n_units < (1ll << 31) && r.dst.n <= kP2Max;
     Pow2Group g{};
     g.n = r.dst.n;
-    int sh = 0;
+    uint32_t sh = 0;
     for (int i = r.dst.n - 1; i >= 0 && p2; --i) {
         uint32_t e = r.dst.ext[i];
         if (e & (e - 1)) p2 = false;
-        g.sh[i] = (uint8_t)sh;
+        g.sh[i] = sh;
         g.mask[i] = e - 1;
         g.st[0][i] = (int32_t)r.dst.st[0][i];
-        while ((1u << sh) < ((1u << g.sh[i]) * e)) ++sh;
+        while ((1u << sh) < e * (1u << g.sh[i])) ++sh;
     }
     if (p2) {
         int lvec = 0;

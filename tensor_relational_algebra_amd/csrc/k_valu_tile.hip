@@ -126,29 +126,31 @@ __global__ __launch_bounds__(VT_THREADS) void k_valu_tile(GemmView v, const T *_
     // Loader assignment: 4 vectors of 4 elements per thread for each operand.
     // K-major operand: vector along k; 8 vectors per row of BK.
     // MN-major operand: vector along m/n; BM/4 vectors per k-row.
+    // Offsets split at the tile boundary (power-of-two digits): off(r0 + d) =
+    // off(r0) + off(d), so the per-thread parts are computed once and every
+    // k-tile adds only the uniform off(k0).
     int32_t a_off[4], b_off[4];
     int a_row[4], a_col[4], b_row[4], b_col[4];
+    const int32_t am0 = p2off<0>(v.gm, m0) + bx, bn0 = p2off<0>(v.gn, n0) + by;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         int q = tid + VT_THREADS * r;
         if constexpr (AK) {
             a_col[r] = (q % (BK / 4)) * 4;  // k
             a_row[r] = q / (BK / 4);        // m
-            a_off[r] = p2off<0>(v.gm, m0 + a_row[r]) + bx;
         } else {
             a_row[r] = (q % (BM / 4)) * 4;  // m
             a_col[r] = q / (BM / 4);        // k
-            a_off[r] = p2off<0>(v.gm, m0 + a_row[r]) + bx;
         }
+        a_off[r] = am0 + p2off<0>(v.gm, a_row[r]) + p2off<0>(v.gk, a_col[r]);
         if constexpr (BKM) {
             b_col[r] = (q % (BK / 4)) * 4;
             b_row[r] = q / (BK / 4);
-            b_off[r] = p2off<0>(v.gn, n0 + b_row[r]) + by;
         } else {
             b_row[r] = (q % (BN / 4)) * 4;
             b_col[r] = q / (BN / 4);
-            b_off[r] = p2off<0>(v.gn, n0 + b_row[r]) + by;
         }
+        b_off[r] = bn0 + p2off<0>(v.gn, b_row[r]) + p2off<1>(v.gk, b_col[r]);
     }
 
     A acc[8][8];
@@ -162,12 +164,11 @@ __global__ __launch_bounds__(VT_THREADS) void k_valu_tile(GemmView v, const T *_
     V4 ra[4], rb[4];
 
     auto gload = [&](uint32_t k0) {
+        const int32_t kx = p2off<0>(v.gk, k0), ky = p2off<1>(v.gk, k0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            if constexpr (AK) ra[r] = *(const V4 *)(x + a_off[r] + p2off<0>(v.gk, k0 + a_col[r]));
-            else ra[r] = *(const V4 *)(x + a_off[r] + p2off<0>(v.gk, k0 + a_col[r]));
-            if constexpr (BKM) rb[r] = *(const V4 *)(y + b_off[r] + p2off<1>(v.gk, k0 + b_col[r]));
-            else rb[r] = *(const V4 *)(y + b_off[r] + p2off<1>(v.gk, k0 + b_col[r]));
+            ra[r] = *(const V4 *)(x + a_off[r] + kx);
+            rb[r] = *(const V4 *)(y + b_off[r] + ky);
         }
     };
     auto lstore = [&]() {
@@ -218,16 +219,17 @@ __global__ __launch_bounds__(VT_THREADS) void k_valu_tile(GemmView v, const T *_
     // Epilogue: rows ty*4+{0..3}, 64+ty*4+{0..3}; columns tx*4+{0..3}, 64+tx*4+{0..3}.
     const bool split = v.split > 1;
     T *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
+    const int32_t zm0 = p2off<1>(v.gm, m0) + bz, zn0 = p2off<1>(v.gn, n0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t m = m0 + (i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4));
-        const int32_t om = p2off<1>(v.gm, m) + bz;
+        const uint32_t m = i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4);
+        const int32_t om = zm0 + p2off<1>(v.gm, m);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t nbase = n0 + h * 64 + tx * 4;
+            const uint32_t nbase = h * 64 + tx * 4;
             int32_t on[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) on[j] = p2off<1>(v.gn, nbase + j);
+            for (int j = 0; j < 4; ++j) on[j] = zn0 + p2off<1>(v.gn, nbase + j);
             const bool vec = on[1] == on[0] + 1 && on[2] == on[0] + 2 && on[3] == on[0] + 3 && ((om + on[0]) & 3) == 0;
             A r4[4];
 #pragma unroll

@@ -159,12 +159,13 @@ static Radix to_radix(const std::vector<SubDim> &v)
 static bool to_pow2(const std::vector<SubDim> &v, Pow2Group &g)
 {
     g = Pow2Group{};
+    if ((int)v.size() > kP2Max) return false;
     g.n = (int32_t)v.size();
     int sh = 0;
     uint64_t total = 1;
     for (int i = (int)v.size() - 1; i >= 0; --i) {
         if (!is_pow2(v[i].ext)) return false;
-        g.sh[i] = (uint8_t)sh;
+        g.sh[i] = (uint32_t)sh;
         g.mask[i] = v[i].ext - 1;
         for (int t = 0; t < 3; ++t) g.st[t][i] = (int32_t)v[i].st[t];
         sh += ilog2(v[i].ext);

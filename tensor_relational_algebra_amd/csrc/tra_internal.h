@@ -25,12 +25,15 @@ struct Radix {
 };
 
 // Power-of-two index group: offset_t(idx) = sum_i ((idx >> sh_i) & mask_i) * st[t][i].
+// At most kP2Max digits; unused digits have mask 0 (they add nothing), so the
+// kernels evaluate all kP2Max digits unrolled, with every field in registers.
+constexpr int kP2Max = 8;
 struct Pow2Group {
     int32_t n;
     uint32_t total;
-    uint8_t sh[kMaxSub];
-    uint32_t mask[kMaxSub];
-    int32_t st[3][kMaxSub];
+    uint32_t sh[kP2Max];
+    uint32_t mask[kP2Max];
+    int32_t st[3][kP2Max];
 };
 
 // Join / aggregate codes (mirror tra.h).
