@@ -251,8 +251,57 @@ def _extra(tra, wl, dev, stream, only):
         res["gemm25d_repartition"] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / ms / 1e6, 1),
                                       "frac_hbm_peak": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
         del xr, ar, yr, dst
+
+    if want("mha"):
+        res["mha"] = _mha(tra, wl, dev, stream)
     torch.cuda.empty_cache()
     return res
+
+
+def _mha(tra, wl, dev, stream):
+    """The attention layer as an EinGraph, d chosen for P = 256; per-node time
+    (its input repartitions included) against the node's own roof."""
+    import torch
+    case = wl.MHA
+    desc = case.graph_desc()
+    g = tra.tra_graph_plan(desc, 256)
+    inputs = {k: v.to(dev) for k, v in case.make_inputs().items()}
+    ws = g.workspace(dev)
+    out = torch.empty(g.info.out_elems, dtype=torch.float32, device=dev)
+    names = [l.split()[0] for l in desc.splitlines()]
+    s, a, h, dh = case.s, case.a, case.h, case.dh
+    gemm = 2.0 * s * a * h * dh          # every projection and the output projection
+    attn_fl = 2.0 * h * s * s * dh       # scores and weighted sum
+    flops = {"Q_proj": gemm, "K_proj": gemm, "V_proj": gemm, "Scores": attn_fl, "O": attn_fl, "Output": gemm}
+    # bytes the HBM-bound nodes must move at least: scores write fp32 S; softmax reads
+    # S twice (logsumexp, then normalise) and writes bf16 Attn; weighted sum reads Attn
+    sbytes = {"Scores": 4.0 * h * s * s, "Attn": 2 * 4.0 * h * s * s + 2.0 * h * s * s, "O": 2.0 * h * s * s}
+    for _ in range(2):
+        tra.tra_graph_execute(g, inputs, out, ws)
+    reps = 5
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record(stream)
+        for i in range(len(names)):
+            tra.tra_graph_run_node(g, i, inputs, out if i == len(names) - 1 else None, ws)
+            ev[r][i + 1].record(stream)
+    torch.cuda.synchronize()
+    nodes = {}
+    total = 0.0
+    for i, n in enumerate(names):
+        ms = sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
+        total += ms
+        e = {"us": round(ms * 1e3, 1), "d": g.node_d(i)}
+        if n in flops:
+            e["TFLOP/s"] = round(flops[n] / ms / 1e9, 1)
+            e["frac_bf16_mfma_peak"] = round(flops[n] / (ms * 1e-3) / BF16_MFMA_PEAK, 4)
+        if n in sbytes:
+            e["GB/s"] = round(sbytes[n] / ms / 1e6, 1)
+            e["frac_hbm_peak"] = round(sbytes[n] / (ms * 1e-3) / HBM_PEAK, 4)
+        nodes[n] = e
+    total_fl = sum(flops.values())
+    return {"ms": round(total, 3), "TFLOP/s": round(total_fl / total / 1e9, 1), "nodes": nodes,
+            "repartitions": g.info.n_repartitions, "workspace_GB": round(g.info.workspace_bytes / 1e9, 2)}
 
 
 if __name__ == "__main__":

@@ -231,6 +231,69 @@ int tra_cost(const char *spec, const int64_t *bounds, const int32_t *d, int n_la
  */
 int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_cap, int64_t *cost_out);
 
+/*
+ * EinGraph executor (section 2.1: an EinGraph is a DAG of EinSum nodes whose
+ * edges are tensors; section 4.1: the compiled plan partitions the inputs,
+ * runs every node's join + aggregation, and reorganises intermediates whose
+ * producer and consumer blockings differ).
+ *
+ * tra_graph_plan -- parse a graph (the tra_choose line format; each line may
+ * end with options in=<dtype> out=<dtype> scale=<float>: the dtype both
+ * operands are stored in, the dtype of the node's output, and post_scale),
+ * pick d for every node (d_all == NULL: the tra_choose DP with task multiple
+ * P; else d_all holds every node's d in canonical order, concatenated, d_len
+ * entries), plan every node, and lay out the device workspace the run needs.
+ * A softmax node "hst->hst" is run as LSE[h,s] = lse_t S (ident + lse, fp32)
+ * then Attn = exp(S - LSE) (exp_sub, aggregate NONE, written in out dtype),
+ * both under the node's d.
+ * Graph inputs ('@' names) are numbered in order of first appearance; each is
+ * passed dense row-major, shaped as its consumer writes it, in the
+ * consumer's in dtype.  The output node's result is returned dense row-major.
+ * Errors: those of tra_choose and tra_plan.
+ */
+typedef struct tra_graph_s *tra_graph_t;
+
+typedef struct {
+    int32_t n_nodes;
+    int32_t n_leaves;
+    size_t workspace_bytes;   /* device scratch tra_graph_execute needs */
+    int64_t out_elems;        /* elements of the output node's result */
+    int32_t out_dtype;
+    int64_t cost;             /* cost-model value of the chosen partition vectors */
+    int32_t n_repartitions;   /* inter-node repartitions the plan contains */
+} tra_graph_info_t;
+
+int tra_graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d_len, tra_graph_t *out_graph);
+
+/* Sizes of a planned graph.  Errors: TRA_E_NULL. */
+int tra_graph_info(tra_graph_t graph, tra_graph_info_t *info);
+
+/* d of node `node` (canonical order) into d_out; returns its length or a
+ * negative status (TRA_E_NULL, TRA_E_GRAPH for a bad index, TRA_E_BUFFER). */
+int tra_graph_node_d(tra_graph_t graph, int node, int32_t *d_out, int d_cap);
+
+/* Graph input `leaf`: NUL-terminated name (without '@') into name, element
+ * count and dtype.  Errors: TRA_E_NULL, TRA_E_GRAPH, TRA_E_BUFFER. */
+int tra_graph_leaf(tra_graph_t graph, int leaf, char *name, int name_cap, int64_t *elems, int32_t *dtype);
+
+/*
+ * tra_graph_run_node -- enqueue one node: the repartitions its inputs need
+ * (graph inputs: dense -> the node's blocking; intermediates: only when the
+ * producer's blocking differs), then its join + aggregation.  For the output
+ * node, `out` (may be NULL otherwise) receives the dense result.  Nodes must
+ * be run in description order.  leaves: n_leaves device pointers.
+ * Errors: TRA_E_NULL, TRA_E_GRAPH, TRA_E_WORKSPACE, TRA_E_ALIGN, TRA_E_HIP.
+ */
+int tra_graph_run_node(tra_graph_t graph, int node, const void *const *leaves, int n_leaves, void *out,
+                       void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Every node in order (tra_graph_run_node for each). */
+int tra_graph_execute(tra_graph_t graph, const void *const *leaves, int n_leaves, void *out, void *workspace,
+                      size_t workspace_bytes, void *hip_stream);
+
+/* Free a graph's host memory.  NULL is accepted. */
+int tra_graph_destroy(tra_graph_t graph);
+
 /* Text of a status code (static storage). */
 const char *tra_status_string(int status);
 

@@ -60,6 +60,13 @@ def lib() -> ctypes.CDLL:
             "tra_d_from_operand_form": ([ctypes.c_char_p, P, I, P, I], I),
             "tra_cost": ([ctypes.c_char_p, P, P, I, P], I),
             "tra_choose": ([ctypes.c_char_p, I, P, I, P], I),
+            "tra_graph_plan": ([ctypes.c_char_p, I, P, I, P], I),
+            "tra_graph_info": ([P, P], I),
+            "tra_graph_node_d": ([P, I, P, I], I),
+            "tra_graph_leaf": ([P, I, ctypes.c_char_p, I, P, P], I),
+            "tra_graph_run_node": ([P, I, P, I, P, P, ctypes.c_size_t, P], I),
+            "tra_graph_execute": ([P, P, I, P, P, ctypes.c_size_t, P], I),
+            "tra_graph_destroy": ([P], I),
             "tra_status_string": ([I], ctypes.c_char_p),
             "tra_last_error": ([], ctypes.c_char_p),
         }
@@ -229,3 +236,79 @@ def tra_choose(graph_desc: str, p: int) -> Tuple[List[List[int]], int]:
         res.append(list(out[pos:pos + n]))
         pos += n
     return res, cost.value
+
+
+class GraphInfo(ctypes.Structure):
+    _fields_ = [("n_nodes", ctypes.c_int32), ("n_leaves", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+                ("out_elems", ctypes.c_int64), ("out_dtype", ctypes.c_int32), ("cost", ctypes.c_int64),
+                ("n_repartitions", ctypes.c_int32)]
+
+
+class Graph:
+    """Owns a tra_graph_t handle (see tra_graph_plan in include/tra.h)."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+        info = GraphInfo()
+        _check(lib().tra_graph_info(handle, ctypes.byref(info)))
+        self.info = info
+        self.leaves = []
+        for i in range(info.n_leaves):
+            name = ctypes.create_string_buffer(64)
+            n, dt = ctypes.c_int64(), ctypes.c_int32()
+            _check(lib().tra_graph_leaf(handle, i, name, 64, ctypes.byref(n), ctypes.byref(dt)))
+            self.leaves.append((name.value.decode(), n.value, TORCH_DTYPES[dt.value]))
+
+    def node_d(self, node: int) -> List[int]:
+        buf = (ctypes.c_int32 * 32)()
+        n = _check(lib().tra_graph_node_d(self.handle, node, buf, 32))
+        return list(buf[:n])
+
+    def workspace(self, device) -> Optional[torch.Tensor]:
+        n = self.info.workspace_bytes
+        return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+    def _leaf_ptrs(self, inputs: Dict[str, torch.Tensor]):
+        ptrs = []
+        for name, n, dt in self.leaves:
+            t = inputs[name]
+            ptrs.append(_dev_ptr(t, name, n, DTYPE_OF_TORCH[dt]))
+        return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.tra_graph_destroy(self.handle)
+            self.handle = None
+
+
+def tra_graph_plan(graph_desc: str, p: int = 256, d_all: Optional[Sequence[int]] = None) -> Graph:
+    h = ctypes.c_void_p()
+    if d_all is None:
+        _check(lib().tra_graph_plan(graph_desc.encode(), int(p), None, 0, ctypes.byref(h)))
+    else:
+        _check(lib().tra_graph_plan(graph_desc.encode(), int(p), _i32(d_all), len(d_all), ctypes.byref(h)))
+    return Graph(h.value)
+
+
+def tra_graph_execute(g: Graph, inputs: Dict[str, torch.Tensor], out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Run every node; `inputs` maps graph-input names (without '@') to dense device tensors."""
+    dev = next(iter(inputs.values())).device
+    if out is None:
+        out = torch.empty(g.info.out_elems, dtype=TORCH_DTYPES[g.info.out_dtype], device=dev)
+    po = _dev_ptr(out, "out", g.info.out_elems, g.info.out_dtype)
+    if workspace is None:
+        workspace = g.workspace(dev)
+    pw = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() if workspace is not None else 0
+    _check(lib().tra_graph_execute(g.handle, g._leaf_ptrs(inputs), len(g.leaves), po, pw, wb, _stream(stream)))
+    return out
+
+
+def tra_graph_run_node(g: Graph, node: int, inputs: Dict[str, torch.Tensor], out: Optional[torch.Tensor],
+                       workspace: Optional[torch.Tensor], stream=None) -> None:
+    po = out.data_ptr() if out is not None else None
+    pw = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() if workspace is not None else 0
+    _check(lib().tra_graph_run_node(g.handle, int(node), g._leaf_ptrs(inputs), len(g.leaves), po, pw, wb,
+                                    _stream(stream)))

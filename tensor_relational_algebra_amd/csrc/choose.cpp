@@ -24,42 +24,24 @@
 #include <string>
 #include <vector>
 
-#include "plan.h"
+#include "graph.h"
 
-namespace {
+namespace tra {
 
-struct Cand {
-    std::vector<int32_t> d;  // canonical order
-    int64_t n_tasks;
-    int64_t cost;            // node cost
-    int64_t dp;              // accumulated
-    std::vector<int> pick;   // chosen producer candidate per input slot (-1 = graph input)
-};
-
-struct GNode {
-    std::string name, kind, spec;
-    std::vector<std::string> ops;
-    std::string out, canon, con;
-    int64_t B[128];
-    std::vector<std::string> inputs;
-    std::vector<int> src;    // producer node index per slot, -1 = graph input
-    std::vector<Cand> cands;
-};
-
-int fail(int code, const std::string &m)
+static int fail(int code, const std::string &m)
 {
-    tra::set_error(m);
+    set_error(m);
     return code;
 }
 
-bool key_less(const Cand &a, int64_t ca, const Cand &b, int64_t cb)
+static bool key_less(const Cand &a, int64_t ca, const Cand &b, int64_t cb)
 {
     if (ca != cb) return ca < cb;
     if (a.n_tasks != b.n_tasks) return a.n_tasks < b.n_tasks;
     return a.d < b.d;
 }
 
-int64_t einsum_cost(const std::vector<std::string> &ops, const std::string &out, const std::string &con,
+static int64_t einsum_cost(const std::vector<std::string> &ops, const std::string &out, const std::string &con,
                     const int64_t *B, const int32_t *D)
 {
     std::string all;
@@ -79,7 +61,7 @@ int64_t einsum_cost(const std::vector<std::string> &ops, const std::string &out,
     return n * in + (n / n_agg) * (n_agg - 1) * blk(out);
 }
 
-int64_t node_cost(const GNode &g, const Cand &c)
+static int64_t node_cost(const GNode &g, const Cand &c)
 {
     int32_t D[128];
     for (int i = 0; i < 128; ++i) D[i] = 1;
@@ -92,7 +74,7 @@ int64_t node_cost(const GNode &g, const Cand &c)
     return einsum_cost(g.ops, g.out, g.con, g.B, D);
 }
 
-std::vector<std::string> split(const std::string &s, char sep)
+static std::vector<std::string> split(const std::string &s, char sep)
 {
     std::vector<std::string> v;
     std::string cur;
@@ -118,8 +100,30 @@ int parse_graph(const char *desc, std::vector<GNode> &nodes)
         std::string w;
         while (ls >> w) f.push_back(w);
         if (f.empty() || f[0][0] == '#') continue;
-        if (f.size() != 5) return fail(TRA_E_GRAPH, "a node line needs 5 fields: " + line);
+        if (f.size() < 5) return fail(TRA_E_GRAPH, "a node line needs 5 fields: " + line);
         GNode g;
+        for (size_t o = 5; o < f.size(); ++o) {
+            const std::string &kv = f[o];
+            size_t eq = kv.find('=');
+            if (eq == std::string::npos) return fail(TRA_E_GRAPH, "option without '=': " + kv);
+            std::string k = kv.substr(0, eq), val = kv.substr(eq + 1);
+            auto dt = [&](int &dst) {
+                if (val == "f32") dst = D_F32;
+                else if (val == "bf16") dst = D_BF16;
+                else if (val == "i32") dst = D_I32;
+                else return false;
+                return true;
+            };
+            if (k == "in") {
+                if (!dt(g.in_dtype)) return fail(TRA_E_GRAPH, "unknown dtype " + val);
+            } else if (k == "out") {
+                if (!dt(g.out_dtype)) return fail(TRA_E_GRAPH, "unknown dtype " + val);
+            } else if (k == "scale") {
+                g.scale = std::strtof(val.c_str(), nullptr);
+            } else {
+                return fail(TRA_E_GRAPH, "unknown option " + k);
+            }
+        }
         g.name = f[0];
         g.kind = f[1];
         g.spec = f[2];
@@ -178,7 +182,7 @@ int parse_graph(const char *desc, std::vector<GNode> &nodes)
     return TRA_OK;
 }
 
-void make_candidates(GNode &g, int P)
+static void make_candidates(GNode &g, int P)
 {
     const size_t L = g.canon.size();
     std::vector<std::vector<int32_t>> opts(L);
@@ -211,25 +215,16 @@ void make_candidates(GNode &g, int P)
 }
 
 // part counts of candidate c on the labels `labels` of node g
-std::vector<int32_t> blocking(const GNode &g, const Cand &c, const std::string &labels)
+static std::vector<int32_t> blocking(const GNode &g, const Cand &c, const std::string &labels)
 {
     std::vector<int32_t> b;
     for (char l : labels) b.push_back(c.d[g.canon.find(l)]);
     return b;
 }
 
-}  // namespace
-
-extern "C" int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_cap, int64_t *cost_out)
+int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &d_out, int64_t &cost)
 {
-    if (!graph_desc || !d_out) return fail(TRA_E_NULL, "graph_desc / d_out is NULL");
     if (P < 1) return fail(TRA_E_GRAPH, "P must be >= 1");
-    std::vector<GNode> nodes;
-    int rc = parse_graph(graph_desc, nodes);
-    if (rc) return rc;
-    size_t need = 0;
-    for (auto &g : nodes) need += g.canon.size();
-    if ((size_t)d_cap < need) return fail(TRA_E_BUFFER, "d_out needs " + std::to_string(need) + " entries");
     for (auto &g : nodes) {
         make_candidates(g, P);
         if (g.cands.empty()) return fail(TRA_E_NO_CANDIDATE, "no admissible partition vector for " + g.name);
@@ -308,9 +303,32 @@ extern "C" int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_c
         for (size_t s = 0; s < nodes[v].src.size(); ++s)
             if (nodes[v].src[s] >= 0) stack.push_back({nodes[v].src[s], nodes[v].cands[i].pick[s]});
     }
+    d_out.clear();
+    for (size_t v = 0; v < nodes.size(); ++v) d_out.push_back(nodes[v].cands[chosen[v]].d);
+    cost = rg.cands[ri].dp;
+    return TRA_OK;
+}
+
+}  // namespace tra
+
+using namespace tra;
+
+extern "C" int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_cap, int64_t *cost_out)
+{
+    if (!graph_desc || !d_out) return fail(TRA_E_NULL, "graph_desc / d_out is NULL");
+    std::vector<GNode> nodes;
+    int rc = parse_graph(graph_desc, nodes);
+    if (rc) return rc;
+    size_t need = 0;
+    for (auto &g : nodes) need += g.canon.size();
+    if ((size_t)d_cap < need) return fail(TRA_E_BUFFER, "d_out needs " + std::to_string(need) + " entries");
+    std::vector<std::vector<int32_t>> ds;
+    int64_t cost = 0;
+    rc = run_dp(nodes, P, ds, cost);
+    if (rc) return rc;
     size_t pos = 0;
-    for (size_t v = 0; v < nodes.size(); ++v)
-        for (int32_t x : nodes[v].cands[chosen[v]].d) d_out[pos++] = x;
-    if (cost_out) *cost_out = rg.cands[ri].dp;
+    for (auto &dv : ds)
+        for (int32_t x : dv) d_out[pos++] = x;
+    if (cost_out) *cost_out = cost;
     return TRA_OK;
 }

@@ -1,0 +1,37 @@
+// graph.h -- EinGraph description, parsing and the partition-vector DP
+// (internal; shared by the chooser and the graph executor).
+#pragma once
+#include <string>
+#include <vector>
+
+#include "plan.h"
+
+namespace tra {
+
+struct Cand {
+    std::vector<int32_t> d;  // canonical order
+    int64_t n_tasks = 0;
+    int64_t cost = 0;        // node cost
+    int64_t dp = 0;          // accumulated
+    std::vector<int> pick;   // chosen producer candidate per input slot (-1 = graph input)
+};
+
+struct GNode {
+    std::string name, kind, spec;
+    std::vector<std::string> ops;
+    std::string out, canon, con;
+    int64_t B[128];
+    std::vector<std::string> inputs;
+    std::vector<int> src;    // producer node index per slot, -1 = graph input
+    std::vector<Cand> cands;
+    int in_dtype = D_BF16, out_dtype = D_F32;
+    float scale = 1.0f;
+};
+
+// Parse the node-per-line description (see tra_choose in tra.h).
+int parse_graph(const char *desc, std::vector<GNode> &nodes);
+
+// Choose d for every node (canonical label order per node) and the total cost.
+int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &d_out, int64_t &cost);
+
+}  // namespace tra

@@ -15,6 +15,7 @@ bfloat16 with round-to-nearest-even (torch's conversion).
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -163,6 +164,25 @@ class MhaCase:
     h: int = 32
     dh: int = 128
     wid: int = WL_MHA
+
+    def graph_desc(self) -> str:
+        """The layer as an EinGraph in the node-per-line format of the C ABI.
+
+        Storage dtypes: the inputs, weights and the projected / weighted
+        tensors are bf16; scores and their logsumexp are fp32; the output is
+        fp32.  The score node carries the 1/sqrt(dh) scale."""
+        s, a, h, d = self.s, self.a, self.h, self.dh
+        pb = f"s={s},a={a},h={h},d={d}"
+        return "\n".join([
+            f"Q_proj einsum sa,ahd->shd {pb} @Q,@W_Q in=bf16 out=bf16",
+            f"K_proj einsum sa,ahd->shd {pb} @K,@W_K in=bf16 out=bf16",
+            f"V_proj einsum sa,ahd->shd {pb} @V,@W_V in=bf16 out=bf16",
+            f"Scores einsum shd,thd->hst s={s},t={s},h={h},d={d} Q_proj,K_proj in=bf16 out=f32 "
+            f"scale={1.0 / math.sqrt(d)!r}",
+            f"Attn softmax hst->hst h={h},s={s},t={s} Scores in=f32 out=bf16",
+            f"O einsum hst,thd->shd h={h},s={s},t={s},d={d} Attn,V_proj in=bf16 out=bf16",
+            f"Output einsum shd,ahd->sa s={s},h={h},d={d},a={a} O,@W_O in=bf16 out=f32",
+        ])
 
     def make_inputs(self) -> Dict[str, torch.Tensor]:
         t = {}

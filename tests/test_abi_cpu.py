@@ -200,3 +200,34 @@ def test_choose_errors():
     with pytest.raises(tra.TraError) as e:
         tra.tra_choose("A einsum ij,jk->ik i=2,j=2,k=2 @X,B", 1)
     assert e.value.code == -13
+
+
+def test_graph_plan_uses_the_chooser_and_lays_out_the_workspace():
+    from tensor_relational_algebra_amd import workloads as wl
+    for case, p in ((wl.MHA, 256), (wl.MHA_SMALL, 16)):
+        desc = case.graph_desc()
+        g = tra.tra_graph_plan(desc, p)
+        ds, cost = tra.tra_choose(desc, p)
+        assert g.info.cost == cost and g.info.n_nodes == 7
+        assert [g.node_d(i) for i in range(7)] == ds
+        assert [n for n, _, _ in g.leaves] == ["Q", "W_Q", "K", "W_K", "V", "W_V", "W_O"]
+        assert g.info.out_elems == case.s * case.a
+        assert g.info.workspace_bytes > 0
+    # explicit d: all ones everywhere needs no repartition between nodes
+    desc = wl.MHA_SMALL.graph_desc()
+    ones = [1] * sum(len(tra.tra_canonical_labels(l.split()[2])) if l.split()[1] == "einsum" else 3
+                     for l in desc.splitlines())
+    g = tra.tra_graph_plan(desc, 1, ones)
+    assert g.info.n_repartitions == 0
+
+
+def test_graph_plan_errors():
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_graph_plan("A softmax hst->hst h=2,s=2,t=2 @S in=bf16 out=bf16", 1)
+    assert e.value.code == -13
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_graph_plan("A einsum ij,jk->ik i=4,j=4,k=4 @X,@Y wat=1", 1)
+    assert e.value.code == -13
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_graph_plan("A einsum ij,jk->ik i=4,j=4,k=4 @X,@Y", 1, [1, 1])
+    assert e.value.code == -5
