@@ -13,11 +13,13 @@
 // a sum over q block products, folded here in registers.)
 //
 // Operands are read in place from their relation layout through per-
-// sub-dimension strides.  An operand stored contiguously along the
-// contracted labels ("K-major") is staged in LDS as [row][k] and fed to the
-// matrix cores with 16-byte LDS reads; one stored contiguously along its
-// output labels ("MN-major") is staged as [k][row] exactly as it arrives and
-// transposed on the way to the matrix cores by gfx950's ds_read_b64_tr_b16.
+// sub-dimension strides, copied straight from HBM into a four-stage LDS ring
+// (global_load_lds_dwordx4: no register staging, three k-tiles in flight).
+// An operand stored contiguously along the contracted labels ("K-major") is
+// staged as [row][k] and fed to the matrix cores with 16-byte LDS reads; one
+// stored contiguously along its output labels ("MN-major") is staged as
+// [k][row] exactly as it arrives and transposed on the way to the matrix
+// cores by gfx950's ds_read_b64_tr_b16.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -30,21 +32,23 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef short shortx8_t __attribute__((ext_vector_type(8)));
 
 struct MfmaCfg {
-    int bm, bn, bk, wm, wn;
+    int bm, bn, wm, wn;
 };
 // variant 0: 256x256 tile, 8 waves (2 x 4), wave tile 128x64
 // variant 1: 128x128 tile, 4 waves (2 x 2), wave tile 64x64
 // variant 2: 64x64 tile, 4 waves (2 x 2), wave tile 32x32
 __host__ __device__ constexpr MfmaCfg mfma_cfg(int v)
 {
-    return v == 0 ? MfmaCfg{256, 256, 64, 2, 4} : v == 1 ? MfmaCfg{128, 128, 64, 2, 2} : MfmaCfg{64, 64, 64, 2, 2};
+    return v == 0 ? MfmaCfg{256, 256, 2, 4} : v == 1 ? MfmaCfg{128, 128, 2, 2} : MfmaCfg{64, 64, 2, 2};
 }
+constexpr int MF_BK = 32;       // k per pipeline stage
+constexpr int MF_STAGES = 4;    // LDS ring: 3 k-tiles in flight while one is consumed
 
 TileShape mfma_tile_shape(int variant)
 {
     if (variant < 0 || variant > 2) return {0, 0, 0};
     MfmaCfg c = mfma_cfg(variant);
-    return {c.bm, c.bn, c.bk};
+    return {c.bm, c.bn, MF_BK};
 }
 
 __device__ __forceinline__ void mfma_tile_of(uint32_t nb, uint32_t tiles_n, uint32_t &tm, uint32_t &tn)
@@ -61,97 +65,90 @@ __device__ __forceinline__ void mfma_tile_of(uint32_t nb, uint32_t tiles_n, uint
     tn = r / gs;
 }
 
-// LDS staging.  K-major operand: [rows][BK + 8] (16-byte fragment reads,
-// conflict-free with the 144-byte row pitch).  MN-major operand: [BK][rows +
-// 32]: rows are written as they arrive from HBM and transposed on the way out
-// by ds_read_b64_tr_b16 (the 64-element pad spreads the four k-rows one read
-// touches over distinct banks).
-template <int V>
-constexpr int lds_elems(bool kmajor, bool is_a)
-{
-    constexpr MfmaCfg c = mfma_cfg(V);
-    int rows = is_a ? c.bm : c.bn;
-    return kmajor ? rows * (c.bk + 8) : c.bk * (rows + 32);
-}
-
-template <int V, bool BKM>
-constexpr size_t mfma_lds_bytes()
-{
-    return 2 * (size_t)(lds_elems<V>(true, true) + lds_elems<V>(BKM, false)) * 2;
-}
-
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef short shortx4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Power-of-two digit layouts split cleanly at aligned boundaries: for r0 a
-// multiple of 2^b and d < 2^b, off(r0 + d) = off(r0) + off(d).  So every
-// per-thread offset below is computed once, and each k-tile only adds the
-// uniform term off(k0).
+// LDS layouts (no padding; 16-byte granules permuted by XOR so that the
+// matrix-core fragment reads hit distinct banks):
+//  * K-major operand, [row][32 k]: 4 granules per row, granule c of row r
+//    stored at c ^ swz_k(r);
+//  * MN-major operand, [32 k][row]: granule g of k-row k stored at
+//    g ^ swz_n(k), read back transposed by ds_read_b64_tr_b16.
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+template <int ROWS>
+__device__ __forceinline__ int swz_n(int k) { return ((k & 3) << 2) & (ROWS / 8 - 1); }
 
-// Loader for one operand tile (rows x BK) into LDS, 16-byte vectors.
-//   KM: operand contiguous along k -> LDS [row][k]; else along rows -> LDS [k][row].
-template <int ROWS, int BK, int NT, bool KM, int T>
-struct TileLoader {
-    static constexpr int NV = ROWS * BK / 8 / NT;   // vectors per thread
-    static constexpr int LD = KM ? BK + 8 : ROWS + 32;
-    int32_t off[NV];      // row part + in-tile k part of each vector's source offset
-    int32_t lds_off[NV];  // destination element offset in the stage
-    uint4 reg[NV];
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Fragment reads issued as raw LDS instructions.  The compiler neither waits
+// for them nor reorders them against each other; lds_ready() then waits for
+// all of them and hands every fragment register through an asm that follows
+// the wait, so no consumer can be scheduled before the data has arrived.
+// (Left to itself the compiler waits for every in-flight global->LDS copy
+// before an LDS read it cannot prove disjoint from them.)
+__device__ __forceinline__ u32x4_t ds_read16(uint32_t addr)
+{
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ u32x2_t ds_read8_tr(uint32_t addr)
+{
+    u32x2_t v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <typename T>
+__device__ __forceinline__ void lds_ready(T &v)
+{
+    asm volatile("" : "+v"(v));
+}
+
+// Per-thread plan of the direct global -> LDS copies of one operand tile
+// (ROWS x 32 k).  Copy r of thread tid moves 16-byte granule p = r*NT + tid of
+// the stage; a wave's 64 copies land on 64 consecutive granules, so the LDS
+// address is wave-uniform and the source address carries the permutation.
+template <int ROWS, int NT, bool KM, int T>
+struct DmaPlan {
+    static constexpr int N = ROWS * MF_BK / 8 / NT;   // copies per thread per stage
+    int32_t src[N];                                    // source offset minus the k-tile term
 
     __device__ __forceinline__ void init(const Pow2Group &g_rows, const Pow2Group &gk, uint32_t r0, int32_t base,
                                          int tid)
     {
         const int32_t rbase = p2off<0>(g_rows, r0) + base;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            int q = tid + NT * i;
-            int row, col;
+        for (int i = 0; i < N; ++i) {
+            const int p = i * NT + tid;
             if constexpr (KM) {
-                col = (q % (BK / 8)) * 8;
-                row = q / (BK / 8);
-                lds_off[i] = row * LD + col;
+                const int row = p >> 2, c = (p & 3) ^ swz_k(p >> 2);
+                src[i] = rbase + p2off<0>(g_rows, row) + p2off<T>(gk, c * 8);
             } else {
-                row = (q % (ROWS / 8)) * 8;
-                col = q / (ROWS / 8);
-                lds_off[i] = col * LD + row;
+                const int k = p / (ROWS / 8), gl = (p % (ROWS / 8)) ^ swz_n<ROWS>(p / (ROWS / 8));
+                src[i] = rbase + p2off<0>(g_rows, gl * 8) + p2off<T>(gk, k);
             }
-            off[i] = rbase + p2off<0>(g_rows, row) + p2off<T>(gk, col);
         }
     }
-    __device__ __forceinline__ void load(const uint16_t *__restrict__ p, int32_t koff)
+    __device__ __forceinline__ void issue(const uint16_t *__restrict__ g, int32_t koff, uint16_t *stage, int wave)
     {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) reg[i] = *(const uint4 *)(p + off[i] + koff);
-    }
-    __device__ __forceinline__ void store(uint16_t *lds)
-    {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) *(uint4 *)&lds[lds_off[i]] = reg[i];
+        for (int i = 0; i < N; ++i)
+            __builtin_amdgcn_global_load_lds(g + src[i] + koff, (lds_void_t *)(stage + (i * NT + wave * 64) * 8), 16,
+                                             0, 0);
     }
 };
-
-// A fragment (K-major staging): 8 consecutive k of row r.
-template <int LD>
-__device__ __forceinline__ bf16x8_t frag_k(const uint16_t *lds, int r, int k)
-{
-    uint4 u = *(const uint4 *)&lds[r * LD + k];
-    return __builtin_bit_cast(bf16x8_t, u);
-}
-
-// B fragment from [k][n] staging via two transposing reads.  Lane l (group
-// g = l/16, s = l%16) addresses row kb + s/4, columns nb + 4*(s%4)..+3 with
-// kb = k + 8*(g/2), nb = n + 16*(g%2); lane l then holds B[k + 8*(l/32) + e][n + l%32].
-template <int LD>
-__device__ __forceinline__ bf16x8_t frag_tr(const uint16_t *lds, int n, int k, int lane)
-{
-    const int g = lane >> 4, sl = lane & 15;
-    const int kb = k + 8 * (g >> 1) + (sl >> 2), nb = n + 16 * (g & 1) + 4 * (sl & 3);
-    typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
-    const uint16_t *p0 = lds + kb * LD + nb;
-    bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4 *)(p0));
-    bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4 *)(p0 + 4 * LD));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 template <int V, bool BKM, typename TO>
 __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf16(
@@ -159,15 +156,19 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     float *__restrict__ ws)
 {
     constexpr MfmaCfg C = mfma_cfg(V);
-    constexpr int BM = C.bm, BN = C.bn, BK = C.bk, WM = C.wm, WN = C.wn;
+    constexpr int BM = C.bm, BN = C.bn, BK = MF_BK, WM = C.wm, WN = C.wn;
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-    constexpr int A_EL = lds_elems<V>(true, true), B_EL = lds_elems<V>(BKM, false);
-    constexpr int LDA = BK + 8, LDB = BKM ? BK + 8 : BN + 32;
-    constexpr int STAGE = A_EL + B_EL;
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    // one array per stage: the compiler can then see that a load into one
+    // stage does not touch the stage being read
+    __shared__ __attribute__((aligned(16))) uint16_t sa0[BM * BK], sa1[BM * BK], sa2[BM * BK], sa3[BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sb0[BN * BK], sb1[BN * BK], sb2[BN * BK], sb3[BN * BK];
+    // stage index -> array (always called with a constant, so it folds away)
+    auto SA = [&](int G) -> uint16_t * { return G == 0 ? sa0 : G == 1 ? sa1 : G == 2 ? sa2 : sa3; };
+    auto SB = [&](int G) -> uint16_t * { return G == 0 ? sb0 : G == 1 ? sb1 : G == 2 ? sb2 : sb3; };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const uint32_t tiles_n = v.gn.total / BN;
     const uint32_t nb = (v.gm.total / BM) * tiles_n;
@@ -177,12 +178,13 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     const uint32_t bidx = blockIdx.y;
     const int32_t bx = p2off<0>(v.gb, bidx), by = p2off<1>(v.gb, bidx), bz = p2off<2>(v.gb, bidx);
     const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
-    const uint32_t kend = kbeg + (uint32_t)v.k_per_split;
+    const uint32_t nk = (uint32_t)v.k_per_split / BK;
 
-    TileLoader<BM, BK, NT, true, 0> la;
-    TileLoader<BN, BK, NT, BKM, 1> lb;
-    la.init(v.gm, v.gk, m0, bx, tid);
-    lb.init(v.gn, v.gk, n0, by, tid);
+    DmaPlan<BM, NT, true, 0> da;
+    DmaPlan<BN, NT, BKM, 1> db;
+    da.init(v.gm, v.gk, m0, bx, tid);
+    db.init(v.gn, v.gk, n0, by, tid);
+    constexpr int L = DmaPlan<BM, NT, true, 0>::N + DmaPlan<BN, NT, BKM, 1>::N;
 
     floatx16_t acc[TM][TN];
 #pragma unroll
@@ -192,63 +194,109 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    la.load(x, p2off<0>(v.gk, kbeg));
-    lb.load(y, p2off<1>(v.gk, kbeg));
-    la.store(smem);
-    lb.store(smem + A_EL);
-    __syncthreads();
-
     const int r_lane = lane & 31, k_lane = (lane >> 5) * 8;
     const int a_row0 = wm * (BM / WM) + r_lane;
     const int b_col0 = wn * (BN / WN);
-    int stage = 0;
-    for (uint32_t k0 = kbeg; k0 < kend; k0 += BK) {
-        const bool more = k0 + BK < kend;
-        if (more) {
-            la.load(x, p2off<0>(v.gk, k0 + BK));
-            lb.load(y, p2off<1>(v.gk, k0 + BK));
-        }
-        const uint16_t *a_s = smem + stage * STAGE, *b_s = a_s + A_EL;
-        bf16x8_t af[2][TM], bf[2][TN];
+
+    auto issue = [&](int stg, uint32_t t) {
+        const uint32_t k0 = kbeg + t * BK;
+        da.issue(x, p2off<0>(v.gk, k0), SA(stg), wave);
+        db.issue(y, p2off<1>(v.gk, k0), SB(stg), wave);
+    };
+    // Both k-steps of a stage: all fragment reads first, one wait, then the
+    // matrix-core work.
+    auto compute = [&](int stg) {
+        const uint32_t a_b = lds_addr(SA(stg)), b_b = lds_addr(SB(stg));
+        u32x4_t af[2][TM];
+        u32x4_t bk[2][TN];
+        u32x2_t bt[2][TN][2];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[0][i] = frag_k<LDA>(a_s, a_row0 + i * 32, k_lane);
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (BKM) bf[0][j] = frag_k<LDB>(b_s, b_col0 + j * 32 + r_lane, k_lane);
-            else bf[0][j] = frag_tr<LDB>(b_s, b_col0 + j * 32, 0, lane);
-        }
+            for (int i = 0; i < TM; ++i) {
+                const int r = a_row0 + i * 32, c = ((ks * 16 + k_lane) >> 3) ^ swz_k(r);
+                af[ks][i] = ds_read16(a_b + (r * MF_BK + c * 8) * 2);
+            }
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int cur = ks & 1, nxt = cur ^ 1;
-            if (ks + 1 < BK / 16) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i) af[nxt][i] = frag_k<LDA>(a_s, a_row0 + i * 32, (ks + 1) * 16 + k_lane);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    if constexpr (BKM) bf[nxt][j] = frag_k<LDB>(b_s, b_col0 + j * 32 + r_lane, (ks + 1) * 16 + k_lane);
-                    else bf[nxt][j] = frag_tr<LDB>(b_s, b_col0 + j * 32, (ks + 1) * 16, lane);
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (BKM) {
+                    const int r = b_col0 + j * 32 + r_lane, c = ((ks * 16 + k_lane) >> 3) ^ swz_k(r);
+                    bk[ks][j] = ds_read16(b_b + (r * MF_BK + c * 8) * 2);
+                } else {
+                    const int g = lane >> 4, sl = lane & 15;
+                    const int kb = ks * 16 + 8 * (g >> 1) + (sl >> 2);
+                    const int nb = b_col0 + j * 32 + 16 * (g & 1) + 4 * (sl & 3);
+                    const uint32_t e0 = kb * BN + (((nb >> 3) ^ swz_n<BN>(kb)) << 3) + (nb & 7);
+                    bt[ks][j][0] = ds_read8_tr(b_b + e0 * 2);
+                    bt[ks][j][1] = ds_read8_tr(b_b + (e0 + 4 * BN) * 2);
                 }
             }
+        }
+        lds_wait_all();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) lds_ready(af[ks][i]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (BKM) {
+                    lds_ready(bk[ks][j]);
+                } else {
+                    lds_ready(bt[ks][j][0]);
+                    lds_ready(bt[ks][j][1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
-        }
-        if (more) {
-            la.store(smem + (stage ^ 1) * STAGE);
-            lb.store(smem + (stage ^ 1) * STAGE + A_EL);
-        }
-        __syncthreads();
-        stage ^= 1;
+                for (int j = 0; j < TN; ++j) {
+                    bf16x8_t a = __builtin_bit_cast(bf16x8_t, af[ks][i]);
+                    bf16x8_t b;
+                    if constexpr (BKM) {
+                        b = __builtin_bit_cast(bf16x8_t, bk[ks][j]);
+                    } else {
+                        u32x4_t w = {bt[ks][j][0][0], bt[ks][j][0][1], bt[ks][j][1][0], bt[ks][j][1][1]};
+                        b = __builtin_bit_cast(bf16x8_t, w);
+                    }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i][j], 0, 0, 0);
+                }
+    };
+    // The copy is issued unconditionally: past the last k-tile it re-reads that
+    // tile into the free stage (never consumed), which keeps the number of
+    // copies in flight, and so the wait below, the same at every step.
+    auto step = [&](int G, uint32_t t) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
+        // the barrier intrinsic does not order memory for the optimiser: keep
+        // every LDS access on its side of it
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue((G + 3) % MF_STAGES, min(t + 3, nk - 1));
+        compute(G);
+    };
+    issue(0, 0);
+    issue(1, min(1u, nk - 1));
+    issue(2, min(2u, nk - 1));
+    uint32_t t = 0;
+    for (; t + MF_STAGES <= nk; t += MF_STAGES) {
+        step(0, t);
+        step(1, t + 1);
+        step(2, t + 2);
+        step(3, t + 3);
     }
+    if (t < nk) step(0, t);
+    if (t + 1 < nk) step(1, t + 1);
+    if (t + 2 < nk) step(2, t + 2);
 
     // Epilogue.  Accumulator element e of lane l holds row
     // 8*(e/4) + 4*(l/32) + e%4 and column l%32 of its 32x32 block.
-    const bool split = v.split > 1;
-    float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
     // row = (wave row + 32 i + 8 (e/4)) + (4 (l/32) + e%4): a multiple of 8 plus
     // a part below 8, so its offset splits into a wave-uniform and a lane part.
+    const bool split = v.split > 1;
+    float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
     const int32_t zm0 = p2off<1>(v.gm, m0) + bz, zn0 = p2off<1>(v.gn, n0);
     int32_t lo[4];
 #pragma unroll
@@ -273,24 +321,37 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     }
 }
 
+// Every (tile, operand layout, output dtype) combination the launcher can
+// pick, instantiated explicitly (the host pass otherwise emits only some).
+#define TRA_MFMA_INST(V, BKM, TO)                                                                              \
+    template __global__ void k_mfma_bf16<V, BKM, TO>(GemmView, const uint16_t *, const uint16_t *, TO *, float *);
+TRA_MFMA_INST(0, true, float)
+TRA_MFMA_INST(0, false, float)
+TRA_MFMA_INST(0, true, bf16_t)
+TRA_MFMA_INST(0, false, bf16_t)
+TRA_MFMA_INST(1, true, float)
+TRA_MFMA_INST(1, false, float)
+TRA_MFMA_INST(1, true, bf16_t)
+TRA_MFMA_INST(1, false, bf16_t)
+TRA_MFMA_INST(2, true, float)
+TRA_MFMA_INST(2, false, float)
+TRA_MFMA_INST(2, true, bf16_t)
+TRA_MFMA_INST(2, false, bf16_t)
+#undef TRA_MFMA_INST
+
 int launch_split_fold(const tra_plan_s &p, const void *ws, void *z, void *stream);
 
 template <int V, bool BKM, typename TO>
 static int launch_v(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, hipStream_t s)
 {
     constexpr MfmaCfg C = mfma_cfg(V);
-    constexpr size_t lds = mfma_lds_bytes<V, BKM>();
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_mfma_bf16<V, BKM, TO>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return (int)e;
-        attr_set = true;
-    }
     const GemmView &v = p.gv;
     dim3 grid((v.gm.total / C.bm) * (v.gn.total / C.bn), v.gb.total, v.split);
-    hipLaunchKernelGGL((k_mfma_bf16<V, BKM, TO>), grid, dim3(C.wm * C.wn * 64), lds, s, v,
-                       (const uint16_t *)x, (const uint16_t *)y, (TO *)z, (float *)ws);
+    // naming the kernel through a pointer makes the host pass emit its launch
+    // stub for every instantiation
+    void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *) = k_mfma_bf16<V, BKM, TO>;
+    hipLaunchKernelGGL(kern, grid, dim3(C.wm * C.wn * 64), 0, s, v, (const uint16_t *)x, (const uint16_t *)y,
+                       (TO *)z, (float *)ws);
     return (int)hipGetLastError();
 }
 

@@ -123,6 +123,129 @@ __global__ __launch_bounds__(256) void k_rowreduce(RowDesc g, int join, int agg,
     }
 }
 
+// Four consecutive elements of a tensor (16 bytes of fp32 / int32, 8 bytes of bf16).
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+    static __device__ __forceinline__ void load(const float *p, float v[4])
+    {
+        float4 u = *(const float4 *)p;
+        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    }
+    static __device__ __forceinline__ void store(float *p, const float v[4]) { *(float4 *)p = float4{v[0], v[1], v[2], v[3]}; }
+};
+template <> struct Vec4<bf16_t> {
+    static __device__ __forceinline__ void load(const bf16_t *p, float v[4])
+    {
+        uint2 u = *(const uint2 *)p;
+        v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+        v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void store(bf16_t *p, const float v[4])
+    {
+        uint2 u;
+        u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(uint2 *)p = u;
+    }
+};
+template <> struct Vec4<int32_t> {
+    static __device__ __forceinline__ void load(const int32_t *p, int32_t v[4])
+    {
+        int4 u = *(const int4 *)p;
+        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    }
+    static __device__ __forceinline__ void store(int32_t *p, const int32_t v[4]) { *(int4 *)p = int4{v[0], v[1], v[2], v[3]}; }
+};
+
+// Aggregate NONE, power-of-two digits: each thread owns groups of 4
+// consecutive outputs (contiguous in X and Z; Y contiguous or broadcast).
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void k_elemwise_p2(ElemDesc g, int join, int two, const TI *__restrict__ x,
+                                                     const TI *__restrict__ y, TO *__restrict__ z)
+{
+    using A = typename Scalar<TI>::acc;
+    const uint32_t n_vec = (uint32_t)(g.n_out / 4);
+    const uint32_t stride = gridDim.x * blockDim.x;
+#pragma unroll 2
+    for (uint32_t v = blockIdx.x * blockDim.x + threadIdx.x; v < n_vec; v += stride) {
+        const uint32_t o = v * 4;
+        const int32_t xo = p2off<0>(g.out_p2, o);
+        A xv[4], yv[4] = {A(0), A(0), A(0), A(0)}, r[4];
+        Vec4<TI>::load(x + xo, xv);
+        if (two) {
+            const int32_t yo = p2off<1>(g.out_p2, o);
+            if (g.y_step) Vec4<TI>::load(y + yo, yv);
+            else yv[0] = yv[1] = yv[2] = yv[3] = Scalar<TI>::load(y, yo);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[i] = join_any(join, xv[i], yv[i]);
+            if constexpr (!std::is_same<A, int32_t>::value) r[i] *= g.post_scale;
+        }
+        if constexpr (std::is_same<A, int32_t>::value || std::is_same<TO, float>::value || std::is_same<TO, bf16_t>::value)
+            Vec4<TO>::store(z + o, r);
+    }
+}
+
+// Row reduction, power-of-two digits: one wavefront per output; each lane
+// folds 4 consecutive elements per step (one 16-byte load), the contracted
+// keys outermost in ascending order; lanes are combined by a butterfly.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void k_rowreduce_p2(RowDesc g, int join, int agg, int two,
+                                                      const TI *__restrict__ x, const TI *__restrict__ y,
+                                                      TO *__restrict__ z)
+{
+    using A = typename Scalar<TI>::acc;
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t n_waves = (gridDim.x * blockDim.x) >> 6;
+    const uint32_t inner = (uint32_t)g.inner, n_outer = (uint32_t)g.n_outer;
+    for (uint32_t o = wave; o < (uint32_t)g.n_out; o += n_waves) {
+        const int32_t xo = p2off<0>(g.out_p2, o), yo = two ? p2off<1>(g.out_p2, o) : 0;
+        Fold<A> f;
+        f.init(agg);
+        for (uint32_t c = 0; c < n_outer; ++c) {
+            const int32_t xc = xo + p2off<0>(g.outer_p2, c);
+            const int32_t yc = two ? yo + p2off<1>(g.outer_p2, c) : 0;
+#pragma unroll 4
+            for (uint32_t e = lane * 4; e < inner; e += 256) {
+                A v[4], w[4] = {A(0), A(0), A(0), A(0)};
+                Vec4<TI>::load(x + xc + e, v);
+                if (two) {
+                    if (g.inner_sy) Vec4<TI>::load(y + yc + e, w);
+                    else w[0] = w[1] = w[2] = w[3] = Scalar<TI>::load(y, yc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = join_any(join, v[i], w[i]);
+                if constexpr (std::is_same<A, float>::value) {
+                    if (agg == A_LSE) {
+                        const float lm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+                        const float nm = fmaxf(f.m, lm);
+                        if (nm != -INFINITY) {
+                            f.s = f.s * __expf(f.m - nm) + __expf(v[0] - nm) + __expf(v[1] - nm) +
+                                  __expf(v[2] - nm) + __expf(v[3] - nm);
+                            f.m = nm;
+                        }
+                        continue;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) f.add(agg, v[i]);
+            }
+        }
+        if constexpr (std::is_same<A, float>::value) {
+            for (int off = 32; off >= 1; off >>= 1) {
+                float om = __shfl_xor(f.m, off, 64);
+                float os = __shfl_xor(f.s, off, 64);
+                f.merge(agg, om, os);
+            }
+        } else {
+            for (int off = 32; off >= 1; off >>= 1) f.merge(agg, __shfl_xor(f.m, off, 64), 0);
+        }
+        if (lane == 0) Scalar<TO>::store(z, o, (A)f.result(agg, g.post_scale));
+    }
+}
+
 // ---------------------------------------------------------------- split fold
 // Deterministic cross-workgroup aggregation: partial s of output o sits at
 // ws[s * n + o]; fold s = 0..S-1 in order, then finish.
@@ -203,6 +326,13 @@ int launch_generic(const tra_plan_s &p, const void *x, const void *y, void *z, v
 int launch_elemwise(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream)
 {
     hipStream_t s = (hipStream_t)stream;
+    if (p.el.p2) {
+        int grid = grid_for(p.el.n_out / 4 / 2);
+        TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
+                        hipLaunchKernelGGL((k_elemwise_p2<TI, TO>), dim3(grid), dim3(256), 0, s, p.el, p.join,
+                                           p.n_ops == 2 ? 1 : 0, (const TI *)x, (const TI *)y, (TO *)z));
+        return (int)hipGetLastError();
+    }
     int grid = grid_for(p.el.n_out / p.el.vec);
     TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
                     hipLaunchKernelGGL((k_elemwise<TI, TO>), dim3(grid), dim3(256), 0, s, p.el, p.join,
@@ -213,6 +343,13 @@ int launch_elemwise(const tra_plan_s &p, const void *x, const void *y, void *z, 
 int launch_rowreduce(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream)
 {
     hipStream_t s = (hipStream_t)stream;
+    if (p.row.p2) {
+        int grid = grid_for(p.row.n_out * 64);
+        TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
+                        hipLaunchKernelGGL((k_rowreduce_p2<TI, TO>), dim3(grid), dim3(256), 0, s, p.row, p.join,
+                                           p.agg, p.n_ops == 2 ? 1 : 0, (const TI *)x, (const TI *)y, (TO *)z));
+        return (int)hipGetLastError();
+    }
     int grid = grid_for(p.row.n_out * 64);
     TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
                     hipLaunchKernelGGL((k_rowreduce<TI, TO>), dim3(grid), dim3(256), 0, s, p.row, p.join, p.agg,

@@ -305,6 +305,11 @@ static bool lower_generic(tra_plan_s &p)
             if (okx && oky && f.ext % 4 == 0) vec = 4;
         }
         p.el.vec = vec;
+        p.el.p2 = 0;
+        if (vec == 4 && so.back().st[0] == 1 && p.info.z_elems < (int64_t)1 << 31 && to_pow2(so, p.el.out_p2)) {
+            p.el.p2 = 1;
+            p.el.y_step = p.n_ops == 2 ? (int32_t)so.back().st[1] : 0;
+        }
         p.kernel = TRA_KERNEL_ELEMWISE;
         return true;
     }
@@ -320,6 +325,11 @@ static bool lower_generic(tra_plan_s &p)
         p.row.inner = sc.back().ext;
         p.row.inner_sy = sc.back().st[1];
         p.row.post_scale = p.post_scale;
+        p.row.p2 = 0;
+        const int64_t sy = sc.back().st[1];
+        if (p.row.inner % 256 == 0 && (p.n_ops == 1 || sy == 0 || sy == 1) && to_pow2(so, p.row.out_p2) &&
+            to_pow2(outer, p.row.outer_p2))
+            p.row.p2 = 1;
         p.kernel = TRA_KERNEL_ROWREDUCE;
     }
     return true;

@@ -75,6 +75,10 @@ struct RowDesc {
     int64_t inner;
     int64_t inner_sy;
     float post_scale;
+    // power-of-two form (p2 != 0): out_p2 / outer_p2 with st[0] = X, st[1] = Y;
+    // inner is a multiple of 256 and inner_sy is 0 or 1
+    int32_t p2;
+    Pow2Group out_p2, outer_p2;
 };
 
 // Elementwise (aggregate NONE): `out` as in GenericDesc; vec elements of the
@@ -85,6 +89,11 @@ struct ElemDesc {
     int64_t n_out;
     int32_t vec;
     float post_scale;
+    // power-of-two form (p2 != 0): out_p2 with st[0] = X, st[1] = Y; groups of
+    // 4 outputs share one decomposition, X stride 1 along them, Y stride y_step (0 or 1)
+    int32_t p2;
+    int32_t y_step;
+    Pow2Group out_p2;
 };
 
 // Repartition: destination positions enumerated in the destination layout;
