@@ -44,6 +44,38 @@ SQDIST_FLOP_PER_TERM = 3
 SQDIST_OPS_PER_TERM = 2
 VALU_SQDIST_PEAK = VALU_LANE_OPS / SQDIST_OPS_PER_TERM * SQDIST_FLOP_PER_TERM  # 117.96e12 flop/s
 
+# HBM traffic of the squared-distance join kernel, from two rocprofv3 --pmc runs of
+# `bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extra` (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, mean over the dispatches), scaled by what the same
+# counters read for a plain 1 GiB same-blocking copy (`bench.py --copy-probe 1024`):
+# FETCH_SIZE read 524,300 KiB and WRITE_SIZE 1,048,576 KiB for 1,048,576 KiB moved,
+# hence factors 2.0 and 1.0.  The record holds only while the kernel sources hash to
+# `src_sha`; otherwise the kernel has changed since the counters were taken and
+# `traffic` is reported as null.
+TRAFFIC_SRCS = ("tensor_relational_algebra_amd/csrc/k_valu_tile.hip",
+                "tensor_relational_algebra_amd/csrc/device_common.h",
+                "tensor_relational_algebra_amd/csrc/tra_internal.h",
+                "tensor_relational_algebra_amd/csrc/plan.h")
+TRAFFIC_SQDIST = {"src_sha": "1abae16c97a92928", "fetch_kib": 71508.3, "write_kib": 262144.0,
+                  "fetch_factor": 2.0, "write_factor": 1.0,
+                  "profile": "profiles/valu_tile_sqdist_8192x256x8192_hbm_traffic.md"}
+
+
+def _src_sha(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(rec) -> "float | None":
+    """Calibrated HBM bytes per launch, or None when the record is stale or absent."""
+    if rec["src_sha"] is None or rec["src_sha"] != _src_sha(TRAFFIC_SRCS):
+        return None
+    return 1024.0 * (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"])
+
 
 def _parse():
     ap = argparse.ArgumentParser()
@@ -53,7 +85,27 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra workloads to run")
+    ap.add_argument("--src-sha", action="store_true", help="print the kernel-source hash the traffic record keys on")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB once per step with tra_repartition (same blocking on both sides); "
+                         "the known-size reference for the HBM traffic counters")
     return ap.parse_args()
+
+
+def _copy_probe(mib: int, reps: int) -> None:
+    """A plain device copy of known size through the library's re-blocking kernel."""
+    import torch
+
+    import tensor_relational_algebra_amd as tra
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    shape = [n // 1024, 1024]
+    for _ in range(reps):
+        tra.tra_repartition(src, shape, [1, 1], [1, 1], dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src[-1024:], dst[-1024:])
+    print(json.dumps({"copy_probe_bytes_each_way": n * 4, "reps": reps}), flush=True)
 
 
 def _events_time(fn, reps: int, stream) -> float:
@@ -75,6 +127,12 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.src_sha:
+        print(_src_sha(TRAFFIC_SRCS))
+        return
+    if args.copy_probe:
+        _copy_probe(args.copy_probe, max(args.steps, 1))
+        return
     import numpy as np
     import torch
 
@@ -136,6 +194,7 @@ def main():
     value = step_ops / (ms_per_step * 1e-3) / 1e9
     sq_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in sq_ms]))
     achieved = terms * SQDIST_FLOP_PER_TERM / (sq_launch_ms * 1e-3)
+    traffic = _traffic(TRAFFIC_SQDIST)
 
     out = {
         "metric": "einsum GFLOP/s & % of MFMA peak; repartition GB/s & % HBM peak (1 GPU)",
@@ -155,8 +214,11 @@ def main():
                    "i": B["i"], "j": B["j"], "k": B["k"], "d": [d["i"], d["j"], d["j"], d["k"]],
                    "kernel": plan_sq.kernel},
         "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": round(VALU_SQDIST_PEAK / 1e12, 3),
-                     "unit": "TFLOP/s", "frac": round(achieved / VALU_SQDIST_PEAK, 4), "traffic": None,
-                     "kernel": "k_valu_tile<sqdiff,sum>", "launch_ms": round(sq_launch_ms, 4)},
+                     "unit": "TFLOP/s", "frac": round(achieved / VALU_SQDIST_PEAK, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": "k_valu_tile<sqdiff,sum>", "launch_ms": round(sq_launch_ms, 4),
+                     # algorithmic bytes: X and Y once, D once
+                     "algorithmic_bytes": (B["i"] * B["j"] + B["j"] * B["k"] + B["i"] * B["k"]) * 4},
     }
 
     # zero-copy check of the timed outputs on a few rows against the oracle

@@ -160,7 +160,9 @@ __global__ __launch_bounds__(VT_THREADS) void k_valu_tile(GemmView v, const T *_
         for (int j = 0; j < 8; ++j) acc[i][j] = vinit<AGG, A>();
 
     const int tx = tid % 16, ty = tid / 16;
-    using V4 = typename std::conditional<std::is_same<A, float>::value, float4, int4>::type;
+    // Native 4-vectors (not HIP's union-based float4/int4): those stop the
+    // compiler from keeping the prefetch registers out of scratch memory.
+    typedef A V4 __attribute__((ext_vector_type(4)));
     V4 ra[4], rb[4];
 
     auto gload = [&](uint32_t k0) {
