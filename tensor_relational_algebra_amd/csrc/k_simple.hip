@@ -266,6 +266,9 @@ __global__ __launch_bounds__(256) void k_split_fold(const A *__restrict__ ws, in
 }
 
 // ---------------------------------------------------------------- repartition
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // Destination positions are enumerated in the destination's own layout, so
 // writes are sequential; each digit of the destination index maps to a
 // source stride.  U is the copy unit (vec elements).
@@ -282,18 +285,64 @@ __global__ __launch_bounds__(256) void k_repartition(RepartDesc r, int vec, cons
     }
 }
 
-// Power-of-two destination digits: 32-bit shifts and masks.
-template <typename U>
+// Power-of-two destination digits: 32-bit shifts and masks.  Each workgroup
+// copies one contiguous chunk of 256 * UPT destination units; every thread
+// issues its UPT independent source loads before any store, so that many
+// 16-byte loads are in flight per wave (the copy is bound by HBM latency x
+// bandwidth, not by issue).  Full chunks take no bounds checks; only the last
+// workgroup's chunk can be partial.  NT marks both sides as streaming
+// (non-temporal), for tensors far larger than the caches.
+template <bool NT, typename U>
+__device__ __forceinline__ U rep_load(const U *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT, typename U>
+__device__ __forceinline__ void rep_store(U *p, U v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+template <typename U, int UPT, bool NT>
 __global__ __launch_bounds__(256) void k_repartition_p2(Pow2Group g, int lvec, uint32_t n_units,
                                                         const U *__restrict__ src, U *__restrict__ dst)
 {
-    const uint32_t stride = gridDim.x * blockDim.x;
-    uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
-#pragma unroll 4
-    for (; u < n_units; u += stride) {
-        const int32_t so = p2off<0>(g, u << lvec);
-        dst[u] = src[so >> lvec];
+    const uint32_t base = blockIdx.x * (256u * UPT) + threadIdx.x;
+    if (base + 256u * (UPT - 1) < n_units) {
+        U v[UPT];
+#pragma unroll
+        for (int i = 0; i < UPT; ++i)
+            v[i] = rep_load<NT>(src + (p2off<0>(g, (base + 256u * i) << lvec) >> lvec));
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) rep_store<NT>(dst + base + 256u * i, v[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) {
+            const uint32_t u = base + 256u * i;
+            if (u < n_units) dst[u] = src[p2off<0>(g, u << lvec) >> lvec];
+        }
     }
+}
+
+template <typename U>
+static void launch_rep_p2(const Pow2Group &g, int lvec, int64_t n_units, const void *src, void *dst,
+                          hipStream_t s)
+{
+    // Measured on MI355X for a 512 MiB fp32 re-blocking: 8 loads in flight per
+    // thread with streaming hints reach 5.7 TB/s (a plain copy 6.3 TB/s);
+    // smaller tensors keep more workgroups and cacheable accesses, since
+    // their consumer usually reads them next.
+    const int64_t bytes = n_units * (int64_t)sizeof(U);
+    const uint32_t n = (uint32_t)n_units;
+#define TRA_REP_GO(UPT, NT)                                                                               \
+    hipLaunchKernelGGL((k_repartition_p2<U, UPT, NT>), dim3((unsigned)((n_units + 256 * UPT - 1) / (256 * UPT))), \
+                       dim3(256), 0, s, g, lvec, n, (const U *)src, (U *)dst)
+    if (bytes >= (64ll << 20)) TRA_REP_GO(8, true);
+    else if (n_units >= 256 * 256 * 4) TRA_REP_GO(4, false);
+    else TRA_REP_GO(1, false);
+#undef TRA_REP_GO
 }
 
 static int grid_for(int64_t work, int per_block = 256)
@@ -381,8 +430,9 @@ int launch_repartition(const RepartDesc &r, int esz, const void *src, void *dst,
     hipStream_t s = (hipStream_t)stream;
     const int unit = r.vec * esz;
     const int64_t n_units = r.n_elems / r.vec;
-    // power-of-two digits (at most kP2Max of them): shift/mask path
-    bool p2 = n_units < (1ll << 31) && r.dst.n <= kP2Max;
+    // power-of-two digits (at most kP2Max of them): shift/mask path.  The
+    // element index and the source offset are 32-bit there.
+    bool p2 = r.n_elems < (1ll << 31) && r.dst.n <= kP2Max;
     Pow2Group g{};
     g.n = r.dst.n;
     uint32_t sh = 0;
@@ -397,16 +447,12 @@ int launch_repartition(const RepartDesc &r, int esz, const void *src, void *dst,
     if (p2) {
         int lvec = 0;
         while ((1 << lvec) < r.vec) ++lvec;
-        int grid = grid_for(n_units / 4 + 1);
-#define TRA_REP_P2(U) hipLaunchKernelGGL((k_repartition_p2<U>), dim3(grid), dim3(256), 0, s, g, lvec, \
-                                          (uint32_t)n_units, (const U *)src, (U *)dst)
         switch (unit) {
-        case 16: TRA_REP_P2(uint4); break;
-        case 8: TRA_REP_P2(uint2); break;
-        case 4: TRA_REP_P2(uint32_t); break;
-        default: TRA_REP_P2(uint16_t); break;
+        case 16: launch_rep_p2<u32x4>(g, lvec, n_units, src, dst, s); break;
+        case 8: launch_rep_p2<u32x2>(g, lvec, n_units, src, dst, s); break;
+        case 4: launch_rep_p2<uint32_t>(g, lvec, n_units, src, dst, s); break;
+        default: launch_rep_p2<uint16_t>(g, lvec, n_units, src, dst, s); break;
         }
-#undef TRA_REP_P2
         return (int)hipGetLastError();
     }
     int grid = grid_for(n_units);
