@@ -83,6 +83,27 @@ __device__ __forceinline__ A vstep2(A acc, A a0, A b0, A a1, A b1)
         return fmaf(a1, b1, fmaf(a0, b0, acc));
     } else if constexpr (AGG == A_SUM) {
         return vfold<AGG>(vfold<AGG>(acc, vjoin<JOIN>(a0, b0)), vjoin<JOIN>(a1, b1));
+    } else if constexpr (std::is_same<A, int32_t>::value) {
+        // one 3-input max / min per two terms, written as the instruction so
+        // that the compiler cannot re-associate the chain into 2-input ones
+        // (which costs 3 half-rate instructions per 4 terms instead of 2)
+        if constexpr (JOIN == J_ADD) {
+            // the two sums and their fold as one block: the sums never wait
+            // in registers for a later fold
+            int32_t t0, t1;
+            if constexpr (AGG == A_MAX)
+                asm("v_add_u32 %1, %3, %4\n\tv_add_u32 %2, %5, %6\n\tv_max3_i32 %0, %0, %1, %2"
+                    : "+v"(acc), "=&v"(t0), "=&v"(t1) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+            else
+                asm("v_add_u32 %1, %3, %4\n\tv_add_u32 %2, %5, %6\n\tv_min3_i32 %0, %0, %1, %2"
+                    : "+v"(acc), "=&v"(t0), "=&v"(t1) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+            return acc;
+        }
+        const int32_t t0 = vjoin<JOIN>(a0, b0), t1 = vjoin<JOIN>(a1, b1);
+        int32_t r;
+        if constexpr (AGG == A_MAX) asm("v_max3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(acc), "v"(t0), "v"(t1));
+        else asm("v_min3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(acc), "v"(t0), "v"(t1));
+        return r;
     } else {
         return vfold<AGG>(acc, vfold<AGG>(vjoin<JOIN>(a0, b0), vjoin<JOIN>(a1, b1)));
     }
