@@ -316,17 +316,21 @@ def _extra(tra, wl, dev, stream, only):
 
     if want("mha"):
         res["mha"] = _mha(tra, wl, dev, stream)
+    if want("mha_fused"):
+        res["mha_fused"] = _mha(tra, wl, dev, stream, fuse=True)
     torch.cuda.empty_cache()
     return res
 
 
-def _mha(tra, wl, dev, stream):
+def _mha(tra, wl, dev, stream, fuse=False):
     """The attention layer as an EinGraph, d chosen for P = 256; per-node time
-    (its input repartitions included) against the node's own roof."""
+    (its input repartitions included) against the node's own roof.  With
+    fuse=True the scores -> softmax -> weighted-sum chain runs as one kernel,
+    timed on the weighted-sum node (the scores and softmax nodes enqueue nothing)."""
     import torch
     case = wl.MHA
     desc = case.graph_desc()
-    g = tra.tra_graph_plan(desc, 256)
+    g = tra.tra_graph_plan_ex(desc, 256, None, tra.GRAPH_FUSE_ATTENTION if fuse else 0)
     inputs = {k: v.to(dev) for k, v in case.make_inputs().items()}
     ws = g.workspace(dev)
     out = torch.empty(g.info.out_elems, dtype=torch.float32, device=dev)
@@ -338,6 +342,10 @@ def _mha(tra, wl, dev, stream):
     # bytes the HBM-bound nodes must move at least: scores write fp32 S; softmax reads
     # S twice (logsumexp, then normalise) and writes bf16 Attn; weighted sum reads Attn
     sbytes = {"Scores": 4.0 * h * s * s, "Attn": 2 * 4.0 * h * s * s + 2.0 * h * s * s, "O": 2.0 * h * s * s}
+    if fuse:
+        # the fused node does the scores and the weighted sum; nothing is HBM-bound
+        flops = dict(flops, O=2 * attn_fl, Scores=0.0)
+        sbytes = {}
     for _ in range(2):
         tra.tra_graph_execute(g, inputs, out, ws)
     reps = 5
@@ -354,7 +362,7 @@ def _mha(tra, wl, dev, stream):
         ms = sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
         total += ms
         e = {"us": round(ms * 1e3, 1), "d": g.node_d(i)}
-        if n in flops:
+        if n in flops and flops[n] > 0:
             e["TFLOP/s"] = round(flops[n] / ms / 1e9, 1)
             e["frac_bf16_mfma_peak"] = round(flops[n] / (ms * 1e-3) / BF16_MFMA_PEAK, 4)
         if n in sbytes:
@@ -363,7 +371,8 @@ def _mha(tra, wl, dev, stream):
         nodes[n] = e
     total_fl = sum(flops.values())
     return {"ms": round(total, 3), "TFLOP/s": round(total_fl / total / 1e9, 1), "nodes": nodes,
-            "repartitions": g.info.n_repartitions, "workspace_GB": round(g.info.workspace_bytes / 1e9, 2)}
+            "repartitions": g.info.n_repartitions, "fused_chains": g.info.n_fused,
+            "workspace_GB": round(g.info.workspace_bytes / 1e9, 2)}
 
 
 if __name__ == "__main__":

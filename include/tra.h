@@ -261,9 +261,36 @@ typedef struct {
     int32_t out_dtype;
     int64_t cost;             /* cost-model value of the chosen partition vectors */
     int32_t n_repartitions;   /* inter-node repartitions the plan contains */
+    int32_t n_fused;          /* attention chains run as one fused kernel */
 } tra_graph_info_t;
 
 int tra_graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d_len, tra_graph_t *out_graph);
+
+/*
+ * tra_graph_plan_ex -- tra_graph_plan with option flags.
+ *
+ * TRA_GRAPH_FUSE_ATTENTION: every chain
+ *     S = scale * sum_d Q[s,h,d] K[t,h,d]   (einsum, 2 inputs, bf16 operands)
+ *     A = softmax over t of S              (softmax node on S, its only consumer)
+ *     O = sum_t A[h,s,t] V[t,h,e]           (einsum, A as first input, its only consumer)
+ * (labels named freely, in any order; one head label h, head dimension
+ * d = e in {32, 64, 128}, S a multiple of 128 and T of 64, power-of-two
+ * partition counts, Q/K/V contiguous along the head dimension) is run as one
+ * kernel that folds the logsumexp over the t blocks online and never writes S
+ * or A (the "super-operator" fusion that the EinDecomp page's closing remarks
+ * point to).  Q, K and V are read in the blockings of their producers (no
+ * repartition), O is written in the O node's blocking.  The score and softmax
+ * nodes then enqueue nothing in tra_graph_run_node.  Chains that do not match
+ * run unfused; tra_graph_info reports how many were fused.
+ * The partition vectors are still chosen per node by the cost model.
+ * Numerics: the probabilities enter the weighted sum as bf16 (the unfused
+ * path also stores A in bf16), relative to the running maximum rather than
+ * normalised; O is divided by the fp32 sum at the end.
+ * Errors: those of tra_graph_plan; TRA_E_OP for an unknown flag.
+ */
+#define TRA_GRAPH_FUSE_ATTENTION 1
+int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d_all, int d_len, int flags,
+                      tra_graph_t *out_graph);
 
 /* Sizes of a planned graph.  Errors: TRA_E_NULL. */
 int tra_graph_info(tra_graph_t graph, tra_graph_info_t *info);

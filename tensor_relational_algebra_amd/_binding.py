@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "tra_cost": ([ctypes.c_char_p, P, P, I, P], I),
             "tra_choose": ([ctypes.c_char_p, I, P, I, P], I),
             "tra_graph_plan": ([ctypes.c_char_p, I, P, I, P], I),
+            "tra_graph_plan_ex": ([ctypes.c_char_p, I, P, I, I, P], I),
             "tra_graph_info": ([P, P], I),
             "tra_graph_node_d": ([P, I, P, I], I),
             "tra_graph_leaf": ([P, I, ctypes.c_char_p, I, P, P], I),
@@ -241,7 +242,7 @@ def tra_choose(graph_desc: str, p: int) -> Tuple[List[List[int]], int]:
 class GraphInfo(ctypes.Structure):
     _fields_ = [("n_nodes", ctypes.c_int32), ("n_leaves", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
                 ("out_elems", ctypes.c_int64), ("out_dtype", ctypes.c_int32), ("cost", ctypes.c_int64),
-                ("n_repartitions", ctypes.c_int32)]
+                ("n_repartitions", ctypes.c_int32), ("n_fused", ctypes.c_int32)]
 
 
 class Graph:
@@ -281,12 +282,27 @@ class Graph:
             self.handle = None
 
 
+GRAPH_FUSE_ATTENTION = 1
+
+
 def tra_graph_plan(graph_desc: str, p: int = 256, d_all: Optional[Sequence[int]] = None) -> Graph:
     h = ctypes.c_void_p()
     if d_all is None:
         _check(lib().tra_graph_plan(graph_desc.encode(), int(p), None, 0, ctypes.byref(h)))
     else:
         _check(lib().tra_graph_plan(graph_desc.encode(), int(p), _i32(d_all), len(d_all), ctypes.byref(h)))
+    return Graph(h.value)
+
+
+def tra_graph_plan_ex(graph_desc: str, p: int = 256, d_all: Optional[Sequence[int]] = None,
+                      flags: int = 0) -> Graph:
+    """tra_graph_plan with option flags (GRAPH_FUSE_ATTENTION)."""
+    h = ctypes.c_void_p()
+    if d_all is None:
+        _check(lib().tra_graph_plan_ex(graph_desc.encode(), int(p), None, 0, int(flags), ctypes.byref(h)))
+    else:
+        _check(lib().tra_graph_plan_ex(graph_desc.encode(), int(p), _i32(d_all), len(d_all), int(flags),
+                                       ctypes.byref(h)))
     return Graph(h.value)
 
 

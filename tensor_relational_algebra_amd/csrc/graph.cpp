@@ -46,6 +46,77 @@ struct NodeExec {
     size_t out = 0, lse = 0, scratch = 0, scratch_bytes = 0;
     int64_t out_elems = 0;
     int out_dtype = D_F32;
+    // attention fusion: 1 = scores / softmax node folded into a later node
+    // (enqueues nothing); 2 = weighted-sum node that runs the whole chain
+    int fused = 0;
+    AttnDesc att{};
+    Slot qkv[3];                   // Q, K, V sources, read in place
+};
+
+// An attention chain found in the graph (node indices) and its kernel descriptor.
+struct AttnChain {
+    int u = -1, a = -1, w = -1;    // scores, softmax, weighted sum
+    AttnDesc desc{};
+};
+
+static bool is_pow2_i(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+static int log2_i(int64_t x)
+{
+    int r = 0;
+    while ((int64_t)1 << r < x) ++r;
+    return r;
+}
+
+// One label as carried by one tensor: in-block stride, key stride, block extent.
+struct LabelUse {
+    int64_t bs, ks, blk;
+};
+
+// Digits of one label shared by tensors blocked differently: the index's bits
+// are cut at every tensor's block boundary, so that within one bit range each
+// tensor's offset is linear (all in-block or all key).
+static bool label_digits(int64_t ext, const std::vector<LabelUse> &uses, Pow2Group &g)
+{
+    if (!is_pow2_i(ext)) return false;
+    std::vector<int> cuts = {0, log2_i(ext)};
+    for (const LabelUse &u : uses) {
+        if (!is_pow2_i(u.blk)) return false;
+        cuts.push_back(log2_i(u.blk));
+    }
+    std::sort(cuts.begin(), cuts.end());
+    cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+    std::vector<SubDim> v;
+    for (int i = (int)cuts.size() - 1; i >= 1; --i) {
+        const int lo = cuts[i - 1], hi = cuts[i];
+        SubDim sd{(uint32_t)1 << (hi - lo), {0, 0, 0}};
+        for (size_t t = 0; t < uses.size(); ++t) {
+            const int split = log2_i(uses[t].blk);
+            sd.st[t] = lo >= split ? uses[t].ks << (lo - split) : uses[t].bs << lo;
+        }
+        v.push_back(sd);
+    }
+    return to_pow2(v, g);
+}
+
+// A tensor operand as stored: its labels (in some node's letters), the
+// extents and its partition vector, both indexed by label character.
+struct Stored {
+    std::string lab;
+    int64_t B[128];
+    int32_t d[128];
+    LabelUse use(char c) const
+    {
+        int64_t bs[kMaxRank], ks[kMaxRank];
+        relation_strides(lab, B, d, bs, ks);
+        const size_t p = lab.find(c);
+        return {bs[p], ks[p], B[(int)c] / d[(int)c]};
+    }
+    int64_t elems() const
+    {
+        int64_t n = 1;
+        for (char c : lab) n *= B[(int)c];
+        return n;
+    }
 };
 
 }  // namespace tra
@@ -60,6 +131,7 @@ struct tra_graph_s {
     int root = -1;
     int64_t cost = 0;
     int n_repart = 0;
+    int n_fused = 0;
 
     ~tra_graph_s()
     {
@@ -79,9 +151,180 @@ static size_t bump(size_t &top, size_t bytes)
     return at;
 }
 
+// Resolve node v's input slot s to its producer output or graph input, with
+// no repartition (the fused kernel reads every operand in its stored blocking).
+static int source_slot(tra_graph_s *g, int v, int s, Slot &sl)
+{
+    const GNode &nd = g->nodes[v];
+    sl = Slot{};
+    sl.dtype = nd.in_dtype;
+    int64_t elems = 1;
+    for (char c : nd.ops[s]) elems *= nd.B[(int)c];
+    if (nd.src[s] >= 0) {
+        sl.node = nd.src[s];
+        return TRA_OK;
+    }
+    const std::string name = nd.inputs[s].substr(1);
+    int li = -1;
+    for (size_t i = 0; i < g->leaves.size(); ++i)
+        if (g->leaves[i] == name) li = (int)i;
+    if (li < 0) {
+        li = (int)g->leaves.size();
+        g->leaves.push_back(name);
+        g->leaf_elems.push_back(elems);
+        g->leaf_dtype.push_back(nd.in_dtype);
+    } else if (g->leaf_elems[li] != elems || g->leaf_dtype[li] != nd.in_dtype) {
+        return gfail(TRA_E_GRAPH, "graph input @" + name + " is used with two shapes or dtypes");
+    }
+    sl.leaf = li;
+    return TRA_OK;
+}
+
+// The weighted-sum node of a fused chain: sources of Q, K (the scores node's
+// inputs) and V, and the node's output buffer in its own blocking.
+static int plan_fused(tra_graph_s *g, int w, size_t &top)
+{
+    NodeExec &e = g->ex[w];
+    const GNode &W = g->nodes[w];
+    const int a = W.src[0], u = g->nodes[a].src[0];
+    int rc = source_slot(g, u, 0, e.qkv[0]);
+    if (!rc) rc = source_slot(g, u, 1, e.qkv[1]);
+    if (!rc) rc = source_slot(g, w, 1, e.qkv[2]);
+    if (rc) return rc;
+    e.out_dtype = W.out_dtype;
+    e.out_elems = 1;
+    for (char c : W.out) e.out_elems *= W.B[(int)c];
+    e.out = bump(top, (size_t)e.out_elems * dsize(W.out_dtype));
+    return TRA_OK;
+}
+
+// The stored form of node v's input slot s (its producer's blocking, or dense
+// for a graph input), in node v's letters.
+static Stored stored_input(const std::vector<GNode> &nodes, const std::vector<std::vector<int32_t>> &ds, int v, int s)
+{
+    const GNode &nd = nodes[v];
+    Stored t;
+    t.lab = nd.ops[s];
+    for (int i = 0; i < 128; ++i) {
+        t.B[i] = nd.B[i];
+        t.d[i] = 1;
+    }
+    const int u = nd.src[s];
+    if (u >= 0)
+        for (size_t i = 0; i < t.lab.size(); ++i) t.d[(int)t.lab[i]] = ds[u][nodes[u].canon.find(nodes[u].out[i])];
+    return t;
+}
+
+// Find every scores -> softmax -> weighted-sum chain the fused kernel can run
+// and build its descriptor; chains that do not fit are left to the unfused path.
+static std::vector<AttnChain> find_attention(const std::vector<GNode> &nodes,
+                                             const std::vector<std::vector<int32_t>> &ds, const std::vector<int> &uses)
+{
+    std::vector<AttnChain> out;
+    const int n = (int)nodes.size();
+    for (int a = 0; a < n; ++a) {
+        const GNode &A = nodes[a];
+        if (A.kind != "softmax" || A.src.size() != 1 || A.src[0] < 0) continue;
+        const int u = A.src[0];
+        const GNode &U = nodes[u];
+        if (U.kind != "einsum" || U.ops.size() != 2 || uses[u] != 1 || uses[a] != 1) continue;
+        int w = -1;
+        for (int x = 0; x < n; ++x)
+            for (int sidx : nodes[x].src)
+                if (sidx == a) w = x;
+        if (w < 0) continue;
+        const GNode &W = nodes[w];
+        if (W.kind != "einsum" || W.ops.size() != 2 || W.src[0] != a || W.src[1] == a) continue;
+        // roles in the scores node: S[h, s, t] from Q[s, h, d] and K[t, h, d]
+        const std::string &Q = U.ops[0], &K = U.ops[1], &S = U.out;
+        if (S.size() != 3 || Q.size() != 3 || K.size() != 3 || U.con.size() != 1) continue;
+        char h = 0, sq = 0, tk = 0;
+        for (char c : S) {
+            const bool inq = Q.find(c) != std::string::npos, ink = K.find(c) != std::string::npos;
+            if (inq && ink) h = c;
+            else if (inq) sq = c;
+            else if (ink) tk = c;
+        }
+        const char dq = U.con[0];
+        if (!h || !sq || !tk || S.back() != tk) continue;
+        // the weighted-sum node in its own letters: A positionally matches S
+        const std::string &Al = W.ops[0], &Vl = W.ops[1], &Ol = W.out;
+        if (Al.size() != 3 || Vl.size() != 3 || Ol.size() != 3 || W.con.size() != 1) continue;
+        const char hw = Al[S.find(h)], sw = Al[S.find(sq)], tw = Al[S.find(tk)];
+        if (W.con[0] != tw) continue;
+        char dv = 0;
+        for (char c : Vl)
+            if (c != tw && c != hw) dv = c;
+        if (!dv || Vl.find(tw) == std::string::npos || Vl.find(hw) == std::string::npos) continue;
+        if (Ol.find(sw) == std::string::npos || Ol.find(hw) == std::string::npos || Ol.find(dv) == std::string::npos)
+            continue;
+        const int64_t Sx = U.B[(int)sq], Tx = U.B[(int)tk], Hx = U.B[(int)h], Dx = U.B[(int)dq];
+        if (W.B[(int)sw] != Sx || W.B[(int)tw] != Tx || W.B[(int)hw] != Hx || W.B[(int)dv] != Dx) continue;
+        if (U.in_dtype != D_BF16 || W.in_dtype != D_BF16 || W.scale != 1.0f) continue;
+        if ((Dx != 32 && Dx != 64 && Dx != 128) || Sx % 128 || Tx % 64) continue;
+
+        const Stored sQ = stored_input(nodes, ds, u, 0), sK = stored_input(nodes, ds, u, 1);
+        const Stored sV = stored_input(nodes, ds, w, 1);
+        Stored sO;
+        sO.lab = Ol;
+        for (int i = 0; i < 128; ++i) {
+            sO.B[i] = W.B[i];
+            sO.d[i] = 1;
+        }
+        for (size_t i = 0; i < W.canon.size(); ++i) sO.d[(int)W.canon[i]] = ds[w][i];
+
+        AttnChain ch;
+        ch.u = u;
+        ch.a = a;
+        ch.w = w;
+        AttnDesc &ad = ch.desc;
+        bool ok = label_digits(Sx, {sQ.use(sq), sO.use(sw)}, ad.gs) &&
+                  label_digits(Tx, {sK.use(tk), sV.use(tw)}, ad.gt) &&
+                  label_digits(Hx, {sQ.use(h), sK.use(h), sV.use(hw)}, ad.gh) &&
+                  label_digits(Hx, {sO.use(hw)}, ad.gho) &&
+                  label_digits(Dx, {sQ.use(dq), sK.use(dq), sV.use(dv)}, ad.gd) &&
+                  label_digits(Dx, {sO.use(dv)}, ad.gdo);
+        if (!ok) continue;
+        // Q, K, V are read in 16-byte runs along the head dimension
+        const int ld = ad.gd.n - 1;
+        if (ld < 0 || ad.gd.mask[ld] + 1 < 8 || ad.gd.st[0][ld] != 1 || ad.gd.st[1][ld] != 1 || ad.gd.st[2][ld] != 1)
+            continue;
+        const int lo = ad.gdo.n - 1;
+        ad.o_vec4 = lo >= 0 && ad.gdo.mask[lo] + 1 >= 4 && ad.gdo.st[0][lo] == 1;
+        if (sQ.elems() >= (1ll << 31) || sK.elems() >= (1ll << 31) || sV.elems() >= (1ll << 31) ||
+            sO.elems() >= (1ll << 31))
+            continue;
+        // the largest offset the kernel can form in each tensor stays inside it
+        auto reach = [](const Pow2Group &g, int t) {
+            int64_t m = 0;
+            for (int i = 0; i < g.n; ++i) m += (int64_t)g.mask[i] * g.st[t][i];
+            return m;
+        };
+        if (reach(ad.gs, 0) + reach(ad.gh, 0) + reach(ad.gd, 0) >= sQ.elems() ||
+            reach(ad.gt, 0) + reach(ad.gh, 1) + reach(ad.gd, 1) >= sK.elems() ||
+            reach(ad.gt, 1) + reach(ad.gh, 2) + reach(ad.gd, 2) >= sV.elems() ||
+            reach(ad.gs, 1) + reach(ad.gho, 0) + reach(ad.gdo, 0) >= sO.elems())
+            continue;   // never true for a valid relation layout
+        ad.S = (uint32_t)Sx;
+        ad.T = (uint32_t)Tx;
+        ad.H = (uint32_t)Hx;
+        ad.D = (uint32_t)Dx;
+        ad.scale_log2 = U.scale * 1.4426950408889634f;
+        out.push_back(ch);
+    }
+    return out;
+}
+
 extern "C" int tra_graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d_len, tra_graph_t *out)
 {
+    return tra_graph_plan_ex(graph_desc, P, d_all, d_len, 0, out);
+}
+
+extern "C" int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d_all, int d_len, int flags,
+                                 tra_graph_t *out)
+{
     if (!graph_desc || !out) return gfail(TRA_E_NULL, "graph_desc / out is NULL");
+    if (flags & ~TRA_GRAPH_FUSE_ATTENTION) return gfail(TRA_E_OP, "unknown graph flag");
     *out = nullptr;
     tra_graph_s *g = new tra_graph_s();
     auto bad = [&](int rc) {
@@ -113,11 +356,26 @@ extern "C" int tra_graph_plan(const char *graph_desc, int P, const int32_t *d_al
         if (!uses[v]) g->root = (int)v;
 
     g->ex.resize(n);
+    if (flags & TRA_GRAPH_FUSE_ATTENTION) {
+        for (const AttnChain &ch : find_attention(g->nodes, ds, uses)) {
+            g->ex[ch.u].fused = 1;
+            g->ex[ch.a].fused = 1;
+            g->ex[ch.w].fused = 2;
+            g->ex[ch.w].att = ch.desc;
+            g->n_fused++;
+        }
+    }
     size_t top = 0;
     for (size_t v = 0; v < n; ++v) {
         GNode &nd = g->nodes[v];
         NodeExec &e = g->ex[v];
         e.d = ds[v];
+        if (e.fused == 1) continue;   // folded into its weighted-sum node
+        if (e.fused == 2) {
+            rc = plan_fused(g, (int)v, top);
+            if (rc) return bad(rc);
+            continue;
+        }
         std::vector<int64_t> bounds;
         for (char c : nd.canon) bounds.push_back(nd.B[(int)c]);
         int32_t dmap[128];
@@ -210,6 +468,7 @@ extern "C" int tra_graph_info(tra_graph_t g, tra_graph_info_t *info)
     info->out_dtype = g->ex[g->root].out_dtype;
     info->cost = g->cost;
     info->n_repartitions = g->n_repart;
+    info->n_fused = g->n_fused;
     return TRA_OK;
 }
 
@@ -234,6 +493,21 @@ extern "C" int tra_graph_leaf(tra_graph_t g, int leaf, char *name, int cap, int6
     return TRA_OK;
 }
 
+// The output node's relation, written dense row-major to `out`.
+static int write_root(tra_graph_t g, int node, void *out, char *ws, void *stream)
+{
+    const NodeExec &e = g->ex[node];
+    const GNode &nd = g->nodes[node];
+    std::vector<int64_t> b;
+    std::vector<int32_t> dz, ones;
+    for (char c : nd.out) {
+        b.push_back(nd.B[(int)c]);
+        dz.push_back(e.d[nd.canon.find(c)]);
+        ones.push_back(1);
+    }
+    return tra_repartition(b.data(), (int)b.size(), dz.data(), ones.data(), e.out_dtype, ws + e.out, out, stream);
+}
+
 extern "C" int tra_graph_run_node(tra_graph_t g, int node, const void *const *leaves, int n_leaves, void *out,
                                   void *workspace, size_t ws_bytes, void *stream)
 {
@@ -247,6 +521,19 @@ extern "C" int tra_graph_run_node(tra_graph_t g, int node, const void *const *le
     char *ws = (char *)workspace;
     NodeExec &e = g->ex[node];
     const GNode &nd = g->nodes[node];
+    if (e.fused == 1) return TRA_OK;   // runs inside its chain's weighted-sum node
+    int rc;
+    if (e.fused == 2) {
+        const void *p[3];
+        for (int i = 0; i < 3; ++i) {
+            const Slot &sl = e.qkv[i];
+            p[i] = sl.node >= 0 ? (const void *)(ws + g->ex[sl.node].out) : leaves[sl.leaf];
+            if (!p[i]) return gfail(TRA_E_NULL, "graph input pointer is NULL");
+        }
+        rc = launch_attention(e.att, e.out_dtype, p[0], p[1], p[2], ws + e.out, stream);
+        if (rc) return gfail(TRA_E_HIP, std::string("fused attention launch: ") + hip_error_text(rc));
+        return node == g->root ? write_root(g, node, out, ws, stream) : TRA_OK;
+    }
     const void *in[2] = {nullptr, nullptr};
     for (size_t s = 0; s < nd.ops.size(); ++s) {
         Slot &sl = e.slot[s];
@@ -262,7 +549,6 @@ extern "C" int tra_graph_run_node(tra_graph_t g, int node, const void *const *le
         }
     }
     void *scratch = e.scratch_bytes ? ws + e.scratch : nullptr;
-    int rc;
     if (e.plan2) {
         rc = tra_execute(e.plan, in[0], nullptr, ws + e.lse, scratch, e.scratch_bytes, stream);
         if (rc) return rc;
@@ -271,18 +557,7 @@ extern "C" int tra_graph_run_node(tra_graph_t g, int node, const void *const *le
         rc = tra_execute(e.plan, in[0], in[1], ws + e.out, scratch, e.scratch_bytes, stream);
     }
     if (rc) return rc;
-    if (node == g->root) {
-        std::vector<int64_t> b;
-        std::vector<int32_t> dz, ones;
-        for (char c : nd.out) {
-            b.push_back(nd.B[(int)c]);
-            dz.push_back(e.d[nd.canon.find(c)]);
-            ones.push_back(1);
-        }
-        rc = tra_repartition(b.data(), (int)b.size(), dz.data(), ones.data(), e.out_dtype, ws + e.out, out, stream);
-        if (rc) return rc;
-    }
-    return TRA_OK;
+    return node == g->root ? write_root(g, node, out, ws, stream) : TRA_OK;
 }
 
 extern "C" int tra_graph_execute(tra_graph_t g, const void *const *leaves, int n_leaves, void *out, void *workspace,

@@ -100,8 +100,7 @@ static int parse_spec(const char *spec, std::vector<std::string> &ops, std::stri
 // Relation-layout strides of a tensor with labels `t`: in-block stride of
 // each label (row-major over block extents) and key stride (row-major over
 // part counts, times the block volume).
-static void relation_strides(const std::string &t, const int64_t *B, const int32_t *d,
-                             int64_t *bs, int64_t *ks)
+void relation_strides(const std::string &t, const int64_t *B, const int32_t *d, int64_t *bs, int64_t *ks)
 {
     int64_t vol = 1;
     for (char c : t) vol *= B[(int)c] / d[(int)c];
@@ -114,11 +113,6 @@ static void relation_strides(const std::string &t, const int64_t *B, const int32
         sk *= d[c];
     }
 }
-
-struct SubDim {
-    uint32_t ext;
-    int64_t st[3];
-};
 
 // Sub-dimensions of a label group: keys first (in group order), then the
 // in-block indices; `tens` are up to three tensors whose strides are recorded.
@@ -156,7 +150,7 @@ static Radix to_radix(const std::vector<SubDim> &v)
     return r;
 }
 
-static bool to_pow2(const std::vector<SubDim> &v, Pow2Group &g)
+bool to_pow2(const std::vector<SubDim> &v, Pow2Group &g)
 {
     g = Pow2Group{};
     if ((int)v.size() > kP2Max) return false;

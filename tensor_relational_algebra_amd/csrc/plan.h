@@ -1,6 +1,7 @@
 // plan.h -- host-side plan object and launcher interface (internal).
 #pragma once
 #include <string>
+#include <vector>
 
 #include "tra.h"
 #include "tra_internal.h"
@@ -42,5 +43,22 @@ TileShape valu_tile_shape(int variant);
 TileShape mfma_tile_shape(int variant);
 
 void set_error(const std::string &msg);
+
+// Relation-layout strides of a tensor with labels `t` (per label: in-block
+// stride bs, key stride ks); B and d are indexed by label character.
+void relation_strides(const std::string &t, const int64_t *B, const int32_t *d, int64_t *bs, int64_t *ks);
+
+// One sub-dimension of a label group: extent and its stride in up to three tensors.
+struct SubDim {
+    uint32_t ext;
+    int64_t st[3];
+};
+// Power-of-two digit group from sub-dimensions (most significant first);
+// false if an extent is not a power of two or there are too many digits.
+bool to_pow2(const std::vector<SubDim> &v, Pow2Group &g);
+
+// Fused attention chain (scores join, softmax over keys, weighted-sum join).
+int launch_attention(const AttnDesc &a, int out_dtype, const void *q, const void *k, const void *v, void *o,
+                     void *stream);
 
 }  // namespace tra

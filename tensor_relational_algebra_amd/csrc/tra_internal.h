@@ -36,6 +36,16 @@ struct Pow2Group {
     int32_t st[3][kP2Max];
 };
 
+// Fused attention: digit groups of the query rows (s), key rows (t), heads
+// (h) and head dimension (d) over the tensors that carry them.  Tensor slots:
+// gs {Q, O}; gt {K, V}; gh {Q, K, V}; gho {O}; gd {Q, K, V}; gdo {O}.
+struct AttnDesc {
+    Pow2Group gs, gt, gh, gho, gd, gdo;
+    uint32_t S, T, H, D;
+    float scale_log2;   // scores scale times log2(e)
+    int32_t o_vec4;     // O's four consecutive d are contiguous (vector stores)
+};
+
 // Join / aggregate codes (mirror tra.h).
 enum Join : int32_t { J_MUL = 0, J_SQDIFF = 1, J_ADD = 2, J_IDENT = 3, J_EXP_SUB = 4 };
 enum Agg : int32_t { A_NONE = 0, A_SUM = 1, A_MAX = 2, A_MIN = 3, A_LSE = 4 };

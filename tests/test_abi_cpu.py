@@ -231,3 +231,30 @@ def test_graph_plan_errors():
     with pytest.raises(tra.TraError) as e:
         tra.tra_graph_plan("A einsum ij,jk->ik i=4,j=4,k=4 @X,@Y", 1, [1, 1])
     assert e.value.code == -5
+
+
+def test_graph_plan_fuses_the_attention_chain():
+    from tensor_relational_algebra_amd import workloads as wl
+    for case, p in ((wl.MHA, 256), (wl.MHA_SMALL, 16), (wl.MhaCase(s=256, a=256, h=8, dh=64), 16)):
+        desc = case.graph_desc()
+        g0 = tra.tra_graph_plan(desc, p)
+        g1 = tra.tra_graph_plan_ex(desc, p, None, tra.GRAPH_FUSE_ATTENTION)
+        assert g0.info.n_fused == 0 and g1.info.n_fused == 1
+        # same chooser result; the scores and softmax buffers are gone
+        assert g1.info.cost == g0.info.cost
+        assert [g1.node_d(i) for i in range(7)] == [g0.node_d(i) for i in range(7)]
+        assert [n for n, _, _ in g1.leaves] == [n for n, _, _ in g0.leaves]
+        s, h = case.s, case.h
+        assert g0.info.workspace_bytes - g1.info.workspace_bytes >= h * s * s * (4 + 2)
+    # a head dimension the kernel is not built for, and a softmax read twice, stay unfused
+    g = tra.tra_graph_plan_ex(wl.MhaCase(s=128, a=128, h=4, dh=48).graph_desc(), 16, None,
+                              tra.GRAPH_FUSE_ATTENTION)
+    assert g.info.n_fused == 0
+    lines = wl.MHA_SMALL.graph_desc().splitlines()
+    lines[5] += " scale=0.5"   # a scaled weighted sum is not the chain the kernel computes
+    assert lines[5].startswith("O einsum")
+    g = tra.tra_graph_plan_ex("\n".join(lines), 16, None, tra.GRAPH_FUSE_ATTENTION)
+    assert g.info.n_fused == 0
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_graph_plan_ex(wl.MHA_SMALL.graph_desc(), 16, None, 2)
+    assert e.value.code == -7

@@ -17,9 +17,9 @@ from tests.gpu_util import DEV, maxnorm_rel_err
 pytestmark = pytest.mark.gpu
 
 
-def _run(case, p=None, d_all=None):
+def _run(case, p=None, d_all=None, fuse=False):
     desc = case.graph_desc()
-    g = tra.tra_graph_plan(desc, p or 1, d_all)
+    g = tra.tra_graph_plan_ex(desc, p or 1, d_all, tra.GRAPH_FUSE_ATTENTION if fuse else 0)
     host = case.make_inputs()
     dev = {k: v.to(DEV) for k, v in host.items()}
     out = tra.tra_graph_execute(g, dev).reshape(case.s, case.a)
@@ -64,3 +64,45 @@ def test_full_layer_sampled_rows():
     err = maxnorm_rel_err(out[rows], want)
     assert err <= 2e-2, err
     assert np.isfinite(out).all()
+
+
+# --- the attention chain fused into one kernel (online logsumexp over t) ---
+
+def test_small_layer_fused_chooser_d():
+    out, host, g = _run(wl.MHA_SMALL, p=16, fuse=True)
+    assert g.info.n_fused == 1
+    want = mha.mha(host)["Output"]
+    assert maxnorm_rel_err(out, want) <= 2e-2
+
+
+def test_small_layer_fused_reads_every_blocking_in_place():
+    case = wl.MHA_SMALL
+    want = mha.mha(case.make_inputs())["Output"]
+    for pick in (lambda c, b: 1, lambda c, b: {"s": 4, "t": 2, "h": 1, "d": 2, "a": 4}[c],
+                 lambda c, b: {"s": 2, "t": 1, "h": 4, "d": 4, "a": 2}[c]):
+        out, _, g = _run(case, d_all=_d_all(case, pick), fuse=True)
+        assert g.info.n_fused == 1
+        err = maxnorm_rel_err(out, want)
+        assert err <= 2e-2, err
+
+
+@pytest.mark.parametrize("s,a,h,dh", [(256, 256, 8, 64), (128, 512, 4, 128), (512, 256, 2, 128)])
+def test_fused_head_dims(s, a, h, dh):
+    case = wl.MhaCase(s=s, a=a, h=h, dh=dh, wid=40 + dh)
+    out, host, g = _run(case, p=16, fuse=True)
+    assert g.info.n_fused == 1
+    want = mha.mha(host)["Output"]
+    err = maxnorm_rel_err(out, want)
+    assert err <= 2e-2, err
+
+
+def test_full_layer_fused_sampled_rows_and_deterministic():
+    case = wl.MHA
+    out, host, g = _run(case, p=256, fuse=True)
+    assert g.info.n_fused == 1
+    rows = np.array([0, 1, 777, 2048, 4095])
+    want = mha.mha(host, rows=rows)["Output"]
+    err = maxnorm_rel_err(out[rows], want)
+    assert err <= 2e-2, err
+    out2, _, _ = _run(case, p=256, fuse=True)
+    assert np.array_equal(out, out2)
