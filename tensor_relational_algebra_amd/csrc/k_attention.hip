@@ -187,29 +187,36 @@ __global__ __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 
     auto tile = [&](const uint16_t *kst, const uint16_t *vst) {
         const uint32_t kb = at_lds_addr(kst), vb = at_lds_addr(vst);
-        // S^T = K Q^T for the two 32-row blocks of the key tile.
+        // S^T = K Q^T for the two 32-row blocks of the key tile; the two
+        // blocks' accumulation chains are interleaved so that consecutive
+        // matrix-core instructions are independent.
         floatx16_t sc[2];
         constexpr int KC = KS < 4 ? KS : 4;   // k steps whose fragments are read together
-        at_static_for<2>([&](auto bbc) {
-            constexpr int bb = decltype(bbc)::value;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) sc[bb][e] = 0.f;
-            at_static_for<KS / KC>([&](auto k0c) {
-                constexpr int k0 = decltype(k0c)::value * KC;
-                u32x4_t kf[KC];
-                at_static_for<KC>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    kf[i] = at_ds_read16<bb * 32 * D * 2>(kb + koff[k0 + i]);
-                });
-                at_lds_wait();
+        at_static_for<KS / KC>([&](auto k0c) {
+            constexpr int k0 = decltype(k0c)::value * KC;
+            u32x4_t kf[2][KC];
+            at_static_for<KC>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                kf[0][i] = at_ds_read16<0>(kb + koff[k0 + i]);
+                kf[1][i] = at_ds_read16<32 * D * 2>(kb + koff[k0 + i]);
+            });
+            at_lds_wait();
 #pragma unroll
-                for (int i = 0; i < KC; ++i) at_ready(kf[i]);
+            for (int i = 0; i < KC; ++i) {
+                at_ready(kf[0][i]);
+                at_ready(kf[1][i]);
+            }
 #pragma unroll
-                for (int i = 0; i < KC; ++i)
-                    sc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[i]),
+            for (int i = 0; i < KC; ++i)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+                    sc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[bb][i]),
                                                                      __builtin_bit_cast(bf16x8_t, qf[k0 + i]), sc[bb],
                                                                      0, 0, 0);
-            });
         });
         // Online logsumexp over this tile's 64 keys of the lane's query column.
         // The running maximum m used in the exponents moves only when a key
@@ -253,29 +260,30 @@ __global__ __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
             }
         l_part += psum;
         // O^T += V^T P^T.  k step kk covers keys 16 kk .. 16 kk + 15 in the order
-        // t = 16 kk + 8 (e'/4) + 4 (l/32) + e'%4 for lane l's element e'.
+        // t = 16 kk + 8 (e'/4) + 4 (l/32) + e'%4 for lane l's element e'.  Per
+        // k step, the DB output blocks are independent accumulation chains.
+        at_static_for<4>([&](auto kkc) {
+            constexpr int kk = decltype(kkc)::value;
+            u32x2_t lo[DB], hi[DB];
 #pragma unroll
-        for (int j = 0; j < DB; ++j) {
-            u32x2_t lo[4], hi[4];
-            at_static_for<4>([&](auto kkc) {
-                constexpr int kk = decltype(kkc)::value;
-                lo[kk] = at_ds_read8_tr<16 * kk * D * 2>(vb + voff[j]);
-                hi[kk] = at_ds_read8_tr<(16 * kk + 8) * D * 2>(vb + voff[j]);
-            });
+            for (int j = 0; j < DB; ++j) {
+                lo[j] = at_ds_read8_tr<16 * kk * D * 2>(vb + voff[j]);
+                hi[j] = at_ds_read8_tr<(16 * kk + 8) * D * 2>(vb + voff[j]);
+            }
             at_lds_wait();
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                at_ready(lo[kk]);
-                at_ready(hi[kk]);
+            for (int j = 0; j < DB; ++j) {
+                at_ready(lo[j]);
+                at_ready(hi[j]);
             }
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const u32x4_t af = {lo[kk][0], lo[kk][1], hi[kk][0], hi[kk][1]};
+            for (int j = 0; j < DB; ++j) {
+                const u32x4_t af = {lo[j][0], lo[j][1], hi[j][0], hi[j][1]};
                 acc_o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af),
                                                                    __builtin_bit_cast(bf16x8_t, pf[kk]), acc_o[j],
                                                                    0, 0, 0);
             }
-        }
+        });
     };
     auto barrier = [&]() {
         asm volatile("" ::: "memory");
