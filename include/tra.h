@@ -96,7 +96,8 @@ typedef enum {
     TRA_KERNEL_ELEMWISE = 1,  /* aggregate NONE, vectorised along the output's last label */
     TRA_KERNEL_ROWREDUCE = 2, /* one wavefront per output element, contiguous contracted run */
     TRA_KERNEL_VALU_TILE = 3, /* register-blocked output tiles on the vector ALUs */
-    TRA_KERNEL_MFMA_BF16 = 4  /* bf16 x bf16 -> fp32 matrix-core tiles (mul + sum only) */
+    TRA_KERNEL_MFMA_BF16 = 4, /* bf16 x bf16 -> fp32 matrix-core tiles (mul + sum only) */
+    TRA_KERNEL_EMPTY = 5      /* the output has no elements: nothing is enqueued */
 } tra_kernel_family;
 
 typedef struct tra_plan_s *tra_plan_t;
@@ -122,14 +123,20 @@ typedef struct {
  *
  *   spec       "xlabels,ylabels->zlabels" or "xlabels->zlabels"; labels are
  *              single ASCII letters; at most 24 distinct labels, rank <= 12.
- *   bounds     n_labels extents B_l in canonical label order.
- *   d          n_labels part counts d_l in canonical order, d_l | B_l.  The
- *              ≥P-tasks rule belongs to the chooser, not here: any d is run.
+ *   bounds     n_labels extents B_l >= 0 in canonical label order.
+ *   d          n_labels part counts d_l in canonical order, d_l | B_l (a zero
+ *              extent takes d_l = 1).  The ≥P-tasks rule belongs to the
+ *              chooser, not here: any d is run.
  *   join_op    tra_join_op; agg_op: tra_agg_op.
  *   in_dtype   dtype of both operands; out_dtype: dtype of Z.  Float
  *              inputs accumulate in fp32, integers in int32.
  *   post_scale multiplies the aggregated value (float only; 1 otherwise).
  *   out_plan   receives a host-only handle (no device work, no HIP call).
+ * Empty tensors: an output with no elements plans to TRA_KERNEL_EMPTY (the
+ * execution enqueues nothing); an empty contracted range (an operand with no
+ * elements, the output not empty) makes every output element post_scale
+ * times the aggregate's identity: 0 for sum, -inf / +inf for float max /
+ * min, INT32_MIN / INT32_MAX for int32 max / min, -inf for lse.
  * Errors: TRA_E_NULL, TRA_E_SPEC, TRA_E_LABELS, TRA_E_DLEN,
  * TRA_E_INDIVISIBLE, TRA_E_DTYPE, TRA_E_OP, TRA_E_RANGE.
  */
@@ -152,6 +159,7 @@ int tra_plan_destroy(tra_plan_t plan);
  *
  *   x_rel, y_rel   operand relations under the plan's d (y_rel NULL for a
  *                  one-operand spec), dtype in_dtype, 16-byte aligned.
+ *                  The pointer of a tensor with no elements may be NULL.
  *   z_rel          output relation under the plan's d restricted to the
  *                  output labels; fully overwritten.  Must not alias inputs.
  *   workspace      device scratch of at least info.workspace_bytes (may be
@@ -168,7 +176,9 @@ int tra_execute(tra_plan_t plan, const void *x_rel, const void *y_rel, void *z_r
  * is the case d_from = all ones).  A pure permutation of elements: every
  * element is read once and written once, bit-exact.
  *
- *   bounds   rank extents; d_from, d_to: rank part counts each.
+ *   bounds   rank extents >= 0; d_from, d_to: rank part counts each (a
+ *            zero extent takes 1).  A tensor with no elements moves
+ *            nothing; src and dst may then be NULL.
  *   dtype    tra_dtype (only its size matters).
  *   src,dst  device relations, 16-byte aligned, non-overlapping.
  * Errors: TRA_E_NULL, TRA_E_DLEN (rank < 1 or > 12), TRA_E_INDIVISIBLE,

@@ -93,6 +93,16 @@ static int next_tuple(int nc, const int32_t *cl, const int64_t *bounds, int64_t 
     return 0;
 }
 
+/* 1 when some contracted label has extent 0: the fold then runs over no
+   terms and the result is the aggregate's identity. */
+static int empty_range(int nc, const int32_t *cl, const int64_t *bounds)
+{
+    for (int p = 0; p < nc; ++p)
+        if (bounds[cl[p]] == 0)
+            return 1;
+    return 0;
+}
+
 static int check_args(int n_labels, int nx, int ny, int nz, int nc, int join, int agg)
 {
     if (n_labels < 1 || n_labels > OR_MAX_LABELS || nx < 0 || ny < 0 || nz < 0 || nc < 0)
@@ -126,6 +136,7 @@ int oracle_einsum_f64(int n_labels, const int64_t *bounds,
     int64_t xs[OR_MAX_LABELS], ys[OR_MAX_LABELS];
     strides_of(nx, xl, bounds, xs);
     strides_of(ny, yl, bounds, ys);
+    const int empty = empty_range(nc, cl, bounds);
 #ifdef _OPENMP
     if (threads > 0)
         omp_set_num_threads(threads);
@@ -143,7 +154,7 @@ int oracle_einsum_f64(int n_labels, const int64_t *bounds,
         } else if (agg == OR_AGG_LSE) {
             /* pass 1: the maximum term; pass 2: the sum of exp(v - max). */
             double m = -INFINITY;
-            do {
+            if (!empty) do {
                 double yv = ny ? y[offset_of(ny, yl, ys, idx)] : 0.0;
                 double v = join_f(join, x[offset_of(nx, xl, xs, idx)], yv);
                 if (v > m) m = v;
@@ -160,7 +171,7 @@ int oracle_einsum_f64(int n_labels, const int64_t *bounds,
             }
         } else {
             double acc = agg == OR_AGG_SUM ? 0.0 : (agg == OR_AGG_MAX ? -INFINITY : INFINITY);
-            do {
+            if (!empty) do {
                 double yv = ny ? y[offset_of(ny, yl, ys, idx)] : 0.0;
                 double v = join_f(join, x[offset_of(nx, xl, xs, idx)], yv);
                 if (agg == OR_AGG_SUM) acc += v;
@@ -189,6 +200,7 @@ int oracle_einsum_i64(int n_labels, const int64_t *bounds,
     int64_t xs[OR_MAX_LABELS], ys[OR_MAX_LABELS];
     strides_of(nx, xl, bounds, xs);
     strides_of(ny, yl, bounds, ys);
+    const int empty = empty_range(nc, cl, bounds);
 #ifdef _OPENMP
     if (threads > 0)
         omp_set_num_threads(threads);
@@ -204,7 +216,7 @@ int oracle_einsum_i64(int n_labels, const int64_t *bounds,
             r = join_i(join, x[offset_of(nx, xl, xs, idx)], yv);
         } else {
             int64_t acc = agg == OR_AGG_SUM ? 0 : (agg == OR_AGG_MAX ? INT64_MIN : INT64_MAX);
-            do {
+            if (!empty) do {
                 int64_t yv = ny ? y[offset_of(ny, yl, ys, idx)] : 0;
                 int64_t v = join_i(join, x[offset_of(nx, xl, xs, idx)], yv);
                 if (agg == OR_AGG_SUM) acc += v;

@@ -180,6 +180,9 @@ def _join(op: str, x, y):
     raise ValueError(op)
 
 
+INT64_MIN, INT64_MAX = -(1 << 63), (1 << 63) - 1
+
+
 def brute_einsum(spec: str, x, y=None, join: str = "mul", agg: str = "sum",
                  post_scale: float = 1.0) -> np.ndarray:
     """Pure-Python loops over every label: for tiny shapes only."""
@@ -203,14 +206,15 @@ def brute_einsum(spec: str, x, y=None, join: str = "mul", agg: str = "sum",
             if contracted:
                 raise ValueError("aggregate none with contracted labels")
             v = terms[0]
+        # a fold over no terms (an empty contracted range) is the identity
         elif agg == "sum":
             v = sum(terms)
         elif agg == "max":
-            v = max(terms)
+            v = max(terms, default=INT64_MIN if is_int else -math.inf)
         elif agg == "min":
-            v = min(terms)
+            v = min(terms, default=INT64_MAX if is_int else math.inf)
         elif agg == "lse":
-            m = max(terms)
+            m = max(terms, default=-math.inf)
             v = m if m == -math.inf else m + math.log(sum(math.exp(t - m) for t in terms))
         else:
             raise ValueError(agg)

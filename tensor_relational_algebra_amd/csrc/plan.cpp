@@ -268,6 +268,22 @@ static bool lower_tile(tra_plan_s &p)
     return false;
 }
 
+// The output of a join over an empty contracted range (an operand with no
+// elements): the generic kernel with no contracted digits reads nothing and
+// writes post_scale times the aggregate's identity to every output element.
+static bool lower_identity(tra_plan_s &p)
+{
+    const std::string *tz[3] = {nullptr, nullptr, nullptr};
+    auto so = group_subdims(p.zl, p.B, p.d, tz);
+    p.gen = GenericDesc{};
+    p.gen.out = to_radix(so);
+    p.gen.n_out = p.info.z_elems;
+    p.gen.n_con = 0;
+    p.gen.post_scale = p.post_scale;
+    p.kernel = TRA_KERNEL_GENERIC;
+    return true;
+}
+
 static bool lower_generic(tra_plan_s &p)
 {
     const std::string *tz[3] = {&p.xl, p.n_ops == 2 ? &p.yl : nullptr, nullptr};
@@ -405,8 +421,10 @@ static int validate_bounds(const std::string &canon, const int64_t *bounds, cons
                                     std::to_string(n_labels));
     for (int i = 0; i < n_labels; ++i) {
         int c = canon[i];
-        if (bounds[i] < 1) return fail(TRA_E_INDIVISIBLE, std::string("extent of '") + (char)c + "' < 1");
-        if (d[i] < 1 || bounds[i] % d[i])
+        if (bounds[i] < 0) return fail(TRA_E_INDIVISIBLE, std::string("extent of '") + (char)c + "' < 0");
+        if (bounds[i] == 0 && d[i] != 1)
+            return fail(TRA_E_INDIVISIBLE, std::string("a zero extent ('") + (char)c + "') takes d = 1");
+        if (d[i] < 1 || (bounds[i] > 0 && bounds[i] % d[i]))
             return fail(TRA_E_INDIVISIBLE, std::string("d of '") + (char)c + "' = " + std::to_string(d[i]) +
                                                " does not divide " + std::to_string(bounds[i]));
         B[c] = bounds[i];
@@ -505,7 +523,14 @@ int tra_plan(const char *spec, const int64_t *bounds, const int32_t *d, int n_la
     std::memset(in.labels, 0, sizeof(in.labels));
     std::memcpy(in.labels, canon.c_str(), canon.size());
 
-    if (!lower_tile(*p) && !lower_generic(*p)) return bad(TRA_E_RANGE, "internal: descriptor exceeds a tensor");
+    if (in.z_elems == 0) {
+        p->kernel = TRA_KERNEL_EMPTY;   // nothing to compute
+    } else if (in.x_elems == 0 || (p->n_ops == 2 && in.y_elems == 0)) {
+        // an empty contracted range: every output element is the aggregate's identity
+        if (!lower_identity(*p)) return bad(TRA_E_RANGE, "internal: descriptor exceeds a tensor");
+    } else if (!lower_tile(*p) && !lower_generic(*p)) {
+        return bad(TRA_E_RANGE, "internal: descriptor exceeds a tensor");
+    }
     in.kernel = p->kernel;
     *out_plan = p;
     return TRA_OK;
@@ -529,11 +554,14 @@ static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 int tra_execute(tra_plan_t p, const void *x, const void *y, void *z, void *ws, size_t ws_bytes, void *stream)
 {
     if (!p) return fail(TRA_E_NULL, "plan is NULL");
-    if (!x || !z || (p->n_ops == 2 && !y)) return fail(TRA_E_NULL, "operand / output pointer is NULL");
+    // pointers of tensors with no elements may be NULL
+    if ((!x && p->info.x_elems) || (!z && p->info.z_elems) || (p->n_ops == 2 && !y && p->info.y_elems))
+        return fail(TRA_E_NULL, "operand / output pointer is NULL");
     if (!aligned16(x) || !aligned16(z) || (y && !aligned16(y)) || (ws && !aligned16(ws)))
         return fail(TRA_E_ALIGN, "device pointers must be 16-byte aligned");
     if (p->info.workspace_bytes > 0 && (!ws || ws_bytes < p->info.workspace_bytes))
         return fail(TRA_E_WORKSPACE, "workspace of " + std::to_string(p->info.workspace_bytes) + " bytes needed");
+    if (p->kernel == TRA_KERNEL_EMPTY) return TRA_OK;
     int err = 0;
     switch (p->kernel) {
     case TRA_KERNEL_MFMA_BF16: err = launch_mfma_bf16(*p, x, y, z, ws, stream); break;
@@ -549,9 +577,20 @@ int tra_execute(tra_plan_t p, const void *x, const void *y, void *z, void *ws, s
 int tra_repartition(const int64_t *bounds, int rank, const int32_t *d_from, const int32_t *d_to, int dtype,
                     const void *src, void *dst, void *stream)
 {
-    if (!bounds || !d_from || !d_to || !src || !dst) return fail(TRA_E_NULL, "NULL argument");
+    if (!bounds || !d_from || !d_to) return fail(TRA_E_NULL, "NULL argument");
     if (rank < 1 || rank > kMaxRank) return fail(TRA_E_DLEN, "rank must be 1..12");
     if (dtype < D_F32 || dtype > D_I32) return fail(TRA_E_DTYPE, "unknown dtype");
+    for (int i = 0; i < rank; ++i) {
+        if (bounds[i] < 0) return fail(TRA_E_INDIVISIBLE, "extent < 0");
+        if (bounds[i] == 0) {   // an empty tensor: nothing to move
+            for (int j = 0; j < rank; ++j)
+                if (d_from[j] < 1 || d_to[j] < 1 || (bounds[j] == 0 && (d_from[j] != 1 || d_to[j] != 1)) ||
+                    (bounds[j] > 0 && (bounds[j] % d_from[j] || bounds[j] % d_to[j])))
+                    return fail(TRA_E_INDIVISIBLE, "part count does not divide extent of dim " + std::to_string(j));
+            return TRA_OK;
+        }
+    }
+    if (!src || !dst) return fail(TRA_E_NULL, "NULL argument");
     if (!aligned16(src) || !aligned16(dst)) return fail(TRA_E_ALIGN, "device pointers must be 16-byte aligned");
     // label i of the tensor is the letter 'a' + i
     int64_t B[128] = {0};

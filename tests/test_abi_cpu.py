@@ -90,7 +90,8 @@ def test_kernel_family_choice():
     (("ij,jk->ik", [2, 2], [1, 1]), -5),                           # wrong label count
     (("ij,jk->ik", [4, 4, 4], [3, 1, 1]), -4),                     # d does not divide
     (("ij,jk->ik", [4, 4, 4], [0, 1, 1]), -4),                     # d < 1
-    (("ij,jk->ik", [4, 0, 4], [1, 1, 1]), -4),                     # extent < 1
+    (("ij,jk->ik", [4, -1, 4], [1, 1, 1]), -4),                    # extent < 0
+    (("ij,jk->ik", [4, 0, 4], [1, 2, 1]), -4),                     # a zero extent takes d = 1
 ])
 def test_plan_validation_errors(args, code):
     spec, b, d = args
@@ -258,3 +259,19 @@ def test_graph_plan_fuses_the_attention_chain():
     with pytest.raises(tra.TraError) as e:
         tra.tra_graph_plan_ex(wl.MHA_SMALL.graph_desc(), 16, None, 2)
     assert e.value.code == -7
+
+
+def test_empty_tensors_plan():
+    # an empty output: nothing to run
+    p = tra.tra_plan("ij,jk->ik", {"i": 0, "j": 4, "k": 5}, {"i": 1, "j": 1, "k": 1})
+    assert p.kernel == "empty" and p.info.z_elems == 0 and p.info.x_elems == 0
+    # an empty contracted range: the output is the aggregate's identity (generic kernel, nothing read)
+    p = tra.tra_plan("ij,jk->ik", {"i": 3, "j": 0, "k": 5}, {"i": 3, "j": 1, "k": 1}, "add", "max", "i32", "i32")
+    assert p.kernel == "generic" and p.info.z_elems == 15 and p.info.x_elems == 0 and p.info.y_elems == 0
+    # a zero extent takes d = 1; negative extents are rejected
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_plan("ij,jk->ik", {"i": 3, "j": 0, "k": 5}, {"i": 1, "j": 2, "k": 1})
+    assert e.value.code == -4
+    with pytest.raises(tra.TraError) as e:
+        tra.tra_plan("ij,jk->ik", {"i": -1, "j": 2, "k": 5}, {"i": 1, "j": 1, "k": 1})
+    assert e.value.code == -4

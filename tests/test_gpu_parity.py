@@ -208,3 +208,49 @@ def test_bitwise_reproducible(case):
     a, _ = run_gpu(case)
     b, _ = run_gpu(case)
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ empty and ragged inputs
+
+@pytest.mark.parametrize("idt,agg", [("f32", "sum"), ("f32", "max"), ("f32", "min"), ("f32", "lse"),
+                                     ("i32", "sum"), ("i32", "max"), ("i32", "min")])
+def test_empty_contracted_range_gives_the_identity(idt, agg):
+    """The fold over no terms is the aggregate's identity; for int32 outputs
+    the identity of max / min is the int32 extreme (the oracle's int64
+    identity does not fit int32)."""
+    join = "add" if agg in ("max", "min") else "mul"
+    case = wl.EinsumCase("empty_j", 301, "ij,jk->ik", {"i": 3, "j": 0, "k": 5}, {"i": 3, "j": 1, "k": 1}, join,
+                         agg, idt, idt, (("int", {"lo": -3, "hi": 3}),) * 2 if idt == "i32" else (wl.U11,) * 2,
+                         2.0 if idt == "f32" else 1.0)
+    xs = case.make_inputs()
+    z, plan = run_gpu(case, xs)
+    assert plan.kernel == "generic"
+    want = ref.einsum(case.spec, xs[0], xs[1], join, agg, case.post_scale)
+    if idt == "i32":
+        want = np.clip(want, np.iinfo(np.int32).min, np.iinfo(np.int32).max)
+        assert np.array_equal(z.numpy().astype(np.int64), want)
+    else:
+        assert np.array_equal(z.double().numpy(), want)
+
+
+def test_empty_output_and_empty_repartition():
+    case = wl.EinsumCase("empty_i", 302, "ij,jk->ik", {"i": 0, "j": 4, "k": 5}, {"i": 1, "j": 2, "k": 5}, "mul",
+                         "sum", "f32", "f32", (wl.U11, wl.U11))
+    z, plan = run_gpu(case)
+    assert plan.kernel == "empty" and z.numel() == 0
+    src = torch.empty(0, dtype=torch.float32, device=DEV)
+    out = tra.tra_repartition(src, [0, 8], [1, 1], [1, 4])
+    assert out.numel() == 0
+
+
+RAGGED = {"i": 300, "j": 70, "k": 260}   # no tile divides these extents
+
+
+@pytest.mark.parametrize("d", [{"i": 1, "j": 1, "k": 1}, {"i": 3, "j": 7, "k": 2}, {"i": 5, "j": 1, "k": 4}])
+@pytest.mark.parametrize("base", [wl.SQDIST, wl.MAXPLUS, wl.MATMUL_F32, wl.GEMM25D],
+                         ids=["sqdist", "maxplus", "matmul", "bf16gemm"])
+def test_ragged_extents(base, d):
+    """Extents no tile divides run on the untiled kernels (generic, or one
+    wavefront per output when the contracted run is contiguous)."""
+    err, plan = check(base.scaled(RAGGED, d))
+    assert plan.kernel in ("generic", "rowreduce")

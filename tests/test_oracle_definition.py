@@ -197,3 +197,27 @@ def test_rejects_undefined_combinations():
         ref.einsum("ij,jk->iq", x, x.T.copy())                           # output label in no operand
     with pytest.raises(ValueError):
         ref.einsum("ii,jk->ik", x, x.T.copy())                           # repeated label
+
+
+def test_empty_ranges_give_the_aggregates_identity():
+    """An empty contracted range folds nothing: sum 0, max -inf, min +inf,
+    lse -inf (float; times post_scale), and INT64_MIN / INT64_MAX / 0 for the
+    integer oracle; an empty output label gives an empty result."""
+    x = np.ones((3, 0))
+    y = np.ones((0, 2))
+    z = ref.einsum("ij,jk->ik", x, y, "mul", "sum")
+    assert z.shape == (3, 2) and np.all(z == 0.0)
+    assert np.all(ref.einsum("ij,jk->ik", x, y, "add", "max") == -np.inf)
+    assert np.all(ref.einsum("ij,jk->ik", x, y, "add", "min") == np.inf)
+    assert np.all(ref.einsum("ij,jk->ik", x, y, "mul", "lse") == -np.inf)
+    assert np.all(ref.einsum("ij,jk->ik", x, y, "add", "max", post_scale=2.0) == -np.inf)
+    xi, yi = np.ones((3, 0), dtype=np.int64), np.ones((0, 2), dtype=np.int64)
+    assert np.all(ref.einsum("ij,jk->ik", xi, yi, "add", "max") == np.iinfo(np.int64).min)
+    assert np.all(ref.einsum("ij,jk->ik", xi, yi, "add", "min") == np.iinfo(np.int64).max)
+    assert np.all(ref.einsum("ij,jk->ik", xi, yi, "mul", "sum") == 0)
+    # an empty output label: nothing to compute
+    z = ref.einsum("ij,jk->ik", np.ones((0, 4)), np.ones((4, 5)), "mul", "sum")
+    assert z.shape == (0, 5)
+    # brute force agrees on the empty range
+    bz = ref.brute_einsum("ij,jk->ik", x, y, "add", "max")
+    assert np.all(np.asarray(bz) == -np.inf)
