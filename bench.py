@@ -313,6 +313,18 @@ def _extra(tra, wl, dev, stream, only):
         res["gemm25d_repartition"] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / ms / 1e6, 1),
                                       "frac_hbm_peak": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
         del xr, ar, yr, dst
+        # backward products under the forward's blocking: dX = dY A^T, dA = X^T dY
+        for name, spec, inputs in (("gemm25d_bwd_dX", "ik,jk->ij", ("ik", "jk")), ("gemm25d_bwd_dA", "ij,ik->jk", ("ij", "ik"))):
+            pb = tra.tra_plan(spec, g.bounds, g.d, "mul", "sum", "bf16", "f32")
+            ops = [wl.draw(1000 * 6 + t, [g.bounds[c] for c in lab], "normal", "bf16", std=0.02).to(dev)
+                   for t, lab in enumerate(inputs)]
+            rels = [tra.to_relation(o, [g.d[c] for c in lab]) for o, lab in zip(ops, inputs)]
+            del ops
+            ms, zb = timed_execute(pb, rels[0], rels[1], reps=10)
+            res[name] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                         "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4), "kernel": pb.kernel,
+                         "operands": "X^T" if spec.startswith("ij,ik") else "Y^T"}
+            del rels, zb
 
     if want("mha"):
         res["mha"] = _mha(tra, wl, dev, stream)

@@ -19,7 +19,9 @@
 // staged as [row][k] and fed to the matrix cores with 16-byte LDS reads; one
 // stored contiguously along its output labels ("MN-major") is staged as
 // [k][row] exactly as it arrives and transposed on the way to the matrix
-// cores by gfx950's ds_read_b64_tr_b16.
+// cores by gfx950's ds_read_b64_tr_b16.  Either operand may be either: a
+// product with a transposed operand (X^T Y, X Y^T, the backward products of
+// a matmul) runs on the same kernel.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -150,7 +152,7 @@ struct DmaPlan {
     }
 };
 
-template <int V, bool BKM, typename TO>
+template <int V, bool AKM, bool BKM, typename TO>
 __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf16(
     GemmView v, const uint16_t *__restrict__ x, const uint16_t *__restrict__ y, TO *__restrict__ z,
     float *__restrict__ ws)
@@ -180,11 +182,11 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
     const uint32_t nk = (uint32_t)v.k_per_split / BK;
 
-    DmaPlan<BM, NT, true, 0> da;
+    DmaPlan<BM, NT, AKM, 0> da;
     DmaPlan<BN, NT, BKM, 1> db;
     da.init(v.gm, v.gk, m0, bx, tid);
     db.init(v.gn, v.gk, n0, by, tid);
-    constexpr int L = DmaPlan<BM, NT, true, 0>::N + DmaPlan<BN, NT, BKM, 1>::N;
+    constexpr int L = DmaPlan<BM, NT, AKM, 0>::N + DmaPlan<BN, NT, BKM, 1>::N;
 
     floatx16_t acc[TM][TN];
 #pragma unroll
@@ -208,14 +210,27 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     auto compute = [&](int stg) {
         const uint32_t a_b = lds_addr(SA(stg)), b_b = lds_addr(SB(stg));
         u32x4_t af[2][TM];
+        u32x2_t at[2][TM][2];
         u32x4_t bk[2][TN];
         u32x2_t bt[2][TN][2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                const int r = a_row0 + i * 32, c = ((ks * 16 + k_lane) >> 3) ^ swz_k(r);
-                af[ks][i] = ds_read16(a_b + (r * MF_BK + c * 8) * 2);
+                if constexpr (AKM) {
+                    const int r = a_row0 + i * 32, c = ((ks * 16 + k_lane) >> 3) ^ swz_k(r);
+                    af[ks][i] = ds_read16(a_b + (r * MF_BK + c * 8) * 2);
+                } else {
+                    // [k][row] stage: the transposing read hands lane l the
+                    // eight k of row l%32 (rows play the part the columns
+                    // play for an MN-major Y)
+                    const int g = lane >> 4, sl = lane & 15;
+                    const int kb = ks * 16 + 8 * (g >> 1) + (sl >> 2);
+                    const int mb = wm * (BM / WM) + i * 32 + 16 * (g & 1) + 4 * (sl & 3);
+                    const uint32_t e0 = kb * BM + (((mb >> 3) ^ swz_n<BM>(kb)) << 3) + (mb & 7);
+                    at[ks][i][0] = ds_read8_tr(a_b + e0 * 2);
+                    at[ks][i][1] = ds_read8_tr(a_b + (e0 + 4 * BM) * 2);
+                }
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
@@ -236,7 +251,14 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) lds_ready(af[ks][i]);
+            for (int i = 0; i < TM; ++i) {
+                if constexpr (AKM) {
+                    lds_ready(af[ks][i]);
+                } else {
+                    lds_ready(at[ks][i][0]);
+                    lds_ready(at[ks][i][1]);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 if constexpr (BKM) {
@@ -253,7 +275,13 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    bf16x8_t a = __builtin_bit_cast(bf16x8_t, af[ks][i]);
+                    bf16x8_t a;
+                    if constexpr (AKM) {
+                        a = __builtin_bit_cast(bf16x8_t, af[ks][i]);
+                    } else {
+                        u32x4_t w = {at[ks][i][0][0], at[ks][i][0][1], at[ks][i][1][0], at[ks][i][1][1]};
+                        a = __builtin_bit_cast(bf16x8_t, w);
+                    }
                     bf16x8_t b;
                     if constexpr (BKM) {
                         b = __builtin_bit_cast(bf16x8_t, bk[ks][j]);
@@ -323,25 +351,26 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
 
 // Every (tile, operand layout, output dtype) combination the launcher can
 // pick, instantiated explicitly (the host pass otherwise emits only some).
-#define TRA_MFMA_INST(V, BKM, TO)                                                                              \
-    template __global__ void k_mfma_bf16<V, BKM, TO>(GemmView, const uint16_t *, const uint16_t *, TO *, float *);
-TRA_MFMA_INST(0, true, float)
-TRA_MFMA_INST(0, false, float)
-TRA_MFMA_INST(0, true, bf16_t)
-TRA_MFMA_INST(0, false, bf16_t)
-TRA_MFMA_INST(1, true, float)
-TRA_MFMA_INST(1, false, float)
-TRA_MFMA_INST(1, true, bf16_t)
-TRA_MFMA_INST(1, false, bf16_t)
-TRA_MFMA_INST(2, true, float)
-TRA_MFMA_INST(2, false, float)
-TRA_MFMA_INST(2, true, bf16_t)
-TRA_MFMA_INST(2, false, bf16_t)
+#define TRA_MFMA_INST(V, AKM, BKM, TO)                                                                         \
+    template __global__ void k_mfma_bf16<V, AKM, BKM, TO>(GemmView, const uint16_t *, const uint16_t *, TO *,    \
+                                                          float *);
+#define TRA_MFMA_INST4(V, TO)                                                                                  \
+    TRA_MFMA_INST(V, true, true, TO)                                                                           \
+    TRA_MFMA_INST(V, true, false, TO)                                                                          \
+    TRA_MFMA_INST(V, false, true, TO)                                                                          \
+    TRA_MFMA_INST(V, false, false, TO)
+TRA_MFMA_INST4(0, float)
+TRA_MFMA_INST4(0, bf16_t)
+TRA_MFMA_INST4(1, float)
+TRA_MFMA_INST4(1, bf16_t)
+TRA_MFMA_INST4(2, float)
+TRA_MFMA_INST4(2, bf16_t)
+#undef TRA_MFMA_INST4
 #undef TRA_MFMA_INST
 
 int launch_split_fold(const tra_plan_s &p, const void *ws, void *z, void *stream);
 
-template <int V, bool BKM, typename TO>
+template <int V, bool AKM, bool BKM, typename TO>
 static int launch_v(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, hipStream_t s)
 {
     constexpr MfmaCfg C = mfma_cfg(V);
@@ -349,7 +378,7 @@ static int launch_v(const tra_plan_s &p, const void *x, const void *y, void *z, 
     dim3 grid((v.gm.total / C.bm) * (v.gn.total / C.bn), v.gb.total, v.split);
     // naming the kernel through a pointer makes the host pass emit its launch
     // stub for every instantiation
-    void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *) = k_mfma_bf16<V, BKM, TO>;
+    void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *) = k_mfma_bf16<V, AKM, BKM, TO>;
     hipLaunchKernelGGL(kern, grid, dim3(C.wm * C.wn * 64), 0, s, v, (const uint16_t *)x, (const uint16_t *)y,
                        (TO *)z, (float *)ws);
     return (int)hipGetLastError();
@@ -358,8 +387,12 @@ static int launch_v(const tra_plan_s &p, const void *x, const void *y, void *z, 
 template <int V, typename TO>
 static int launch_layout(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, hipStream_t s)
 {
-    if (p.b_kmajor) return launch_v<V, true, TO>(p, x, y, z, ws, s);
-    return launch_v<V, false, TO>(p, x, y, z, ws, s);
+    if (p.a_kmajor) {
+        if (p.b_kmajor) return launch_v<V, true, true, TO>(p, x, y, z, ws, s);
+        return launch_v<V, true, false, TO>(p, x, y, z, ws, s);
+    }
+    if (p.b_kmajor) return launch_v<V, false, true, TO>(p, x, y, z, ws, s);
+    return launch_v<V, false, false, TO>(p, x, y, z, ws, s);
 }
 
 template <typename TO>

@@ -246,7 +246,7 @@ static bool lower_tile(tra_plan_s &p)
     const int vec = mfma ? 8 : 4;
     bool ak, bk;
     if (contiguous_last(sk, 0, vec)) ak = true;
-    else if (!mfma && contiguous_last(sm, 0, vec)) ak = false;  // matrix cores: K-major X only
+    else if (contiguous_last(sm, 0, vec)) ak = false;
     else return false;
     if (contiguous_last(sk, 1, vec)) bk = true;
     else if (contiguous_last(sn, 0, vec)) bk = false;

@@ -254,3 +254,35 @@ def test_ragged_extents(base, d):
     wavefront per output when the contracted run is contiguous)."""
     err, plan = check(base.scaled(RAGGED, d))
     assert plan.kernel in ("generic", "rowreduce")
+
+
+# ------------------------------------------------------------ transposed operands on the matrix cores
+
+N002 = ("normal", {"std": 0.02})
+SMALL_T = {"i": 1024, "j": 512, "k": 256}
+
+
+@pytest.mark.parametrize("spec", ["ik,jk->ij", "ij,ik->jk", "ji,jk->ik", "ji,kj->ik"],
+                         ids=["XYt", "XtY", "XtY2", "XtYt"])
+@pytest.mark.parametrize("d", [{"i": 1, "j": 1, "k": 1}, {"i": 4, "j": 2, "k": 1}, {"i": 2, "j": 1, "k": 4}])
+def test_transposed_operands_on_the_matrix_cores(spec, d):
+    """Products whose operands are stored contiguous along an output label
+    (X^T Y, X Y^T, X^T Y^T) run on the matrix-core kernel with transposing
+    LDS reads for either operand."""
+    case = wl.EinsumCase(f"t_{spec}", 61, spec, SMALL_T, d, "mul", "sum", "bf16", "f32", (N002, N002))
+    err, plan = check(case)
+    assert plan.kernel == "mfma_bf16"
+
+
+@pytest.mark.parametrize("which", ["dX", "dA"])
+def test_blocked_gemm_backward_full_size_sampled(which):
+    """The blocked GEMM's backward products at full size: dX = dY A^T
+    (16384 x 8192, sum over 8192) and dA = X^T dY (8192 x 8192, sum over
+    16384), under the forward's blocking (i, j, k) = (16, 4, 4)."""
+    b = {"i": 16384, "j": 8192, "k": 8192}
+    d = {"i": 16, "j": 4, "k": 4}
+    spec = "ik,jk->ij" if which == "dX" else "ij,ik->jk"
+    case = wl.EinsumCase(f"gemm25d_{which}", 62 if which == "dX" else 63, spec, b, d, "mul", "sum", "bf16", "f32",
+                         (N002, N002))
+    err, plan = check(case, sample=2048, seed=5)
+    assert plan.kernel == "mfma_bf16"
