@@ -330,6 +330,8 @@ def _extra(tra, wl, dev, stream, only):
         res["mha"] = _mha(tra, wl, dev, stream)
     if want("mha_fused"):
         res["mha_fused"] = _mha(tra, wl, dev, stream, fuse=True)
+    if want("mha_bwd"):
+        res["mha_bwd"] = _mha_backward(tra, wl, dev, stream)
     torch.cuda.empty_cache()
     return res
 
@@ -385,6 +387,48 @@ def _mha(tra, wl, dev, stream, fuse=False):
     return {"ms": round(total, 3), "TFLOP/s": round(total_fl / total / 1e9, 1), "nodes": nodes,
             "repartitions": g.info.n_repartitions, "fused_chains": g.info.n_fused,
             "workspace_GB": round(g.info.workspace_bytes / 1e9, 2)}
+
+
+def _mha_backward(tra, wl, dev, stream):
+    """Backward EinSums of the attention layer (dense layouts), per step and in
+    total, each step against its own roof: the products against the bf16 matrix-core
+    peak, the [h,s,t] elementwise steps against HBM."""
+    import torch
+    case = wl.MHA
+    s, a, h, dh = case.s, case.a, case.h, case.dh
+    layer = tra.AttentionLayer(s, a, h, dh)
+    inputs = {k: v.to(dev) for k, v in case.make_inputs().items()}
+    ws = layer.workspace(dev)
+    saved = layer.forward(inputs, ws)
+    g = case.make_output_gradient().to(dev)
+    grads = layer.backward(saved, g, ws)
+    proj, attn = 2.0 * s * a * h * dh, 2.0 * h * s * s * dh
+    flops = {n: proj for n in ("dO", "dW_O", "dW_Q", "dQ", "dW_K", "dK", "dW_V", "dV")}
+    flops.update({n: attn for n in ("dAttn", "dV_proj", "dQ_proj", "dK_proj")})
+    hst = float(h * s * s)
+    sbytes = {"P": 8 * hst, "dAttn_c": 8 * hst, "dScores": 10 * hst}   # fp32 in / out, bf16 out for dScores
+    names = [n for n, *_ in tra.attention.BACKWARD]
+    reps = 5
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
+    for r in range(reps):
+        k = iter(range(1, len(names) + 1))
+        ev[r][0].record(stream)
+        grads = layer.backward(saved, g, ws, on_step=lambda n: ev[r][next(k)].record(stream), out=grads)
+    torch.cuda.synchronize()
+    steps, total = {}, 0.0
+    for i, n in enumerate(names):
+        ms = sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
+        total += ms
+        e = {"us": round(ms * 1e3, 1), "kernel": layer.plans[n].kernel}
+        if n in flops:
+            e["TFLOP/s"] = round(flops[n] / ms / 1e9, 1)
+            e["frac_bf16_mfma_peak"] = round(flops[n] / (ms * 1e-3) / BF16_MFMA_PEAK, 4)
+        if n in sbytes:
+            e["GB/s"] = round(sbytes[n] / ms / 1e6, 1)
+            e["frac_hbm_peak"] = round(sbytes[n] / (ms * 1e-3) / HBM_PEAK, 4)
+        steps[n] = e
+    fl = sum(flops.values())
+    return {"ms": round(total, 3), "TFLOP/s": round(fl / total / 1e9, 1), "steps": steps}
 
 
 if __name__ == "__main__":

@@ -78,7 +78,8 @@ typedef enum {
     TRA_JOIN_SQDIFF = 1,  /* (x - y)^2 */
     TRA_JOIN_ADD = 2,     /* x + y */
     TRA_JOIN_IDENT = 3,   /* x (one operand) */
-    TRA_JOIN_EXP_SUB = 4  /* exp(x - y) (float only) */
+    TRA_JOIN_EXP_SUB = 4, /* exp(x - y) (float only) */
+    TRA_JOIN_SUB = 5      /* x - y (integers wrap) */
 } tra_join_op;
 
 /* Aggregates (section 2.1: any associative and commutative reduction). */

@@ -37,7 +37,7 @@
 
 #define OR_MAX_LABELS 26
 
-enum { OR_JOIN_MUL = 0, OR_JOIN_SQDIFF = 1, OR_JOIN_ADD = 2, OR_JOIN_IDENT = 3, OR_JOIN_EXP_SUB = 4 };
+enum { OR_JOIN_MUL = 0, OR_JOIN_SQDIFF = 1, OR_JOIN_ADD = 2, OR_JOIN_IDENT = 3, OR_JOIN_EXP_SUB = 4, OR_JOIN_SUB = 5 };
 enum { OR_AGG_NONE = 0, OR_AGG_SUM = 1, OR_AGG_MAX = 2, OR_AGG_MIN = 3, OR_AGG_LSE = 4 };
 
 static double join_f(int op, double x, double y)
@@ -48,6 +48,7 @@ static double join_f(int op, double x, double y)
     case OR_JOIN_ADD: return x + y;
     case OR_JOIN_IDENT: return x;
     case OR_JOIN_EXP_SUB: return exp(x - y);
+    case OR_JOIN_SUB: return x - y;
     }
     return NAN;
 }
@@ -59,6 +60,7 @@ static int64_t join_i(int op, int64_t x, int64_t y)
     case OR_JOIN_SQDIFF: return (x - y) * (x - y);
     case OR_JOIN_ADD: return x + y;
     case OR_JOIN_IDENT: return x;
+    case OR_JOIN_SUB: return x - y;
     }
     return 0;
 }

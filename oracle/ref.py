@@ -20,7 +20,7 @@ Three independent evaluators of that one formula live here:
                        applied over the contracted axes. Small shapes.
 
 Joins: mul x*y, sqdiff (x-y)^2, add x+y, ident x (one operand),
-exp_sub exp(x-y).  Aggregates: none, sum, max, min, lse.
+exp_sub exp(x-y), sub x-y.  Aggregates: none, sum, max, min, lse.
 Floating inputs are widened exactly to float64, integers to int64.
 """
 from __future__ import annotations
@@ -35,7 +35,7 @@ import numpy as np
 
 from . import build as _build
 
-JOINS = {"mul": 0, "sqdiff": 1, "add": 2, "ident": 3, "exp_sub": 4}
+JOINS = {"mul": 0, "sqdiff": 1, "add": 2, "ident": 3, "exp_sub": 4, "sub": 5}
 AGGS = {"none": 0, "sum": 1, "max": 2, "min": 3, "lse": 4}
 
 _lib = None
@@ -177,6 +177,8 @@ def _join(op: str, x, y):
         return x
     if op == "exp_sub":
         return math.exp(x - y)
+    if op == "sub":
+        return x - y
     raise ValueError(op)
 
 
@@ -256,6 +258,8 @@ def dense_einsum(spec: str, x, y=None, join: str = "mul", agg: str = "sum",
         v = xv + 0 * yv
     elif join == "exp_sub":
         v = np.exp(xv - yv)
+    elif join == "sub":
+        v = xv - yv
     else:
         raise ValueError(join)
     v = np.broadcast_to(v, tuple(ext[c] for c in full))

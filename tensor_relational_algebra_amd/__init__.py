@@ -9,3 +9,4 @@ from ._binding import (  # noqa: F401
     GRAPH_FUSE_ATTENTION, LIB_PATH, Graph, Plan, TraError, from_relation, lib, to_relation, tra_canonical_labels,
     tra_choose, tra_cost, tra_d_from_operand_form, tra_execute, tra_graph_execute, tra_graph_plan, tra_graph_plan_ex,
     tra_graph_run_node, tra_plan, tra_repartition)
+from .attention import AttentionLayer  # noqa: F401

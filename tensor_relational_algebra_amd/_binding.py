@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "_build", "libtra.so")
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
 TORCH_DTYPES = {0: torch.float32, 1: torch.bfloat16, 2: torch.int32}
 DTYPE_OF_TORCH = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2}
-JOINS = {"mul": 0, "sqdiff": 1, "add": 2, "ident": 3, "exp_sub": 4}
+JOINS = {"mul": 0, "sqdiff": 1, "add": 2, "ident": 3, "exp_sub": 4, "sub": 5}
 AGGS = {"none": 0, "sum": 1, "max": 2, "min": 3, "lse": 4}
 KERNELS = {0: "generic", 1: "elemwise", 2: "rowreduce", 3: "valu_tile", 4: "mfma_bf16", 5: "empty"}
 

@@ -52,6 +52,7 @@ __device__ __forceinline__ float join_f(int j, float x, float y)
     case J_SQDIFF: { float t = x - y; return t * t; }
     case J_ADD: return x + y;
     case J_IDENT: return x;
+    case J_SUB: return x - y;
     default: return __expf(x - y);
     }
 }
@@ -61,6 +62,7 @@ __device__ __forceinline__ int32_t join_i(int j, int32_t x, int32_t y)
     case J_MUL: return wmul(x, y);
     case J_SQDIFF: { int32_t t = wsub(x, y); return wmul(t, t); }
     case J_ADD: return wadd(x, y);
+    case J_SUB: return wsub(x, y);
     default: return x;
     }
 }

@@ -480,7 +480,7 @@ int tra_plan(const char *spec, const int64_t *bounds, const int32_t *d, int n_la
     };
     if (in_dtype < D_F32 || in_dtype > D_I32 || out_dtype < D_F32 || out_dtype > D_I32)
         return bad(TRA_E_DTYPE, "unknown dtype");
-    if (join_op < J_MUL || join_op > J_EXP_SUB) return bad(TRA_E_OP, "unknown join");
+    if (join_op < J_MUL || join_op > J_SUB) return bad(TRA_E_OP, "unknown join");
     if (agg_op < A_NONE || agg_op > A_LSE) return bad(TRA_E_OP, "unknown aggregate");
     if (agg_op == A_NONE && !con.empty()) return bad(TRA_E_OP, "aggregate NONE with contracted labels " + con);
     if (ops.size() == 1 && join_op != J_IDENT) return bad(TRA_E_OP, "a one-operand spec takes the ident join");

@@ -47,7 +47,7 @@ struct AttnDesc {
 };
 
 // Join / aggregate codes (mirror tra.h).
-enum Join : int32_t { J_MUL = 0, J_SQDIFF = 1, J_ADD = 2, J_IDENT = 3, J_EXP_SUB = 4 };
+enum Join : int32_t { J_MUL = 0, J_SQDIFF = 1, J_ADD = 2, J_IDENT = 3, J_EXP_SUB = 4, J_SUB = 5 };
 enum Agg : int32_t { A_NONE = 0, A_SUM = 1, A_MAX = 2, A_MIN = 3, A_LSE = 4 };
 enum DType : int32_t { D_F32 = 0, D_BF16 = 1, D_I32 = 2 };
 

@@ -192,6 +192,10 @@ class MhaCase:
             t[name] = draw(1000 * self.wid + 3 + i, (self.a, self.h, self.dh), "normal", "bf16", std=0.02)
         return t
 
+    def make_output_gradient(self) -> torch.Tensor:
+        """dL/dOutput [s, a] for the backward pass: bf16 N(0, 1), tensor index 7."""
+        return draw(1000 * self.wid + 7, (self.s, self.a), "normal", "bf16", std=1.0)
+
 
 MHA = MhaCase()
 MHA_SMALL = MhaCase(s=128, a=128, h=4, dh=32)

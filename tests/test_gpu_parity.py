@@ -188,8 +188,8 @@ def test_every_join_aggregate_dtype_on_small_shapes(spec, bounds):
     rng = np.random.default_rng(21)
     labels = tra.tra_canonical_labels(spec)
     for idt in ("i32", "f32", "bf16"):
-        joins = ["ident"] if len(ops) == 1 else (["mul", "sqdiff", "add"] if idt == "i32"
-                                                  else ["mul", "sqdiff", "add", "exp_sub"])
+        joins = ["ident"] if len(ops) == 1 else (["mul", "sqdiff", "add", "sub"] if idt == "i32"
+                                                  else ["mul", "sqdiff", "add", "exp_sub", "sub"])
         aggs = (["none"] if not con else []) + ["sum", "max", "min"] + ([] if idt == "i32" else ["lse"])
         for join, agg in itertools.product(joins, aggs):
             dmap = {c: int(rng.choice(_divisors(bounds[c]))) for c in labels}

@@ -24,8 +24,8 @@ TWO_OPERAND_SPECS = [
     "hst,thd->shd",
 ]
 UNARY_SPECS = ["ij->i", "ijk->ik", "ij->ij", "ij->", "hst->hs"]
-FLOAT_JOINS = ["mul", "sqdiff", "add", "exp_sub"]
-INT_JOINS = ["mul", "sqdiff", "add"]
+FLOAT_JOINS = ["mul", "sqdiff", "add", "exp_sub", "sub"]
+INT_JOINS = ["mul", "sqdiff", "add", "sub"]
 AGGS = ["none", "sum", "max", "min", "lse"]
 
 
@@ -158,6 +158,27 @@ def test_max_plus_special_cases():
     # against an explicit broadcast maximum
     want = (x[:, :, None] + y[None, :, :]).max(axis=1)
     np.testing.assert_array_equal(ref.einsum("ij,jk->ik", x, y, "add", "max"), want)
+
+
+def test_sub_join_closed_forms():
+    # The difference join (used by the softmax backward, dS = P * (dP - rowsum)):
+    # summed over j it separates into row sums of X minus column sums of Y.
+    rng = np.random.default_rng(11)
+    x = rng.uniform(-1, 1, (12, 9))
+    y = rng.uniform(-1, 1, (9, 7))
+    got = ref.einsum("ij,jk->ik", x, y, "sub", "sum")
+    np.testing.assert_allclose(got, x.sum(1)[:, None] - y.sum(0)[None, :], rtol=1e-12, atol=1e-12)
+    # broadcast over a missing label, no aggregate: S[h,s,t] - L[h,s]
+    s3 = rng.uniform(-2, 2, (3, 5, 6))
+    l2 = rng.uniform(-2, 2, (3, 5))
+    np.testing.assert_array_equal(ref.einsum("hst,hs->hst", s3, l2, "sub", "none"), s3 - l2[:, :, None])
+    # integers: max_j (x - y) with y == 0 is the row maximum; exact
+    xi = rng.integers(-1000, 1001, (8, 11)).astype(np.int64)
+    yi = np.zeros((11, 4), dtype=np.int64)
+    np.testing.assert_array_equal(ref.einsum("ij,jk->ik", xi, yi, "sub", "max"),
+                                  np.repeat(xi.max(1)[:, None], 4, axis=1))
+    # the operand order matters: x - y, not y - x
+    assert ref.einsum("i,i->i", np.array([5.0]), np.array([2.0]), "sub", "none")[0] == 3.0
 
 
 def test_logsumexp_closed_forms():

@@ -57,3 +57,55 @@ def test_row_sample_equals_full():
     part = mha.mha(t, rows=rows)
     np.testing.assert_allclose(part["Output"], full["Output"][rows], rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(part["Attn"], full["Attn"][:, rows], rtol=1e-13, atol=1e-13)
+
+
+def _autograd_reference(t, d_out):
+    """The same layer in float64 torch with autograd: an independent backward."""
+    leaves = {n: torch.tensor(mha.ref._as_np(t[n]), dtype=torch.float64, requires_grad=True)
+              for n in ("Q", "K", "V", "W_Q", "W_K", "W_V", "W_O")}
+    dh = leaves["W_Q"].shape[2]
+    qp = torch.einsum("sa,ahd->shd", leaves["Q"], leaves["W_Q"])
+    kp = torch.einsum("sa,ahd->shd", leaves["K"], leaves["W_K"])
+    vp = torch.einsum("sa,ahd->shd", leaves["V"], leaves["W_V"])
+    sc = torch.einsum("shd,thd->hst", qp, kp) / math.sqrt(dh)
+    attn = torch.softmax(sc, dim=2)
+    o = torch.einsum("hst,thd->shd", attn, vp)
+    out = torch.einsum("shd,ahd->sa", o, leaves["W_O"])
+    g = torch.tensor(mha.ref._as_np(d_out), dtype=torch.float64)
+    out.backward(g)
+    return {"d" + n: leaves[n].grad.numpy() for n in leaves}
+
+
+def test_backward_equals_autograd():
+    t = _inputs(24, 16, 2, 8, seed=4)
+    g = workloads.draw(4242, (24, 16), "normal", "bf16", std=1.0)
+    got = mha.mha_backward(t, g)
+    want = _autograd_reference(t, g)
+    for name in ("dQ", "dK", "dV", "dW_Q", "dW_K", "dW_V", "dW_O"):
+        np.testing.assert_allclose(got[name], want[name], rtol=1e-9, atol=1e-12, err_msg=name)
+
+
+def test_backward_with_unequal_query_and_key_lengths():
+    # s != t is allowed by the EinSums; the projections of K and V run over t
+    case = workloads.MhaCase(s=8, a=16, h=2, dh=4, wid=95)
+    t = case.make_inputs()
+    t["K"] = workloads.draw(9501, (13, 16), "normal", "bf16", std=1.0)
+    t["V"] = workloads.draw(9502, (13, 16), "normal", "bf16", std=1.0)
+    g = workloads.draw(9503, (8, 16), "normal", "bf16", std=1.0)
+    got = mha.mha_backward(t, g)
+    want = _autograd_reference(t, g)
+    for name in ("dQ", "dK", "dV", "dW_Q", "dW_K", "dW_V", "dW_O"):
+        np.testing.assert_allclose(got[name], want[name], rtol=1e-9, atol=1e-12, err_msg=name)
+
+
+def test_softmax_backward_row_sum_identity():
+    # sum_t Attn * dAttn equals sum_d dO * O (both are dOut . Output restricted to one
+    # row and head), which lets the row term be formed from [s,h,d] tensors instead of
+    # [h,s,t] ones.
+    t = _inputs(20, 16, 2, 8, seed=5)
+    g = workloads.draw(4343, (20, 16), "normal", "bf16", std=1.0)
+    fwd = mha.mha(t)
+    b = mha.mha_backward(t, g)
+    lhs = (fwd["Attn"] * b["dAttn"]).sum(axis=2)                       # [h, s]
+    rhs = np.transpose((b["dO"] * fwd["O"]).sum(axis=2), (1, 0))        # [h, s]
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-10, atol=1e-12)

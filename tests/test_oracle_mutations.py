@@ -28,6 +28,8 @@ MUTATIONS = {
                    "else if (agg == OR_AGG_MAX) acc = v < acc ? v : acc;\n                else acc = v < acc ? v : acc;\n            } while (next_tuple(nc, cl, bounds, idx));\n            r = acc;\n        }\n        z[o] = post_scale * r;"),
     "scale_dropped": ("z[o] = post_scale * r;", "z[o] = r;"),
     "lse_without_max": ("r = m + log(s);", "r = log(s);"),
+    "sub_operands_swapped": ("case OR_JOIN_SUB: return x - y;\n    }\n    return NAN;",
+                             "case OR_JOIN_SUB: return y - x;\n    }\n    return NAN;"),
     "int_add_is_sub": ("static int64_t join_i(int op, int64_t x, int64_t y)\n{\n    switch (op) {\n    case OR_JOIN_MUL: return x * y;\n    case OR_JOIN_SQDIFF: return (x - y) * (x - y);\n    case OR_JOIN_ADD: return x + y;",
                        "static int64_t join_i(int op, int64_t x, int64_t y)\n{\n    switch (op) {\n    case OR_JOIN_MUL: return x * y;\n    case OR_JOIN_SQDIFF: return (x - y) * (x - y);\n    case OR_JOIN_ADD: return x - y;"),
 }
@@ -39,6 +41,7 @@ PIN_FUNCS = [
     pins.test_squared_distance_closed_form,
     pins.test_max_plus_special_cases,
     pins.test_logsumexp_closed_forms,
+    pins.test_sub_join_closed_forms,
     pins.test_batched_and_attention_specs_equal_library,
 ]
 
