@@ -86,6 +86,8 @@ def _parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra workloads to run")
     ap.add_argument("--src-sha", action="store_true", help="print the kernel-source hash the traffic record keys on")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="measure the constants of the chooser's time model and print them as one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB once per step with tra_repartition (same blocking on both sides); "
                          "the known-size reference for the HBM traffic counters")
@@ -106,6 +108,76 @@ def _copy_probe(mib: int, reps: int) -> None:
     torch.cuda.synchronize()
     assert torch.equal(src[-1024:], dst[-1024:])
     print(json.dumps({"copy_probe_bytes_each_way": n * 4, "reps": reps}), flush=True)
+
+
+# (name, spec, bounds, d, join, agg, in dtype, out dtype, reps): one case per constant of
+# the time model, each at a size where its kernel family is the planner's pick
+CALIBRATION_CASES = [
+    ("latency", "i,i->i", {"i": 8}, {"i": 1}, "add", "none", "f32", "f32", 400),
+    ("mfma_tile0", "sa,ahd->shd", {"s": 4096, "a": 4096, "h": 32, "d": 128}, None, "mul", "sum", "bf16", "bf16", 20),
+    ("mfma_tile1", "bij,bjk->bik", {"b": 256, "i": 128, "j": 512, "k": 128}, None, "mul", "sum", "bf16", "f32", 50),
+    ("mfma_tile2", "bij,bjk->bik", {"b": 2048, "i": 64, "j": 256, "k": 64}, None, "mul", "sum", "bf16", "f32", 50),
+    ("valu_tile", "ij,jk->ik", {"i": 8192, "j": 256, "k": 8192}, {"i": 16, "j": 1, "k": 16}, "sqdiff", "sum",
+     "f32", "f32", 10),
+    ("rowreduce_compute", "ij,kj->ik", {"i": 2000, "j": 1000, "k": 2000}, None, "mul", "sum", "f32", "f32", 10),
+    ("rowreduce_stream", "hst->hs", {"h": 32, "s": 4096, "t": 4096}, None, "ident", "lse", "f32", "f32", 10),
+    ("generic", "ji,jk->ik", {"i": 1000, "j": 1000, "k": 1000}, None, "mul", "sum", "f32", "f32", 3),
+    ("stream", "hst,hs->hst", {"h": 32, "s": 4096, "t": 4096}, None, "exp_sub", "none", "f32", "bf16", 10),
+]
+
+
+def _calibrate() -> None:
+    """Measure the time model's constants: per case the average time of one
+    tra_execute, join terms per ns, bytes per ns, and the model's prediction."""
+    import torch
+
+    import tensor_relational_algebra_amd as tra
+    from tensor_relational_algebra_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for k, (name, spec, bounds, d, join, agg, idt, odt, reps) in enumerate(CALIBRATION_CASES):
+        labels = tra.tra_canonical_labels(spec)
+        d = d or {c: 1 for c in labels}
+        p = tra.tra_plan(spec, bounds, d, join, agg, idt, odt)
+        ops = spec.split("->")[0].split(",")
+        xs = [wl.draw(9000 + 10 * k + i, [bounds[c] for c in o], "normal", idt, std=0.1).to(dev).reshape(-1)
+              for i, o in enumerate(ops)]
+        z = torch.empty(p.info.z_elems, dtype=tra._binding.TORCH_DTYPES[p.out_dtype], device=dev)
+        ws = p.workspace(dev)
+        f = lambda: tra.tra_execute(p, xs[0], xs[1] if len(xs) > 1 else None, z, ws)
+        f()
+        ms = _events_time(f, reps, stream)
+        terms = 1.0
+        for c in labels:
+            terms *= bounds[c]
+        nbytes = p.info.x_bytes + p.info.y_bytes + p.info.z_bytes
+        out[name] = {"kernel": p.kernel, "tile": p.info.tile, "split": p.info.agg_split, "us": round(ms * 1e3, 2),
+                     "terms_per_ns": round(terms / (ms * 1e6), 2), "bytes_per_ns": round(nbytes / (ms * 1e6), 1),
+                     "predicted_us": round(tra.tra_predict_ns(p) / 1e3, 2)}
+        del xs, z, ws
+    # back-to-back launches from the library (no Python between them): a chain of
+    # 16 one-wavefront elementwise EinSum nodes run by one tra_graph_execute
+    nodes = ["n0 einsum i,i->i i=64 @X,@Y0 in=f32 out=f32"]
+    nodes += [f"n{i} einsum i,i->i i=64 n{i - 1},@Y{i} in=f32 out=f32" for i in range(1, 16)]
+    g = tra.tra_graph_plan("\n".join(nodes), 1, [1] * 16)
+    leaves = {n: torch.zeros(64, dtype=torch.float32, device=dev) for n in ["X"] + [f"Y{i}" for i in range(16)]}
+    gw = g.workspace(dev)
+    gout = torch.empty(64, dtype=torch.float32, device=dev)
+    f = lambda: tra.tra_graph_execute(g, leaves, gout, gw)
+    f()
+    ms = _events_time(f, 50, stream)
+    out["latency_graph_node"] = {"us_per_node": round(ms * 1e3 / 17, 2), "nodes_per_call": 16,
+                                 "note": "16 nodes + the dense write-back of the output"}
+    shape = [16384, 8192]
+    src = torch.empty(shape, dtype=torch.float32, device=dev).reshape(-1)
+    dst = torch.empty_like(src)
+    f = lambda: tra.tra_repartition(src, shape, [16, 4], [4, 16], dst)
+    f()
+    ms = _events_time(f, 20, stream)
+    out["copy"] = {"us": round(ms * 1e3, 2), "bytes_per_ns": round(2 * src.numel() * 4 / (ms * 1e6), 1),
+                   "predicted_us": round(tra.tra_predict_repartition_ns(shape, "f32") / 1e3, 2)}
+    print(json.dumps({"calibration": out}), flush=True)
 
 
 def _events_time(fn, reps: int, stream) -> float:
@@ -132,6 +204,9 @@ def main():
         return
     if args.copy_probe:
         _copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+    if args.calibrate:
+        _calibrate()
         return
     import numpy as np
     import torch
@@ -330,13 +405,17 @@ def _extra(tra, wl, dev, stream, only):
         res["mha"] = _mha(tra, wl, dev, stream)
     if want("mha_fused"):
         res["mha_fused"] = _mha(tra, wl, dev, stream, fuse=True)
+    if want("mha_time"):
+        res["mha_time"] = _mha(tra, wl, dev, stream, time_model=True)
+    if want("mha_fused_time"):
+        res["mha_fused_time"] = _mha(tra, wl, dev, stream, fuse=True, time_model=True)
     if want("mha_bwd"):
         res["mha_bwd"] = _mha_backward(tra, wl, dev, stream)
     torch.cuda.empty_cache()
     return res
 
 
-def _mha(tra, wl, dev, stream, fuse=False):
+def _mha(tra, wl, dev, stream, fuse=False, time_model=False):
     """The attention layer as an EinGraph, d chosen for P = 256; per-node time
     (its input repartitions included) against the node's own roof.  With
     fuse=True the scores -> softmax -> weighted-sum chain runs as one kernel,
@@ -344,7 +423,8 @@ def _mha(tra, wl, dev, stream, fuse=False):
     import torch
     case = wl.MHA
     desc = case.graph_desc()
-    g = tra.tra_graph_plan_ex(desc, 256, None, tra.GRAPH_FUSE_ATTENTION if fuse else 0)
+    flags = (tra.GRAPH_FUSE_ATTENTION if fuse else 0) | (tra.GRAPH_CHOOSE_TIME if time_model else 0)
+    g = tra.tra_graph_plan_ex(desc, 256, None, flags)
     inputs = {k: v.to(dev) for k, v in case.make_inputs().items()}
     ws = g.workspace(dev)
     out = torch.empty(g.info.out_elems, dtype=torch.float32, device=dev)
@@ -384,9 +464,13 @@ def _mha(tra, wl, dev, stream, fuse=False):
             e["frac_hbm_peak"] = round(sbytes[n] / (ms * 1e-3) / HBM_PEAK, 4)
         nodes[n] = e
     total_fl = sum(flops.values())
-    return {"ms": round(total, 3), "TFLOP/s": round(total_fl / total / 1e9, 1), "nodes": nodes,
-            "repartitions": g.info.n_repartitions, "fused_chains": g.info.n_fused,
-            "workspace_GB": round(g.info.workspace_bytes / 1e9, 2)}
+    r = {"ms": round(total, 3), "TFLOP/s": round(total_fl / total / 1e9, 1), "nodes": nodes,
+         "repartitions": g.info.n_repartitions, "fused_chains": g.info.n_fused,
+         "workspace_GB": round(g.info.workspace_bytes / 1e9, 2),
+         "chooser": "time model" if time_model else "pages (numbers moved, P = 256)"}
+    if time_model and not fuse:
+        r["predicted_ms"] = round(g.info.cost / 1e6, 3)
+    return r
 
 
 def _mha_backward(tra, wl, dev, stream):

@@ -114,6 +114,7 @@ typedef struct {
     int32_t kernel;           /* tra_kernel_family */
     int32_t n_labels;
     char labels[32];          /* canonical label order, NUL-terminated */
+    int32_t tile;             /* tile-kernel variant (mfma: 0 = 256x256, 1 = 128x128, 2 = 64x64); -1 if none */
 } tra_plan_info_t;
 
 /*
@@ -243,6 +244,44 @@ int tra_cost(const char *spec, const int64_t *bounds, const int32_t *d, int n_la
 int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_cap, int64_t *cost_out);
 
 /*
+ * tra_choose_ex -- tra_choose with option flags.
+ *
+ * TRA_CHOOSE_TIME: replace the numbers-moved cost model by a time model
+ * measured on one MI355X (the calibration that the EinDecomp page's closing
+ * remarks ask a deployment to make: measured kernel and copy costs, a
+ * per-launch latency, task granularity).  On one GPU every kernel reads its
+ * operands in place under any blocking, so a node costs its kernels'
+ * predicted time (tra_predict_ns of its plan under that d: launches times
+ * the launch latency plus the larger of join terms / the measured rate of
+ * the kernel family and tile the planner picks, and bytes / the measured
+ * bandwidth), and a blocking change costs a repartition
+ * (tra_predict_repartition_ns).  Graph inputs arrive dense and the output is
+ * returned dense, so a node that needs an input, or leaves its output, in a
+ * blocking other than all-ones pays that repartition too.  Every
+ * power-of-two d is a candidate (P must still be >= 1 but is not a
+ * constraint: the planner fills the chip by tiling and splitting).  The DP,
+ * its tie-break and the output are those of tra_choose; cost_out is in
+ * nanoseconds.
+ * Errors: those of tra_choose; TRA_E_OP for an unknown flag.
+ */
+#define TRA_CHOOSE_TIME 1
+int tra_choose_ex(const char *graph_desc, int P, int flags, int32_t *d_out, int d_cap, int64_t *cost_out);
+
+/*
+ * tra_predict_ns -- the time model's prediction, in nanoseconds, for one
+ * tra_execute of `plan` (see TRA_CHOOSE_TIME).  Errors: TRA_E_NULL.
+ */
+int tra_predict_ns(tra_plan_t plan, int64_t *ns_out);
+
+/*
+ * tra_predict_repartition_ns -- predicted time of one tra_repartition of a
+ * tensor of extents bounds[0..rank) and `dtype` whose blocking changes.
+ * Errors: TRA_E_NULL, TRA_E_LABELS (rank outside 0..12), TRA_E_DTYPE,
+ * TRA_E_INDIVISIBLE (a negative extent).
+ */
+int tra_predict_repartition_ns(const int64_t *bounds, int rank, int dtype, int64_t *ns_out);
+
+/*
  * EinGraph executor (section 2.1: an EinGraph is a DAG of EinSum nodes whose
  * edges are tensors; section 4.1: the compiled plan partitions the inputs,
  * runs every node's join + aggregation, and reorganises intermediates whose
@@ -300,6 +339,12 @@ int tra_graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d_le
  * Errors: those of tra_graph_plan; TRA_E_OP for an unknown flag.
  */
 #define TRA_GRAPH_FUSE_ATTENTION 1
+/*
+ * TRA_GRAPH_CHOOSE_TIME: when d_all is NULL, choose the partition vectors
+ * with the measured time model (TRA_CHOOSE_TIME) instead of the pages'
+ * numbers-moved model; tra_graph_info's cost is then in nanoseconds.
+ */
+#define TRA_GRAPH_CHOOSE_TIME 2
 int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d_all, int d_len, int flags,
                       tra_graph_t *out_graph);
 

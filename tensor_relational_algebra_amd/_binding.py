@@ -36,7 +36,7 @@ class PlanInfo(ctypes.Structure):
                 ("agg_split", ctypes.c_int64), ("x_elems", ctypes.c_int64), ("y_elems", ctypes.c_int64),
                 ("z_elems", ctypes.c_int64), ("x_bytes", ctypes.c_size_t), ("y_bytes", ctypes.c_size_t),
                 ("z_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int32),
-                ("n_labels", ctypes.c_int32), ("labels", ctypes.c_char * 32)]
+                ("n_labels", ctypes.c_int32), ("labels", ctypes.c_char * 32), ("tile", ctypes.c_int32)]
 
 
 _lib = None
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
             "tra_d_from_operand_form": ([ctypes.c_char_p, P, I, P, I], I),
             "tra_cost": ([ctypes.c_char_p, P, P, I, P], I),
             "tra_choose": ([ctypes.c_char_p, I, P, I, P], I),
+            "tra_choose_ex": ([ctypes.c_char_p, I, I, P, I, P], I),
+            "tra_predict_ns": ([P, P], I),
+            "tra_predict_repartition_ns": ([P, I, I, P], I),
             "tra_graph_plan": ([ctypes.c_char_p, I, P, I, P], I),
             "tra_graph_plan_ex": ([ctypes.c_char_p, I, P, I, I, P], I),
             "tra_graph_info": ([P, P], I),
@@ -221,12 +224,16 @@ def from_relation(rel: torch.Tensor, shape: Sequence[int], d: Sequence[int], out
     return tra_repartition(rel.reshape(-1), list(shape), d, [1] * len(shape), out, stream).reshape(shape)
 
 
-def tra_choose(graph_desc: str, p: int) -> Tuple[List[List[int]], int]:
-    """Partition vectors for every node of an EinGraph (see include/tra.h)."""
+CHOOSE_TIME = 1
+
+
+def tra_choose(graph_desc: str, p: int, flags: int = 0) -> Tuple[List[List[int]], int]:
+    """Partition vectors for every node of an EinGraph (see include/tra.h);
+    flags=CHOOSE_TIME selects the measured time model (cost in ns)."""
     cap = 24 * max(1, graph_desc.count("\n") + 1)
     out = (ctypes.c_int32 * cap)()
     cost = ctypes.c_int64()
-    _check(lib().tra_choose(graph_desc.encode(), int(p), out, cap, ctypes.byref(cost)))
+    _check(lib().tra_choose_ex(graph_desc.encode(), int(p), int(flags), out, cap, ctypes.byref(cost)))
     res, pos = [], 0
     for line in graph_desc.splitlines():
         f = line.split()
@@ -283,6 +290,21 @@ class Graph:
 
 
 GRAPH_FUSE_ATTENTION = 1
+GRAPH_CHOOSE_TIME = 2
+
+
+def tra_predict_ns(plan: Plan) -> int:
+    """The time model's prediction for one tra_execute of the plan, in ns."""
+    ns = ctypes.c_int64()
+    _check(lib().tra_predict_ns(plan.handle, ctypes.byref(ns)))
+    return ns.value
+
+
+def tra_predict_repartition_ns(bounds: Sequence[int], dtype: str) -> int:
+    """The time model's prediction for one tra_repartition of the tensor, in ns."""
+    ns = ctypes.c_int64()
+    _check(lib().tra_predict_repartition_ns(_i64(bounds), len(bounds), DTYPES[dtype], ctypes.byref(ns)))
+    return ns.value
 
 
 def tra_graph_plan(graph_desc: str, p: int = 256, d_all: Optional[Sequence[int]] = None) -> Graph:

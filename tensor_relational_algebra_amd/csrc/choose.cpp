@@ -182,7 +182,49 @@ int parse_graph(const char *desc, std::vector<GNode> &nodes)
     return TRA_OK;
 }
 
-static void make_candidates(GNode &g, int P)
+// Predicted time of node g under candidate c (time model): the node's own
+// kernels, plus the repartition of every graph input it needs in a blocking
+// other than dense, plus, for the output node, the repartition back to dense.
+// Returns false when the planner rejects the candidate.
+static bool node_time(const GNode &g, const Cand &c, bool is_root, int64_t &ns)
+{
+    std::vector<int64_t> b;
+    for (char l : g.canon) b.push_back(g.B[(int)l]);
+    ns = 0;
+    auto plan_ns = [&](const std::string &spec, const std::vector<int32_t> &d, const std::vector<int64_t> &bb,
+                       int join, int agg, int idt, int odt, float scale) {
+        tra_plan_t p = nullptr;
+        if (tra_plan(spec.c_str(), bb.data(), d.data(), (int)bb.size(), join, agg, idt, odt, scale, &p)) return false;
+        ns += predict_plan_ns(*p);
+        tra_plan_destroy(p);
+        return true;
+    };
+    if (g.kind == "softmax") {
+        // LSE over the last label (fp32), then exp(S - LSE) in the node's out dtype
+        const std::string hst = g.out, hs = hst.substr(0, hst.size() - 1);
+        if (!plan_ns(hst + "->" + hs, c.d, b, TRA_JOIN_IDENT, TRA_AGG_LSE, D_F32, D_F32, 1.0f)) return false;
+        if (!plan_ns(hst + "," + hs + "->" + hst, c.d, b, TRA_JOIN_EXP_SUB, TRA_AGG_NONE, D_F32, g.out_dtype, 1.0f))
+            return false;
+    } else if (!plan_ns(g.spec, c.d, b, TRA_JOIN_MUL, TRA_AGG_SUM, g.in_dtype, g.out_dtype, g.scale)) {
+        return false;
+    }
+    auto dense = [&](const std::string &labels) {
+        for (char l : labels)
+            if (c.d[g.canon.find(l)] != 1) return false;
+        return true;
+    };
+    auto elems = [&](const std::string &labels) {
+        int64_t n = 1;
+        for (char l : labels) n *= g.B[(int)l];
+        return n;
+    };
+    for (size_t s = 0; s < g.src.size(); ++s)
+        if (g.src[s] < 0 && !dense(g.ops[s])) ns += predict_repartition_ns(elems(g.ops[s]), g.in_dtype);
+    if (is_root && !dense(g.out)) ns += predict_repartition_ns(elems(g.out), g.out_dtype);
+    return true;
+}
+
+static void make_candidates(GNode &g, int P, int model, bool is_root)
 {
     const size_t L = g.canon.size();
     std::vector<std::vector<int32_t>> opts(L);
@@ -198,7 +240,10 @@ static void make_candidates(GNode &g, int P)
             c.d[i] = opts[i][idx[i]];
             n *= c.d[i];
         }
-        if (n >= P && n % P == 0) {
+        if (model == COST_TIME) {
+            c.n_tasks = n;
+            if (node_time(g, c, is_root, c.cost)) g.cands.push_back(std::move(c));
+        } else if (n >= P && n % P == 0) {
             c.n_tasks = n;
             c.cost = node_cost(g, c);
             g.cands.push_back(std::move(c));
@@ -222,11 +267,16 @@ static std::vector<int32_t> blocking(const GNode &g, const Cand &c, const std::s
     return b;
 }
 
-int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &d_out, int64_t &cost)
+int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &d_out, int64_t &cost, int model)
 {
     if (P < 1) return fail(TRA_E_GRAPH, "P must be >= 1");
-    for (auto &g : nodes) {
-        make_candidates(g, P);
+    std::vector<int> used(nodes.size(), 0);
+    for (auto &g : nodes)
+        for (int s : g.src)
+            if (s >= 0) used[s]++;
+    for (size_t v = 0; v < nodes.size(); ++v) {
+        GNode &g = nodes[v];
+        make_candidates(g, P, model, used[v] == 0);
         if (g.cands.empty()) return fail(TRA_E_NO_CANDIDATE, "no admissible partition vector for " + g.name);
     }
     for (size_t v = 0; v < nodes.size(); ++v) {
@@ -246,7 +296,8 @@ int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &
             GNode &pu = nodes[u];
             int64_t size = 1;
             for (char c : pu.out) size *= pu.B[(int)c];
-            slots[s].size = size;
+            // the repartition term: numbers moved, or the predicted copy time
+            slots[s].size = model == COST_TIME ? predict_repartition_ns(size, pu.out_dtype) : size;
             for (int i = 0; i < (int)pu.cands.size(); ++i) {
                 const Cand &c = pu.cands[i];
                 if (slots[s].best < 0 || key_less(c, c.dp, pu.cands[slots[s].best], pu.cands[slots[s].best].dp))
@@ -315,7 +366,13 @@ using namespace tra;
 
 extern "C" int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_cap, int64_t *cost_out)
 {
+    return tra_choose_ex(graph_desc, P, 0, d_out, d_cap, cost_out);
+}
+
+extern "C" int tra_choose_ex(const char *graph_desc, int P, int flags, int32_t *d_out, int d_cap, int64_t *cost_out)
+{
     if (!graph_desc || !d_out) return fail(TRA_E_NULL, "graph_desc / d_out is NULL");
+    if (flags & ~TRA_CHOOSE_TIME) return fail(TRA_E_OP, "unknown chooser flag");
     std::vector<GNode> nodes;
     int rc = parse_graph(graph_desc, nodes);
     if (rc) return rc;
@@ -324,7 +381,7 @@ extern "C" int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_c
     if ((size_t)d_cap < need) return fail(TRA_E_BUFFER, "d_out needs " + std::to_string(need) + " entries");
     std::vector<std::vector<int32_t>> ds;
     int64_t cost = 0;
-    rc = run_dp(nodes, P, ds, cost);
+    rc = run_dp(nodes, P, ds, cost, (flags & TRA_CHOOSE_TIME) ? COST_TIME : COST_PAGES);
     if (rc) return rc;
     size_t pos = 0;
     for (auto &dv : ds)

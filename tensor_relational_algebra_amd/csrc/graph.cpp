@@ -324,7 +324,7 @@ extern "C" int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d
                                  tra_graph_t *out)
 {
     if (!graph_desc || !out) return gfail(TRA_E_NULL, "graph_desc / out is NULL");
-    if (flags & ~TRA_GRAPH_FUSE_ATTENTION) return gfail(TRA_E_OP, "unknown graph flag");
+    if (flags & ~(TRA_GRAPH_FUSE_ATTENTION | TRA_GRAPH_CHOOSE_TIME)) return gfail(TRA_E_OP, "unknown graph flag");
     *out = nullptr;
     tra_graph_s *g = new tra_graph_s();
     auto bad = [&](int rc) {
@@ -345,7 +345,7 @@ extern "C" int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d
         if (pos != (size_t)d_len) return bad(gfail(TRA_E_DLEN, "d_all has extra entries"));
         g->cost = -1;
     } else {
-        rc = run_dp(g->nodes, P, ds, g->cost);
+        rc = run_dp(g->nodes, P, ds, g->cost, (flags & TRA_GRAPH_CHOOSE_TIME) ? COST_TIME : COST_PAGES);
         if (rc) return bad(rc);
     }
     std::vector<int> uses(n, 0);

@@ -31,7 +31,19 @@ struct GNode {
 // Parse the node-per-line description (see tra_choose in tra.h).
 int parse_graph(const char *desc, std::vector<GNode> &nodes);
 
+// Cost models of the chooser: the pages' numbers-moved model (admissible d:
+// N >= P and N % P == 0), or the measured one-GPU time model (nanoseconds;
+// every power-of-two d is a candidate, graph inputs arrive dense and the
+// output is returned dense, so blockings other than all-ones on either
+// cost a repartition).
+enum CostModel { COST_PAGES = 0, COST_TIME = 1 };
+
 // Choose d for every node (canonical label order per node) and the total cost.
-int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &d_out, int64_t &cost);
+int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &d_out, int64_t &cost,
+           int model = COST_PAGES);
+
+// Measured time model (timemodel.cpp).
+int64_t predict_plan_ns(const tra_plan_s &p);
+int64_t predict_repartition_ns(int64_t elems, int dtype);
 
 }  // namespace tra

@@ -257,7 +257,7 @@ def test_graph_plan_fuses_the_attention_chain():
     g = tra.tra_graph_plan_ex("\n".join(lines), 16, None, tra.GRAPH_FUSE_ATTENTION)
     assert g.info.n_fused == 0
     with pytest.raises(tra.TraError) as e:
-        tra.tra_graph_plan_ex(wl.MHA_SMALL.graph_desc(), 16, None, 2)
+        tra.tra_graph_plan_ex(wl.MHA_SMALL.graph_desc(), 16, None, 4)
     assert e.value.code == -7
 
 

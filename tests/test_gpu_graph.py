@@ -17,9 +17,10 @@ from tests.gpu_util import DEV, maxnorm_rel_err
 pytestmark = pytest.mark.gpu
 
 
-def _run(case, p=None, d_all=None, fuse=False):
+def _run(case, p=None, d_all=None, fuse=False, time_model=False):
     desc = case.graph_desc()
-    g = tra.tra_graph_plan_ex(desc, p or 1, d_all, tra.GRAPH_FUSE_ATTENTION if fuse else 0)
+    flags = (tra.GRAPH_FUSE_ATTENTION if fuse else 0) | (tra.GRAPH_CHOOSE_TIME if time_model else 0)
+    g = tra.tra_graph_plan_ex(desc, p or 1, d_all, flags)
     host = case.make_inputs()
     dev = {k: v.to(DEV) for k, v in host.items()}
     out = tra.tra_graph_execute(g, dev).reshape(case.s, case.a)
@@ -106,3 +107,24 @@ def test_full_layer_fused_sampled_rows_and_deterministic():
     assert err <= 2e-2, err
     out2, _, _ = _run(case, p=256, fuse=True)
     assert np.array_equal(out, out2)
+
+
+# --- partition vectors chosen by the measured time model ---
+
+@pytest.mark.parametrize("fuse", [False, True], ids=["unfused", "fused"])
+def test_small_layer_time_model(fuse):
+    out, host, g = _run(wl.MHA_SMALL, p=16, fuse=fuse, time_model=True)
+    assert g.info.n_repartitions == 0
+    assert g.info.n_fused == (1 if fuse else 0)
+    want = mha.mha(host)["Output"]
+    assert maxnorm_rel_err(out, want) <= 2e-2
+
+
+def test_full_layer_time_model_sampled_rows():
+    case = wl.MHA
+    out, host, g = _run(case, p=256, time_model=True)
+    assert g.info.n_repartitions == 0
+    rows = np.array([0, 3, 1500, 4095])
+    want = mha.mha(host, rows=rows)["Output"]
+    err = maxnorm_rel_err(out[rows], want)
+    assert err <= 2e-2, err
