@@ -27,13 +27,13 @@ TileShape valu_tile_shape(int variant)
 
 // Map the linear workgroup id to an output tile.  Consecutive ids land on
 // different XCDs (round-robin dispatch); regroup them so each XCD owns a
-// contiguous run of tiles, then sweep tile columns within groups of rows so
+// contiguous run of tiles, then sweep tile columns within groups of 8 rows so
 // that neighbouring workgroups share operand panels in that XCD's L2.
 __device__ __forceinline__ void tile_of(uint32_t nb, uint32_t tiles_n, uint32_t &tm, uint32_t &tn)
 {
     uint32_t b = blockIdx.x;
     if (nb % 8 == 0) b = (b % 8) * (nb / 8) + b / 8;
-    const uint32_t G = 4;
+    const uint32_t G = 8;
     uint32_t tiles_m = nb / tiles_n;
     uint32_t per = G * tiles_n;
     uint32_t g = b / per, first = g * G;
