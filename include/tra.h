@@ -265,7 +265,31 @@ int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_cap, int64_t
  * Errors: those of tra_choose; TRA_E_OP for an unknown flag.
  */
 #define TRA_CHOOSE_TIME 1
-int tra_choose_ex(const char *graph_desc, int P, int flags, int32_t *d_out, int d_cap, int64_t *cost_out);
+/*
+ * mem_cap_bytes (0 = none): the memory-aware variant of the DP (the
+ * EinDecomp page's closing remarks: count the memory of outputs and
+ * intermediates, prune plans over the limit).  The graph executor's
+ * workspace at a node's step holds every output produced so far that is
+ * still to be read, the node's own output, its repartitioned input copies,
+ * a softmax node's logsumexp and the node's scratch; candidates, and
+ * producer choices that would need a copy, are pruned when that exceeds the
+ * cap (the executor's layout reaches that bound up to first-fit
+ * fragmentation).  TRA_E_NO_CANDIDATE when nothing fits; TRA_E_OP for a
+ * negative cap.
+ * Results are memoised per (graph, P, flags, cap) for the life of the
+ * process (the page's "optimise offline, load online"): a repeated call, or
+ * tra_graph_plan* of the same graph, skips the DP (tra_choose_cache_stats,
+ * tra_choose_cache_clear).
+ */
+int tra_choose_ex(const char *graph_desc, int P, int flags, int64_t mem_cap_bytes, int32_t *d_out, int d_cap,
+                  int64_t *cost_out);
+
+/* Hits and misses of the DP memo since the process started or the last clear.
+ * Either pointer may be NULL.  Never fails. */
+int tra_choose_cache_stats(int64_t *hits, int64_t *misses);
+
+/* Empty the DP memo and zero its counters.  Never fails. */
+int tra_choose_cache_clear(void);
 
 /*
  * tra_predict_ns -- the time model's prediction, in nanoseconds, for one
@@ -306,7 +330,8 @@ typedef struct tra_graph_s *tra_graph_t;
 typedef struct {
     int32_t n_nodes;
     int32_t n_leaves;
-    size_t workspace_bytes;   /* device scratch tra_graph_execute needs */
+    size_t workspace_bytes;   /* device scratch tra_graph_execute needs: buffers whose
+                                 live steps overlap are disjoint, others share bytes */
     int64_t out_elems;        /* elements of the output node's result */
     int32_t out_dtype;
     int64_t cost;             /* cost-model value of the chosen partition vectors */
@@ -347,6 +372,14 @@ int tra_graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d_le
 #define TRA_GRAPH_CHOOSE_TIME 2
 int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d_all, int d_len, int flags,
                       tra_graph_t *out_graph);
+
+/*
+ * tra_graph_plan_cap -- tra_graph_plan_ex with the partition vectors chosen
+ * under a workspace cap (see tra_choose_ex's mem_cap_bytes; 0 = none).
+ * Errors: those of tra_graph_plan_ex; TRA_E_NO_CANDIDATE when nothing fits;
+ * TRA_E_OP for a negative cap.
+ */
+int tra_graph_plan_cap(const char *graph_desc, int P, int flags, int64_t mem_cap_bytes, tra_graph_t *out_graph);
 
 /* Sizes of a planned graph.  Errors: TRA_E_NULL. */
 int tra_graph_info(tra_graph_t graph, tra_graph_info_t *info);

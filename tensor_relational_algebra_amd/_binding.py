@@ -60,7 +60,10 @@ def lib() -> ctypes.CDLL:
             "tra_d_from_operand_form": ([ctypes.c_char_p, P, I, P, I], I),
             "tra_cost": ([ctypes.c_char_p, P, P, I, P], I),
             "tra_choose": ([ctypes.c_char_p, I, P, I, P], I),
-            "tra_choose_ex": ([ctypes.c_char_p, I, I, P, I, P], I),
+            "tra_choose_ex": ([ctypes.c_char_p, I, I, I64, P, I, P], I),
+            "tra_choose_cache_stats": ([P, P], I),
+            "tra_choose_cache_clear": ([], I),
+            "tra_graph_plan_cap": ([ctypes.c_char_p, I, I, I64, P], I),
             "tra_predict_ns": ([P, P], I),
             "tra_predict_repartition_ns": ([P, I, I, P], I),
             "tra_graph_plan": ([ctypes.c_char_p, I, P, I, P], I),
@@ -227,13 +230,14 @@ def from_relation(rel: torch.Tensor, shape: Sequence[int], d: Sequence[int], out
 CHOOSE_TIME = 1
 
 
-def tra_choose(graph_desc: str, p: int, flags: int = 0) -> Tuple[List[List[int]], int]:
+def tra_choose(graph_desc: str, p: int, flags: int = 0, mem_cap: int = 0) -> Tuple[List[List[int]], int]:
     """Partition vectors for every node of an EinGraph (see include/tra.h);
-    flags=CHOOSE_TIME selects the measured time model (cost in ns)."""
+    flags=CHOOSE_TIME selects the measured time model (cost in ns); mem_cap > 0
+    bounds the workspace live at every node's step (bytes)."""
     cap = 24 * max(1, graph_desc.count("\n") + 1)
     out = (ctypes.c_int32 * cap)()
     cost = ctypes.c_int64()
-    _check(lib().tra_choose_ex(graph_desc.encode(), int(p), int(flags), out, cap, ctypes.byref(cost)))
+    _check(lib().tra_choose_ex(graph_desc.encode(), int(p), int(flags), int(mem_cap), out, cap, ctypes.byref(cost)))
     res, pos = [], 0
     for line in graph_desc.splitlines():
         f = line.split()
@@ -291,6 +295,24 @@ class Graph:
 
 GRAPH_FUSE_ATTENTION = 1
 GRAPH_CHOOSE_TIME = 2
+
+
+def tra_choose_cache_stats() -> Tuple[int, int]:
+    """(hits, misses) of the chooser's DP memo."""
+    h, m = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().tra_choose_cache_stats(ctypes.byref(h), ctypes.byref(m)))
+    return h.value, m.value
+
+
+def tra_choose_cache_clear() -> None:
+    _check(lib().tra_choose_cache_clear())
+
+
+def tra_graph_plan_cap(graph_desc: str, p: int = 256, flags: int = 0, mem_cap: int = 0) -> Graph:
+    """tra_graph_plan_ex with the DP run under a workspace cap (bytes; 0 = none)."""
+    h = ctypes.c_void_p()
+    _check(lib().tra_graph_plan_cap(graph_desc.encode(), int(p), int(flags), int(mem_cap), ctypes.byref(h)))
+    return Graph(h.value)
 
 
 def tra_predict_ns(plan: Plan) -> int:

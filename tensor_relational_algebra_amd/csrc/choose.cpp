@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <sstream>
 #include <string>
 #include <vector>
@@ -182,20 +183,31 @@ int parse_graph(const char *desc, std::vector<GNode> &nodes)
     return TRA_OK;
 }
 
-// Predicted time of node g under candidate c (time model): the node's own
-// kernels, plus the repartition of every graph input it needs in a blocking
-// other than dense, plus, for the output node, the repartition back to dense.
-// Returns false when the planner rejects the candidate.
-static bool node_time(const GNode &g, const Cand &c, bool is_root, int64_t &ns)
+static int64_t tensor_bytes(const GNode &g, const std::string &labels, int dtype)
+{
+    int64_t n = dtype == D_BF16 ? 2 : 4;
+    for (char l : labels) n *= g.B[(int)l];
+    return n;
+}
+
+// Plan node g under candidate c.  Time model: ns = the node's own kernels'
+// predicted time, plus the repartition of every graph input it needs in a
+// blocking other than dense, plus, for the output node, the repartition back
+// to dense.  mem = the d-dependent workspace of its step: the plans' scratch
+// and the repartitioned copies of graph inputs.  False when the planner
+// rejects the candidate.
+static bool node_eval(const GNode &g, const Cand &c, bool is_root, int64_t &ns, int64_t &mem)
 {
     std::vector<int64_t> b;
     for (char l : g.canon) b.push_back(g.B[(int)l]);
     ns = 0;
+    int64_t scratch = 0;
     auto plan_ns = [&](const std::string &spec, const std::vector<int32_t> &d, const std::vector<int64_t> &bb,
                        int join, int agg, int idt, int odt, float scale) {
         tra_plan_t p = nullptr;
         if (tra_plan(spec.c_str(), bb.data(), d.data(), (int)bb.size(), join, agg, idt, odt, scale, &p)) return false;
         ns += predict_plan_ns(*p);
+        scratch = std::max(scratch, (int64_t)p->info.workspace_bytes);
         tra_plan_destroy(p);
         return true;
     };
@@ -208,6 +220,7 @@ static bool node_time(const GNode &g, const Cand &c, bool is_root, int64_t &ns)
     } else if (!plan_ns(g.spec, c.d, b, TRA_JOIN_MUL, TRA_AGG_SUM, g.in_dtype, g.out_dtype, g.scale)) {
         return false;
     }
+    mem = scratch ? ws_round(scratch) : 0;
     auto dense = [&](const std::string &labels) {
         for (char l : labels)
             if (c.d[g.canon.find(l)] != 1) return false;
@@ -219,12 +232,15 @@ static bool node_time(const GNode &g, const Cand &c, bool is_root, int64_t &ns)
         return n;
     };
     for (size_t s = 0; s < g.src.size(); ++s)
-        if (g.src[s] < 0 && !dense(g.ops[s])) ns += predict_repartition_ns(elems(g.ops[s]), g.in_dtype);
+        if (g.src[s] < 0 && !dense(g.ops[s])) {
+            ns += predict_repartition_ns(elems(g.ops[s]), g.in_dtype);
+            mem += ws_round(tensor_bytes(g, g.ops[s], g.in_dtype));
+        }
     if (is_root && !dense(g.out)) ns += predict_repartition_ns(elems(g.out), g.out_dtype);
     return true;
 }
 
-static void make_candidates(GNode &g, int P, int model, bool is_root)
+static void make_candidates(GNode &g, int P, int model, bool is_root, int64_t mem_cap, int64_t base)
 {
     const size_t L = g.canon.size();
     std::vector<std::vector<int32_t>> opts(L);
@@ -240,13 +256,17 @@ static void make_candidates(GNode &g, int P, int model, bool is_root)
             c.d[i] = opts[i][idx[i]];
             n *= c.d[i];
         }
-        if (model == COST_TIME) {
+        if (model == COST_TIME || (n >= P && n % P == 0)) {
             c.n_tasks = n;
-            if (node_time(g, c, is_root, c.cost)) g.cands.push_back(std::move(c));
-        } else if (n >= P && n % P == 0) {
-            c.n_tasks = n;
-            c.cost = node_cost(g, c);
-            g.cands.push_back(std::move(c));
+            bool ok = true;
+            if (model == COST_TIME || mem_cap > 0) {
+                int64_t ns = 0;
+                ok = node_eval(g, c, is_root, ns, c.mem);
+                if (model == COST_TIME) c.cost = ns;
+            }
+            if (model != COST_TIME) c.cost = node_cost(g, c);
+            if (ok && mem_cap > 0 && base + c.mem > mem_cap) ok = false;
+            if (ok) g.cands.push_back(std::move(c));
         }
         size_t i = L;
         while (i > 0) {
@@ -267,19 +287,75 @@ static std::vector<int32_t> blocking(const GNode &g, const Cand &c, const std::s
     return b;
 }
 
-int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &d_out, int64_t &cost, int model)
+// Memo of DP results (the EinDecomp page's closing remarks: optimise plans
+// offline, load them online).  Keyed by everything the DP reads.
+struct DpMemo {
+    std::mutex mu;
+    std::map<std::string, std::pair<std::vector<std::vector<int32_t>>, int64_t>> table;
+    int64_t hits = 0, misses = 0;
+};
+static DpMemo &memo()
+{
+    static DpMemo m;
+    return m;
+}
+
+static std::string dp_key(const std::vector<GNode> &nodes, int P, int model, int64_t mem_cap)
+{
+    std::ostringstream k;
+    k << P << '|' << model << '|' << mem_cap;
+    for (const GNode &g : nodes) {
+        k << '\n' << g.name << ' ' << g.kind << ' ' << g.spec << ' ' << g.in_dtype << ' ' << g.out_dtype << ' '
+          << g.scale;
+        for (char c : g.canon) k << ' ' << c << '=' << g.B[(int)c];
+        for (int s : g.src) k << ' ' << s;
+    }
+    return k.str();
+}
+
+int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &d_out, int64_t &cost, int model,
+           int64_t mem_cap)
 {
     if (P < 1) return fail(TRA_E_GRAPH, "P must be >= 1");
-    std::vector<int> used(nodes.size(), 0);
-    for (auto &g : nodes)
-        for (int s : g.src)
-            if (s >= 0) used[s]++;
-    for (size_t v = 0; v < nodes.size(); ++v) {
-        GNode &g = nodes[v];
-        make_candidates(g, P, model, used[v] == 0);
-        if (g.cands.empty()) return fail(TRA_E_NO_CANDIDATE, "no admissible partition vector for " + g.name);
+    const std::string key = dp_key(nodes, P, model, mem_cap);
+    {
+        DpMemo &m = memo();
+        std::lock_guard<std::mutex> lk(m.mu);
+        auto it = m.table.find(key);
+        if (it != m.table.end()) {
+            m.hits++;
+            d_out = it->second.first;
+            cost = it->second.second;
+            return TRA_OK;
+        }
+        m.misses++;
     }
-    for (size_t v = 0; v < nodes.size(); ++v) {
+    const int n = (int)nodes.size();
+    std::vector<int> consumer(n, -1);
+    for (int x = 0; x < n; ++x)
+        for (int s : nodes[x].src)
+            if (s >= 0) consumer[s] = x;
+    // workspace live at step v whatever d is: outputs produced at or before v
+    // that are read at or after v, and a softmax node's logsumexp
+    std::vector<int64_t> base(n, 0);
+    if (mem_cap > 0)
+        for (int v = 0; v < n; ++v) {
+            for (int u = 0; u <= v; ++u)
+                if (u == v || consumer[u] >= v)
+                    base[v] += ws_round(tensor_bytes(nodes[u], nodes[u].out, nodes[u].out_dtype));
+            if (nodes[v].kind == "softmax") {
+                const std::string &o = nodes[v].out;
+                base[v] += ws_round(tensor_bytes(nodes[v], o.substr(0, o.size() - 1), D_F32));
+            }
+        }
+    for (int v = 0; v < n; ++v) {
+        GNode &g = nodes[v];
+        make_candidates(g, P, model, consumer[v] < 0, mem_cap, base[v]);
+        if (g.cands.empty())
+            return fail(TRA_E_NO_CANDIDATE, mem_cap > 0 ? "no partition vector for " + g.name + " fits the memory cap"
+                                                        : "no admissible partition vector for " + g.name);
+    }
+    for (int v = 0; v < n; ++v) {
         GNode &g = nodes[v];
         // per input slot: producer's global best and best per output blocking
         struct SlotInfo {
@@ -287,6 +363,7 @@ int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &
             int best = -1;
             std::map<std::vector<int32_t>, int> by_block;
             int64_t size = 0;
+            int64_t copy_bytes = 0;
         };
         std::vector<SlotInfo> slots(g.src.size());
         for (size_t s = 0; s < g.src.size(); ++s) {
@@ -298,8 +375,10 @@ int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &
             for (char c : pu.out) size *= pu.B[(int)c];
             // the repartition term: numbers moved, or the predicted copy time
             slots[s].size = model == COST_TIME ? predict_repartition_ns(size, pu.out_dtype) : size;
+            slots[s].copy_bytes = ws_round(tensor_bytes(pu, pu.out, pu.out_dtype));
             for (int i = 0; i < (int)pu.cands.size(); ++i) {
                 const Cand &c = pu.cands[i];
+                if (!c.feasible) continue;
                 if (slots[s].best < 0 || key_less(c, c.dp, pu.cands[slots[s].best], pu.cands[slots[s].best].dp))
                     slots[s].best = i;
                 auto blk = blocking(pu, c, pu.out);
@@ -312,40 +391,50 @@ int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &
         for (Cand &c : g.cands) {
             c.dp = c.cost;
             c.pick.assign(g.src.size(), -1);
-            for (size_t s = 0; s < g.src.size(); ++s) {
+            int64_t used = base[v] + c.mem;   // checked against the cap as copies are added
+            for (size_t s = 0; s < g.src.size() && c.feasible; ++s) {
                 if (slots[s].u < 0) continue;
                 GNode &pu = nodes[slots[s].u];
+                if (slots[s].best < 0) {
+                    c.feasible = false;
+                    break;
+                }
                 auto want = blocking(g, c, g.ops[s]);
                 const Cand &gb = pu.cands[slots[s].best];
-                int64_t gcost = gb.dp + (blocking(pu, gb, pu.out) == want ? 0 : slots[s].size);
+                const bool gb_copies = blocking(pu, gb, pu.out) != want;
+                int64_t gcost = gb.dp + (gb_copies ? slots[s].size : 0);
                 int pick = slots[s].best;
                 int64_t pcost = gcost;
+                bool copies = gb_copies;
                 auto it = slots[s].by_block.find(want);
                 if (it != slots[s].by_block.end()) {
                     const Cand &mb = pu.cands[it->second];
-                    if (key_less(mb, mb.dp, gb, gcost)) {
+                    if (key_less(mb, mb.dp, gb, gcost) || (mem_cap > 0 && copies && used + slots[s].copy_bytes > mem_cap)) {
                         pick = it->second;
                         pcost = mb.dp;
+                        copies = false;
                     }
+                }
+                if (copies && mem_cap > 0) {
+                    if (used + slots[s].copy_bytes > mem_cap) {
+                        c.feasible = false;
+                        break;
+                    }
+                    used += slots[s].copy_bytes;
                 }
                 c.pick[s] = pick;
                 c.dp += pcost;
             }
         }
     }
-    // the output node is the one nobody consumes (the last one in a valid tree)
-    std::vector<int> uses(nodes.size(), 0);
-    for (auto &g : nodes)
-        for (int s : g.src)
-            if (s >= 0) uses[s]++;
-    int root = -1;
-    for (size_t j = 0; j < nodes.size(); ++j)
-        if (!uses[j]) root = (int)j;
+    const int root = (int)(std::find(consumer.begin(), consumer.end(), -1) - consumer.begin());
     GNode &rg = nodes[root];
-    int ri = 0;
-    for (int i = 1; i < (int)rg.cands.size(); ++i)
-        if (key_less(rg.cands[i], rg.cands[i].dp, rg.cands[ri], rg.cands[ri].dp)) ri = i;
-    std::vector<int> chosen(nodes.size(), -1);
+    int ri = -1;
+    for (int i = 0; i < (int)rg.cands.size(); ++i)
+        if (rg.cands[i].feasible && (ri < 0 || key_less(rg.cands[i], rg.cands[i].dp, rg.cands[ri], rg.cands[ri].dp)))
+            ri = i;
+    if (ri < 0) return fail(TRA_E_NO_CANDIDATE, "no choice of partition vectors fits the memory cap");
+    std::vector<int> chosen(n, -1);
     std::vector<std::pair<int, int>> stack{{root, ri}};
     while (!stack.empty()) {
         auto [v, i] = stack.back();
@@ -355,8 +444,12 @@ int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &
             if (nodes[v].src[s] >= 0) stack.push_back({nodes[v].src[s], nodes[v].cands[i].pick[s]});
     }
     d_out.clear();
-    for (size_t v = 0; v < nodes.size(); ++v) d_out.push_back(nodes[v].cands[chosen[v]].d);
+    for (int v = 0; v < n; ++v) d_out.push_back(nodes[v].cands[chosen[v]].d);
     cost = rg.cands[ri].dp;
+    DpMemo &m = memo();
+    std::lock_guard<std::mutex> lk(m.mu);
+    if (m.table.size() >= 256) m.table.clear();
+    m.table[key] = {d_out, cost};
     return TRA_OK;
 }
 
@@ -366,13 +459,33 @@ using namespace tra;
 
 extern "C" int tra_choose(const char *graph_desc, int P, int32_t *d_out, int d_cap, int64_t *cost_out)
 {
-    return tra_choose_ex(graph_desc, P, 0, d_out, d_cap, cost_out);
+    return tra_choose_ex(graph_desc, P, 0, 0, d_out, d_cap, cost_out);
 }
 
-extern "C" int tra_choose_ex(const char *graph_desc, int P, int flags, int32_t *d_out, int d_cap, int64_t *cost_out)
+extern "C" int tra_choose_cache_stats(int64_t *hits, int64_t *misses)
+{
+    DpMemo &m = memo();
+    std::lock_guard<std::mutex> lk(m.mu);
+    if (hits) *hits = m.hits;
+    if (misses) *misses = m.misses;
+    return TRA_OK;
+}
+
+extern "C" int tra_choose_cache_clear(void)
+{
+    DpMemo &m = memo();
+    std::lock_guard<std::mutex> lk(m.mu);
+    m.table.clear();
+    m.hits = m.misses = 0;
+    return TRA_OK;
+}
+
+extern "C" int tra_choose_ex(const char *graph_desc, int P, int flags, int64_t mem_cap_bytes, int32_t *d_out,
+                             int d_cap, int64_t *cost_out)
 {
     if (!graph_desc || !d_out) return fail(TRA_E_NULL, "graph_desc / d_out is NULL");
     if (flags & ~TRA_CHOOSE_TIME) return fail(TRA_E_OP, "unknown chooser flag");
+    if (mem_cap_bytes < 0) return fail(TRA_E_OP, "negative memory cap");
     std::vector<GNode> nodes;
     int rc = parse_graph(graph_desc, nodes);
     if (rc) return rc;
@@ -381,7 +494,7 @@ extern "C" int tra_choose_ex(const char *graph_desc, int P, int flags, int32_t *
     if ((size_t)d_cap < need) return fail(TRA_E_BUFFER, "d_out needs " + std::to_string(need) + " entries");
     std::vector<std::vector<int32_t>> ds;
     int64_t cost = 0;
-    rc = run_dp(nodes, P, ds, cost, (flags & TRA_CHOOSE_TIME) ? COST_TIME : COST_PAGES);
+    rc = run_dp(nodes, P, ds, cost, (flags & TRA_CHOOSE_TIME) ? COST_TIME : COST_PAGES, mem_cap_bytes);
     if (rc) return rc;
     size_t pos = 0;
     for (auto &dv : ds)

@@ -144,11 +144,73 @@ struct tra_graph_s {
 
 using namespace tra;
 
-static size_t bump(size_t &top, size_t bytes)
+// Workspace layout.  Every buffer is requested with the steps (node indices in
+// execution order) during which it is live: a node's output from its own
+// step to its last reader's, a repartitioned copy, the logsumexp of a softmax
+// node and a node's scratch for their node's step only.  Buffers whose live
+// ranges overlap get disjoint byte ranges; others may share bytes, since one
+// stream runs the nodes in order (section 4.1's "reorganise intermediates",
+// and the memory-aware planning of the EinDecomp page's closing remarks).
+struct WsReq {
+    size_t *at;        // where the assigned offset is written
+    size_t bytes;
+    int first, last;   // live steps, inclusive
+};
+
+static void request(std::vector<WsReq> &reqs, size_t *at, size_t bytes, int first, int last = -1)
 {
-    size_t at = (top + 255) & ~(size_t)255;
-    top = at + bytes;
-    return at;
+    reqs.push_back({at, bytes, first, last < 0 ? first : last});
+}
+
+// First fit in a given order; returns the extent and the offsets.
+static size_t first_fit(const std::vector<WsReq> &reqs, const std::vector<size_t> &order, std::vector<size_t> &at_out)
+{
+    at_out.assign(reqs.size(), 0);
+    struct Placed {
+        size_t lo, hi;
+        int first, last;
+    };
+    std::vector<Placed> placed;
+    size_t extent = 0;
+    for (size_t i : order) {
+        const WsReq &r = reqs[i];
+        const size_t need = (r.bytes + 255) & ~(size_t)255;
+        std::vector<std::pair<size_t, size_t>> busy;
+        for (const Placed &p : placed)
+            if (p.first <= r.last && r.first <= p.last) busy.push_back({p.lo, p.hi});
+        std::sort(busy.begin(), busy.end());
+        size_t at = 0;
+        for (auto &b : busy) {
+            if (at + need <= b.first) break;
+            at = std::max(at, b.second);
+        }
+        at_out[i] = at;
+        placed.push_back({at, at + need, r.first, r.last});
+        extent = std::max(extent, at + need);
+    }
+    return extent;
+}
+
+// Two first-fit layouts, largest buffer first (the large long-lived tensors
+// leave holes the small ones fill) and in order of first use; the smaller
+// extent is kept and its offsets written.  Returns the extent.
+static size_t assign_offsets(std::vector<WsReq> &reqs)
+{
+    std::vector<size_t> by_size(reqs.size()), by_use(reqs.size());
+    for (size_t i = 0; i < reqs.size(); ++i) by_size[i] = by_use[i] = i;
+    std::stable_sort(by_size.begin(), by_size.end(), [&](size_t a, size_t b) {
+        if (reqs[a].bytes != reqs[b].bytes) return reqs[a].bytes > reqs[b].bytes;
+        return reqs[a].first < reqs[b].first;
+    });
+    std::stable_sort(by_use.begin(), by_use.end(), [&](size_t a, size_t b) {
+        if (reqs[a].first != reqs[b].first) return reqs[a].first < reqs[b].first;
+        return reqs[a].bytes > reqs[b].bytes;
+    });
+    std::vector<size_t> at_a, at_b;
+    const size_t ea = first_fit(reqs, by_size, at_a), eb = first_fit(reqs, by_use, at_b);
+    const std::vector<size_t> &at = ea <= eb ? at_a : at_b;
+    for (size_t i = 0; i < reqs.size(); ++i) *reqs[i].at = at[i];
+    return std::min(ea, eb);
 }
 
 // Resolve node v's input slot s to its producer output or graph input, with
@@ -182,7 +244,7 @@ static int source_slot(tra_graph_s *g, int v, int s, Slot &sl)
 
 // The weighted-sum node of a fused chain: sources of Q, K (the scores node's
 // inputs) and V, and the node's output buffer in its own blocking.
-static int plan_fused(tra_graph_s *g, int w, size_t &top)
+static int plan_fused(tra_graph_s *g, int w, std::vector<WsReq> &reqs, std::vector<int> &out_req)
 {
     NodeExec &e = g->ex[w];
     const GNode &W = g->nodes[w];
@@ -194,7 +256,8 @@ static int plan_fused(tra_graph_s *g, int w, size_t &top)
     e.out_dtype = W.out_dtype;
     e.out_elems = 1;
     for (char c : W.out) e.out_elems *= W.B[(int)c];
-    e.out = bump(top, (size_t)e.out_elems * dsize(W.out_dtype));
+    out_req[w] = (int)reqs.size();
+    request(reqs, &e.out, (size_t)e.out_elems * dsize(W.out_dtype), w, w);
     return TRA_OK;
 }
 
@@ -315,13 +378,28 @@ static std::vector<AttnChain> find_attention(const std::vector<GNode> &nodes,
     return out;
 }
 
+static int graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d_len, int flags, int64_t mem_cap,
+                      tra_graph_t *out);
+
 extern "C" int tra_graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d_len, tra_graph_t *out)
 {
-    return tra_graph_plan_ex(graph_desc, P, d_all, d_len, 0, out);
+    return graph_plan(graph_desc, P, d_all, d_len, 0, 0, out);
 }
 
 extern "C" int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d_all, int d_len, int flags,
                                  tra_graph_t *out)
+{
+    return graph_plan(graph_desc, P, d_all, d_len, flags, 0, out);
+}
+
+extern "C" int tra_graph_plan_cap(const char *graph_desc, int P, int flags, int64_t mem_cap_bytes, tra_graph_t *out)
+{
+    if (mem_cap_bytes < 0) return gfail(TRA_E_OP, "negative memory cap");
+    return graph_plan(graph_desc, P, nullptr, 0, flags, mem_cap_bytes, out);
+}
+
+static int graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d_len, int flags, int64_t mem_cap,
+                      tra_graph_t *out)
 {
     if (!graph_desc || !out) return gfail(TRA_E_NULL, "graph_desc / out is NULL");
     if (flags & ~(TRA_GRAPH_FUSE_ATTENTION | TRA_GRAPH_CHOOSE_TIME)) return gfail(TRA_E_OP, "unknown graph flag");
@@ -345,7 +423,7 @@ extern "C" int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d
         if (pos != (size_t)d_len) return bad(gfail(TRA_E_DLEN, "d_all has extra entries"));
         g->cost = -1;
     } else {
-        rc = run_dp(g->nodes, P, ds, g->cost, (flags & TRA_GRAPH_CHOOSE_TIME) ? COST_TIME : COST_PAGES);
+        rc = run_dp(g->nodes, P, ds, g->cost, (flags & TRA_GRAPH_CHOOSE_TIME) ? COST_TIME : COST_PAGES, mem_cap);
         if (rc) return bad(rc);
     }
     std::vector<int> uses(n, 0);
@@ -365,14 +443,15 @@ extern "C" int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d
             g->n_fused++;
         }
     }
-    size_t top = 0;
+    std::vector<WsReq> reqs;
+    std::vector<int> out_req(n, -1);   // index of each node's output request
     for (size_t v = 0; v < n; ++v) {
         GNode &nd = g->nodes[v];
         NodeExec &e = g->ex[v];
         e.d = ds[v];
         if (e.fused == 1) continue;   // folded into its weighted-sum node
         if (e.fused == 2) {
-            rc = plan_fused(g, (int)v, top);
+            rc = plan_fused(g, (int)v, reqs, out_req);
             if (rc) return bad(rc);
             continue;
         }
@@ -435,13 +514,14 @@ extern "C" int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d
                 if (sl.d_from != sl.d_to) g->n_repart++;
             }
             sl.repart = sl.d_from != sl.d_to;
-            if (sl.repart) sl.buf = bump(top, (size_t)elems * dsize(nd.in_dtype));
+            if (sl.repart) request(reqs, &sl.buf, (size_t)elems * dsize(nd.in_dtype), (int)v);
         }
-        e.out = bump(top, (size_t)e.out_elems * dsize(nd.out_dtype));
+        out_req[v] = (int)reqs.size();
+        request(reqs, &e.out, (size_t)e.out_elems * dsize(nd.out_dtype), (int)v, (int)v);
         if (e.plan2) {
             tra_plan_info_t li{};
             tra_plan_info(e.plan, &li);
-            e.lse = bump(top, (size_t)li.z_elems * 4);
+            request(reqs, &e.lse, (size_t)li.z_elems * 4, (int)v);
         }
         tra_plan_info(e.plan, &pi);
         size_t sb = pi.workspace_bytes;
@@ -451,9 +531,26 @@ extern "C" int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d
             sb = std::max(sb, p2.workspace_bytes);
         }
         e.scratch_bytes = sb;
-        if (sb) e.scratch = bump(top, sb);
+        if (sb) request(reqs, &e.scratch, sb, (int)v);
     }
-    g->ws = (top + 255) & ~(size_t)255;
+    // an output stays live until its last reader's step (the root's until its
+    // own step, which writes it back dense)
+    for (size_t x = 0; x < n; ++x) {
+        const NodeExec &e = g->ex[x];
+        if (e.fused == 1) continue;
+        auto reads = [&](int p) {
+            if (p >= 0 && out_req[p] >= 0) reqs[out_req[p]].last = std::max(reqs[out_req[p]].last, (int)x);
+        };
+        if (e.fused == 2) {
+            for (const Slot &sl : e.qkv) reads(sl.node);
+        } else {
+            for (size_t s = 0; s < g->nodes[x].ops.size(); ++s) reads(e.slot[s].node);
+        }
+    }
+    g->ws = assign_offsets(reqs);
+    if (mem_cap > 0 && (int64_t)g->ws > mem_cap)
+        return bad(gfail(TRA_E_NO_CANDIDATE, "the chosen plan's workspace layout needs " + std::to_string(g->ws) +
+                                                 " bytes, over the memory cap (layout fragmentation)"));
     *out = g;
     return TRA_OK;
 }

@@ -12,7 +12,9 @@ struct Cand {
     std::vector<int32_t> d;  // canonical order
     int64_t n_tasks = 0;
     int64_t cost = 0;        // node cost
+    int64_t mem = 0;         // workspace bytes of its own step that depend on d (scratch, input copies)
     int64_t dp = 0;          // accumulated
+    bool feasible = true;    // false: every way to feed it breaks the memory cap
     std::vector<int> pick;   // chosen producer candidate per input slot (-1 = graph input)
 };
 
@@ -39,8 +41,15 @@ int parse_graph(const char *desc, std::vector<GNode> &nodes);
 enum CostModel { COST_PAGES = 0, COST_TIME = 1 };
 
 // Choose d for every node (canonical label order per node) and the total cost.
+// mem_cap > 0: the workspace live at every node's step (outputs still to be
+// read, the node's repartition copies, its scratch) must fit in mem_cap bytes;
+// candidates and producer choices that break it are pruned.  Results are
+// memoised per (graph, P, model, cap).
 int run_dp(std::vector<GNode> &nodes, int P, std::vector<std::vector<int32_t>> &d_out, int64_t &cost,
-           int model = COST_PAGES);
+           int model = COST_PAGES, int64_t mem_cap = 0);
+
+// Workspace bytes of one buffer as the graph executor lays it out.
+inline int64_t ws_round(int64_t bytes) { return (bytes + 255) & ~(int64_t)255; }
 
 // Measured time model (timemodel.cpp).
 int64_t predict_plan_ns(const tra_plan_s &p);

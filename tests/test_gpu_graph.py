@@ -128,3 +128,25 @@ def test_full_layer_time_model_sampled_rows():
     want = mha.mha(host, rows=rows)["Output"]
     err = maxnorm_rel_err(out[rows], want)
     assert err <= 2e-2, err
+
+
+# --- workspace reuse and the memory cap ---
+
+def test_memory_capped_chain_of_products():
+    # three fp32 products; the cap forces a costlier, smaller plan, and the
+    # executor reuses dead buffers; parity with the fp64 chain either way
+    from oracle import ref
+    desc = "\n".join([
+        "A einsum ij,jk->ik i=256,j=256,k=256 @X,@Y in=f32 out=f32",
+        "B einsum ik,kl->il i=256,k=256,l=256 A,@W in=f32 out=f32",
+        "C einsum il,lm->im i=256,l=256,m=256 B,@V in=f32 out=f32",
+    ])
+    host = {n: wl.draw(7700 + i, (256, 256), "uniform", "f32") for i, n in enumerate(("X", "Y", "W", "V"))}
+    want = ref.einsum("il,lm->im", ref.einsum("ik,kl->il", ref.einsum("ij,jk->ik", host["X"], host["Y"]), host["W"]),
+                      host["V"])
+    g0 = tra.tra_graph_plan(desc, 16)
+    for g in (g0, tra.tra_graph_plan_cap(desc, 16, 0, g0.info.workspace_bytes - 1)):
+        dev = {k: v.to(DEV) for k, v in host.items()}
+        out = tra.tra_graph_execute(g, dev).reshape(256, 256)
+        torch.cuda.synchronize()
+        assert maxnorm_rel_err(out.cpu().double().numpy(), want) <= 1e-4
