@@ -124,6 +124,63 @@ __global__ __launch_bounds__(256) void k_rowreduce(RowDesc g, int join, int agg,
 }
 
 // Four consecutive elements of a tensor (16 bytes of fp32 / int32, 8 bytes of bf16).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16- and 8-byte vector accesses, optionally with the streaming
+// (non-temporal) hint for tensors far larger than the caches.
+template <bool NT, typename U>
+__device__ __forceinline__ U ld_hint(const U *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT, typename U>
+__device__ __forceinline__ void st_hint(U *p, U v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// Four consecutive elements through native vector registers.
+template <typename T> struct Vec4R;
+template <> struct Vec4R<float> {
+    template <bool NT> static __device__ __forceinline__ void load(const float *p, float v[4])
+    {
+        const u32x4 u = ld_hint<NT>((const u32x4 *)p);
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(u[i]);
+    }
+    template <bool NT> static __device__ __forceinline__ void store(float *p, const float v[4])
+    {
+        st_hint<NT>((u32x4 *)p, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                      __float_as_uint(v[3])});
+    }
+};
+template <> struct Vec4R<bf16_t> {
+    template <bool NT> static __device__ __forceinline__ void load(const bf16_t *p, float v[4])
+    {
+        const u32x2 u = ld_hint<NT>((const u32x2 *)p);
+        v[0] = __uint_as_float(u[0] << 16); v[1] = __uint_as_float(u[0] & 0xffff0000u);
+        v[2] = __uint_as_float(u[1] << 16); v[3] = __uint_as_float(u[1] & 0xffff0000u);
+    }
+    template <bool NT> static __device__ __forceinline__ void store(bf16_t *p, const float v[4])
+    {
+        st_hint<NT>((u32x2 *)p, u32x2{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                                      (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)});
+    }
+};
+template <> struct Vec4R<int32_t> {
+    template <bool NT> static __device__ __forceinline__ void load(const int32_t *p, int32_t v[4])
+    {
+        const u32x4 u = ld_hint<NT>((const u32x4 *)p);
+        for (int i = 0; i < 4; ++i) v[i] = (int32_t)u[i];
+    }
+    template <bool NT> static __device__ __forceinline__ void store(int32_t *p, const int32_t v[4])
+    {
+        st_hint<NT>((u32x4 *)p, u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]});
+    }
+};
+
 template <typename T> struct Vec4;
 template <> struct Vec4<float> {
     static __device__ __forceinline__ void load(const float *p, float v[4])
@@ -157,33 +214,43 @@ template <> struct Vec4<int32_t> {
     static __device__ __forceinline__ void store(int32_t *p, const int32_t v[4]) { *(int4 *)p = int4{v[0], v[1], v[2], v[3]}; }
 };
 
-// Aggregate NONE, power-of-two digits: each thread owns groups of 4
-// consecutive outputs (contiguous in X and Z; Y contiguous or broadcast).
-template <typename TI, typename TO>
+// Aggregate NONE, power-of-two digits: each thread owns UPT groups of 4
+// consecutive outputs (contiguous in X and Z; Y contiguous or broadcast),
+// 256 groups apart; every load is issued before the first store.
+template <typename TI, typename TO, int UPT, bool NT>
 __global__ __launch_bounds__(256) void k_elemwise_p2(ElemDesc g, int join, int two, const TI *__restrict__ x,
                                                      const TI *__restrict__ y, TO *__restrict__ z)
 {
     using A = typename Scalar<TI>::acc;
     const uint32_t n_vec = (uint32_t)(g.n_out / 4);
-    const uint32_t stride = gridDim.x * blockDim.x;
-#pragma unroll 2
-    for (uint32_t v = blockIdx.x * blockDim.x + threadIdx.x; v < n_vec; v += stride) {
-        const uint32_t o = v * 4;
-        const int32_t xo = p2off<0>(g.out_p2, o);
-        A xv[4], yv[4] = {A(0), A(0), A(0), A(0)}, r[4];
-        Vec4<TI>::load(x + xo, xv);
-        if (two) {
-            const int32_t yo = p2off<1>(g.out_p2, o);
-            if (g.y_step) Vec4<TI>::load(y + yo, yv);
-            else yv[0] = yv[1] = yv[2] = yv[3] = Scalar<TI>::load(y, yo);
+    const uint32_t base = blockIdx.x * (256u * UPT) + threadIdx.x;
+    A xv[UPT][4], yv[UPT][4];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+        const uint32_t v = base + 256u * u;
+        for (int i = 0; i < 4; ++i) xv[u][i] = yv[u][i] = A(0);
+        if (v < n_vec) {
+            const uint32_t o = v * 4;
+            Vec4R<TI>::template load<NT>(x + p2off<0>(g.out_p2, o), xv[u]);
+            if (two) {
+                const int32_t yo = p2off<1>(g.out_p2, o);
+                if (g.y_step) Vec4R<TI>::template load<NT>(y + yo, yv[u]);
+                else yv[u][0] = yv[u][1] = yv[u][2] = yv[u][3] = Scalar<TI>::load(y, yo);
+            }
         }
+    }
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+        const uint32_t v = base + 256u * u;
+        if (v >= n_vec) break;
+        A r[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            r[i] = join_any(join, xv[i], yv[i]);
+            r[i] = join_any(join, xv[u][i], yv[u][i]);
             if constexpr (!std::is_same<A, int32_t>::value) r[i] *= g.post_scale;
         }
         if constexpr (std::is_same<A, int32_t>::value || std::is_same<TO, float>::value || std::is_same<TO, bf16_t>::value)
-            Vec4<TO>::store(z + o, r);
+            Vec4R<TO>::template store<NT>(z + v * 4, r);
     }
 }
 
@@ -207,14 +274,8 @@ __global__ __launch_bounds__(256) void k_rowreduce_p2(RowDesc g, int join, int a
         for (uint32_t c = 0; c < n_outer; ++c) {
             const int32_t xc = xo + p2off<0>(g.outer_p2, c);
             const int32_t yc = two ? yo + p2off<1>(g.outer_p2, c) : 0;
-#pragma unroll 4
-            for (uint32_t e = lane * 4; e < inner; e += 256) {
-                A v[4], w[4] = {A(0), A(0), A(0), A(0)};
-                Vec4<TI>::load(x + xc + e, v);
-                if (two) {
-                    if (g.inner_sy) Vec4<TI>::load(y + yc + e, w);
-                    else w[0] = w[1] = w[2] = w[3] = Scalar<TI>::load(y, yc);
-                }
+            // fold one lane's group of 4 (in ascending order of e)
+            auto fold4 = [&](A v[4], const A w[4]) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v[i] = join_any(join, v[i], w[i]);
                 if constexpr (std::is_same<A, float>::value) {
@@ -226,11 +287,33 @@ __global__ __launch_bounds__(256) void k_rowreduce_p2(RowDesc g, int join, int a
                                   __expf(v[2] - nm) + __expf(v[3] - nm);
                             f.m = nm;
                         }
-                        continue;
+                        return;
                     }
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) f.add(agg, v[i]);
+            };
+            auto load4 = [&](uint32_t e, A v[4], A w[4]) {
+                Vec4R<TI>::template load<false>(x + xc + e, v);
+                w[0] = w[1] = w[2] = w[3] = A(0);
+                if (two) {
+                    if (g.inner_sy) Vec4R<TI>::template load<false>(y + yc + e, w);
+                    else w[0] = w[1] = w[2] = w[3] = Scalar<TI>::load(y, yc);
+                }
+            };
+            uint32_t e = lane * 4;
+            // eight 16-byte loads per lane in flight, then their folds
+            for (; e + 256 * 7 < inner; e += 256 * 8) {
+                A v[8][4], w[8][4];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) load4(e + 256 * j, v[j], w[j]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) fold4(v[j], w[j]);
+            }
+            for (; e < inner; e += 256) {
+                A v[4], w[4];
+                load4(e, v, w);
+                fold4(v, w);
             }
         }
         if constexpr (std::is_same<A, float>::value) {
@@ -266,8 +349,6 @@ __global__ __launch_bounds__(256) void k_split_fold(const A *__restrict__ ws, in
 }
 
 // ---------------------------------------------------------------- repartition
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Destination positions are enumerated in the destination's own layout, so
 // writes are sequential; each digit of the destination index maps to a
@@ -376,10 +457,21 @@ int launch_elemwise(const tra_plan_s &p, const void *x, const void *y, void *z, 
 {
     hipStream_t s = (hipStream_t)stream;
     if (p.el.p2) {
-        int grid = grid_for(p.el.n_out / 4 / 2);
-        TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
-                        hipLaunchKernelGGL((k_elemwise_p2<TI, TO>), dim3(grid), dim3(256), 0, s, p.el, p.join,
-                                           p.n_ops == 2 ? 1 : 0, (const TI *)x, (const TI *)y, (TO *)z));
+        // as the repartition: four groups per thread, and streaming accesses for
+        // tensors far beyond the caches (the [h,s,t] tensors of attention)
+        const int64_t n_vec = p.el.n_out / 4;
+        const int64_t bytes = p.info.x_bytes + (p.el.y_step ? p.info.y_bytes : 0) + p.info.z_bytes;
+        const bool big = bytes >= (64ll << 20), wide = n_vec >= 256 * 256 * 4;
+        const int upt = big || wide ? 4 : 1;
+        const unsigned grid = (unsigned)((n_vec + 256 * upt - 1) / (256 * upt));
+#define TRA_EL_GO(UPT, NT)                                                                                    \
+    TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,                                                                  \
+                    hipLaunchKernelGGL((k_elemwise_p2<TI, TO, UPT, NT>), dim3(grid), dim3(256), 0, s, p.el,     \
+                                       p.join, p.n_ops == 2 ? 1 : 0, (const TI *)x, (const TI *)y, (TO *)z))
+        if (big) TRA_EL_GO(4, true);
+        else if (wide) TRA_EL_GO(4, false);
+        else TRA_EL_GO(1, false);
+#undef TRA_EL_GO
         return (int)hipGetLastError();
     }
     int grid = grid_for(p.el.n_out / p.el.vec);
