@@ -39,8 +39,8 @@ struct Calibration {
     double valu_terms = 22.1e3;        // register-tiled vector-ALU joins (squared distance)
     double rowreduce_terms = 1155.0;   // one wavefront per output element, compute-bound
     double generic_terms = 1046.0;     // one thread per output element
-    double rowreduce_bw = 4340.0;      // row-reduce, bandwidth-bound (logsumexp over t)
-    double stream_bw = 5270.0;         // elementwise and one-thread-per-output kernels
+    double rowreduce_bw = 5025.0;      // row-reduce, bandwidth-bound (logsumexp over t)
+    double stream_bw = 5520.0;         // elementwise and one-thread-per-output kernels
     double tile_bw = 6080.0;           // bandwidth bound of the tile kernels (small-tile matrix-core case)
     double copy_bw = 5755.0;           // repartition
 };
