@@ -10,9 +10,10 @@ silently wrong.  This test compiles the kernels to AMD assembly on the host
 and checks every kernel for an instruction that reads, or overwrites, a VGPR
 whose LDS read is still in flight.
 
-LDS reads retire in issue order, so ``s_waitcnt lgkmcnt(n)`` completes all but
-the newest n.  The scan follows straight-line order (a label keeps the state of
-the fall-through path) and counts scalar memory loads as in-flight entries too.
+LDS operations retire in issue order, so ``s_waitcnt lgkmcnt(n)`` completes all
+but the newest n.  The scan follows straight-line order (a label keeps the state
+of the fall-through path) and counts every other LDS operation (writes too) and
+scalar memory loads as in-flight entries.
 """
 from __future__ import annotations
 
@@ -51,9 +52,21 @@ def scan_function(body: str) -> list[str]:
         if not line or line.startswith(".") or line.endswith(":"):
             continue
         op = line.split()[0]
+        pending = set().union(*queue) if queue else set()
+        parts = line.split(None, 1)
+        ops = [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
         m = _LDS_READ.match(line)
         if m:
+            if any(_regs(o) & pending for o in ops):        # its address, or its destination
+                bad.append(line)
             queue.append(set(range(int(m.group(2)), int(m.group(3)) + 1)) if m.group(2) else {int(m.group(4))})
+            continue
+        if op.startswith("ds_"):
+            # any other LDS operation (a write, an atomic) counts against lgkmcnt
+            # and reads its register operands when issued
+            if any(_regs(o) & pending for o in ops):
+                bad.append(line)
+            queue.append(set())
             continue
         if op.startswith(("s_load", "s_buffer_load")):
             queue.append(set())
@@ -63,11 +76,8 @@ def scan_function(body: str) -> list[str]:
             n = int(w.group(1))
             queue = queue[len(queue) - n:] if n < len(queue) else queue
             continue
-        if op.startswith("s_") or op.startswith("global_load_lds") or not queue:
+        if op.startswith("s_") or op.startswith("global_load_lds") or not pending:
             continue
-        pending = set().union(*queue)
-        parts = line.split(None, 1)
-        ops = [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
         if op.startswith(_STORE_PREFIXES):
             srcs, dst = ops, []
         else:
@@ -99,6 +109,13 @@ def test_scanner_flags_a_copy_of_an_in_flight_register():
     """
     bad = scan_function(body)
     assert bad == ["v_mov_b32_e32 v41, v14", "v_add_u32_e32 v20, 1, v5"]
+    # LDS writes count against lgkmcnt too: a wait for "14 outstanding" after a
+    # read and 14 younger writes covers the read; an LDS write of a register whose
+    # read is in flight is caught
+    body = "ds_read_b128 v[76:79], v67\n" + "ds_write_b32 v70, v68\n" * 14 + \
+        "s_waitcnt lgkmcnt(14)\nglobal_store_dwordx4 v[72:73], v[76:79], off\n" + \
+        "ds_read_b32 v90, v1\nds_write_b32 v2, v90\n"
+    assert scan_function(body) == ["ds_write_b32 v2, v90"]
 
 
 @pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not installed")
