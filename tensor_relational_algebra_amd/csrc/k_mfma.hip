@@ -53,10 +53,28 @@ TileShape mfma_tile_shape(int variant)
     return {c.bm, c.bn, MF_BK};
 }
 
-__device__ __forceinline__ void mfma_tile_of(uint32_t nb, uint32_t tiles_n, uint32_t &tm, uint32_t &tn)
+// Output group (batch index) and tile of this workgroup.  Consecutive
+// workgroup ids land on different XCDs (round-robin dispatch); the ids are
+// regrouped so that each XCD owns a contiguous run of tiles, and tile columns
+// are swept within groups of 4 tile-rows so that neighbouring tiles share
+// operand panels in L2.  With few tiles per output group (a batched product
+// whose per-group operand is read by every tile of the group, such as the
+// attention weighted sum) the run is taken over all groups, so that a
+// group's tiles share one XCD and its operand is fetched once.
+__device__ __forceinline__ void mfma_tile_of(uint32_t nb, uint32_t tiles_n, uint32_t n_groups, uint32_t &bidx,
+                                             uint32_t &tm, uint32_t &tn)
 {
     uint32_t b = blockIdx.x;
-    if (nb % 8 == 0) b = (b % 8) * (nb / 8) + b / 8;
+    bidx = blockIdx.y;
+    const uint32_t n_lin = nb * n_groups;
+    if (nb <= 64 && n_groups > 1 && n_lin % 8 == 0) {
+        const uint32_t l = blockIdx.x + nb * blockIdx.y;
+        const uint32_t lin = (l % 8) * (n_lin / 8) + l / 8;
+        bidx = lin / nb;
+        b = lin % nb;
+    } else if (nb % 8 == 0) {
+        b = (b % 8) * (nb / 8) + b / 8;
+    }
     const uint32_t G = 4;
     uint32_t tiles_m = nb / tiles_n;
     uint32_t per = G * tiles_n;
@@ -174,10 +192,9 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     const int wm = wave / WN, wn = wave % WN;
     const uint32_t tiles_n = v.gn.total / BN;
     const uint32_t nb = (v.gm.total / BM) * tiles_n;
-    uint32_t tm, tn;
-    mfma_tile_of(nb, tiles_n, tm, tn);
+    uint32_t tm, tn, bidx;
+    mfma_tile_of(nb, tiles_n, v.gb.total, bidx, tm, tn);
     const uint32_t m0 = tm * BM, n0 = tn * BN;
-    const uint32_t bidx = blockIdx.y;
     const int32_t bx = p2off<0>(v.gb, bidx), by = p2off<1>(v.gb, bidx), bz = p2off<2>(v.gb, bidx);
     const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
     const uint32_t nk = (uint32_t)v.k_per_split / BK;
