@@ -114,7 +114,9 @@ typedef struct {
     int32_t kernel;           /* tra_kernel_family */
     int32_t n_labels;
     char labels[32];          /* canonical label order, NUL-terminated */
-    int32_t tile;             /* tile-kernel variant (mfma: 0 = 256x256, 1 = 128x128, 2 = 64x64); -1 if none */
+    int32_t tile;             /* tile-kernel variant (mfma: 0 = 256x256, 1 = 128x128, 2 = 64x64;
+                                 valu_tile: 1 = int32 max-plus / min-plus with the packed 16-bit
+                                 path, see tra_execute, else 0); -1 if none */
 } tra_plan_info_t;
 
 /*
@@ -167,6 +169,13 @@ int tra_plan_destroy(tra_plan_t plan);
  *   workspace      device scratch of at least info.workspace_bytes (may be
  *                  NULL when that is 0); contents on entry are ignored.
  *   hip_stream     hipStream_t the kernels are enqueued on.
+ * An int32 add join aggregated by max or min on the vector-ALU tile kernel
+ * (info.tile == 1) first checks on the device whether every element of X
+ * and Y lies in [-1024, 1024].  If so, the join runs on packed binary16
+ * halves, which hold every such sum exactly, so the output is the int32
+ * result bit for bit; otherwise the 32-bit kernel runs.  The check writes its
+ * flags into the last 1024 bytes of the workspace (so such plans always need
+ * one), and the choice is made on the device with no host synchronisation.
  * Errors: TRA_E_NULL, TRA_E_ALIGN, TRA_E_WORKSPACE, TRA_E_HIP.
  */
 int tra_execute(tra_plan_t plan, const void *x_rel, const void *y_rel, void *z_rel,

@@ -263,6 +263,12 @@ static bool lower_tile(tra_plan_s &p)
         p.kernel = mfma ? TRA_KERNEL_MFMA_BF16 : TRA_KERNEL_VALU_TILE;
         int64_t tiles = (int64_t)(gv.gm.total / ts.bm) * (gv.gn.total / ts.bn) * gv.gb.total;
         choose_split(p, tiles, gv.gk.total / ts.bk, ts.bk);
+        if (!mfma && p.in_dtype == D_I32 && p.join == J_ADD && (p.agg == A_MAX || p.agg == A_MIN)) {
+            // int32 max-plus / min-plus: the packed 16-bit kernel behind a
+            // range check whose flags live in the workspace
+            p.tile = 1;
+            p.info.workspace_bytes = small_int_flags_offset(p.gv.split, p.info.z_elems) + SMALL_INT_FLAG_BYTES;
+        }
         return true;
     }
     return false;

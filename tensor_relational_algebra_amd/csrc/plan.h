@@ -37,6 +37,14 @@ int launch_mfma_bf16(const tra_plan_s &p, const void *x, const void *y, void *z,
 int launch_repartition(const RepartDesc &r, int elem_bytes, const void *src, void *dst, void *stream);
 const char *hip_error_text(int err);
 
+// Workspace of an int32 max-plus / min-plus tile plan: the split partials (if
+// any), then the range-check flag words at this byte offset.
+inline size_t small_int_flags_offset(int split, int64_t z_elems)
+{
+    return split > 1 ? ((size_t)split * (size_t)z_elems * 4 + 255) / 256 * 256 : 0;
+}
+constexpr size_t SMALL_INT_FLAG_BYTES = 256 * 4;
+
 // Tile shapes the tile kernels are instantiated for.
 struct TileShape { int bm, bn, bk; };
 TileShape valu_tile_shape(int variant);

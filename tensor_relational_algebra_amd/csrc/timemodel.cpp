@@ -37,6 +37,8 @@ struct Calibration {
     double latency_ns = 3700.0;        // per node of back-to-back launches from the library
     double mfma_terms[3] = {487e3, 163e3, 90e3};   // bf16 matrix cores, tile variants 0/1/2 (launch latency taken out)
     double valu_terms = 22.1e3;        // register-tiled vector-ALU joins (squared distance)
+    double valu_small_int_terms = 35.0e3;   // int32 max / min-plus on packed 16-bit halves, range check included
+                                            // (inputs within +-1024; outside, the 32-bit path runs at valu_terms)
     double rowreduce_terms = 1155.0;   // one wavefront per output element, compute-bound
     double generic_terms = 1046.0;     // one thread per output element
     double rowreduce_bw = 5025.0;      // row-reduce, bandwidth-bound (logsumexp over t)
@@ -63,7 +65,7 @@ int64_t predict_plan_ns(const tra_plan_s &p)
         bw = kCal.tile_bw;
         break;
     case TRA_KERNEL_VALU_TILE:
-        rate = kCal.valu_terms;
+        rate = p.tile == 1 ? kCal.valu_small_int_terms : kCal.valu_terms;
         bw = kCal.tile_bw;
         break;
     case TRA_KERNEL_GENERIC: rate = kCal.generic_terms; break;

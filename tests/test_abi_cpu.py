@@ -67,7 +67,16 @@ def test_kernel_family_choice():
     assert p.kernel == "valu_tile"
     p = tra.tra_plan("ij,jk->ik", {"i": 8192, "j": 256, "k": 8192}, {"i": 16, "j": 1, "k": 16},
                      "add", "max", "i32", "i32")
-    assert p.kernel == "valu_tile"
+    # int32 max-plus: the packed 16-bit variant, with 256 range-check flag words
+    # in the workspace
+    assert p.kernel == "valu_tile" and p.info.tile == 1 and p.info.workspace_bytes == 1024
+    p = tra.tra_plan("ij,jk->ik", {"i": 256, "j": 1024, "k": 256}, {"i": 1, "j": 1, "k": 1}, "add", "min", "i32",
+                     "i32")
+    assert p.info.tile == 1 and p.info.agg_split > 1
+    assert p.info.workspace_bytes == p.info.agg_split * 65536 * 4 + 1024
+    for idt, join, agg in (("f32", "add", "max"), ("f32", "sqdiff", "sum"), ("i32", "mul", "sum")):
+        p = tra.tra_plan("ij,jk->ik", [256, 256, 256], [1, 1, 1], join, agg, idt, idt)
+        assert p.kernel == "valu_tile" and p.info.tile == 0
     p = tra.tra_plan("hst->hs", {"h": 32, "s": 4096, "t": 4096}, {"h": 32, "s": 8, "t": 1},
                      "ident", "lse", "f32", "f32")
     assert p.kernel == "rowreduce"

@@ -107,6 +107,88 @@ def test_min_plus_variant():
                         (("int", {"lo": -50, "hi": 50}), ("int", {"lo": -50, "hi": 50}))))
 
 
+
+# ------------------------------------------------------------ int32 max-plus / min-plus: packed 16-bit path
+
+def _run_small_int(spec, bounds, d, agg, xs):
+    """Run an int32 add-join through the C ABI with an explicit workspace;
+    returns (dense output, plan, the range-check flag words)."""
+    case = wl.EinsumCase("si", 0, spec, bounds, d, "add", agg, "i32", "i32", ())
+    plan = tra.tra_plan(spec, bounds, d, "add", agg, "i32", "i32")
+    ws = torch.empty(plan.info.workspace_bytes, dtype=torch.uint8, device=DEV)
+    rels = [tra.to_relation(t.to(DEV), [d[c] for c in o]) for t, o in zip(xs, case.operand_labels())]
+    zr = tra.tra_execute(plan, rels[0], rels[1], None, ws)
+    out = case.out_labels()
+    z = tra.from_relation(zr, [bounds[c] for c in out], [d[c] for c in out])
+    torch.cuda.synchronize()
+    flags = ws[-1024:].view(torch.int32).cpu().numpy()
+    return z.cpu(), plan, flags
+
+
+def _si_inputs(spec, bounds, seed, lo, hi):
+    ops = spec.split("->")[0].split(",")
+    rng = np.random.default_rng(seed)
+    return [torch.from_numpy(rng.integers(lo, hi, size=[bounds[c] for c in o], endpoint=True, dtype=np.int32))
+            for o in ops]
+
+
+SI_CASES = [
+    ("ij,jk->ik", {"i": 2048, "j": 64, "k": 1024}, {"i": 2, "j": 2, "k": 4}),   # 128 tiles, no split
+    ("ij,jk->ik", {"i": 512, "j": 128, "k": 256}, {"i": 2, "j": 4, "k": 1}),    # X K-major, Y MN-major
+    ("ji,kj->ik", {"i": 256, "j": 64, "k": 128}, {"i": 1, "j": 2, "k": 2}),     # X MN-major, Y K-major
+    ("ij,kj->ik", {"i": 128, "j": 64, "k": 256}, {"i": 2, "j": 1, "k": 2}),     # both K-major
+    ("ji,jk->ik", {"i": 128, "j": 128, "k": 256}, {"i": 1, "j": 2, "k": 2}),    # both MN-major
+    ("ij,jk->ik", {"i": 256, "j": 2048, "k": 256}, {"i": 1, "j": 4, "k": 1}),   # 64-way split of the contraction
+]
+
+
+@pytest.mark.parametrize("agg", ["max", "min"])
+@pytest.mark.parametrize("spec,bounds,d", SI_CASES, ids=["nosplit", "ij,jk", "ji,kj", "ij,kj", "ji,jk", "split64"])
+def test_small_int_packed_path_is_exact(spec, bounds, d, agg):
+    """Inputs within [-1024, 1024], the extremes included: the range check
+    clears every flag (so the packed 16-bit kernel produced the output) and
+    the result equals the oracle's exactly."""
+    xs = _si_inputs(spec, bounds, 5, -1024, 1024)
+    for t, v in zip(xs, (-1024, 1024)):     # both extremes present in both operands
+        t.view(-1)[0] = v
+        t.view(-1)[-1] = -v
+    z, plan, flags = _run_small_int(spec, bounds, d, agg, xs)
+    assert plan.kernel == "valu_tile" and plan.info.tile == 1
+    assert not flags.any()
+    want = ref.einsum(spec, xs[0], xs[1], "add", agg)
+    assert np.array_equal(z.numpy().astype(np.int64), want)
+
+
+@pytest.mark.parametrize("agg", ["max", "min"])
+@pytest.mark.parametrize("where", ["x", "y", "both_wide"])
+@pytest.mark.parametrize("spec,bounds,d", SI_CASES[:3] + SI_CASES[5:], ids=["nosplit", "ij,jk", "ji,kj", "split64"])
+def test_small_int_out_of_range_takes_the_32_bit_path(spec, bounds, d, agg, where):
+    """One input just outside [-1024, 1024] (or every input spread over +-2^29):
+    the range check sets a flag, the 32-bit kernel produces the output, and it
+    equals the oracle's exactly."""
+    if where == "both_wide":
+        xs = _si_inputs(spec, bounds, 6, -(1 << 29), 1 << 29)
+    else:
+        xs = _si_inputs(spec, bounds, 6, -1024, 1024)
+        t = xs[0] if where == "x" else xs[1]
+        t.view(-1)[t.numel() // 3] = 1025 if agg == "max" else -1025
+    z, plan, flags = _run_small_int(spec, bounds, d, agg, xs)
+    assert flags.any()
+    want = ref.einsum(spec, xs[0], xs[1], "add", agg)
+    assert np.array_equal(z.numpy().astype(np.int64), want)
+
+
+def test_small_int_path_on_the_full_workload_sampled():
+    """The max-plus workload (values in [-1000, 1000]) at its full size and
+    blocking, as the bench runs it: flags clear, sampled outputs exact."""
+    c = wl.MAXPLUS
+    xs = c.make_inputs()
+    z, plan, flags = _run_small_int(c.spec, c.bounds, c.d, c.agg, xs)
+    assert not flags.any() and plan.info.tile == 1
+    idx = np.sort(np.random.default_rng(3).choice(z.numel(), size=4096, replace=False))
+    want = ref.einsum(c.spec, xs[0], xs[1], "add", "max", out_index=idx)
+    assert np.array_equal(z.reshape(-1)[torch.from_numpy(idx)].numpy().astype(np.int64), want)
+
 # ------------------------------------------------------------ four-index contraction
 
 C3_SMALL = {"a": 16, "b": 8, "c": 16, "d": 32, "e": 16, "f": 8}
