@@ -379,6 +379,20 @@ int tra_graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d_le
  * numbers-moved model; tra_graph_info's cost is then in nanoseconds.
  */
 #define TRA_GRAPH_CHOOSE_TIME 2
+/*
+ * TRA_GRAPH_OVERLAP_COPIES: tra_graph_execute runs every repartition copy on
+ * a second stream of the current device (created on first use, default
+ * priority, kept for the life of the process) while the nodes run in order on
+ * the caller's stream: a graph input's copy starts at once, an intermediate's
+ * as soon as its producer has run, and each consumer waits for its copies
+ * through events.  The workspace layout keeps each copy live from its
+ * producer's step (a graph input's: from the start) to its consumer's, so it
+ * can be larger than without the flag.  All work is joined back into the
+ * caller's stream before the output node runs, so the call's completion is
+ * still observed on that stream; calls on one graph object must not overlap
+ * in time (they share its events).  tra_graph_run_node is unaffected.
+ */
+#define TRA_GRAPH_OVERLAP_COPIES 4
 int tra_graph_plan_ex(const char *graph_desc, int P, const int32_t *d_all, int d_len, int flags,
                       tra_graph_t *out_graph);
 
@@ -412,7 +426,8 @@ int tra_graph_leaf(tra_graph_t graph, int leaf, char *name, int name_cap, int64_
 int tra_graph_run_node(tra_graph_t graph, int node, const void *const *leaves, int n_leaves, void *out,
                        void *workspace, size_t workspace_bytes, void *hip_stream);
 
-/* Every node in order (tra_graph_run_node for each). */
+/* Every node in order (tra_graph_run_node for each; with
+ * TRA_GRAPH_OVERLAP_COPIES the copies run on a side stream, see above). */
 int tra_graph_execute(tra_graph_t graph, const void *const *leaves, int n_leaves, void *out, void *workspace,
                       size_t workspace_bytes, void *hip_stream);
 

@@ -295,6 +295,7 @@ class Graph:
 
 GRAPH_FUSE_ATTENTION = 1
 GRAPH_CHOOSE_TIME = 2
+GRAPH_OVERLAP_COPIES = 4
 
 
 def tra_choose_cache_stats() -> Tuple[int, int]:

@@ -132,6 +132,10 @@ struct tra_graph_s {
     int64_t cost = 0;
     int n_repart = 0;
     int n_fused = 0;
+    bool overlap = false;          // copies run on a side stream (TRA_GRAPH_OVERLAP_COPIES)
+    int n_copies = 0;              // input slots that need a repartition copy (graph inputs included)
+    std::vector<void *> events;    // the overlapped executor's events, created on first use
+    int events_device = -1;        // the device they belong to
 
     ~tra_graph_s()
     {
@@ -139,6 +143,7 @@ struct tra_graph_s {
             tra_plan_destroy(e.plan);
             tra_plan_destroy(e.plan2);
         }
+        tra::events_destroy((int)events.size(), events.data());
     }
 };
 
@@ -151,6 +156,8 @@ using namespace tra;
 // ranges overlap get disjoint byte ranges; others may share bytes, since one
 // stream runs the nodes in order (section 4.1's "reorganise intermediates",
 // and the memory-aware planning of the EinDecomp page's closing remarks).
+// When copies run on a side stream, a copy is live from its producer's step
+// (step 0 for a graph input), when it may start, to its consumer's.
 struct WsReq {
     size_t *at;        // where the assigned offset is written
     size_t bytes;
@@ -402,9 +409,11 @@ static int graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d
                       tra_graph_t *out)
 {
     if (!graph_desc || !out) return gfail(TRA_E_NULL, "graph_desc / out is NULL");
-    if (flags & ~(TRA_GRAPH_FUSE_ATTENTION | TRA_GRAPH_CHOOSE_TIME)) return gfail(TRA_E_OP, "unknown graph flag");
+    if (flags & ~(TRA_GRAPH_FUSE_ATTENTION | TRA_GRAPH_CHOOSE_TIME | TRA_GRAPH_OVERLAP_COPIES))
+        return gfail(TRA_E_OP, "unknown graph flag");
     *out = nullptr;
     tra_graph_s *g = new tra_graph_s();
+    g->overlap = (flags & TRA_GRAPH_OVERLAP_COPIES) != 0;
     auto bad = [&](int rc) {
         delete g;
         return rc;
@@ -514,7 +523,11 @@ static int graph_plan(const char *graph_desc, int P, const int32_t *d_all, int d
                 if (sl.d_from != sl.d_to) g->n_repart++;
             }
             sl.repart = sl.d_from != sl.d_to;
-            if (sl.repart) request(reqs, &sl.buf, (size_t)elems * dsize(nd.in_dtype), (int)v);
+            if (sl.repart) {
+                g->n_copies++;
+                request(reqs, &sl.buf, (size_t)elems * dsize(nd.in_dtype),
+                        g->overlap ? std::max(sl.node, 0) : (int)v, (int)v);
+            }
         }
         out_req[v] = (int)reqs.size();
         request(reqs, &e.out, (size_t)e.out_elems * dsize(nd.out_dtype), (int)v, (int)v);
@@ -605,17 +618,30 @@ static int write_root(tra_graph_t g, int node, void *out, char *ws, void *stream
     return tra_repartition(b.data(), (int)b.size(), dz.data(), ones.data(), e.out_dtype, ws + e.out, out, stream);
 }
 
-extern "C" int tra_graph_run_node(tra_graph_t g, int node, const void *const *leaves, int n_leaves, void *out,
-                                  void *workspace, size_t ws_bytes, void *stream)
+static int check_run_args(tra_graph_t g, const void *const *leaves, int n_leaves, void *workspace, size_t ws_bytes)
 {
     if (!g) return gfail(TRA_E_NULL, "graph is NULL");
-    if (node < 0 || node >= (int)g->nodes.size()) return gfail(TRA_E_GRAPH, "node index out of range");
     if (g->ws && (!workspace || ws_bytes < g->ws))
         return gfail(TRA_E_WORKSPACE, "graph workspace of " + std::to_string(g->ws) + " bytes needed");
     if (n_leaves != (int)g->leaves.size() || (n_leaves && !leaves))
         return gfail(TRA_E_NULL, "expected " + std::to_string(g->leaves.size()) + " graph inputs");
-    if (node == g->root && !out) return gfail(TRA_E_NULL, "the output node needs `out`");
-    char *ws = (char *)workspace;
+    return TRA_OK;
+}
+
+// The repartition of one input slot into its workspace copy.
+static int run_copy(tra_graph_t g, const Slot &sl, const void *const *leaves, char *ws, void *stream)
+{
+    const void *src = sl.node >= 0 ? (const void *)(ws + g->ex[sl.node].out) : leaves[sl.leaf];
+    if (!src) return gfail(TRA_E_NULL, "graph input pointer is NULL");
+    return tra_repartition(sl.bounds.data(), (int)sl.bounds.size(), sl.d_from.data(), sl.d_to.data(), sl.dtype, src,
+                           ws + sl.buf, stream);
+}
+
+// One node on `stream`; its input copies too unless copies_done (the
+// overlapped executor has run them on its side stream).
+static int run_node(tra_graph_t g, int node, const void *const *leaves, void *out, char *ws, void *stream,
+                    bool copies_done)
+{
     NodeExec &e = g->ex[node];
     const GNode &nd = g->nodes[node];
     if (e.fused == 1) return TRA_OK;   // runs inside its chain's weighted-sum node
@@ -633,16 +659,16 @@ extern "C" int tra_graph_run_node(tra_graph_t g, int node, const void *const *le
     }
     const void *in[2] = {nullptr, nullptr};
     for (size_t s = 0; s < nd.ops.size(); ++s) {
-        Slot &sl = e.slot[s];
-        const void *src = sl.node >= 0 ? (const void *)(ws + g->ex[sl.node].out) : leaves[sl.leaf];
-        if (!src) return gfail(TRA_E_NULL, "graph input pointer is NULL");
+        const Slot &sl = e.slot[s];
         if (sl.repart) {
-            int rc = tra_repartition(sl.bounds.data(), (int)sl.bounds.size(), sl.d_from.data(), sl.d_to.data(),
-                                     sl.dtype, src, ws + sl.buf, stream);
-            if (rc) return rc;
+            if (!copies_done) {
+                rc = run_copy(g, sl, leaves, ws, stream);
+                if (rc) return rc;
+            }
             in[s] = ws + sl.buf;
         } else {
-            in[s] = src;
+            in[s] = sl.node >= 0 ? (const void *)(ws + g->ex[sl.node].out) : leaves[sl.leaf];
+            if (!in[s]) return gfail(TRA_E_NULL, "graph input pointer is NULL");
         }
     }
     void *scratch = e.scratch_bytes ? ws + e.scratch : nullptr;
@@ -657,13 +683,91 @@ extern "C" int tra_graph_run_node(tra_graph_t g, int node, const void *const *le
     return node == g->root ? write_root(g, node, out, ws, stream) : TRA_OK;
 }
 
+extern "C" int tra_graph_run_node(tra_graph_t g, int node, const void *const *leaves, int n_leaves, void *out,
+                                  void *workspace, size_t ws_bytes, void *stream)
+{
+    int rc = check_run_args(g, leaves, n_leaves, workspace, ws_bytes);
+    if (rc) return rc;
+    if (node < 0 || node >= (int)g->nodes.size()) return gfail(TRA_E_GRAPH, "node index out of range");
+    if (node == g->root && !out) return gfail(TRA_E_NULL, "the output node needs `out`");
+    return run_node(g, node, leaves, out, (char *)workspace, stream, false);
+}
+
+static int hip_fail(int rc, const char *what)
+{
+    return gfail(TRA_E_HIP, std::string(what) + ": " + hip_error_text(rc));
+}
+
+// Nodes in order on `stream`; every repartition copy on the device's side
+// stream, started as soon as its source exists (graph inputs at once, an
+// intermediate when its producer has run), the consumer waiting for it.
+// Events: [0] start, [1 + v] node v done, [1 + n + 2v + s] copy of v's slot s.
+static int execute_overlapped(tra_graph_t g, const void *const *leaves, void *out, char *ws, void *stream)
+{
+    const int n = (int)g->nodes.size();
+    int dev = 0, rc = current_device(&dev);
+    if (rc) return hip_fail(rc, "hipGetDevice");
+    void *side = nullptr;
+    rc = side_stream(&side);
+    if (rc) return hip_fail(rc, "side stream");
+    if (g->events.empty() || g->events_device != dev) {
+        events_destroy((int)g->events.size(), g->events.data());
+        g->events.assign(1 + 3 * (size_t)n, nullptr);
+        rc = events_create((int)g->events.size(), g->events.data());
+        if (rc) {
+            g->events.clear();
+            return hip_fail(rc, "hipEventCreate");
+        }
+        g->events_device = dev;
+    }
+    void **ev = g->events.data();
+    auto ev_node = [&](int v) { return ev[1 + v]; };
+    auto ev_copy = [&](int v, int s) { return ev[1 + n + 2 * v + s]; };
+    auto copy_on_side = [&](int v, int s) -> int {
+        int r = run_copy(g, g->ex[v].slot[s], leaves, ws, side);
+        if (r) return r;
+        r = event_record(ev_copy(v, s), side);
+        return r ? hip_fail(r, "hipEventRecord") : TRA_OK;
+    };
+    auto copies_of = [&](int v) {   // (slot count) of a node that reads through copies
+        return g->ex[v].fused == 0 ? (int)g->nodes[v].ops.size() : 0;
+    };
+    if ((rc = event_record(ev[0], stream)) || (rc = stream_wait_event(side, ev[0])))
+        return hip_fail(rc, "stream fork");
+    for (int v = 0; v < n; ++v)
+        for (int s = 0; s < copies_of(v); ++s)
+            if (g->ex[v].slot[s].repart && g->ex[v].slot[s].node < 0 && (rc = copy_on_side(v, s))) return rc;
+    for (int v = 0; v < n; ++v) {
+        for (int s = 0; s < copies_of(v); ++s)
+            if (g->ex[v].slot[s].repart && (rc = stream_wait_event(stream, ev_copy(v, s))))
+                return hip_fail(rc, "hipStreamWaitEvent");
+        rc = run_node(g, v, leaves, v == g->root ? out : nullptr, ws, stream, true);
+        if (rc) return rc;
+        bool forked = false;
+        for (int w = v + 1; w < n; ++w)
+            for (int s = 0; s < copies_of(w); ++s) {
+                const Slot &sl = g->ex[w].slot[s];
+                if (!sl.repart || sl.node != v) continue;
+                if (!forked) {
+                    if ((rc = event_record(ev_node(v), stream)) || (rc = stream_wait_event(side, ev_node(v))))
+                        return hip_fail(rc, "stream fork");
+                    forked = true;
+                }
+                if ((rc = copy_on_side(w, s))) return rc;
+            }
+    }
+    return TRA_OK;
+}
+
 extern "C" int tra_graph_execute(tra_graph_t g, const void *const *leaves, int n_leaves, void *out, void *workspace,
                                  size_t ws_bytes, void *stream)
 {
-    if (!g) return gfail(TRA_E_NULL, "graph is NULL");
+    int rc = check_run_args(g, leaves, n_leaves, workspace, ws_bytes);
+    if (rc) return rc;
+    if (!out) return gfail(TRA_E_NULL, "the output node needs `out`");
+    if (g->overlap && g->n_copies > 0) return execute_overlapped(g, leaves, out, (char *)workspace, stream);
     for (int v = 0; v < (int)g->nodes.size(); ++v) {
-        int rc = tra_graph_run_node(g, v, leaves, n_leaves, v == g->root ? out : nullptr, workspace, ws_bytes,
-                                    stream);
+        rc = run_node(g, v, leaves, v == g->root ? out : nullptr, (char *)workspace, stream, false);
         if (rc) return rc;
     }
     return TRA_OK;

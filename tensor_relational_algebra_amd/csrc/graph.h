@@ -55,4 +55,13 @@ inline int64_t ws_round(int64_t bytes) { return (bytes + 255) & ~(int64_t)255; }
 int64_t predict_plan_ns(const tra_plan_s &p);
 int64_t predict_repartition_ns(int64_t elems, int dtype);
 
+// Streams and events for the overlapped graph executor (streams.hip).  Return a
+// hipError_t value (0 = success).
+int current_device(int *dev);
+int side_stream(void **out);
+int events_create(int n, void **ev);
+void events_destroy(int n, void **ev);
+int event_record(void *ev, void *stream);
+int stream_wait_event(void *stream, void *ev);
+
 }  // namespace tra

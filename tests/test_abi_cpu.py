@@ -271,8 +271,24 @@ def test_graph_plan_fuses_the_attention_chain():
     g = tra.tra_graph_plan_ex("\n".join(lines), 16, None, tra.GRAPH_FUSE_ATTENTION)
     assert g.info.n_fused == 0
     with pytest.raises(tra.TraError) as e:
-        tra.tra_graph_plan_ex(wl.MHA_SMALL.graph_desc(), 16, None, 4)
+        tra.tra_graph_plan_ex(wl.MHA_SMALL.graph_desc(), 16, None, 8)
     assert e.value.code == -7
+
+
+def test_graph_plan_overlapped_copies_layout():
+    """TRA_GRAPH_OVERLAP_COPIES keeps the chooser's blockings; a graph input's
+    copy is live from the first step, so on the full attention layer (every
+    input copied into its node's blocking) all seven input copies are live at
+    once and the workspace holds at least their bytes."""
+    from tensor_relational_algebra_amd import workloads as wl
+    desc = wl.MHA.graph_desc()
+    g0 = tra.tra_graph_plan(desc, 256)
+    g1 = tra.tra_graph_plan_ex(desc, 256, None, tra.GRAPH_OVERLAP_COPIES)
+    assert [g1.node_d(i) for i in range(7)] == [g0.node_d(i) for i in range(7)]
+    assert g1.info.n_repartitions == g0.info.n_repartitions and g1.info.cost == g0.info.cost
+    leaf_bytes = sum(n * 2 for _, n, _ in g1.leaves)      # bf16 inputs
+    assert g1.info.workspace_bytes >= g0.info.workspace_bytes
+    assert g1.info.workspace_bytes >= leaf_bytes
 
 
 def test_empty_tensors_plan():

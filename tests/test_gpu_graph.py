@@ -17,9 +17,10 @@ from tests.gpu_util import DEV, maxnorm_rel_err
 pytestmark = pytest.mark.gpu
 
 
-def _run(case, p=None, d_all=None, fuse=False, time_model=False):
+def _run(case, p=None, d_all=None, fuse=False, time_model=False, overlap=False):
     desc = case.graph_desc()
-    flags = (tra.GRAPH_FUSE_ATTENTION if fuse else 0) | (tra.GRAPH_CHOOSE_TIME if time_model else 0)
+    flags = (tra.GRAPH_FUSE_ATTENTION if fuse else 0) | (tra.GRAPH_CHOOSE_TIME if time_model else 0) | \
+        (tra.GRAPH_OVERLAP_COPIES if overlap else 0)
     g = tra.tra_graph_plan_ex(desc, p or 1, d_all, flags)
     host = case.make_inputs()
     dev = {k: v.to(DEV) for k, v in host.items()}
@@ -150,3 +151,44 @@ def test_memory_capped_chain_of_products():
         out = tra.tra_graph_execute(g, dev).reshape(256, 256)
         torch.cuda.synchronize()
         assert maxnorm_rel_err(out.cpu().double().numpy(), want) <= 1e-4
+
+
+# --- repartition copies on a second stream, overlapped with the nodes ---
+
+@pytest.mark.parametrize("fuse", [False, True], ids=["unfused", "fused"])
+def test_overlapped_copies_match_the_in_order_run(fuse):
+    """With TRA_GRAPH_OVERLAP_COPIES every copy runs on a side stream while the
+    nodes run on the caller's: blockings that disagree between consecutive
+    nodes force repartitions, and three calls in a row give the in-order run's
+    output bit for bit (and the oracle's to the bf16 tolerance)."""
+    case = wl.MHA_SMALL
+    flip = {"s": 4, "t": 2, "h": 1, "d": 2, "a": 4}
+    d_all = _d_all(case, lambda c, b: flip[c])
+    host = case.make_inputs()
+    dev = {k: v.to(DEV) for k, v in host.items()}
+    flags = tra.GRAPH_FUSE_ATTENTION if fuse else 0
+    g0 = tra.tra_graph_plan_ex(case.graph_desc(), 1, d_all, flags)
+    g1 = tra.tra_graph_plan_ex(case.graph_desc(), 1, d_all, flags | tra.GRAPH_OVERLAP_COPIES)
+    # fused, the chain reads its operands in place and only the graph inputs are copied
+    assert g1.info.n_repartitions == g0.info.n_repartitions
+    assert fuse or g0.info.n_repartitions > 0
+    assert g1.info.workspace_bytes >= g0.info.workspace_bytes
+    want = tra.tra_graph_execute(g0, dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        got = tra.tra_graph_execute(g1, dev)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want)
+    ref_out = mha.mha(host)["Output"]
+    assert maxnorm_rel_err(want.reshape(case.s, case.a).cpu().double().numpy(), ref_out) <= 2e-2
+
+
+def test_overlapped_copies_full_layer_sampled_rows():
+    """The full layer under the pages' chooser (four repartitions between nodes
+    and a copy of every graph input) with the copies overlapped."""
+    case = wl.MHA
+    out, host, g = _run(case, p=256, overlap=True)
+    assert g.info.n_repartitions > 0
+    rows = np.array([0, 3, 1500, 4095])
+    want = mha.mha(host, rows=rows)["Output"]
+    assert maxnorm_rel_err(out[rows], want) <= 2e-2
