@@ -515,7 +515,7 @@ def _mha_backward(tra, wl, dev, stream):
     flops = {n: proj for n in ("dO", "dW_O", "dW_Q", "dQ", "dW_K", "dK", "dW_V", "dV")}
     flops.update({n: attn for n in ("dAttn", "dV_proj", "dQ_proj", "dK_proj")})
     hst = float(h * s * s)
-    sbytes = {"P": 8 * hst, "dAttn_c": 8 * hst, "dScores": 10 * hst}   # fp32 in / out, bf16 out for dScores
+    sbytes = {"dAttn_c": 6 * hst, "dScores": 6 * hst}   # fp32 in, bf16 out; bf16 in and out
     names = [n for n, *_ in tra.attention.BACKWARD]
     reps = 5
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]

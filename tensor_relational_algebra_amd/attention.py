@@ -12,14 +12,19 @@ those EinSums, one EinSum per step, with two joins beyond the product:
   r[h,s] = sum_t Attn[h,s,t] dAttn[h,s,t] equals sum_d dO[s,h,d] O[s,h,d]
   (both are the derivative of the layer output along one query row and head),
   so r is formed from [s,h,d] tensors instead of a second pass over [h,s,t];
-* Attn is re-formed in fp32 from the saved scores and their logsumexp
-  (join exp_sub), and dAttn - r is the join sub with r broadcast over t.
+* dAttn - r is the join sub with r broadcast over t, formed in fp32 from the
+  fp32 product dAttn and stored in bf16; the Jacobian then multiplies it by
+  the forward's stored bf16 Attn (as the autograd of a bf16 softmax does, from
+  its saved output), so the backward never re-reads the fp32 scores.
 
 Storage dtypes follow the forward EinGraph: operands of the matrix-core
-products are bf16, scores and everything of shape [h,s,t] that feeds an
-elementwise step are fp32, weight and input gradients are fp32.  All tensors
-are dense (the all-ones partition vector): every kernel reads its operands in
-place through per-label strides, so the layout costs nothing here.
+products are bf16, the product dAttn that feeds the subtraction is fp32,
+weight and input gradients are fp32.  Of the [h,s,t] tensors, only dAttn is
+written in fp32: the three elementwise steps of the first version (re-forming
+Attn in fp32, the subtraction and the product, all in fp32) moved 15 bytes per
+[h,s,t] element, these two move 6.  All tensors are dense (the all-ones
+partition vector): every kernel reads its operands in place through per-label
+strides, so the layout costs nothing here.
 """
 from __future__ import annotations
 
@@ -48,9 +53,8 @@ BACKWARD: List[Tuple[str, str, Tuple[str, ...], str, str, str, str, bool]] = [
     ("dAttn", "shd,thd->hst", ("dO", "V_proj"), "mul", "sum", "bf16", "f32", False),
     ("dV_proj", "hst,shd->thd", ("Attn", "dO"), "mul", "sum", "bf16", "bf16", False),
     ("Rows", "shd,shd->hs", ("dO", "O"), "mul", "sum", "bf16", "f32", False),
-    ("P", "hst,hs->hst", ("Scores", "LSE"), "exp_sub", "none", "f32", "f32", False),
-    ("dAttn_c", "hst,hs->hst", ("dAttn", "Rows"), "sub", "none", "f32", "f32", False),
-    ("dScores", "hst,hst->hst", ("P", "dAttn_c"), "mul", "none", "f32", "bf16", False),
+    ("dAttn_c", "hst,hs->hst", ("dAttn", "Rows"), "sub", "none", "f32", "bf16", False),
+    ("dScores", "hst,hst->hst", ("Attn", "dAttn_c"), "mul", "none", "bf16", "bf16", False),
     ("dQ_proj", "hst,thd->shd", ("dScores", "K_proj"), "mul", "sum", "bf16", "bf16", True),
     ("dK_proj", "hst,shd->thd", ("dScores", "Q_proj"), "mul", "sum", "bf16", "bf16", True),
     ("dW_Q", "sa,shd->ahd", ("Q", "dQ_proj"), "mul", "sum", "bf16", "f32", False),
