@@ -305,3 +305,21 @@ def test_empty_tensors_plan():
     with pytest.raises(tra.TraError) as e:
         tra.tra_plan("ij,jk->ik", {"i": -1, "j": 2, "k": 5}, {"i": 1, "j": 1, "k": 1})
     assert e.value.code == -4
+
+
+def test_binding_fails_loudly_without_the_library():
+    """No fallback: with the shared library absent, the first call raises (in a
+    fresh interpreter, so this process's loaded library is not involved)."""
+    import subprocess
+    import sys
+    code = ("import tensor_relational_algebra_amd._binding as B\n"
+            "B.LIB_PATH = '/nonexistent/libtra.so'\n"
+            "import tensor_relational_algebra_amd as tra\n"
+            "try:\n"
+            "    tra.tra_plan('ij,jk->ik', {'i': 4, 'j': 4, 'k': 4}, {'i': 1, 'j': 1, 'k': 1})\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "raised: libtra is not built" in r.stdout
