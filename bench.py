@@ -454,8 +454,8 @@ def _mha(tra, wl, dev, stream, fuse=False, time_model=False, overlap=False):
     attn_fl = 2.0 * h * s * s * dh       # scores and weighted sum
     flops = {"Q_proj": gemm, "K_proj": gemm, "V_proj": gemm, "Scores": attn_fl, "O": attn_fl, "Output": gemm}
     # bytes the HBM-bound nodes must move at least: scores write fp32 S; softmax reads
-    # S twice (logsumexp, then normalise) and writes bf16 Attn; weighted sum reads Attn
-    sbytes = {"Scores": 4.0 * h * s * s, "Attn": 2 * 4.0 * h * s * s + 2.0 * h * s * s, "O": 2.0 * h * s * s}
+    # S once (one pass per row) and writes bf16 Attn; weighted sum reads Attn
+    sbytes = {"Scores": 4.0 * h * s * s, "Attn": 4.0 * h * s * s + 2.0 * h * s * s, "O": 2.0 * h * s * s}
     if fuse:
         # the fused node does the scores and the weighted sum; nothing is HBM-bound
         flops = dict(flops, O=2 * attn_fl, Scores=0.0)

@@ -212,11 +212,22 @@ static bool node_eval(const GNode &g, const Cand &c, bool is_root, int64_t &ns, 
         return true;
     };
     if (g.kind == "softmax") {
-        // LSE over the last label (fp32), then exp(S - LSE) in the node's out dtype
+        // LSE over the last label (fp32), then exp(S - LSE) in the node's out
+        // dtype; as the executor runs it: one pass when the rows allow
         const std::string hst = g.out, hs = hst.substr(0, hst.size() - 1);
-        if (!plan_ns(hst + "->" + hs, c.d, b, TRA_JOIN_IDENT, TRA_AGG_LSE, D_F32, D_F32, 1.0f)) return false;
-        if (!plan_ns(hst + "," + hs + "->" + hst, c.d, b, TRA_JOIN_EXP_SUB, TRA_AGG_NONE, D_F32, g.out_dtype, 1.0f))
-            return false;
+        tra_plan_t pl = nullptr, pn = nullptr;
+        bool ok = !tra_plan((hst + "->" + hs).c_str(), b.data(), c.d.data(), (int)b.size(), TRA_JOIN_IDENT,
+                            TRA_AGG_LSE, D_F32, D_F32, 1.0f, &pl) &&
+                  !tra_plan((hst + "," + hs + "->" + hst).c_str(), b.data(), c.d.data(), (int)b.size(),
+                            TRA_JOIN_EXP_SUB, TRA_AGG_NONE, D_F32, g.out_dtype, 1.0f, &pn);
+        if (ok) {
+            ns += softmax_one_pass(*pl, *pn) ? predict_softmax_one_pass_ns(*pl, *pn)
+                                             : predict_plan_ns(*pl) + predict_plan_ns(*pn);
+            scratch = std::max((int64_t)pl->info.workspace_bytes, (int64_t)pn->info.workspace_bytes);
+        }
+        tra_plan_destroy(pl);
+        tra_plan_destroy(pn);
+        if (!ok) return false;
     } else if (!plan_ns(g.spec, c.d, b, TRA_JOIN_MUL, TRA_AGG_SUM, g.in_dtype, g.out_dtype, g.scale)) {
         return false;
     }

@@ -672,7 +672,11 @@ static int run_node(tra_graph_t g, int node, const void *const *leaves, void *ou
         }
     }
     void *scratch = e.scratch_bytes ? ws + e.scratch : nullptr;
-    if (e.plan2) {
+    if (e.plan2 && softmax_one_pass(*e.plan, *e.plan2)) {
+        if (!in[0]) return gfail(TRA_E_NULL, "softmax input is NULL");
+        rc = launch_softmax_rows(*e.plan, *e.plan2, in[0], ws + e.lse, ws + e.out, stream);
+        if (rc) return gfail(TRA_E_HIP, std::string("softmax launch: ") + hip_error_text(rc));
+    } else if (e.plan2) {
         rc = tra_execute(e.plan, in[0], nullptr, ws + e.lse, scratch, e.scratch_bytes, stream);
         if (rc) return rc;
         rc = tra_execute(e.plan2, in[0], ws + e.lse, ws + e.out, scratch, e.scratch_bytes, stream);

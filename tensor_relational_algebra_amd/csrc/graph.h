@@ -55,6 +55,15 @@ inline int64_t ws_round(int64_t bytes) { return (bytes + 255) & ~(int64_t)255; }
 int64_t predict_plan_ns(const tra_plan_s &p);
 int64_t predict_repartition_ns(int64_t elems, int dtype);
 
+// The softmax node in one pass (k_simple.hip): true when the node's
+// logsumexp plan `lse` and normalising plan `norm` can run as one kernel that
+// holds each row in registers; the launcher writes the logsumexp and the
+// normalised values.  Returns a hipError_t value.
+bool softmax_one_pass(const tra_plan_s &lse, const tra_plan_s &norm);
+int launch_softmax_rows(const tra_plan_s &lse, const tra_plan_s &norm, const void *s, void *lse_out, void *out,
+                        void *stream);
+int64_t predict_softmax_one_pass_ns(const tra_plan_s &lse, const tra_plan_s &norm);
+
 // Streams and events for the overlapped graph executor (streams.hip).  Return a
 // hipError_t value (0 = success).
 int current_device(int *dev);

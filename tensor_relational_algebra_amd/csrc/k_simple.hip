@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
+#include "graph.h"
 #include "plan.h"
 
 namespace tra {
@@ -478,6 +479,109 @@ int launch_elemwise(const tra_plan_s &p, const void *x, const void *y, void *z, 
     TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
                     hipLaunchKernelGGL((k_elemwise<TI, TO>), dim3(grid), dim3(256), 0, s, p.el, p.join,
                                        p.n_ops == 2 ? 1 : 0, (const TI *)x, (const TI *)y, (TO *)z));
+    return (int)hipGetLastError();
+}
+
+// The softmax node in one pass over its rows: the logsumexp of the row and
+// exp(S - LSE) at every element, with the row held in registers in between
+// (rows of at most SM_GROUPS * 256 elements).  The two-kernel form reads S
+// twice; this one reads it once.  One wavefront per row; lane l owns
+// elements 4l..4l+3 of every 256-element group of the row, the groups walked
+// as the row-reduce kernel walks them (contracted-key digits outer, the
+// contiguous in-block run inner).  The logsumexp is the row maximum plus the
+// log of the sum of exp(v - max), each combined across the wavefront by a
+// butterfly.  S and the output share one relation layout, so an element's
+// output offset is its input offset.
+constexpr int SM_GROUPS = 16;
+template <typename TO, int NG>
+__global__ __launch_bounds__(256) void k_softmax_rows_p2(RowDesc g, const float *__restrict__ x,
+                                                         float *__restrict__ lse, TO *__restrict__ z, int per_log2)
+{
+    // NG = n_outer * inner / 256 groups per row, a compile-time count so that
+    // the row stays in registers
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t n_waves = (gridDim.x * blockDim.x) >> 6;
+    const int per_mask = (1 << per_log2) - 1;
+    for (uint32_t o = wave; o < (uint32_t)g.n_out; o += n_waves) {
+        const int32_t xo = p2off<0>(g.out_p2, o);
+        float v[NG][4];
+        int32_t off[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            off[j] = xo + p2off<0>(g.outer_p2, (uint32_t)(j >> per_log2)) + (j & per_mask) * 256 + lane * 4;
+            Vec4R<float>::load<true>(x + off[j], v[j]);
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) m = fmaxf(m, fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3])));
+        for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
+        float sum = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int j = 0; j < NG; ++j)
+                sum += (__expf(v[j][0] - m) + __expf(v[j][1] - m)) + (__expf(v[j][2] - m) + __expf(v[j][3] - m));
+        }
+        for (int sh = 32; sh >= 1; sh >>= 1) sum += __shfl_xor(sum, sh, 64);
+        const float l = m == -INFINITY ? -INFINITY : m + __logf(sum);
+        if (lane == 0) lse[o] = l;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            float w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = __expf(v[j][i] - l);
+            Vec4R<TO>::template store<true>(z + off[j], w);
+        }
+    }
+}
+
+bool softmax_one_pass(const tra_plan_s &lse, const tra_plan_s &norm)
+{
+    if (lse.kernel != TRA_KERNEL_ROWREDUCE || !lse.row.p2 || lse.agg != A_LSE || lse.n_ops != 1 ||
+        lse.in_dtype != D_F32 || lse.post_scale != 1.0f)
+        return false;
+    if (norm.kernel != TRA_KERNEL_ELEMWISE || norm.join != J_EXP_SUB || norm.info.z_elems != lse.info.x_elems ||
+        (norm.out_dtype != D_F32 && norm.out_dtype != D_BF16))
+        return false;
+    const int64_t inner = lse.row.inner, n_outer = lse.row.n_outer;
+    if (inner < 256 || (inner & (inner - 1)) || n_outer < 1 || (n_outer & (n_outer - 1)) ||
+        n_outer * inner > SM_GROUPS * 256)
+        return false;
+    return true;
+}
+
+template <typename TO, int NG>
+static void launch_softmax_ng(const RowDesc &g, int grid, int per_log2, const void *s, void *lse_out, void *out,
+                              hipStream_t st)
+{
+    hipLaunchKernelGGL((k_softmax_rows_p2<TO, NG>), dim3(grid), dim3(256), 0, st, g, (const float *)s,
+                       (float *)lse_out, (TO *)out, per_log2);
+}
+
+template <typename TO>
+static void launch_softmax_t(const RowDesc &g, int n_groups, int grid, int per_log2, const void *s, void *lse_out,
+                             void *out, hipStream_t st)
+{
+    switch (n_groups) {
+    case 1: launch_softmax_ng<TO, 1>(g, grid, per_log2, s, lse_out, out, st); break;
+    case 2: launch_softmax_ng<TO, 2>(g, grid, per_log2, s, lse_out, out, st); break;
+    case 4: launch_softmax_ng<TO, 4>(g, grid, per_log2, s, lse_out, out, st); break;
+    case 8: launch_softmax_ng<TO, 8>(g, grid, per_log2, s, lse_out, out, st); break;
+    default: launch_softmax_ng<TO, SM_GROUPS>(g, grid, per_log2, s, lse_out, out, st); break;
+    }
+}
+
+int launch_softmax_rows(const tra_plan_s &lse, const tra_plan_s &norm, const void *s, void *lse_out, void *out,
+                        void *stream)
+{
+    const RowDesc &g = lse.row;
+    int per_log2 = 0;
+    while ((int64_t)256 << per_log2 < g.inner) ++per_log2;
+    const int n_groups = (int)(g.n_outer << per_log2);   // a power of two, at most SM_GROUPS (softmax_one_pass)
+    const int grid = grid_for(g.n_out * 64);
+    hipStream_t st = (hipStream_t)stream;
+    if (norm.out_dtype == D_BF16) launch_softmax_t<bf16_t>(g, n_groups, grid, per_log2, s, lse_out, out, st);
+    else launch_softmax_t<float>(g, n_groups, grid, per_log2, s, lse_out, out, st);
     return (int)hipGetLastError();
 }
 

@@ -81,6 +81,14 @@ int64_t predict_plan_ns(const tra_plan_s &p)
     return (int64_t)std::llround(t);
 }
 
+// The softmax node as one pass: S read once, the output written once, at the
+// row-reduce bandwidth.
+int64_t predict_softmax_one_pass_ns(const tra_plan_s &lse, const tra_plan_s &norm)
+{
+    const double bytes = (double)lse.info.x_bytes + (double)norm.info.z_bytes + (double)lse.info.z_bytes;
+    return (int64_t)std::llround(kCal.latency_ns + bytes / kCal.rowreduce_bw);
+}
+
 int64_t predict_repartition_ns(int64_t elems, int dtype)
 {
     if (elems <= 0) return 0;

@@ -192,3 +192,29 @@ def test_overlapped_copies_full_layer_sampled_rows():
     rows = np.array([0, 3, 1500, 4095])
     want = mha.mha(host, rows=rows)["Output"]
     assert maxnorm_rel_err(out[rows], want) <= 2e-2
+
+
+# --- the softmax node: one pass over each row when it fits in registers ---
+
+@pytest.mark.parametrize("t,d_t,out_dtype", [(4096, 1, "bf16"), (4096, 2, "bf16"), (2048, 8, "f32"), (256, 1, "f32"),
+                                             (8192, 1, "bf16"), (128, 1, "f32")],
+                         ids=["4096", "4096-2blocks", "2048-8blocks-f32", "256-f32", "8192-twopass",
+                              "128-twopass"])
+def test_softmax_node(t, d_t, out_dtype):
+    """Rows of up to 4096 elements run as one kernel (logsumexp and normalise
+    with the row in registers); longer or shorter rows as the two EinSums.
+    Both against the oracle's logsumexp: exp(S - lse) to the output dtype's
+    tolerance, and every row summing to 1."""
+    from oracle import ref
+    h, s = 4, 64
+    desc = f"A softmax hst->hst h={h},s={s},t={t} @S in=f32 out={out_dtype}"
+    host = {"S": wl.draw(7900 + t, (h, s, t), "normal", "f32", std=3.0)}
+    g = tra.tra_graph_plan(desc, 1, [2, 4, d_t])
+    out = tra.tra_graph_execute(g, {"S": host["S"].to(DEV)}).reshape(h, s, t)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    lse = ref.einsum("hst->hs", host["S"], None, "ident", "lse")
+    want = np.exp(host["S"].double().numpy() - lse[..., None])
+    tol = 2e-2 if out_dtype == "bf16" else 1e-4
+    assert maxnorm_rel_err(got, want) <= tol
+    assert np.abs(got.sum(axis=2) - 1).max() <= (2e-2 if out_dtype == "bf16" else 1e-4)
