@@ -45,6 +45,7 @@ struct Calibration {
     double stream_bw = 5520.0;         // elementwise and one-thread-per-output kernels
     double tile_bw = 6080.0;           // bandwidth bound of the tile kernels (small-tile matrix-core case)
     double copy_bw = 5755.0;           // repartition
+    double softmax_bw = 5700.0;        // the softmax node in one pass (5511 and 5935 on the attention layer)
 };
 static const Calibration kCal;
 
@@ -81,12 +82,12 @@ int64_t predict_plan_ns(const tra_plan_s &p)
     return (int64_t)std::llround(t);
 }
 
-// The softmax node as one pass: S read once, the output written once, at the
-// row-reduce bandwidth.
+// The softmax node as one pass: S read once, the output and the logsumexp
+// written once.
 int64_t predict_softmax_one_pass_ns(const tra_plan_s &lse, const tra_plan_s &norm)
 {
     const double bytes = (double)lse.info.x_bytes + (double)norm.info.z_bytes + (double)lse.info.z_bytes;
-    return (int64_t)std::llround(kCal.latency_ns + bytes / kCal.rowreduce_bw);
+    return (int64_t)std::llround(kCal.latency_ns + bytes / kCal.softmax_bw);
 }
 
 int64_t predict_repartition_ns(int64_t elems, int dtype)
