@@ -199,7 +199,7 @@ def _events_time(fn, reps: int, stream) -> float:
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the executor has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     if args.src_sha:
