@@ -19,9 +19,11 @@
  * - All validation happens on the host before anything is launched; an
  *   error return means nothing was enqueued.
  * - Device pointers are plain HIP device addresses owned by the caller
- *   (libtra never allocates device memory).  Streams are hipStream_t passed
- *   as void*; NULL means the legacy default stream.  Calls are asynchronous
- *   with respect to the host: nothing synchronises.
+ *   (libtra never allocates device memory; the only device resources it
+ *   creates are, for TRA_GRAPH_OVERLAP_COPIES, one side stream per device and
+ *   a graph's events).  Streams are hipStream_t passed as void*; NULL means
+ *   the legacy default stream.  Calls are asynchronous with respect to the
+ *   host: nothing synchronises.
  * - A "relation" is a tensor stored in the relation layout: given the
  *   tensor's labels l_1..l_n, extents B_l and part counts d_l (d_l | B_l,
  *   block extent b_l = B_l / d_l), the element with global index g sits at
