@@ -515,8 +515,9 @@ def _mha_backward(tra, wl, dev, stream):
     flops = {n: proj for n in ("dO", "dW_O", "dW_Q", "dQ", "dW_K", "dK", "dW_V", "dV")}
     flops.update({n: attn for n in ("dAttn", "dV_proj", "dQ_proj", "dK_proj")})
     hst = float(h * s * s)
-    sbytes = {"dAttn_c": 6 * hst, "dScores": 6 * hst}   # fp32 in, bf16 out; bf16 in and out
-    names = [n for n, *_ in tra.attention.BACKWARD]
+    # dScores runs chained with dAttn_c: reads dAttn (fp32) and Attn (bf16), writes bf16
+    sbytes = {"dScores": 8 * hst}
+    names = list(tra.attention.BACKWARD_LAUNCHES)
     reps = 5
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
     for r in range(reps):
@@ -529,6 +530,9 @@ def _mha_backward(tra, wl, dev, stream):
         ms = sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
         total += ms
         e = {"us": round(ms * 1e3, 1), "kernel": layer.plans[n].kernel}
+        chained = [a for a, b in tra.attention.CHAINED.items() if b == n]
+        if chained:
+            e["chained_with"] = chained[0]
         if n in flops:
             e["TFLOP/s"] = round(flops[n] / ms / 1e9, 1)
             e["frac_bf16_mfma_peak"] = round(flops[n] / (ms * 1e-3) / BF16_MFMA_PEAK, 4)

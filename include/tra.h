@@ -184,6 +184,29 @@ int tra_execute(tra_plan_t plan, const void *x_rel, const void *y_rel, void *z_r
                 void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * tra_execute_chain -- two elementwise EinSums (aggregate NONE, section 2.1's
+ * joins) as one pass, the first one's output never written:
+ *     t = plan_a(xa, ya)       (rounded to plan_a's output dtype)
+ *     z = plan_b(xb, t)        (t is plan_b's second operand)
+ * The result is bit-identical to tra_execute(plan_a, ...) into a buffer t
+ * followed by tra_execute(plan_b, xb, t, z): the fusion of consecutive
+ * operators into one that the EinDecomp page's closing remarks point to.
+ *
+ *   plan_a, plan_b  elementwise plans whose outputs are the same relation
+ *                   (same labels in the same order, same extents and d);
+ *                   plan_b's second operand has plan_b's output labels in
+ *                   the output's order; float dtypes, plan_b's input dtype
+ *                   equal to plan_a's output dtype.
+ *   xa, ya          plan_a's operand relations (ya NULL for one operand).
+ *   xb              plan_b's first operand relation.
+ *   z               plan_b's output relation; fully overwritten.
+ * Errors: TRA_E_NULL, TRA_E_OP (the plans do not chain), TRA_E_ALIGN,
+ * TRA_E_HIP.
+ */
+int tra_execute_chain(tra_plan_t plan_a, tra_plan_t plan_b, const void *xa, const void *ya, const void *xb,
+                      void *z, void *hip_stream);
+
+/*
  * tra_repartition -- re-cut one tensor from partition vector d_from to d_to
  * (section 2.2, repartition; the initial partition of section 4.1's runtime
  * is the case d_from = all ones).  A pure permutation of elements: every

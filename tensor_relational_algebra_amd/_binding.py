@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
             "tra_plan_info": ([P, P], I),
             "tra_plan_destroy": ([P], I),
             "tra_execute": ([P, P, P, P, P, ctypes.c_size_t, P], I),
+            "tra_execute_chain": ([P, P, P, P, P, P, P], I),
             "tra_repartition": ([P, I, P, P, I, P, P, P], I),
             "tra_canonical_labels": ([ctypes.c_char_p, ctypes.c_char_p, I], I),
             "tra_d_from_operand_form": ([ctypes.c_char_p, P, I, P, I], I),
@@ -197,6 +198,20 @@ def tra_execute(plan: Plan, x: torch.Tensor, y: Optional[torch.Tensor] = None, z
     pw = workspace.data_ptr() if workspace is not None else None
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().tra_execute(plan.handle, px, py, pz, pw, wb, _stream(stream)))
+    return z
+
+
+def tra_execute_chain(plan_a: Plan, plan_b: Plan, xa: torch.Tensor, ya: Optional[torch.Tensor],
+                      xb: torch.Tensor, z: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """z = plan_b(xb, plan_a(xa, ya)) in one pass (the intermediate is never written)."""
+    ia, ib = plan_a.info, plan_b.info
+    pxa = _dev_ptr(xa, "xa", ia.x_elems, plan_a.in_dtype)
+    pya = _dev_ptr(ya, "ya", ia.y_elems, plan_a.in_dtype) if ia.y_elems else None
+    pxb = _dev_ptr(xb, "xb", ib.x_elems, plan_b.in_dtype)
+    if z is None:
+        z = torch.empty(ib.z_elems, dtype=TORCH_DTYPES[plan_b.out_dtype], device=xa.device)
+    pz = _dev_ptr(z, "z", ib.z_elems, plan_b.out_dtype)
+    _check(lib().tra_execute_chain(plan_a.handle, plan_b.handle, pxa, pya, pxb, pz, _stream(stream)))
     return z
 
 

@@ -64,6 +64,12 @@ int launch_softmax_rows(const tra_plan_s &lse, const tra_plan_s &norm, const voi
                         void *stream);
 int64_t predict_softmax_one_pass_ns(const tra_plan_s &lse, const tra_plan_s &norm);
 
+// Two elementwise plans as one pass (k_simple.hip, tra_execute_chain): true
+// when plan b's second operand is plan a's output in plan b's output layout.
+bool elemwise_chainable(const tra_plan_s &a, const tra_plan_s &b);
+int launch_elemwise_chain(const tra_plan_s &a, const tra_plan_s &b, const void *xa, const void *ya, const void *xb,
+                          void *z, void *stream);
+
 // Streams and events for the overlapped graph executor (streams.hip).  Return a
 // hipError_t value (0 = success).
 int current_device(int *dev);

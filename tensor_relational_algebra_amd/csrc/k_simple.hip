@@ -255,6 +255,71 @@ __global__ __launch_bounds__(256) void k_elemwise_p2(ElemDesc g, int join, int t
     }
 }
 
+// Two elementwise EinSums as one pass (tra_execute_chain): t = join_a(xa, ya)
+// rounded to plan a's output dtype, then z = join_b(xb, t), with t never
+// written.  Both plans enumerate the same output positions in the same
+// layout, and plan b's second operand is laid out as its output, so t for
+// output group o is the value plan a would have stored at o: the result is
+// bit-identical to the two launches.
+template <typename TIA, typename TM, typename TO, int UPT, bool NT>
+__global__ __launch_bounds__(256) void k_elemwise_chain_p2(ElemDesc ga, int join_a, int two_a, ElemDesc gb,
+                                                           int join_b, const TIA *__restrict__ xa,
+                                                           const TIA *__restrict__ ya, const TM *__restrict__ xb,
+                                                           TO *__restrict__ z)
+{
+    const uint32_t n_vec = (uint32_t)(ga.n_out / 4);
+    const uint32_t base = blockIdx.x * (256u * UPT) + threadIdx.x;
+    float av[UPT][4], bv[UPT][4], cv[UPT][4];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+        const uint32_t v = base + 256u * u;
+        for (int i = 0; i < 4; ++i) av[u][i] = bv[u][i] = cv[u][i] = 0.f;
+        if (v < n_vec) {
+            const uint32_t o = v * 4;
+            Vec4R<TIA>::template load<NT>(xa + p2off<0>(ga.out_p2, o), av[u]);
+            if (two_a) {
+                const int32_t yo = p2off<1>(ga.out_p2, o);
+                if (ga.y_step) Vec4R<TIA>::template load<NT>(ya + yo, bv[u]);
+                else bv[u][0] = bv[u][1] = bv[u][2] = bv[u][3] = Scalar<TIA>::load(ya, yo);
+            }
+            Vec4R<TM>::template load<NT>(xb + p2off<0>(gb.out_p2, o), cv[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+        const uint32_t v = base + 256u * u;
+        if (v >= n_vec) break;
+        float r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float t = join_any(join_a, av[u][i], bv[u][i]) * ga.post_scale;
+            if constexpr (std::is_same<TM, bf16_t>::value) t = bf16_to_f32(f32_to_bf16(t));
+            r[i] = join_any(join_b, cv[u][i], t) * gb.post_scale;
+        }
+        Vec4R<TO>::template store<NT>(z + v * 4, r);
+    }
+}
+
+// The same chain for layouts without the power-of-two form: one output
+// element per thread, offsets from each plan's radix decomposition.
+template <typename TIA, typename TM, typename TO>
+__global__ __launch_bounds__(256) void k_elemwise_chain(ElemDesc ga, int join_a, int two_a, ElemDesc gb, int join_b,
+                                                        const TIA *__restrict__ xa, const TIA *__restrict__ ya,
+                                                        const TM *__restrict__ xb, TO *__restrict__ z)
+{
+    for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < ga.n_out;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        int64_t xo = 0, yo = 0, xbo = 0, ybo = 0;
+        radix_offsets(ga.out, o, xo, yo);
+        radix_offsets(gb.out, o, xbo, ybo);   // ybo == o: plan b's second operand is laid out as its output
+        const float av = Scalar<TIA>::load(xa, xo), bv = two_a ? (float)Scalar<TIA>::load(ya, yo) : 0.f;
+        float t = join_any(join_a, av, bv) * ga.post_scale;
+        if constexpr (std::is_same<TM, bf16_t>::value) t = bf16_to_f32(f32_to_bf16(t));
+        Scalar<TO>::store(z, o, join_any(join_b, (float)Scalar<TM>::load(xb, xbo), t) * gb.post_scale);
+    }
+}
+
+
 // Row reduction, power-of-two digits: one wavefront per output; each lane
 // folds 4 consecutive elements per step (one 16-byte load), the contracted
 // keys outermost in ascending order; lanes are combined by a butterfly.
@@ -583,6 +648,65 @@ int launch_softmax_rows(const tra_plan_s &lse, const tra_plan_s &norm, const voi
     if (norm.out_dtype == D_BF16) launch_softmax_t<bf16_t>(g, n_groups, grid, per_log2, s, lse_out, out, st);
     else launch_softmax_t<float>(g, n_groups, grid, per_log2, s, lse_out, out, st);
     return (int)hipGetLastError();
+}
+
+static bool is_float_dtype(int dt) { return dt == D_F32 || dt == D_BF16; }
+
+bool elemwise_chainable(const tra_plan_s &a, const tra_plan_s &b)
+{
+    if (a.kernel != TRA_KERNEL_ELEMWISE || b.kernel != TRA_KERNEL_ELEMWISE) return false;
+    if (b.n_ops != 2 || a.info.z_elems != b.info.z_elems) return false;
+    if (!is_float_dtype(a.in_dtype) || !is_float_dtype(a.out_dtype) || b.in_dtype != a.out_dtype ||
+        !is_float_dtype(b.out_dtype))
+        return false;
+    // t is plan a's output and plan b's second operand: both must be the
+    // output relation of plan b (same labels in the same order, same d)
+    if (a.zl != b.zl || b.yl != b.zl) return false;
+    for (char c : b.zl)
+        if (a.d[(int)c] != b.d[(int)c] || a.B[(int)c] != b.B[(int)c]) return false;
+    return true;
+}
+
+template <typename TIA, typename TM, typename TO>
+static int launch_chain_t(const tra_plan_s &a, const tra_plan_s &b, const void *xa, const void *ya, const void *xb,
+                          void *z, hipStream_t s)
+{
+    if (!a.el.p2 || !b.el.p2 || !b.el.y_step) {
+        hipLaunchKernelGGL((k_elemwise_chain<TIA, TM, TO>), dim3(grid_for(a.el.n_out)), dim3(256), 0, s, a.el,
+                           a.join, a.n_ops == 2 ? 1 : 0, b.el, b.join, (const TIA *)xa, (const TIA *)ya,
+                           (const TM *)xb, (TO *)z);
+        return (int)hipGetLastError();
+    }
+    const int64_t n_vec = a.el.n_out / 4;
+    const int64_t bytes = a.info.x_bytes + (a.el.y_step ? a.info.y_bytes : 0) + b.info.x_bytes + b.info.z_bytes;
+    const bool big = bytes >= (64ll << 20), wide = n_vec >= 256 * 256 * 4;
+    const int upt = big || wide ? 4 : 1;
+    const unsigned grid = (unsigned)((n_vec + 256 * upt - 1) / (256 * upt));
+#define TRA_CH_GO(UPT, NT)                                                                                  \
+    hipLaunchKernelGGL((k_elemwise_chain_p2<TIA, TM, TO, UPT, NT>), dim3(grid), dim3(256), 0, s, a.el, a.join, \
+                       a.n_ops == 2 ? 1 : 0, b.el, b.join, (const TIA *)xa, (const TIA *)ya, (const TM *)xb,  \
+                       (TO *)z)
+    if (big) TRA_CH_GO(4, true);
+    else if (wide) TRA_CH_GO(4, false);
+    else TRA_CH_GO(1, false);
+#undef TRA_CH_GO
+    return (int)hipGetLastError();
+}
+
+int launch_elemwise_chain(const tra_plan_s &a, const tra_plan_s &b, const void *xa, const void *ya, const void *xb,
+                          void *z, void *stream)
+{
+    if (a.el.n_out == 0) return 0;
+    hipStream_t s = (hipStream_t)stream;
+    const bool ia = a.in_dtype == D_BF16, im = a.out_dtype == D_BF16, ob = b.out_dtype == D_BF16;
+    if (!ia && !im && !ob) return launch_chain_t<float, float, float>(a, b, xa, ya, xb, z, s);
+    if (!ia && !im && ob) return launch_chain_t<float, float, bf16_t>(a, b, xa, ya, xb, z, s);
+    if (!ia && im && !ob) return launch_chain_t<float, bf16_t, float>(a, b, xa, ya, xb, z, s);
+    if (!ia && im && ob) return launch_chain_t<float, bf16_t, bf16_t>(a, b, xa, ya, xb, z, s);
+    if (ia && !im && !ob) return launch_chain_t<bf16_t, float, float>(a, b, xa, ya, xb, z, s);
+    if (ia && !im && ob) return launch_chain_t<bf16_t, float, bf16_t>(a, b, xa, ya, xb, z, s);
+    if (ia && im && !ob) return launch_chain_t<bf16_t, bf16_t, float>(a, b, xa, ya, xb, z, s);
+    return launch_chain_t<bf16_t, bf16_t, bf16_t>(a, b, xa, ya, xb, z, s);
 }
 
 int launch_rowreduce(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream)

@@ -16,6 +16,7 @@
 #include <string>
 #include <vector>
 
+#include "graph.h"
 #include "plan.h"
 
 namespace tra {
@@ -581,6 +582,23 @@ int tra_execute(tra_plan_t p, const void *x, const void *y, void *z, void *ws, s
     case TRA_KERNEL_ELEMWISE: err = launch_elemwise(*p, x, y, z, stream); break;
     default: err = launch_generic(*p, x, y, z, stream); break;
     }
+    if (err) return fail(TRA_E_HIP, std::string("kernel launch failed: ") + hip_error_text(err));
+    return TRA_OK;
+}
+
+int tra_execute_chain(tra_plan_t a, tra_plan_t b, const void *xa, const void *ya, const void *xb, void *z,
+                      void *stream)
+{
+    if (!a || !b) return fail(TRA_E_NULL, "plan is NULL");
+    if (!elemwise_chainable(*a, *b))
+        return fail(TRA_E_OP, "the plans do not chain: both must be elementwise (aggregate none) over the same "
+                              "output relation, the second plan's second operand laid out as its output, "
+                              "float dtypes with the second plan's input dtype the first plan's output dtype");
+    if (a->info.z_elems && (!xa || !xb || !z || (a->n_ops == 2 && !ya && a->info.y_elems)))
+        return fail(TRA_E_NULL, "operand / output pointer is NULL");
+    if (!aligned16(xa) || !aligned16(xb) || !aligned16(z) || (ya && !aligned16(ya)))
+        return fail(TRA_E_ALIGN, "device pointers must be 16-byte aligned");
+    int err = launch_elemwise_chain(*a, *b, xa, ya, xb, z, stream);
     if (err) return fail(TRA_E_HIP, std::string("kernel launch failed: ") + hip_error_text(err));
     return TRA_OK;
 }

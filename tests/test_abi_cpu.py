@@ -323,3 +323,27 @@ def test_binding_fails_loudly_without_the_library():
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 0, r.stderr[-2000:]
     assert "raised: libtra is not built" in r.stdout
+
+
+def test_execute_chain_host_errors():
+    """tra_execute_chain validates on the host: plans that do not chain are
+    refused before anything is launched."""
+    L = tra.lib()
+    a = tra.tra_plan("hst,hs->hst", {"h": 2, "s": 4, "t": 256}, {"h": 1, "s": 1, "t": 1}, "sub", "none", "f32",
+                     "bf16")
+    b = tra.tra_plan("hst,hst->hst", {"h": 2, "s": 4, "t": 256}, {"h": 1, "s": 1, "t": 1}, "mul", "none", "bf16",
+                     "bf16")
+    assert L.tra_execute_chain(None, b.handle, None, None, None, None, None) == -1
+    # b's input dtype must be a's output dtype
+    b32 = tra.tra_plan("hst,hst->hst", {"h": 2, "s": 4, "t": 256}, {"h": 1, "s": 1, "t": 1}, "mul", "none", "f32",
+                       "bf16")
+    assert L.tra_execute_chain(a.handle, b32.handle, 16, 16, 16, 16, None) == -7
+    # the outputs must be the same relation (here: another blocking)
+    b2 = tra.tra_plan("hst,hst->hst", {"h": 2, "s": 4, "t": 256}, {"h": 2, "s": 1, "t": 1}, "mul", "none", "bf16",
+                      "bf16")
+    assert L.tra_execute_chain(a.handle, b2.handle, 16, 16, 16, 16, None) == -7
+    # not elementwise
+    r = tra.tra_plan("hst->hs", {"h": 2, "s": 4, "t": 256}, {"h": 1, "s": 1, "t": 1}, "ident", "lse", "f32", "f32")
+    assert L.tra_execute_chain(r.handle, b.handle, 16, 16, 16, 16, None) == -7
+    # misaligned pointers
+    assert L.tra_execute_chain(a.handle, b.handle, 16, 16, 16, 8, None) == -9

@@ -368,3 +368,38 @@ def test_blocked_gemm_backward_full_size_sampled(which):
                          (N002, N002))
     err, plan = check(case, sample=2048, seed=5)
     assert plan.kernel == "mfma_bf16"
+
+
+# ------------------------------------------------------------ two elementwise EinSums in one pass
+
+CHAIN_CASES = [
+    # (spec a, join a, in a, out a, spec b, join b, out b, bounds, d)
+    ("hst,hs->hst", "sub", "f32", "bf16", "hst,hst->hst", "mul", "bf16", {"h": 4, "s": 64, "t": 512},
+     {"h": 2, "s": 4, "t": 2}),
+    ("hst,hs->hst", "exp_sub", "f32", "f32", "hst,hst->hst", "mul", "f32", {"h": 2, "s": 32, "t": 1024},
+     {"h": 1, "s": 1, "t": 1}),
+    ("ij,j->ij", "add", "bf16", "f32", "ij,ij->ij", "sub", "bf16", {"i": 128, "j": 256}, {"i": 4, "j": 2}),
+    # extents without the power-of-two form: the one-thread-per-element chain
+    ("hst,hs->hst", "sub", "f32", "bf16", "hst,hst->hst", "mul", "bf16", {"h": 3, "s": 20, "t": 384},
+     {"h": 3, "s": 2, "t": 3}),
+]
+
+
+@pytest.mark.parametrize("case", CHAIN_CASES, ids=["sub-mul-bf16", "expsub-mul-f32", "add-sub-mixed", "ragged"])
+def test_execute_chain_matches_two_launches(case):
+    """z = b(xb, a(xa, ya)) in one pass is bit-identical to the two launches
+    through an intermediate buffer."""
+    spec_a, join_a, ia, oa, spec_b, join_b, ob, bounds, d = case
+    pa = tra.tra_plan(spec_a, bounds, d, join_a, "none", ia, oa)
+    pb = tra.tra_plan(spec_b, bounds, d, join_b, "none", oa, ob)
+    assert pa.kernel == pb.kernel == "elemwise"
+    g = torch.Generator().manual_seed(11)
+    t_a = {"f32": torch.float32, "bf16": torch.bfloat16}
+    xa = torch.randn(pa.info.x_elems, generator=g).to(t_a[ia]).to(DEV)
+    ya = torch.randn(pa.info.y_elems, generator=g).to(t_a[ia]).to(DEV)
+    xb = torch.randn(pb.info.x_elems, generator=g).to(t_a[oa]).to(DEV)
+    t = tra.tra_execute(pa, xa, ya)
+    want = tra.tra_execute(pb, xb, t)
+    got = tra.tra_execute_chain(pa, pb, xa, ya, xb)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
