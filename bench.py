@@ -56,7 +56,7 @@ TRAFFIC_SRCS = ("tensor_relational_algebra_amd/csrc/k_valu_tile.hip",
                 "tensor_relational_algebra_amd/csrc/device_common.h",
                 "tensor_relational_algebra_amd/csrc/tra_internal.h",
                 "tensor_relational_algebra_amd/csrc/plan.h")
-TRAFFIC_SQDIST = {"src_sha": "439559b799ea0b06", "fetch_kib": 40686.9, "write_kib": 262144.0,
+TRAFFIC_SQDIST = {"src_sha": "439559b799ea0b06", "fetch_kib": 40664.8, "write_kib": 262144.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
                   "profile": "profiles/valu_tile_sqdist_8192x256x8192_hbm_traffic.md"}
 
