@@ -430,6 +430,8 @@ def _extra(tra, wl, dev, stream, only):
         res["mha_fused_time"] = _mha(tra, wl, dev, stream, fuse=True, time_model=True)
     if want("mha_bwd"):
         res["mha_bwd"] = _mha_backward(tra, wl, dev, stream)
+        # the softmax Jacobian in the dAttn product's epilogue (opt-in, for comparison)
+        res["mha_bwd_product_chain"] = _mha_backward(tra, wl, dev, stream, fuse=True)
     torch.cuda.empty_cache()
     return res
 
@@ -498,14 +500,14 @@ def _mha(tra, wl, dev, stream, fuse=False, time_model=False, overlap=False):
     return r
 
 
-def _mha_backward(tra, wl, dev, stream):
+def _mha_backward(tra, wl, dev, stream, fuse=False):
     """Backward EinSums of the attention layer (dense layouts), per step and in
     total, each step against its own roof: the products against the bf16 matrix-core
     peak, the [h,s,t] elementwise steps against HBM."""
     import torch
     case = wl.MHA
     s, a, h, dh = case.s, case.a, case.h, case.dh
-    layer = tra.AttentionLayer(s, a, h, dh)
+    layer = tra.AttentionLayer(s, a, h, dh, fuse_product_chain=fuse)
     inputs = {k: v.to(dev) for k, v in case.make_inputs().items()}
     ws = layer.workspace(dev)
     saved = layer.forward(inputs, ws)
@@ -515,9 +517,14 @@ def _mha_backward(tra, wl, dev, stream):
     flops = {n: proj for n in ("dO", "dW_O", "dW_Q", "dQ", "dW_K", "dK", "dW_V", "dV")}
     flops.update({n: attn for n in ("dAttn", "dV_proj", "dQ_proj", "dK_proj")})
     hst = float(h * s * s)
-    # dScores runs chained with dAttn_c: reads dAttn (fp32) and Attn (bf16), writes bf16
-    sbytes = {"dScores": 8 * hst}
-    names = list(tra.attention.BACKWARD_LAUNCHES)
+    names = list(layer.backward_launches)
+    if layer.fuse_product_chain:
+        # dScores = Attn * (dO.V^T - Rows) in the product's epilogue
+        flops["dScores"] = attn
+        sbytes = {}
+    else:
+        # dScores runs chained with dAttn_c: reads dAttn (fp32) and Attn (bf16), writes bf16
+        sbytes = {"dScores": 8 * hst}
     reps = 5
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
     for r in range(reps):
@@ -531,7 +538,10 @@ def _mha_backward(tra, wl, dev, stream):
         total += ms
         e = {"us": round(ms * 1e3, 1), "kernel": layer.plans[n].kernel}
         chained = [a for a, b in tra.attention.CHAINED.items() if b == n]
-        if chained:
+        if chained and layer.fuse_product_chain:
+            e["kernel"] = layer.plans["dAttn"].kernel
+            e["chained_with"] = ["dAttn", chained[0]]
+        elif chained:
             e["chained_with"] = chained[0]
         if n in flops:
             e["TFLOP/s"] = round(flops[n] / ms / 1e9, 1)

@@ -207,6 +207,36 @@ int tra_execute_chain(tra_plan_t plan_a, tra_plan_t plan_b, const void *xa, cons
                       void *z, void *hip_stream);
 
 /*
+ * tra_execute_contract_chain -- a contraction on the matrix cores followed by
+ * two elementwise EinSums, all in the contraction's epilogue, so neither the
+ * product nor the intermediate is ever written:
+ *     p = plan_c(xc, yc)        (fp32, as tra_execute would store it)
+ *     t = plan_a(p, ya)         (rounded to plan_a's output dtype)
+ *     z = plan_b(xb, t)
+ * The result is bit-identical to the three plans run one after the other.
+ * This is the fusion of consecutive operators into one that the EinDecomp
+ * page's closing remarks point to; the attention backward uses it for the
+ * softmax Jacobian (dScores = Attn * (dO.V^T - r)).
+ *
+ *   plan_c   a bf16 mul/sum plan on the matrix-core kernel (info.kernel
+ *            TRA_KERNEL_MFMA_BF16) with info.agg_split 1 and an fp32 output.
+ *   plan_a   elementwise, two operands: its first operand and its output are
+ *            plan_c's output relation (same labels, order, extents and d);
+ *            its second operand ya carries output labels only (any subset,
+ *            e.g. a per-row vector); fp32 input.
+ *   plan_b   elementwise, two operands: both operands and the output are
+ *            that same relation; t is its second operand.
+ *   plan_a's output dtype, plan_b's input and output dtypes: one dtype,
+ *   bf16 or fp32.
+ *   xc, yc   plan_c's operand relations; ya, xb the steps' other operands;
+ *   z        plan_b's output relation, fully overwritten.
+ * Errors: TRA_E_NULL, TRA_E_OP (the plans do not fit the description
+ * above), TRA_E_ALIGN, TRA_E_HIP.
+ */
+int tra_execute_contract_chain(tra_plan_t plan_c, tra_plan_t plan_a, tra_plan_t plan_b, const void *xc,
+                               const void *yc, const void *ya, const void *xb, void *z, void *hip_stream);
+
+/*
  * tra_repartition -- re-cut one tensor from partition vector d_from to d_to
  * (section 2.2, repartition; the initial partition of section 4.1's runtime
  * is the case d_from = all ones).  A pure permutation of elements: every

@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
             "tra_plan_destroy": ([P], I),
             "tra_execute": ([P, P, P, P, P, ctypes.c_size_t, P], I),
             "tra_execute_chain": ([P, P, P, P, P, P, P], I),
+            "tra_execute_contract_chain": ([P, P, P, P, P, P, P, P, P], I),
             "tra_repartition": ([P, I, P, P, I, P, P, P], I),
             "tra_canonical_labels": ([ctypes.c_char_p, ctypes.c_char_p, I], I),
             "tra_d_from_operand_form": ([ctypes.c_char_p, P, I, P, I], I),
@@ -212,6 +213,23 @@ def tra_execute_chain(plan_a: Plan, plan_b: Plan, xa: torch.Tensor, ya: Optional
         z = torch.empty(ib.z_elems, dtype=TORCH_DTYPES[plan_b.out_dtype], device=xa.device)
     pz = _dev_ptr(z, "z", ib.z_elems, plan_b.out_dtype)
     _check(lib().tra_execute_chain(plan_a.handle, plan_b.handle, pxa, pya, pxb, pz, _stream(stream)))
+    return z
+
+
+def tra_execute_contract_chain(plan_c: Plan, plan_a: Plan, plan_b: Plan, xc: torch.Tensor, yc: torch.Tensor,
+                               ya: torch.Tensor, xb: torch.Tensor, z: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """z = plan_b(xb, plan_a(plan_c(xc, yc), ya)) in the product's epilogue."""
+    ic, ia, ib = plan_c.info, plan_a.info, plan_b.info
+    pxc = _dev_ptr(xc, "xc", ic.x_elems, plan_c.in_dtype)
+    pyc = _dev_ptr(yc, "yc", ic.y_elems, plan_c.in_dtype)
+    pya = _dev_ptr(ya, "ya", ia.y_elems, plan_a.in_dtype)
+    pxb = _dev_ptr(xb, "xb", ib.x_elems, plan_b.in_dtype)
+    if z is None:
+        z = torch.empty(ib.z_elems, dtype=TORCH_DTYPES[plan_b.out_dtype], device=xc.device)
+    pz = _dev_ptr(z, "z", ib.z_elems, plan_b.out_dtype)
+    _check(lib().tra_execute_contract_chain(plan_c.handle, plan_a.handle, plan_b.handle, pxc, pyc, pya, pxb, pz,
+                                            _stream(stream)))
     return z
 
 

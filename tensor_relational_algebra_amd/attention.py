@@ -33,7 +33,7 @@ from typing import Dict, List, Optional, Tuple
 
 import torch
 
-from ._binding import Plan, tra_execute, tra_execute_chain, tra_plan
+from ._binding import Plan, tra_execute, tra_execute_chain, tra_execute_contract_chain, tra_plan
 
 # (output name, spec, operand names, join, aggregate, input dtype, output dtype, scaled by 1/sqrt(dh))
 FORWARD: List[Tuple[str, str, Tuple[str, ...], str, str, str, str, bool]] = [
@@ -50,9 +50,9 @@ FORWARD: List[Tuple[str, str, Tuple[str, ...], str, str, str, str, bool]] = [
 BACKWARD: List[Tuple[str, str, Tuple[str, ...], str, str, str, str, bool]] = [
     ("dO", "sa,ahd->shd", ("dOutput", "W_O"), "mul", "sum", "bf16", "bf16", False),
     ("dW_O", "sa,shd->ahd", ("dOutput", "O"), "mul", "sum", "bf16", "f32", False),
+    ("Rows", "shd,shd->hs", ("dO", "O"), "mul", "sum", "bf16", "f32", False),
     ("dAttn", "shd,thd->hst", ("dO", "V_proj"), "mul", "sum", "bf16", "f32", False),
     ("dV_proj", "hst,shd->thd", ("Attn", "dO"), "mul", "sum", "bf16", "bf16", False),
-    ("Rows", "shd,shd->hs", ("dO", "O"), "mul", "sum", "bf16", "f32", False),
     ("dAttn_c", "hst,hs->hst", ("dAttn", "Rows"), "sub", "none", "f32", "bf16", False),
     ("dScores", "hst,hst->hst", ("Attn", "dAttn_c"), "mul", "none", "bf16", "bf16", False),
     ("dQ_proj", "hst,thd->shd", ("dScores", "K_proj"), "mul", "sum", "bf16", "bf16", True),
@@ -72,8 +72,22 @@ _TORCH = {"bf16": torch.bfloat16, "f32": torch.float32}
 # subtraction dAttn - r and the Jacobian product read dAttn, Attn and r once
 # and write dScores, 8 bytes per [h,s,t] element instead of 12.
 CHAINED = {"dAttn_c": "dScores"}
-# The steps as they are launched (and reported to on_step).
-BACKWARD_LAUNCHES = [n for n, *_ in BACKWARD if n not in CHAINED]
+# A product whose epilogue runs such a chain (tra_execute_contract_chain):
+# dScores = Attn * (dO.V^T - Rows) in one launch, dAttn never written.  Used
+# when the layer is built with fuse_product_chain and the product's plan runs
+# on the matrix-core kernel with no split.
+CONTRACT_CHAINED = {"dAttn": ("dAttn_c", "dScores")}
+
+
+def _launches(fused: bool) -> List[str]:
+    skip = set(CHAINED) | ({"dAttn"} if fused else set())
+    return [n for n, *_ in BACKWARD if n not in skip]
+
+
+# The steps as they are launched (and reported to on_step), with the product
+# chain fused (the full-size layer) and without it.
+BACKWARD_LAUNCHES = _launches(True)
+BACKWARD_LAUNCHES_UNFUSED = _launches(False)
 
 
 class AttentionLayer:
@@ -82,7 +96,7 @@ class AttentionLayer:
     s query positions, t key positions, a model width, h heads of width dh.
     """
 
-    def __init__(self, s: int, a: int, h: int, dh: int, t: Optional[int] = None):
+    def __init__(self, s: int, a: int, h: int, dh: int, t: Optional[int] = None, fuse_product_chain: bool = False):
         self.s, self.a, self.h, self.dh = s, a, h, dh
         self.t = s if t is None else t
         self.bounds = {"s": s, "t": self.t, "a": a, "h": h, "d": dh}
@@ -95,6 +109,11 @@ class AttentionLayer:
             self.plans[name] = tra_plan(spec, b, {c: 1 for c in labels}, join, agg, idt, odt,
                                         self.scale if scaled else 1.0)
         self.workspace_bytes = max(p.info.workspace_bytes for p in self.plans.values())
+        pc = self.plans["dAttn"]
+        # opt-in: correct (bit-identical), but its epilogue is slower than the
+        # two launches it replaces on the full-size layer
+        self.fuse_product_chain = fuse_product_chain and pc.kernel == "mfma_bf16" and pc.info.agg_split == 1
+        self.backward_launches = BACKWARD_LAUNCHES if self.fuse_product_chain else BACKWARD_LAUNCHES_UNFUSED
 
     def shape(self, name: str) -> Tuple[int, ...]:
         for out, spec, *_ in FORWARD + BACKWARD:
@@ -104,9 +123,27 @@ class AttentionLayer:
 
     def _run(self, steps, env: Dict[str, torch.Tensor], ws: Optional[torch.Tensor], stream, on_step) -> None:
         by_name = {st[0]: st for st in steps}
+        done = set()
         for name, _, ins, *_rest in steps:
-            if any(second == name and first in by_name for first, second in CHAINED.items()):
+            if name in done or any(second == name and first in by_name for first, second in CHAINED.items()):
                 continue   # ran with its first step
+            if name in CONTRACT_CHAINED and self.fuse_product_chain:
+                a_name, b_name = CONTRACT_CHAINED[name]
+                _, _, ins_a, *_ = by_name[a_name]
+                _, _, ins_b, *rest_b = by_name[b_name]
+                assert ins_a[0] == name and ins_b[1] == a_name, "the chain reads the product, then its first step"
+                pb = self.plans[b_name]
+                z = env.get(b_name)
+                if z is None or z.numel() != pb.info.z_elems or z.dtype != _TORCH[rest_b[3]]:
+                    z = torch.empty(pb.info.z_elems, dtype=_TORCH[rest_b[3]], device=env[ins[0]].device)
+                tra_execute_contract_chain(self.plans[name], self.plans[a_name], pb, env[ins[0]].reshape(-1),
+                                           env[ins[1]].reshape(-1), env[ins_a[1]].reshape(-1),
+                                           env[ins_b[0]].reshape(-1), z.reshape(-1), stream)
+                env[b_name] = z.view(self.shape(b_name))
+                done.update((a_name, b_name))
+                if on_step is not None:
+                    on_step(b_name)
+                continue
             out_name = CHAINED.get(name, name)
             p = self.plans[name]
             x = env[ins[0]].reshape(-1)

@@ -67,6 +67,22 @@ int64_t predict_softmax_one_pass_ns(const tra_plan_s &lse, const tra_plan_s &nor
 // Two elementwise plans as one pass (k_simple.hip, tra_execute_chain): true
 // when plan b's second operand is plan a's output in plan b's output layout.
 bool elemwise_chainable(const tra_plan_s &a, const tra_plan_s &b);
+// A matrix-core product followed by two elementwise steps in its epilogue:
+//     t = join_a(product, ya) * scale_a       (rounded to the chain's dtype)
+//     z = join_b(xb, t) * scale_b
+// xb and z are laid out as the product's output; ya's offset is the sum of
+// the st[0] strides of rb, rm and rn over the product's batch, row and column
+// digits (the digits of the plan's gb, gm and gn).
+struct ChainEpi {
+    Pow2Group rb, rm, rn;
+    const void *ya, *xb;
+    int join_a, join_b;
+    float scale_a, scale_b;
+};
+// The intermediate and output dtypes are equal (bf16, or fp32 when out_f32).
+int launch_mfma_chain(const tra_plan_s &p, const ChainEpi &ce, bool out_f32, const void *x, const void *y, void *z,
+                      void *stream);
+
 int launch_elemwise_chain(const tra_plan_s &a, const tra_plan_s &b, const void *xa, const void *ya, const void *xb,
                           void *z, void *stream);
 

@@ -24,7 +24,10 @@
 // a matmul) runs on the same kernel.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
+#include "graph.h"
 #include "plan.h"
 
 namespace tra {
@@ -170,10 +173,13 @@ struct DmaPlan {
     }
 };
 
-template <int V, bool AKM, bool BKM, typename TO>
-__global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf16(
-    GemmView v, const uint16_t *__restrict__ x, const uint16_t *__restrict__ y, TO *__restrict__ z,
-    float *__restrict__ ws)
+// The tile kernel's body.  TC is void for a plain product; otherwise the
+// epilogue applies the two elementwise steps of a ChainEpi to each element
+// (TC = their intermediate dtype) instead of storing the product.
+template <int V, bool AKM, bool BKM, typename TO, typename TC>
+__device__ __forceinline__ void mfma_body(const GemmView &v, const uint16_t *__restrict__ x,
+                                          const uint16_t *__restrict__ y, TO *__restrict__ z,
+                                          float *__restrict__ ws, const ChainEpi &ce)
 {
     constexpr MfmaCfg C = mfma_cfg(V);
     constexpr int BM = C.bm, BN = C.bn, BK = MF_BK, WM = C.wm, WN = C.wn;
@@ -358,12 +364,42 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
                 for (int r = 0; r < 4; ++r) {
                     const int32_t o = hi + lo[r] + on;
                     const float val = acc[i][j][4 * q + r];
-                    if (split) wsp[o] = val;
-                    else Scalar<TO>::store(z, o, val * v.post_scale);
+                    if constexpr (std::is_void<TC>::value) {
+                        if (split) wsp[o] = val;
+                        else Scalar<TO>::store(z, o, val * v.post_scale);
+                    } else {
+                        // the product as the fp32 output it would be stored as,
+                        // then the two steps exactly as the chained
+                        // elementwise kernel computes them
+                        const int32_t ro = p2off<0>(ce.rb, bidx) + p2off<0>(ce.rm, m0) +
+                                           p2off<0>(ce.rm, wm * (BM / WM) + i * 32 + 8 * q) +
+                                           p2off<0>(ce.rm, 4 * (lane >> 5) + r) +
+                                           p2off<0>(ce.rn, n0 + b_col0 + j * 32 + r_lane);
+                        const float av = val * v.post_scale;
+                        float t = join_any(ce.join_a, av, ((const float *)ce.ya)[ro]) * ce.scale_a;
+                        if constexpr (std::is_same<TC, bf16_t>::value) t = bf16_to_f32(f32_to_bf16(t));
+                        const float xv = (float)Scalar<TC>::load((const TC *)ce.xb, o);
+                        Scalar<TO>::store(z, o, join_any(ce.join_b, xv, t) * ce.scale_b);
+                    }
                 }
             }
         }
     }
+}
+
+template <int V, bool AKM, bool BKM, typename TO>
+__global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf16(
+    GemmView v, const uint16_t *__restrict__ x, const uint16_t *__restrict__ y, TO *__restrict__ z,
+    float *__restrict__ ws)
+{
+    mfma_body<V, AKM, BKM, TO, void>(v, x, y, z, ws, ChainEpi{});
+}
+
+template <int V, bool AKM, bool BKM, typename TO>
+__global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_chain(
+    GemmView v, const uint16_t *__restrict__ x, const uint16_t *__restrict__ y, TO *__restrict__ z, ChainEpi ce)
+{
+    mfma_body<V, AKM, BKM, TO, TO>(v, x, y, z, nullptr, ce);
 }
 
 // Every (tile, operand layout, output dtype) combination the launcher can
@@ -420,6 +456,40 @@ static int launch_tile(const tra_plan_s &p, const void *x, const void *y, void *
     case 1: return launch_layout<1, TO>(p, x, y, z, ws, s);
     default: return launch_layout<2, TO>(p, x, y, z, ws, s);
     }
+}
+
+template <int V, typename TO>
+static int launch_chain_v(const tra_plan_s &p, const void *x, const void *y, void *z, const ChainEpi &ce,
+                          hipStream_t s)
+{
+    constexpr MfmaCfg C = mfma_cfg(V);
+    const GemmView &v = p.gv;
+    dim3 grid((v.gm.total / C.bm) * (v.gn.total / C.bn), v.gb.total, 1);
+    void (*k)(GemmView, const uint16_t *, const uint16_t *, TO *, ChainEpi);
+    if (p.a_kmajor) k = p.b_kmajor ? k_mfma_chain<V, true, true, TO> : k_mfma_chain<V, true, false, TO>;
+    else k = p.b_kmajor ? k_mfma_chain<V, false, true, TO> : k_mfma_chain<V, false, false, TO>;
+    hipLaunchKernelGGL(k, grid, dim3(C.wm * C.wn * 64), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z,
+                       ce);
+    return (int)hipGetLastError();
+}
+
+template <typename TO>
+static int launch_chain_t(const tra_plan_s &p, const void *x, const void *y, void *z, const ChainEpi &ce,
+                          hipStream_t s)
+{
+    switch (p.tile) {
+    case 0: return launch_chain_v<0, TO>(p, x, y, z, ce, s);
+    case 1: return launch_chain_v<1, TO>(p, x, y, z, ce, s);
+    default: return launch_chain_v<2, TO>(p, x, y, z, ce, s);
+    }
+}
+
+int launch_mfma_chain(const tra_plan_s &p, const ChainEpi &ce, bool out_f32, const void *x, const void *y, void *z,
+                      void *stream)
+{
+    if (p.gv.split != 1) return TRA_E_OP;
+    hipStream_t s = (hipStream_t)stream;
+    return out_f32 ? launch_chain_t<float>(p, x, y, z, ce, s) : launch_chain_t<bf16_t>(p, x, y, z, ce, s);
 }
 
 int launch_mfma_bf16(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream)

@@ -208,17 +208,24 @@ static void choose_split(tra_plan_s &p, int64_t tiles, int64_t k_steps, int bk)
 }
 
 // Try the tile kernels (GEMM view).  Returns true and fills p when eligible.
+// Output labels of a two-operand product split into its batch (in both
+// operands), row (X only) and column (Y only) groups, in output order.
+static void tile_groups(const tra_plan_s &p, std::string &M, std::string &N, std::string &Bt)
+{
+    for (char c : p.zl) {
+        bool inx = p.xl.find(c) != std::string::npos, iny = p.yl.find(c) != std::string::npos;
+        if (inx && iny) Bt.push_back(c);
+        else if (inx) M.push_back(c);
+        else N.push_back(c);
+    }
+}
+
 static bool lower_tile(tra_plan_s &p)
 {
     if (p.n_ops != 2) return false;
     const std::string &X = p.xl, &Y = p.yl, &Z = p.zl;
     std::string M, N, Bt, K;
-    for (char c : Z) {
-        bool inx = X.find(c) != std::string::npos, iny = Y.find(c) != std::string::npos;
-        if (inx && iny) Bt.push_back(c);
-        else if (inx) M.push_back(c);
-        else N.push_back(c);
-    }
+    tile_groups(p, M, N, Bt);
     for (char c : p.con) {
         bool inx = X.find(c) != std::string::npos, iny = Y.find(c) != std::string::npos;
         if (!(inx && iny)) return false;  // contracted label in one operand only
@@ -599,6 +606,53 @@ int tra_execute_chain(tra_plan_t a, tra_plan_t b, const void *xa, const void *ya
     if (!aligned16(xa) || !aligned16(xb) || !aligned16(z) || (ya && !aligned16(ya)))
         return fail(TRA_E_ALIGN, "device pointers must be 16-byte aligned");
     int err = launch_elemwise_chain(*a, *b, xa, ya, xb, z, stream);
+    if (err) return fail(TRA_E_HIP, std::string("kernel launch failed: ") + hip_error_text(err));
+    return TRA_OK;
+}
+
+int tra_execute_contract_chain(tra_plan_t c, tra_plan_t a, tra_plan_t b, const void *xc, const void *yc,
+                               const void *ya, const void *xb, void *z, void *stream)
+{
+    if (!c || !a || !b) return fail(TRA_E_NULL, "plan is NULL");
+    if (c->kernel != TRA_KERNEL_MFMA_BF16 || c->gv.split != 1 || c->out_dtype != D_F32)
+        return fail(TRA_E_OP, "the product must run on the matrix-core kernel with no split of its contracted "
+                              "range and an fp32 output");
+    if (a->kernel != TRA_KERNEL_ELEMWISE || b->kernel != TRA_KERNEL_ELEMWISE || a->n_ops != 2 || b->n_ops != 2)
+        return fail(TRA_E_OP, "both steps must be two-operand elementwise plans (aggregate none)");
+    if (a->in_dtype != D_F32 || (a->out_dtype != D_F32 && a->out_dtype != D_BF16) || b->in_dtype != a->out_dtype ||
+        b->out_dtype != a->out_dtype)
+        return fail(TRA_E_OP, "dtypes: the first step reads fp32, and its output, the second step's input and "
+                              "the result share one dtype, bf16 or fp32");
+    const std::string &Z = c->zl;
+    if (a->xl != Z || a->zl != Z || b->xl != Z || b->yl != Z || b->zl != Z)
+        return fail(TRA_E_OP, "the product's output, the first step's first operand and output, and both "
+                              "operands and the output of the second step must be one relation (same labels "
+                              "in the same order)");
+    for (char ch : Z)
+        if (a->B[(int)ch] != c->B[(int)ch] || b->B[(int)ch] != c->B[(int)ch] || a->d[(int)ch] != c->d[(int)ch] ||
+            b->d[(int)ch] != c->d[(int)ch])
+            return fail(TRA_E_OP, "the three plans must agree on the output's extents and d");
+    for (char ch : a->yl)
+        if (Z.find(ch) == std::string::npos)
+            return fail(TRA_E_OP, "the first step's second operand may only carry output labels");
+    if (c->info.z_elems && (!xc || !yc || !ya || !xb || !z)) return fail(TRA_E_NULL, "operand / output pointer is NULL");
+    if (!aligned16(xc) || !aligned16(yc) || !aligned16(ya) || !aligned16(xb) || !aligned16(z))
+        return fail(TRA_E_ALIGN, "device pointers must be 16-byte aligned");
+    if (c->info.z_elems == 0) return TRA_OK;
+    std::string M, N, Bt;
+    tile_groups(*c, M, N, Bt);
+    const std::string *tr[3] = {&a->yl, nullptr, nullptr};
+    ChainEpi ce{};
+    if (!to_pow2(group_subdims(Bt, c->B, c->d, tr), ce.rb) || !to_pow2(group_subdims(M, c->B, c->d, tr), ce.rm) ||
+        !to_pow2(group_subdims(N, c->B, c->d, tr), ce.rn))
+        return fail(TRA_E_OP, "the first step's second operand has no power-of-two digit layout");
+    ce.ya = ya;
+    ce.xb = xb;
+    ce.join_a = a->join;
+    ce.join_b = b->join;
+    ce.scale_a = a->el.post_scale;
+    ce.scale_b = b->el.post_scale;
+    int err = launch_mfma_chain(*c, ce, a->out_dtype == D_F32, xc, yc, z, stream);
     if (err) return fail(TRA_E_HIP, std::string("kernel launch failed: ") + hip_error_text(err));
     return TRA_OK;
 }

@@ -347,3 +347,34 @@ def test_execute_chain_host_errors():
     assert L.tra_execute_chain(r.handle, b.handle, 16, 16, 16, 16, None) == -7
     # misaligned pointers
     assert L.tra_execute_chain(a.handle, b.handle, 16, 16, 16, 8, None) == -9
+
+
+def test_execute_contract_chain_host_errors():
+    """tra_execute_contract_chain validates on the host before any launch."""
+    L = tra.lib()
+    b3 = {"s": 512, "t": 512, "h": 2, "d": 32}
+    pc = tra.tra_plan("shd,thd->hst", b3, {c: 1 for c in b3}, "mul", "sum", "bf16", "f32")
+    out = {c: b3[c] for c in "hst"}
+    pa = tra.tra_plan("hst,hs->hst", out, {c: 1 for c in out}, "sub", "none", "f32", "bf16")
+    pb = tra.tra_plan("hst,hst->hst", out, {c: 1 for c in out}, "mul", "none", "bf16", "bf16")
+    assert pc.kernel == "mfma_bf16" and pc.info.agg_split == 1
+    assert L.tra_execute_contract_chain(None, pa.handle, pb.handle, 16, 16, 16, 16, 16, None) == -1
+    # the product must be on the matrix cores (an fp32 product is not)
+    p32 = tra.tra_plan("shd,thd->hst", b3, {c: 1 for c in b3}, "mul", "sum", "f32", "f32")
+    assert L.tra_execute_contract_chain(p32.handle, pa.handle, pb.handle, 16, 16, 16, 16, 16, None) == -7
+    # the steps must share the product's output relation (here: another blocking)
+    pb2 = tra.tra_plan("hst,hst->hst", out, {"h": 2, "s": 1, "t": 1}, "mul", "none", "bf16", "bf16")
+    assert L.tra_execute_contract_chain(pc.handle, pa.handle, pb2.handle, 16, 16, 16, 16, 16, None) == -7
+    # one dtype for the intermediate and the result
+    pb3 = tra.tra_plan("hst,hst->hst", out, {c: 1 for c in out}, "mul", "none", "bf16", "f32")
+    assert L.tra_execute_contract_chain(pc.handle, pa.handle, pb3.handle, 16, 16, 16, 16, 16, None) == -7
+    # a split contracted range is refused
+    ps = tra.tra_plan("ik,kj->ij", {"i": 256, "j": 256, "k": 1024}, {"i": 1, "j": 1, "k": 1}, "mul", "sum", "bf16",
+                      "f32")
+    assert ps.info.agg_split > 1
+    sa = tra.tra_plan("ij,i->ij", {"i": 256, "j": 256}, {"i": 1, "j": 1}, "sub", "none", "f32", "f32")
+    sb = tra.tra_plan("ij,ij->ij", {"i": 256, "j": 256}, {"i": 1, "j": 1}, "mul", "none", "f32", "f32")
+    assert L.tra_execute_contract_chain(ps.handle, sa.handle, sb.handle, 16, 16, 16, 16, 16, None) == -7
+    # null and misaligned pointers
+    assert L.tra_execute_contract_chain(pc.handle, pa.handle, pb.handle, 16, 16, None, 16, 16, None) == -1
+    assert L.tra_execute_contract_chain(pc.handle, pa.handle, pb.handle, 16, 16, 16, 16, 8, None) == -9

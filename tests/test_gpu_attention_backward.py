@@ -20,13 +20,13 @@ pytestmark = pytest.mark.gpu
 GRADS = ("dQ", "dK", "dV", "dW_Q", "dW_K", "dW_V", "dW_O")
 
 
-def _run(case, t_len=None):
+def _run(case, t_len=None, fuse=False):
     host = case.make_inputs()
     if t_len is not None and t_len != case.s:
         host["K"] = wl.draw(1000 * case.wid + 8, (t_len, case.a), "normal", "bf16", std=1.0)
         host["V"] = wl.draw(1000 * case.wid + 9, (t_len, case.a), "normal", "bf16", std=1.0)
     g = case.make_output_gradient()
-    layer = tra.AttentionLayer(case.s, case.a, case.h, case.dh, t=t_len)
+    layer = tra.AttentionLayer(case.s, case.a, case.h, case.dh, t=t_len, fuse_product_chain=fuse)
     dev = {k: v.to(DEV) for k, v in host.items()}
     ws = layer.workspace(DEV)
     saved = layer.forward(dev, ws)
@@ -62,11 +62,13 @@ def test_mid_size_layer_on_the_matrix_cores():
     # head width and tile multiples of the full layer: every contraction of the
     # backward plans onto the matrix-core kernel
     case = wl.MhaCase(s=1024, a=512, h=8, dh=128, wid=44)
-    got, host, g, layer = _run(case)
+    got, host, g, layer = _run(case, fuse=True)
     contractions = [n for n, spec, *_ in tra.attention.BACKWARD if "->" in spec and n not in
                     ("Rows", "dAttn_c", "dScores")]
     assert all(layer.plans[n].kernel == "mfma_bf16" for n in contractions), \
         {n: layer.plans[n].kernel for n in contractions}
+    # the softmax Jacobian runs in the dAttn product's epilogue
+    assert layer.fuse_product_chain and "dAttn" not in layer.backward_launches
     _check(got, host, g)
 
 

@@ -403,3 +403,49 @@ def test_execute_chain_matches_two_launches(case):
     got = tra.tra_execute_chain(pa, pb, xa, ya, xb)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+
+
+CONTRACT_CHAIN_CASES = [
+    # (product spec, bounds, d, step a (spec, join), chain dtype, step b join); one
+    # 32-deep k-tile each, so that no plan splits its contracted range
+    # the attention backward's softmax Jacobian: Attn * (dO.V^T - Rows), dense
+    ("shd,thd->hst", {"s": 512, "t": 512, "h": 2, "d": 32}, {"s": 1, "t": 1, "h": 1, "d": 1},
+     ("hst,hs->hst", "sub"), "bf16", "mul"),
+    # the same, blocked: every label of the output cut in two
+    ("shd,thd->hst", {"s": 512, "t": 512, "h": 2, "d": 32}, {"s": 2, "t": 2, "h": 2, "d": 1},
+     ("hst,hs->hst", "sub"), "bf16", "mul"),
+    # a column vector, fp32 chain, a one-tile (128 x 128) product
+    ("ik,kj->ij", {"i": 128, "j": 128, "k": 32}, {"i": 1, "j": 2, "k": 1},
+     ("ij,j->ij", "add"), "f32", "sqdiff"),
+    # a full operand for the first step, a batched product with a K-major Y
+    ("bik,bjk->bij", {"b": 4, "i": 256, "j": 256, "k": 32}, {"b": 2, "i": 1, "j": 1, "k": 1},
+     ("bij,bij->bij", "mul"), "bf16", "sub"),
+]
+
+
+@pytest.mark.parametrize("case", CONTRACT_CHAIN_CASES, ids=["jacobian", "jacobian-blocked", "colvec-f32", "full-op"])
+def test_execute_contract_chain_matches_three_launches(case):
+    """A matrix-core product with two elementwise steps in its epilogue is
+    bit-identical to the product, then the two steps, each launched alone."""
+    spec_c, bounds, d, (spec_a, join_a), dt, join_b = case
+    dd = {k: v for k, v in d.items()}
+    pc = tra.tra_plan(spec_c, bounds, dd, "mul", "sum", "bf16", "f32")
+    out = spec_c.split("->")[1]
+    ba = {c: bounds[c] for c in set(spec_a.replace(",", "").replace("->", ""))}
+    da = {c: d[c] for c in ba}
+    pa = tra.tra_plan(spec_a, ba, da, join_a, "none", "f32", dt)
+    pb = tra.tra_plan(f"{out},{out}->{out}", {c: bounds[c] for c in out}, {c: d[c] for c in out}, join_b, "none",
+                      dt, dt)
+    assert pc.kernel == "mfma_bf16" and pc.info.agg_split == 1, (pc.kernel, pc.info.agg_split)
+    g = torch.Generator().manual_seed(12)
+    t_a = {"f32": torch.float32, "bf16": torch.bfloat16}
+    xc = torch.randn(pc.info.x_elems, generator=g).to(torch.bfloat16).to(DEV)
+    yc = torch.randn(pc.info.y_elems, generator=g).to(torch.bfloat16).to(DEV)
+    ya = torch.randn(pa.info.y_elems, generator=g).to(DEV)
+    xb = torch.randn(pb.info.x_elems, generator=g).to(t_a[dt]).to(DEV)
+    prod = tra.tra_execute(pc, xc, yc)
+    t = tra.tra_execute(pa, prod, ya)
+    want = tra.tra_execute(pb, xb, t)
+    got = tra.tra_execute_contract_chain(pc, pa, pb, xc, yc, ya, xb)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
