@@ -20,5 +20,16 @@ def build(force: bool = True) -> str:
     return LIB
 
 
+def build_sanitized(out_dir: str) -> str:
+    """The same library built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (host code only), for the sanitizer run of the CPU suite."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "liboracle_san.so")
+    subprocess.run(["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-fPIC", "-shared", "-fopenmp", "-std=c11",
+                    "-Wall", "-Wextra", "-o", lib, SRC, "-lm"], check=True)
+    return lib
+
+
 if __name__ == "__main__":
     print(build())

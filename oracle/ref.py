@@ -44,7 +44,9 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        path = _build.LIB
+        # TRA_ORACLE_LIBRARY names another build of einsum_ref.c (the
+        # sanitizer run of the CPU suite loads an ASan/UBSan build this way)
+        path = os.environ.get("TRA_ORACLE_LIBRARY") or _build.LIB
         if not os.path.exists(path):
             path = _build.build()
         lib = ctypes.CDLL(path)

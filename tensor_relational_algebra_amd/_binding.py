@@ -15,7 +15,9 @@ from typing import Dict, List, Optional, Sequence, Tuple, Union
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_build", "libtra.so")
+# TRA_LIBRARY names another build of the library (the sanitizer run of the CPU
+# suite loads an ASan/UBSan build of the host code this way)
+LIB_PATH = os.environ.get("TRA_LIBRARY") or os.path.join(_PKG, "_build", "libtra.so")
 
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
 TORCH_DTYPES = {0: torch.float32, 1: torch.bfloat16, 2: torch.int32}

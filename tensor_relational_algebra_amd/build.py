@@ -56,6 +56,31 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"]
+
+
+def build_sanitized(out_dir: str) -> str:
+    """libtra with its host code (csrc/*.cpp: parser, planner, chooser, graph
+    executor) built by g++ under AddressSanitizer and UndefinedBehaviorSanitizer,
+    linked with the device objects of the last build() (built first if absent).
+    Only the host code is instrumented; the kernels are the normal ones."""
+    if not os.path.exists(LIB):
+        build()
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".san.o")
+        subprocess.run(["g++"] + SAN_FLAGS + ["-fPIC", "-std=c++17", "-Wall", "-Wextra", "-I", INCLUDE,
+                                              "-I", CSRC, "-c", src, "-o", obj], check=True)
+        objs.append(obj)
+    dev_objs = sorted(glob.glob(os.path.join(OUT, "*.hip.o")))
+    lib = os.path.join(out_dir, "libtra_san.so")
+    subprocess.run(["g++", "-shared", "-fsanitize=address,undefined", "-o", lib] + objs + dev_objs +
+                   ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"], check=True)
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -21,6 +21,29 @@ def test_hand_worked_costs():
         assert chooser.einsum_cost(c["spec"], c["bounds"], c["d"]) == c["cost"], c["_work"]
 
 
+def _softmax_node(bounds):
+    return chooser.Node("Attn", "hst->hst", dict(bounds), ["S"], kind="softmax")
+
+
+def test_hand_worked_softmax_node_costs():
+    """The softmax node (LSE = lse_t S, then Attn = exp(S - LSE), one d over
+    h, s, t) costs the sum of its two EinSums' terms; worked by hand."""
+    g = json.load(open(os.path.join(GOLDEN, "chooser_costs.json")))
+    assert len(g["softmax_cases"]) >= 4
+    for c in g["softmax_cases"]:
+        assert chooser.node_cost(_softmax_node(c["bounds"]), c["d"]) == c["cost"], c["_work"]
+
+
+def test_softmax_node_best_blocking_closed_form():
+    """2*H*S*T + (2*d_t - 1)*H*S is least at d_t = 1: for P = 8 on h=2, s=4, t=4
+    the search must pick d_t = 1, h and s cut 8 ways, at cost 2*32 + 8 = 72."""
+    node = _softmax_node({"h": 2, "s": 4, "t": 4})
+    total, asg = chooser.dp([node], 8)
+    assert total == 72
+    assert asg["Attn"]["t"] == 1 and asg["Attn"]["h"] * asg["Attn"]["s"] == 8
+    assert chooser.exhaustive([node], 8)[0] == 72
+
+
 def test_candidates_respect_pruning_rules():
     node = chooser.Node("n", "ij,jk->ik", {"i": 24, "j": 16, "k": 8}, ["@x", "@y"])
     cands = chooser.candidates(node, 16)

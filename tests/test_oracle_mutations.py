@@ -69,3 +69,43 @@ def test_planted_mistake_is_caught(name, tmp_path, monkeypatch):
         except AssertionError:
             caught.append(f.__name__)
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+# Planted mistakes in the oracle's cost model (oracle/chooser.py).  A mutated
+# copy of the module is loaded in place of the real one, and the cost pins of
+# test_oracle_chooser must fail against it.
+CHOOSER_SRC = os.path.join(os.path.dirname(SRC), "chooser.py")
+CHOOSER_MUTATIONS = {
+    "softmax_drops_normalisation": ("        return lse + nrm\n", "        return lse\n"),
+    "softmax_lse_over_s": ('lse = einsum_cost(f"{h}{s}{t}->{h}{s}"', 'lse = einsum_cost(f"{h}{s}{t}->{h}{t}"'),
+    "softmax_broadcast_row_dropped": ('nrm = einsum_cost(f"{h}{s}{t},{h}{s}->{h}{s}{t}"',
+                                      'nrm = einsum_cost(f"{h}{s}{t}->{h}{s}{t}"'),
+    "aggregation_term_dropped": ("    return join_in + agg\n", "    return join_in\n"),
+    "join_term_counts_groups": ("    join_in = n * sum(blk(o) for o in ops)",
+                                "    join_in = (n // n_agg) * sum(blk(o) for o in ops)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CHOOSER_MUTATIONS))
+def test_planted_cost_model_mistake_is_caught(name, monkeypatch):
+    import importlib.util
+    import sys
+
+    from tests import test_oracle_chooser as cpins
+    old, new = CHOOSER_MUTATIONS[name]
+    src = open(CHOOSER_SRC).read()
+    assert old in src, f"mutation {name} no longer applies"
+    spec = importlib.util.spec_from_loader("oracle._chooser_mutant", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__package__ = "oracle"
+    monkeypatch.setitem(sys.modules, "oracle._chooser_mutant", mod)
+    exec(compile(src.replace(old, new, 1), CHOOSER_SRC, "exec"), mod.__dict__)
+    monkeypatch.setattr(cpins, "chooser", mod)
+    caught = []
+    for f in (cpins.test_hand_worked_costs, cpins.test_hand_worked_softmax_node_costs,
+              cpins.test_softmax_node_best_blocking_closed_form):
+        try:
+            f()
+        except AssertionError:
+            caught.append(f.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
