@@ -1,24 +1,30 @@
 """Benchmark of the extended-EinSum / TRA hot path on one MI355X.
 
-Workload (one step): the pairwise squared distance D[i,k] = sum_j (X[i,j] -
-Y[j,k])^2 with i = k = 8192, j = 256 (fp32, N(0,1) inputs) and its max-plus
-variant Z[i,k] = max_j (X[i,j] + Y[j,k]) (int32, uniform [-1000, 1000]), both
-under the partition vector d = [16, 1, 1, 16]:
-  dense -> relation for X and Y (tra_repartition), join + aggregation
-  (tra_execute), relation -> dense for the output (tra_repartition).
-Plans are made once, before timing (host only).  Inputs are resident in HBM
-before the timed region.
+Workload (one step): the 2.5D-blocked product Y = X A of the page "ColossalAI
+2.5D 张量并行深度解析" (section on partitioning Y = XA) with X 16384 x 8192 and
+A 8192 x 8192 (bf16, N(0, 0.02) inputs, fp32 accumulate and output): X cut
+into depth*q = 16 row blocks and q = 4 column blocks, A into 4 x 4 blocks, so
+the TRA partition vector over (i, k, j) is [16, 4, 4].  One step is
+  join + aggregation (tra_execute: 256 key-matched block products folded
+  4 per output block) and
+  the re-cut of Y from [16, 4] to [4, 16] blocks for the next layer
+  (tra_repartition),
+with X and A already resident in HBM in their relation layout (the initial
+dense -> relation copy is timed once, apart, and reported as layout_ms).
+Plans are made once, before timing (host only).
 
-value = algorithmic operations of one step / step time, in GFLOP/s, counting
-3 per (x-y)^2 + sum term and 2 per x+y / max term.
+value = the product's 2*16384*8192*8192 flop per step / step time (GFLOP/s).
 
 The JSON line also carries:
-  roofline      the dominant kernel (squared-distance join) against the
-                vector-ALU issue ceiling, timed with HIP events on its stream;
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload;
-  extra         the other workloads measured in the same run (partitioned
-                matmul, four-index contraction, blocked GEMM and its output
-                repartition, attention EinGraph), each against its own roof.
+  roofline              the product's kernel against the bf16 matrix-core peak,
+                        timed with HIP events on its stream;
+  roofline_repartition  the re-cut against HBM bandwidth;
+  parity                the timed output on sampled rows against the oracle;
+  cpu_baseline          the CPU oracle on those rows;
+  extra                 the other workloads measured in the same run (pairwise
+                        squared distance and max-plus, partitioned matmul,
+                        four-index contraction, the product's backward, the
+                        attention EinGraph), each against its own roof.
 """
 from __future__ import annotations
 
@@ -44,21 +50,29 @@ SQDIST_FLOP_PER_TERM = 3
 SQDIST_OPS_PER_TERM = 2
 VALU_SQDIST_PEAK = VALU_LANE_OPS / SQDIST_OPS_PER_TERM * SQDIST_FLOP_PER_TERM  # 117.96e12 flop/s
 
-# HBM traffic of the squared-distance join kernel, from two rocprofv3 --pmc runs of
-# `bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extra` (FETCH_SIZE, then
-# WRITE_SIZE, KiB per dispatch, mean over the dispatches), scaled by what the same
-# counters read for a plain 1 GiB same-blocking copy (`bench.py --copy-probe 1024`):
-# FETCH_SIZE read 524,300 KiB and WRITE_SIZE 1,048,576 KiB for 1,048,576 KiB moved,
-# hence factors 2.0 and 1.0.  The record holds only while the kernel sources hash to
-# `src_sha`; otherwise the kernel has changed since the counters were taken and
-# `traffic` is reported as null.
-TRAFFIC_SRCS = ("tensor_relational_algebra_amd/csrc/k_valu_tile.hip",
-                "tensor_relational_algebra_amd/csrc/device_common.h",
-                "tensor_relational_algebra_amd/csrc/tra_internal.h",
-                "tensor_relational_algebra_amd/csrc/plan.h")
-TRAFFIC_SQDIST = {"src_sha": "439559b799ea0b06", "fetch_kib": 40664.8, "write_kib": 262144.0,
-                  "fetch_factor": 2.0, "write_factor": 1.0,
-                  "profile": "profiles/valu_tile_sqdist_8192x256x8192_hbm_traffic.md"}
+# HBM traffic per launch of a kernel, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch, mean over the kernel's dispatches), scaled by
+# what the same counters read for a plain 1 GiB same-blocking copy
+# (`bench.py --copy-probe 1024`).  A record holds only while the kernel's sources
+# hash to `src_sha`; otherwise the kernel has changed since the counters were taken
+# and `traffic` is reported as null.
+COMMON_SRCS = ("tensor_relational_algebra_amd/csrc/device_common.h",
+               "tensor_relational_algebra_amd/csrc/tra_internal.h",
+               "tensor_relational_algebra_amd/csrc/plan.h")
+TRAFFIC_SRCS = {
+    "sqdist": ("tensor_relational_algebra_amd/csrc/k_valu_tile.hip",) + COMMON_SRCS,
+    "gemm": ("tensor_relational_algebra_amd/csrc/k_mfma.hip",) + COMMON_SRCS,
+}
+# squared distance: `bench.py --steps 3 --warmup 1 --no-cpu-baseline --only sqdist`;
+# FETCH_SIZE read 524,300 KiB and WRITE_SIZE 1,048,576 KiB for the 1,048,576 KiB
+# copy, hence factors 2.0 and 1.0
+TRAFFIC = {
+    "sqdist": {"src_sha": "439559b799ea0b06", "fetch_kib": 40664.8, "write_kib": 262144.0,
+               "fetch_factor": 2.0, "write_factor": 1.0,
+               "profile": "profiles/valu_tile_sqdist_8192x256x8192_hbm_traffic.md"},
+    "gemm": {"src_sha": None, "fetch_kib": None, "write_kib": None, "fetch_factor": None, "write_factor": None,
+             "profile": None},
+}
 
 
 def _src_sha(paths) -> str:
@@ -70,9 +84,10 @@ def _src_sha(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(rec) -> "float | None":
+def _traffic(name: str) -> "float | None":
     """Calibrated HBM bytes per launch, or None when the record is stale or absent."""
-    if rec["src_sha"] is None or rec["src_sha"] != _src_sha(TRAFFIC_SRCS):
+    rec = TRAFFIC[name]
+    if rec["src_sha"] is None or rec["src_sha"] != _src_sha(TRAFFIC_SRCS[name]):
         return None
     return 1024.0 * (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"])
 
@@ -85,7 +100,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra workloads to run")
-    ap.add_argument("--src-sha", action="store_true", help="print the kernel-source hash the traffic record keys on")
+    ap.add_argument("--src-sha", action="store_true", help="print the kernel-source hashes the traffic records key on")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure the constants of the chooser's time model and print them as one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -114,7 +129,7 @@ def _copy_probe(mib: int, reps: int) -> None:
 # the time model, each at a size where its kernel family is the planner's pick
 CALIBRATION_CASES = [
     ("latency", "i,i->i", {"i": 8}, {"i": 1}, "add", "none", "f32", "f32", 400),
-    ("mfma_tile0", "sa,ahd->shd", {"s": 4096, "a": 4096, "h": 32, "d": 128}, None, "mul", "sum", "bf16", "bf16", 20),
+    ("mfma_tile3", "sa,ahd->shd", {"s": 4096, "a": 4096, "h": 32, "d": 128}, None, "mul", "sum", "bf16", "bf16", 20),
     ("mfma_tile1", "bij,bjk->bik", {"b": 256, "i": 128, "j": 512, "k": 128}, None, "mul", "sum", "bf16", "f32", 50),
     ("mfma_tile2", "bij,bjk->bik", {"b": 2048, "i": 64, "j": 256, "k": 64}, None, "mul", "sum", "bf16", "f32", 50),
     ("valu_tile", "ij,jk->ik", {"i": 8192, "j": 256, "k": 8192}, {"i": 16, "j": 1, "k": 16}, "sqdiff", "sum",
@@ -196,6 +211,57 @@ def _events_time(fn, reps: int, stream) -> float:
     return start.elapsed_time(end) / reps
 
 
+def _events_time_flushed(fn, reps: int, stream, scratch) -> float:
+    """Average milliseconds of fn() over `reps` calls, HIP events on `stream`
+    around each call, with a read-modify-write pass over `scratch` (>= 1 GiB)
+    before each so that no call finds its inputs in the 256 MB Infinity Cache."""
+    import torch
+    evs = []
+    for _ in range(reps):
+        scratch.add_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _sample_rows(n_rows: int, n_blocks: int, per_block: int, seed: int):
+    """`per_block` distinct rows in each of `n_blocks` equal row blocks, seeded."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    b = n_rows // n_blocks
+    return np.sort(np.concatenate([k * b + rng.choice(b, size=per_block, replace=False) for k in range(n_blocks)]))
+
+
+def rel_errors(got, want, floor: float = 1e-2) -> dict:
+    """Max-norm relative error max|g - r| / max|r| (the gate) and the element-wise
+    relative error |g - r| / |r| over elements with |r| >= floor * max|r|."""
+    import numpy as np
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    big = float(np.abs(want).max()) if want.size else 0.0
+    diff = np.abs(got - want)
+    mask = np.abs(want) >= floor * big
+    return {"maxnorm": float(diff.max() / big) if big > 0 else float(diff.max(initial=0.0)),
+            "elementwise_floored": float((diff[mask] / np.abs(want[mask])).max()) if mask.any() else 0.0,
+            "floor": floor, "elements": int(want.size)}
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -203,7 +269,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.src_sha:
-        print(_src_sha(TRAFFIC_SRCS))
+        print(json.dumps({k: _src_sha(v) for k, v in TRAFFIC_SRCS.items()}))
         return
     if args.copy_probe:
         _copy_probe(args.copy_probe, max(args.steps, 1))
@@ -220,73 +286,58 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
-    sq, mp = wl.SQDIST, wl.MAXPLUS
-    B = sq.bounds
-    d = sq.d
-    xs_h, ys_h = sq.make_inputs()
-    xm_h, ym_h = mp.make_inputs()
-    xs, ys, xm, ym = (t.to(dev) for t in (xs_h, ys_h, xm_h, ym_h))
-    plan_sq = tra.tra_plan(sq.spec, B, d, sq.join, sq.agg, sq.in_dtype, sq.out_dtype)
-    plan_mp = tra.tra_plan(mp.spec, B, d, mp.join, mp.agg, mp.in_dtype, mp.out_dtype)
-    dx, dy, dz = [d["i"], d["j"]], [d["j"], d["k"]], [d["i"], d["k"]]
-    sx, sy, sz = [B["i"], B["j"]], [B["j"], B["k"]], [B["i"], B["k"]]
-    # resident buffers
-    xr_s = torch.empty_like(xs).reshape(-1)
-    yr_s = torch.empty_like(ys).reshape(-1)
-    xr_m = torch.empty_like(xm).reshape(-1)
-    yr_m = torch.empty_like(ym).reshape(-1)
-    zr_s = torch.empty(plan_sq.info.z_elems, dtype=torch.float32, device=dev)
-    zr_m = torch.empty(plan_mp.info.z_elems, dtype=torch.int32, device=dev)
-    zd_s = torch.empty(sz, dtype=torch.float32, device=dev)
-    zd_m = torch.empty(sz, dtype=torch.int32, device=dev)
-    ws_m = plan_mp.workspace(dev)
-    sq_ms, mp_ms = [], []
+    g = wl.GEMM25D
+    B = g.bounds
+    shape_y = [B["i"], B["k"]]
+    x_h, a_h = g.make_inputs()
+    plan = tra.tra_plan(g.spec, B, g.d, g.join, g.agg, g.in_dtype, g.out_dtype)
+    dx, da = [g.d["i"], g.d["j"]], [g.d["j"], g.d["k"]]
+    x, a = x_h.to(dev), a_h.to(dev)
+    xr = torch.empty(x.numel(), dtype=x.dtype, device=dev)
+    ar = torch.empty(a.numel(), dtype=a.dtype, device=dev)
+    # the initial partition of the inputs (dense -> relation), timed apart
+    layout_ms = _events_time(lambda: (tra.to_relation(x, dx, xr), tra.to_relation(a, da, ar)), 3, stream)
+    del x, a
+    yr = torch.empty(plan.info.z_elems, dtype=torch.float32, device=dev)
+    y2 = torch.empty_like(yr)
+    ws = plan.workspace(dev)
+    y_from, y_to = list(wl.GEMM25D_Y_FROM), list(wl.GEMM25D_Y_TO)
+    gemm_ev, recut_ev = [], []
 
-    def step(time_dominant: bool = False):
-        tra.to_relation(xs, dx, xr_s)
-        tra.to_relation(ys, dy, yr_s)
-        if time_dominant:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-        tra.tra_execute(plan_sq, xr_s, yr_s, zr_s)
-        if time_dominant:
-            e1.record(stream)
-            sq_ms.append((e0, e1))
-        tra.from_relation(zr_s, sz, dz, zd_s)
-        tra.to_relation(xm, dx, xr_m)
-        tra.to_relation(ym, dy, yr_m)
-        if time_dominant:
-            e2 = torch.cuda.Event(enable_timing=True)
-            e3 = torch.cuda.Event(enable_timing=True)
-            e2.record(stream)
-        tra.tra_execute(plan_mp, xr_m, yr_m, zr_m, ws_m)
-        if time_dominant:
-            e3.record(stream)
-            mp_ms.append((e2, e3))
-        tra.from_relation(zr_m, sz, dz, zd_m)
+    def step(rec: bool = False):
+        if rec:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+        tra.tra_execute(plan, xr, ar, yr, ws)
+        if rec:
+            e[1].record(stream)
+        tra.tra_repartition(yr, shape_y, y_from, y_to, y2)
+        if rec:
+            e[2].record(stream)
+            gemm_ev.append((e[0], e[1]))
+            recut_ev.append((e[1], e[2]))
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(time_dominant=True)
+        step(rec=True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    terms = B["i"] * B["j"] * B["k"]
-    step_ops = terms * SQDIST_FLOP_PER_TERM + terms * 2
-    value = step_ops / (ms_per_step * 1e-3) / 1e9
-    sq_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in sq_ms]))
-    mp_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in mp_ms]))
-    mp_packed = not ws_m[-1024:].view(torch.int32).any().item()
-    achieved = terms * SQDIST_FLOP_PER_TERM / (sq_launch_ms * 1e-3)
-    traffic = _traffic(TRAFFIC_SQDIST)
+    flops = 2.0 * B["i"] * B["j"] * B["k"]
+    value = flops / (ms_per_step * 1e-3) / 1e9
+    gemm_ms = float(np.mean([p.elapsed_time(q) for p, q in gemm_ev]))
+    recut_ms = float(np.mean([p.elapsed_time(q) for p, q in recut_ev]))
+    achieved = flops / (gemm_ms * 1e-3)
+    recut_bytes = 2.0 * yr.numel() * 4
+    recut_rate = recut_bytes / (recut_ms * 1e-3)
+    traffic = _traffic("gemm")
 
     out = {
         "metric": "einsum GFLOP/s & % of MFMA peak; repartition GB/s & % HBM peak (1 GPU)",
-        "value": round(value, 2),
+        "value": round(value, 1),
         "unit": "GFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -295,56 +346,114 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32+i32",
+        "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "pairwise squared distance + max-plus, i=k=8192, j=256, d=[16,1,1,16] "
-                               "(dense->relation, join+aggregate, relation->dense)",
-                   "i": B["i"], "j": B["j"], "k": B["k"], "d": [d["i"], d["j"], d["j"], d["k"]],
-                   "kernel": plan_sq.kernel},
-        "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": round(VALU_SQDIST_PEAK / 1e12, 3),
-                     "unit": "TFLOP/s", "frac": round(achieved / VALU_SQDIST_PEAK, 4),
+        "config": {"workload": "2.5D-blocked GEMM Y = X A, X 16384x8192, A 8192x8192, bf16 in, fp32 accumulate "
+                               "and out, TRA partition (i,k,j) = [16,4,4] (depth 4, q 4), then Y re-cut from "
+                               "[16,4] to [4,16] blocks; inputs resident as relations",
+                   "i": B["i"], "j": B["j"], "k": B["k"], "d_ikj": [g.d["i"], g.d["k"], g.d["j"]],
+                   "y_from": y_from, "y_to": y_to, "kernel": plan.kernel, "tile": plan.info.tile,
+                   "agg_split": plan.info.agg_split},
+        "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(BF16_MFMA_PEAK / 1e12, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": "k_valu_tile<sqdiff,sum>", "launch_ms": round(sq_launch_ms, 4),
-                     # algorithmic bytes: X and Y once, D once
-                     "algorithmic_bytes": (B["i"] * B["j"] + B["j"] * B["k"] + B["i"] * B["k"]) * 4},
-        # the max-plus join: range check + packed 16-bit kernel (exact on
-        # integers within +-1024) or, if an input lies outside, the 32-bit kernel
-        "maxplus": {"launch_ms": round(mp_launch_ms, 4), "Gterms/s": round(terms / (mp_launch_ms * 1e-3) / 1e9, 1),
-                    "path": "packed f16, exact (inputs within +-1024)" if mp_packed else "int32"},
+                     "kernel": "k_mfma_bf16", "launch_ms": round(gemm_ms, 4),
+                     "flop_per_launch": flops,
+                     # algorithmic bytes: X and A read once, Y written once
+                     "algorithmic_bytes": (B["i"] * B["j"] + B["j"] * B["k"]) * 2 + B["i"] * B["k"] * 4},
+        "roofline_repartition": {"bound": "hbm", "achieved": round(recut_rate / 1e9, 1),
+                                 "peak": round(HBM_PEAK / 1e9, 1), "unit": "GB/s",
+                                 "frac": round(recut_rate / HBM_PEAK, 4), "traffic": None,
+                                 "kernel": "k_repartition_p2", "launch_ms": round(recut_ms, 4),
+                                 "algorithmic_bytes": recut_bytes},
+        "layout_ms": round(layout_ms, 4),
     }
 
-    # zero-copy check of the timed outputs on a few rows against the oracle
+    # the timed output (re-cut to [4,16]) on sampled rows against the oracle
+    rows = _sample_rows(B["i"], g.d["i"], 4, seed=5005)
+    y_dense = tra.from_relation(y2, shape_y, y_to)
+    got = y_dense[torch.from_numpy(rows).to(dev)].cpu().double().numpy()
+    del y_dense
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline(xs_h, ys_h, xm_h, ym_h, zd_s, zd_m)
+        out["cpu_baseline"], want = _cpu_baseline(x_h, a_h, rows, g)
+        err = rel_errors(got.reshape(-1), want)
+        err["rows"] = len(rows)
+        out["parity"] = err
+        assert err["maxnorm"] <= 2e-2, f"blocked GEMM differs from the oracle: {err}"
     if not args.no_extra:
         only = set(filter(None, args.only.split(",")))
+        del xr, ar, yr, y2
+        torch.cuda.empty_cache()
         out["extra"] = _extra(tra, wl, dev, stream, only)
     print(json.dumps(out), flush=True)
 
 
-def _cpu_baseline(xs_h, ys_h, xm_h, ym_h, zd_s, zd_m):
-    """The oracle (as it stands) on the first `rows` output rows of both joins."""
+def _cpu_baseline(x_h, a_h, rows, g):
+    """The oracle (as it stands) on the sampled output rows of the blocked GEMM."""
     import numpy as np
     from oracle import ref
 
-    rows = 8192
-    n_k = zd_s.shape[1]
-    idx = np.arange(rows * n_k, dtype=np.int64)
+    n_k = g.bounds["k"]
+    idx = (rows[:, None] * n_k + np.arange(n_k)[None, :]).reshape(-1)
     t = time.perf_counter()
-    ws = ref.einsum("ij,jk->ik", xs_h, ys_h, "sqdiff", "sum", out_index=idx)
-    wm = ref.einsum("ij,jk->ik", xm_h, ym_h, "add", "max", out_index=idx)
+    want = ref.einsum(g.spec, x_h, a_h, g.join, g.agg, out_index=idx)
     dt = time.perf_counter() - t
-    terms = rows * n_k * xs_h.shape[1]
-    # the sampled rows of the timed GPU outputs agree with the oracle
-    gs = zd_s[:rows].reshape(-1).cpu().double().numpy()
-    gm = zd_m[:rows].reshape(-1).cpu().numpy().astype(np.int64)
-    err = float(np.abs(gs - ws).max() / np.abs(ws).max())
-    assert err <= 1e-4, f"squared distance differs from the oracle: {err}"
-    assert np.array_equal(gm, wm), "max-plus differs from the oracle"
-    return {"value": round(terms * (SQDIST_FLOP_PER_TERM + 2) / dt / 1e9, 3), "unit": "GFLOP/s",
-            "cores": int(ref.max_threads()), "kind": "oracle",
-            "sample": f"first {rows} of 8192 output rows of both joins ({terms / 1e9:.2f} G terms each), "
-                      f"{dt:.1f} s; GPU rows checked: rel err {err:.2e}, max-plus exact"}
+    fl = 2.0 * len(rows) * n_k * g.bounds["j"]
+    return ({"value": round(fl / dt / 1e9, 3), "unit": "GFLOP/s", "cores": int(ref.max_threads()),
+             "cpu_model": _cpu_model(), "kind": "oracle",
+             "sample": f"{len(rows)} of 16384 output rows of the blocked GEMM (4 seeded rows in each of the 16 row "
+                       f"blocks), every column: {fl / 1e9:.1f} GFLOP in {dt:.1f} s"}, want)
+
+
+def _sqdist(tra, wl, dev, stream, scratch, check_rows: int = 256):
+    """Pairwise squared distance and max-plus, 8192 x 256 x 8192, d = [16,1,1,16];
+    each join timed alone (inputs resident as relations, caches flushed between
+    calls), the squared distance against the vector-ALU ceiling."""
+    import numpy as np
+    import torch
+    from oracle import ref
+    res = {}
+    for case in (wl.SQDIST, wl.MAXPLUS):
+        B, d = case.bounds, case.d
+        x_h, y_h = case.make_inputs()
+        p = tra.tra_plan(case.spec, B, d, case.join, case.agg, case.in_dtype, case.out_dtype)
+        xr = tra.to_relation(x_h.to(dev), [d["i"], d["j"]])
+        yr = tra.to_relation(y_h.to(dev), [d["j"], d["k"]])
+        z = torch.empty(p.info.z_elems, dtype=tra._binding.TORCH_DTYPES[p.out_dtype], device=dev)
+        ws = p.workspace(dev)
+        f = lambda: tra.tra_execute(p, xr, yr, z, ws)
+        f()
+        ms = _events_time_flushed(f, 10, stream, scratch)
+        terms = B["i"] * B["j"] * B["k"]
+        zd = tra.from_relation(z, [B["i"], B["k"]], [d["i"], d["k"]])
+        rows = _sample_rows(B["i"], d["i"], check_rows // d["i"], seed=2000 + case.wid)
+        idx = (rows[:, None] * B["k"] + np.arange(B["k"])[None, :]).reshape(-1)
+        want = ref.einsum(case.spec, x_h, y_h, case.join, case.agg, out_index=idx)
+        got = zd[torch.from_numpy(rows).to(dev)].cpu().reshape(-1)
+        if case.join == "sqdiff":
+            achieved = terms * SQDIST_FLOP_PER_TERM / (ms * 1e-3)
+            traffic = _traffic("sqdist")
+            err = rel_errors(got.double().numpy(), want)
+            assert err["maxnorm"] <= 1e-4, f"squared distance differs from the oracle: {err}"
+            res["sqdist"] = {
+                "ms": round(ms, 4), "TFLOP/s": round(achieved / 1e12, 2), "kernel": p.kernel,
+                "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3),
+                             "peak": round(VALU_SQDIST_PEAK / 1e12, 3), "unit": "TFLOP/s",
+                             "frac": round(achieved / VALU_SQDIST_PEAK, 4),
+                             "traffic": None if traffic is None else round(traffic),
+                             "kernel": "k_valu_tile<sqdiff,sum>",
+                             "algorithmic_bytes": (B["i"] * B["j"] + B["j"] * B["k"] + B["i"] * B["k"]) * 4},
+                "parity": dict(err, rows=len(rows))}
+        else:
+            exact = bool(np.array_equal(got.numpy().astype(np.int64), want))
+            assert exact, "max-plus differs from the oracle"
+            packed = not ws[-1024:].view(torch.int32).any().item()
+            res["maxplus"] = {"ms": round(ms, 4), "Gterms/s": round(terms / (ms * 1e-3) / 1e9, 1),
+                              "kernel": p.kernel,
+                              "path": "packed f16, exact (inputs within +-1024)" if packed else "int32",
+                              "parity": {"exact": exact, "rows": len(rows)}}
+        del xr, yr, z, zd, ws
+    return res
 
 
 def _extra(tra, wl, dev, stream, only):
@@ -354,12 +463,22 @@ def _extra(tra, wl, dev, stream, only):
     def want(name):
         return not only or name in only
 
-    def timed_execute(plan, x, y, reps=10):
+    # a read-modify-write pass over 1 GiB between timed calls of the small
+    # workloads, so that their inputs never sit in the 256 MB Infinity Cache
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+
+    def timed_execute(plan, x, y, reps=10, flush=False):
         z = torch.empty(plan.info.z_elems, dtype=tra._binding.TORCH_DTYPES[plan.out_dtype], device=dev)
         ws = plan.workspace(dev)
         for _ in range(2):
             tra.tra_execute(plan, x, y, z, ws)
-        return _events_time(lambda: tra.tra_execute(plan, x, y, z, ws), reps, stream), z
+        f = lambda: tra.tra_execute(plan, x, y, z, ws)
+        if flush:
+            return _events_time_flushed(f, reps, stream, scratch), z
+        return _events_time(f, reps, stream), z
+
+    if want("sqdist"):
+        res.update(_sqdist(tra, wl, dev, stream, scratch))
 
     if want("matmul"):
         for base in (wl.MATMUL_F32, wl.MATMUL_I32):
@@ -369,42 +488,35 @@ def _extra(tra, wl, dev, stream, only):
                 p = tra.tra_plan(base.spec, base.bounds, dm, base.join, base.agg, base.in_dtype, base.out_dtype)
                 xr = tra.to_relation(x, [dm["i"], dm["j"]])
                 yr = tra.to_relation(y, [dm["j"], dm["k"]])
-                ms, _ = timed_execute(p, xr, yr, reps=50)
+                ms, _ = timed_execute(p, xr, yr, reps=50, flush=True)
                 res[f"matmul_{base.in_dtype}_{'x'.join(map(str, d4))}"] = {
                     "us": round(ms * 1e3, 2), "GFLOP/s": round(2 * 256 ** 3 / ms / 1e6, 1), "kernel": p.kernel,
                     "split": p.info.agg_split}
 
     if want("contract4"):
+        import numpy as np
+        from oracle import ref
         c = wl.CONTRACT4
-        a, b = (t.to(dev) for t in c.make_inputs())
+        a_h, b_h = c.make_inputs()
         p = tra.tra_plan(c.spec, c.bounds, c.d, c.join, c.agg, c.in_dtype, c.out_dtype)
-        ar = tra.to_relation(a, [c.d[l] for l in "abef"])
-        br = tra.to_relation(b, [c.d[l] for l in "cfed"])
-        ms, _ = timed_execute(p, ar, br, reps=50)
+        ar = tra.to_relation(a_h.to(dev), [c.d[l] for l in "abef"])
+        br = tra.to_relation(b_h.to(dev), [c.d[l] for l in "cfed"])
+        ms, zr = timed_execute(p, ar, br, reps=50, flush=True)
+        ms_warm, _ = timed_execute(p, ar, br, reps=50)
         fl = 2 * 64 ** 4 * 32 ** 2
+        zd = tra.from_relation(zr, [64] * 4, [c.d[l] for l in "abcd"]).reshape(-1)
+        idx = np.sort(np.random.default_rng(3003).choice(zd.numel(), size=1 << 14, replace=False))
+        ref_vals = ref.einsum(c.spec, a_h, b_h, c.join, c.agg, out_index=idx)
+        err = rel_errors(zd[torch.from_numpy(idx).to(dev)].cpu().double().numpy(), ref_vals)
+        assert err["maxnorm"] <= 2e-2, f"four-index contraction differs from the oracle: {err}"
         res["contract4"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
-                            "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4), "kernel": p.kernel}
+                            "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4), "kernel": p.kernel,
+                            "us_cache_warm": round(ms_warm * 1e3, 2), "split": p.info.agg_split,
+                            "parity": err}
 
-    if want("gemm25d"):
+    if want("gemm25d_bwd"):
         g = wl.GEMM25D
-        x, a = (t.to(dev) for t in g.make_inputs())
-        p = tra.tra_plan(g.spec, g.bounds, g.d, g.join, g.agg, g.in_dtype, g.out_dtype)
-        xr = tra.to_relation(x, [g.d["i"], g.d["j"]])
-        ar = tra.to_relation(a, [g.d["j"], g.d["k"]])
-        del x, a
-        ms, yr = timed_execute(p, xr, ar, reps=10)
         fl = 2 * 16384 * 8192 * 8192
-        res["gemm25d"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
-                          "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4), "kernel": p.kernel}
-        shape = [16384, 8192]
-        dst = torch.empty_like(yr)
-        f = lambda: tra.tra_repartition(yr, shape, list(wl.GEMM25D_Y_FROM), list(wl.GEMM25D_Y_TO), dst)
-        f()
-        ms = _events_time(f, 20, stream)
-        nbytes = 2 * yr.numel() * 4
-        res["gemm25d_repartition"] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / ms / 1e6, 1),
-                                      "frac_hbm_peak": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
-        del xr, ar, yr, dst
         # backward products under the forward's blocking: dX = dY A^T, dA = X^T dY
         for name, spec, inputs in (("gemm25d_bwd_dX", "ik,jk->ij", ("ik", "jk")), ("gemm25d_bwd_dA", "ij,ik->jk", ("ij", "ik"))):
             pb = tra.tra_plan(spec, g.bounds, g.d, "mul", "sum", "bf16", "f32")
@@ -429,9 +541,10 @@ def _extra(tra, wl, dev, stream, only):
     if want("mha_fused_time"):
         res["mha_fused_time"] = _mha(tra, wl, dev, stream, fuse=True, time_model=True)
     if want("mha_bwd"):
+        # the default: the softmax Jacobian in the dAttn product's epilogue
         res["mha_bwd"] = _mha_backward(tra, wl, dev, stream)
-        # the softmax Jacobian in the dAttn product's epilogue (opt-in, for comparison)
-        res["mha_bwd_product_chain"] = _mha_backward(tra, wl, dev, stream, fuse=True)
+        # for comparison: the product writes the fp32 dAttn, the chain follows
+        res["mha_bwd_three_launches"] = _mha_backward(tra, wl, dev, stream, fuse=False)
     torch.cuda.empty_cache()
     return res
 
@@ -500,7 +613,7 @@ def _mha(tra, wl, dev, stream, fuse=False, time_model=False, overlap=False):
     return r
 
 
-def _mha_backward(tra, wl, dev, stream, fuse=False):
+def _mha_backward(tra, wl, dev, stream, fuse=True):
     """Backward EinSums of the attention layer (dense layouts), per step and in
     total, each step against its own roof: the products against the bf16 matrix-core
     peak, the [h,s,t] elementwise steps against HBM."""
@@ -517,7 +630,9 @@ def _mha_backward(tra, wl, dev, stream, fuse=False):
     flops = {n: proj for n in ("dO", "dW_O", "dW_Q", "dQ", "dW_K", "dK", "dW_V", "dV")}
     flops.update({n: attn for n in ("dAttn", "dV_proj", "dQ_proj", "dK_proj")})
     hst = float(h * s * s)
-    names = list(layer.backward_launches)
+    names = []
+    grads = layer.backward(saved, g, ws, on_step=names.append, out=grads)
+    assert names == list(layer.backward_launches)
     if layer.fuse_product_chain:
         # dScores = Attn * (dO.V^T - Rows) in the product's epilogue
         flops["dScores"] = attn

@@ -471,6 +471,24 @@ int tra_graph_node_d(tra_graph_t graph, int node, int32_t *d_out, int d_cap);
 int tra_graph_leaf(tra_graph_t graph, int leaf, char *name, int name_cap, int64_t *elems, int32_t *dtype);
 
 /*
+ * tra_graph_node_output -- where node `node` leaves its output relation in the
+ * workspace (EinDecomp page, section 2.2: every intermediate is a relation
+ * blocked by its producer's d).  After tra_graph_run_node of that node, and
+ * until a later node reuses those bytes (the workspace is laid out by
+ * liveness), the relation is at byte `*offset` of the workspace: `*elems`
+ * elements of `*dtype`, blocked by the node's d (tra_graph_node_d) restricted
+ * to its output labels, in output-label order.  A softmax node also leaves its
+ * logsumexp over the last label (fp32, blocked the same way over the other
+ * labels, `*lse_elems` elements) at `*lse_offset`; for any other node
+ * `*lse_elems` is 0 and `*lse_offset` SIZE_MAX.  Nothing is read or written
+ * on the device.
+ * Errors: TRA_E_NULL, TRA_E_GRAPH (bad index), TRA_E_OP for a node folded
+ * into a fused attention chain (it writes no output of its own).
+ */
+int tra_graph_node_output(tra_graph_t graph, int node, size_t *offset, int64_t *elems, int32_t *dtype,
+                          size_t *lse_offset, int64_t *lse_elems);
+
+/*
  * tra_graph_run_node -- enqueue one node: the repartitions its inputs need
  * (graph inputs: dense -> the node's blocking; intermediates: only when the
  * producer's blocking differs), then its join + aggregation.  For the output

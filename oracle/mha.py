@@ -52,8 +52,14 @@ def mha(t: Dict[str, object], rows: Optional[np.ndarray] = None) -> Dict[str, np
             "LSE": lse[..., 0], "Attn": attn, "O": o, "Output": out}
 
 
-def mha_backward(t: Dict[str, object], d_out) -> Dict[str, np.ndarray]:
+def mha_backward(t: Dict[str, object], d_out, rows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Gradients of sum(Output * d_out) with respect to the layer's inputs and weights.
+
+    With ``rows``, only the gradients that belong to those query positions s
+    are formed, each from those rows alone: dO, dAttn, dScores, dQ_proj and dQ
+    (row s of each depends on row s of the forward and on all of K_proj and
+    V_proj); the key-side and weight gradients, which sum over every row, are
+    omitted.
 
     The pages give the forward EinSums only; the backward is their chain rule,
     one EinSum per step, all in float64:
@@ -68,21 +74,26 @@ def mha_backward(t: Dict[str, object], d_out) -> Dict[str, np.ndarray]:
         dK_proj      = (1/sqrt(d_k)) sum_s dScores[h,s,t] Q_proj[s,h,d]
         dW_X[a,h,d]  = sum_s X[s,a] dX_proj[s,h,d],   dX[s,a] = sum_hd dX_proj[s,h,d] W_X[a,h,d]
     """
-    fwd = mha(t)
+    fwd = mha(t, rows=rows)
     q, k, v = (ref._as_np(t[n]) for n in ("Q", "K", "V"))
     wq, wk, wv, wo = (ref._as_np(t[n]) for n in ("W_Q", "W_K", "W_V", "W_O"))
     g = ref._as_np(d_out)                                        # [s, a]
     a, h, dh = wq.shape
+    if rows is not None:
+        q, g = q[np.asarray(rows)], g[np.asarray(rows)]
     attn, o = fwd["Attn"], fwd["O"]                               # [h,s,t], [s,h,d]
     qp, kp, vp = fwd["Q_proj"], fwd["K_proj"], fwd["V_proj"]
-    d_wo = np.tensordot(g, o, axes=([0], [0]))                    # [a, h, d]
     d_o = np.tensordot(g, wo, axes=([1], [0]))                    # [s, h, d]
     d_attn = np.matmul(np.transpose(d_o, (1, 0, 2)), np.transpose(vp, (1, 2, 0)))   # [h, s, t]
-    d_vp = np.transpose(np.matmul(np.transpose(attn, (0, 2, 1)), np.transpose(d_o, (1, 0, 2))), (1, 0, 2))
     row = (attn * d_attn).sum(axis=2, keepdims=True)              # [h, s, 1]
     d_scores = attn * (d_attn - row)
     scale = 1.0 / np.sqrt(dh)
     d_qp = np.transpose(np.matmul(d_scores, np.transpose(kp, (1, 0, 2))), (1, 0, 2)) * scale
+    if rows is not None:
+        return {"dO": d_o, "dAttn": d_attn, "dScores": d_scores, "dQ_proj": d_qp,
+                "dQ": np.tensordot(d_qp, wq, axes=([1, 2], [1, 2]))}
+    d_wo = np.tensordot(g, o, axes=([0], [0]))                    # [a, h, d]
+    d_vp = np.transpose(np.matmul(np.transpose(attn, (0, 2, 1)), np.transpose(d_o, (1, 0, 2))), (1, 0, 2))
     d_kp = np.transpose(np.matmul(np.transpose(d_scores, (0, 2, 1)), np.transpose(qp, (1, 0, 2))),
                         (1, 0, 2)) * scale
     out = {"dW_O": d_wo, "dO": d_o, "dAttn": d_attn, "dV_proj": d_vp, "dScores": d_scores,

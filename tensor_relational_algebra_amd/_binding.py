@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "tra_graph_info": ([P, P], I),
             "tra_graph_node_d": ([P, I, P, I], I),
             "tra_graph_leaf": ([P, I, ctypes.c_char_p, I, P, P], I),
+            "tra_graph_node_output": ([P, I, P, P, P, P, P], I),
             "tra_graph_run_node": ([P, I, P, I, P, P, ctypes.c_size_t, P], I),
             "tra_graph_execute": ([P, P, I, P, P, ctypes.c_size_t, P], I),
             "tra_graph_destroy": ([P], I),
@@ -314,6 +315,20 @@ class Graph:
     def workspace(self, device) -> Optional[torch.Tensor]:
         n = self.info.workspace_bytes
         return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+    def node_output(self, node: int, workspace: torch.Tensor) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        """Views of node `node`'s output relation (and a softmax node's
+        logsumexp, else None) inside `workspace`, valid after
+        tra_graph_run_node of that node until a later node reuses the bytes."""
+        off, n, dt = ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int32()
+        lse, n_lse = ctypes.c_size_t(), ctypes.c_int64()
+        _check(lib().tra_graph_node_output(self.handle, node, ctypes.byref(off), ctypes.byref(n), ctypes.byref(dt),
+                                           ctypes.byref(lse), ctypes.byref(n_lse)))
+        tdt = TORCH_DTYPES[dt.value]
+        size = torch.empty(0, dtype=tdt).element_size()
+        out = workspace[off.value:off.value + n.value * size].view(tdt)
+        lse_view = workspace[lse.value:lse.value + n_lse.value * 4].view(torch.float32) if n_lse.value else None
+        return out, lse_view
 
     def _leaf_ptrs(self, inputs: Dict[str, torch.Tensor]):
         ptrs = []

@@ -74,14 +74,30 @@ _TORCH = {"bf16": torch.bfloat16, "f32": torch.float32}
 CHAINED = {"dAttn_c": "dScores"}
 # A product whose epilogue runs such a chain (tra_execute_contract_chain):
 # dScores = Attn * (dO.V^T - Rows) in one launch, dAttn never written.  Used
-# when the layer is built with fuse_product_chain and the product's plan runs
-# on the matrix-core kernel with no split.
+# (the default) when the product's plan runs on the matrix-core kernel with no
+# split; otherwise, or with fuse_product_chain=False, the product writes dAttn
+# and the chain above follows.
 CONTRACT_CHAINED = {"dAttn": ("dAttn_c", "dScores")}
 
 
 def _launches(fused: bool) -> List[str]:
-    skip = set(CHAINED) | ({"dAttn"} if fused else set())
-    return [n for n, *_ in BACKWARD if n not in skip]
+    """The names on_step reports, in launch order: a chained pair reports its
+    second step's name at its first step's position; with the product chain
+    fused, the product dAttn runs the pair in its epilogue and reports dScores
+    at dAttn's position."""
+    order: List[str] = []
+    chained_into = {b: a for a, b in CHAINED.items()}
+    in_contract = {m for v in CONTRACT_CHAINED.values() for m in v}
+    for n, *_ in BACKWARD:
+        if fused and n in CONTRACT_CHAINED:
+            order.append(CONTRACT_CHAINED[n][-1])
+        elif (fused and n in in_contract) or n in chained_into:
+            continue
+        elif n in CHAINED:
+            order.append(CHAINED[n])
+        else:
+            order.append(n)
+    return order
 
 
 # The steps as they are launched (and reported to on_step), with the product
@@ -96,7 +112,7 @@ class AttentionLayer:
     s query positions, t key positions, a model width, h heads of width dh.
     """
 
-    def __init__(self, s: int, a: int, h: int, dh: int, t: Optional[int] = None, fuse_product_chain: bool = False):
+    def __init__(self, s: int, a: int, h: int, dh: int, t: Optional[int] = None, fuse_product_chain: bool = True):
         self.s, self.a, self.h, self.dh = s, a, h, dh
         self.t = s if t is None else t
         self.bounds = {"s": s, "t": self.t, "a": a, "h": h, "d": dh}
@@ -110,8 +126,9 @@ class AttentionLayer:
                                         self.scale if scaled else 1.0)
         self.workspace_bytes = max(p.info.workspace_bytes for p in self.plans.values())
         pc = self.plans["dAttn"]
-        # opt-in: correct (bit-identical), but its epilogue is slower than the
-        # two launches it replaces on the full-size layer
+        # the default where the product runs unsplit on the matrix cores: its
+        # result is bit-identical to the three launches it replaces, and it
+        # never writes the fp32 dAttn
         self.fuse_product_chain = fuse_product_chain and pc.kernel == "mfma_bf16" and pc.info.agg_split == 1
         self.backward_launches = BACKWARD_LAUNCHES if self.fuse_product_chain else BACKWARD_LAUNCHES_UNFUSED
 

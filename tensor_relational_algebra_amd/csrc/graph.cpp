@@ -12,6 +12,7 @@
 // On one GPU the "devices" of the pages are the workgroups of each kernel,
 // and every intermediate relation lives in one caller-provided workspace.
 #include <algorithm>
+#include <cstdint>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -590,6 +591,23 @@ extern "C" int tra_graph_node_d(tra_graph_t g, int node, int32_t *d_out, int cap
     if ((int)d.size() > cap) return gfail(TRA_E_BUFFER, "d_out too small");
     for (size_t i = 0; i < d.size(); ++i) d_out[i] = d[i];
     return (int)d.size();
+}
+
+extern "C" int tra_graph_node_output(tra_graph_t g, int node, size_t *offset, int64_t *elems, int32_t *dtype,
+                                     size_t *lse_offset, int64_t *lse_elems)
+{
+    if (!g || !offset || !elems || !dtype || !lse_offset || !lse_elems) return gfail(TRA_E_NULL, "NULL argument");
+    if (node < 0 || node >= (int)g->nodes.size()) return gfail(TRA_E_GRAPH, "node index out of range");
+    const NodeExec &e = g->ex[node];
+    if (e.fused == 1) return gfail(TRA_E_OP, "node is folded into a fused attention chain");
+    *offset = e.out;
+    *elems = e.out_elems;
+    *dtype = e.out_dtype;
+    const GNode &nd = g->nodes[node];
+    const bool sm = nd.kind == "softmax";
+    *lse_offset = sm ? e.lse : SIZE_MAX;
+    *lse_elems = sm ? e.out_elems / nd.B[(int)nd.out.back()] : 0;
+    return TRA_OK;
 }
 
 extern "C" int tra_graph_leaf(tra_graph_t g, int leaf, char *name, int cap, int64_t *elems, int32_t *dtype)

@@ -25,6 +25,12 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
+
+// k-tiles the four-wave tile keeps in its LDS ring (32 KiB each)
+#ifndef TRA_MFMA4_STAGES
+#define TRA_MFMA4_STAGES 4
+#endif
 
 #include "device_common.h"
 #include "graph.h"
@@ -51,6 +57,7 @@ constexpr int MF_STAGES = 4;    // LDS ring: 3 k-tiles in flight while one is co
 
 TileShape mfma_tile_shape(int variant)
 {
+    if (variant == 3) return {256, 256, MF_BK};
     if (variant < 0 || variant > 2) return {0, 0, 0};
     MfmaCfg c = mfma_cfg(variant);
     return {c.bm, c.bn, MF_BK};
@@ -86,6 +93,18 @@ __device__ __forceinline__ void mfma_tile_of(uint32_t nb, uint32_t tiles_n, uint
     uint32_t r = b % per;
     tm = first + r % gs;
     tn = r / gs;
+}
+
+template <int... Is, typename F>
+__device__ __forceinline__ void sfor_seq(std::integer_sequence<int, Is...>, F &&f)
+{
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int N, typename F>
+__device__ __forceinline__ void sfor(F &&f)
+{
+    sfor_seq(std::make_integer_sequence<int, N>{}, f);
 }
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -171,12 +190,19 @@ struct DmaPlan {
             __builtin_amdgcn_global_load_lds(g + src[i] + koff, (lds_void_t *)(stage + (i * NT + wave * 64) * 8), 16,
                                              0, 0);
     }
+    // copy i alone (i a compile-time constant at every call)
+    __device__ __forceinline__ void issue_one(int i, const uint16_t *__restrict__ g, int32_t koff, uint16_t *stage,
+                                              int wave)
+    {
+        __builtin_amdgcn_global_load_lds(g + src[i] + koff, (lds_void_t *)(stage + (i * NT + wave * 64) * 8), 16, 0,
+                                         0);
+    }
 };
 
 // The tile kernel's body.  TC is void for a plain product; otherwise the
 // epilogue applies the two elementwise steps of a ChainEpi to each element
 // (TC = their intermediate dtype) instead of storing the product.
-template <int V, bool AKM, bool BKM, typename TO, typename TC>
+template <int V, bool AKM, bool BKM, typename TO, typename TC, int CH = 0>
 __device__ __forceinline__ void mfma_body(const GemmView &v, const uint16_t *__restrict__ x,
                                           const uint16_t *__restrict__ y, TO *__restrict__ z,
                                           float *__restrict__ ws, const ChainEpi &ce)
@@ -345,7 +371,428 @@ __device__ __forceinline__ void mfma_body(const GemmView &v, const uint16_t *__r
     // Epilogue.  Accumulator element e of lane l holds row
     // 8*(e/4) + 4*(l/32) + e%4 and column l%32 of its 32x32 block.
     // row = (wave row + 32 i + 8 (e/4)) + (4 (l/32) + e%4): a multiple of 8 plus
-    // a part below 8, so its offset splits into a wave-uniform and a lane part.
+    // a part below 8, so its offset splits into a wave-uniform and a lane part
+    // (likewise the column into the block's and the lane's).  The loops are
+    // unrolled at compile time: an accumulator indexed at run time would live
+    // in scratch memory.
+    const bool split = v.split > 1;
+    float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
+    const int32_t zm0 = p2off<1>(v.gm, m0) + bz, zn0 = p2off<1>(v.gn, n0);
+    int32_t lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lo[r] = p2off<1>(v.gm, 4 * (lane >> 5) + r);
+    if constexpr (std::is_void<TC>::value) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int32_t hi = zm0 + p2off<1>(v.gm, wm * (BM / WM) + i * 32 + 8 * q);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int32_t on = zn0 + p2off<1>(v.gn, b_col0 + j * 32 + r_lane);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int32_t o = hi + lo[r] + on;
+                        const float val = acc[i][j][4 * q + r];
+                        if (split) wsp[o] = val;
+                        else Scalar<TO>::store(z, o, val * v.post_scale);
+                    }
+                }
+            }
+        }
+    } else {
+        // The product as the fp32 output it would be stored as, then the two
+        // elementwise steps exactly as the chained elementwise kernel computes
+        // them.  The row operand's offset splits like the output's.  CH = 1
+        // is the pair (x - y, then x * y) with the joins fixed at compile time
+        // (the softmax Jacobian of the attention backward); CH = 0 takes any
+        // pair, branching on the joins per element.
+        const int32_t rm0 = p2off<0>(ce.rb, bidx) + p2off<0>(ce.rm, m0) + p2off<0>(ce.rn, n0);
+        int32_t rlo[4], ron[TN], zon[TN];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rlo[r] = p2off<0>(ce.rm, 4 * (lane >> 5) + r);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            ron[j] = p2off<0>(ce.rn, b_col0 + j * 32 + r_lane);
+            zon[j] = zn0 + p2off<1>(v.gn, b_col0 + j * 32 + r_lane);
+        }
+        const float *__restrict__ ya = (const float *)ce.ya;
+        const TC *__restrict__ xb = (const TC *)ce.xb;
+        // Rows are done in groups of TN * 4 elements (one (i, q) pair).  The
+        // two operands of group g + 1 are loaded before group g is computed
+        // and stored, so each group's loads are in flight together and under
+        // the previous group's work instead of one element at a time (a load
+        // cannot be moved above a store the compiler cannot prove disjoint).
+        constexpr int GE = TN * 4;
+        float yv[2][GE], xv[2][GE];
+        auto load_group = [&](auto IQ, int buf) {
+            constexpr int i = decltype(IQ)::value / 4, q = decltype(IQ)::value % 4;
+            const int32_t row = wm * (BM / WM) + i * 32 + 8 * q;
+            const int32_t hi = zm0 + p2off<1>(v.gm, row), rhi = rm0 + p2off<0>(ce.rm, row);
+            sfor<GE>([&](auto JR) {
+                constexpr int j = decltype(JR)::value / 4, r = decltype(JR)::value % 4;
+                yv[buf][decltype(JR)::value] = ya[rhi + rlo[r] + ron[j]];
+                xv[buf][decltype(JR)::value] = Scalar<TC>::load(xb, hi + lo[r] + zon[j]);
+            });
+        };
+        load_group(std::integral_constant<int, 0>{}, 0);
+        sfor<TM * 4>([&](auto IQ) {
+            constexpr int g = decltype(IQ)::value, i = g / 4, q = g % 4, buf = g % 2;
+            if constexpr (g + 1 < TM * 4) load_group(std::integral_constant<int, g + 1>{}, 1 - buf);
+            const int32_t hi = zm0 + p2off<1>(v.gm, wm * (BM / WM) + i * 32 + 8 * q);
+            sfor<GE>([&](auto JR) {
+                constexpr int e = decltype(JR)::value, j = e / 4, r = e % 4;
+                const float av = acc[i][j][4 * q + r] * v.post_scale;
+                float t;
+                if constexpr (CH == 1) t = (av - yv[buf][e]) * ce.scale_a;
+                else t = join_any(ce.join_a, av, yv[buf][e]) * ce.scale_a;
+                if constexpr (std::is_same<TC, bf16_t>::value) t = bf16_to_f32(f32_to_bf16(t));
+                float o;
+                if constexpr (CH == 1) o = xv[buf][e] * t;
+                else o = join_any(ce.join_b, xv[buf][e], t);
+                Scalar<TO>::store(z, hi + lo[r] + zon[j], o * ce.scale_b);
+            });
+        });
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Four-wave 256 x 256 tile (variant 3).  Each wave owns a 128 x 128 block of
+// the tile, 4 x 4 products of 32 x 32, so the 256 fp32 accumulators of a lane
+// sit in the accumulator registers (one wave per SIMD leaves all 512 of a
+// lane's registers to it) and each byte read from LDS feeds 1.5x the matrix
+// work of the eight-wave tile.  With one wave per SIMD there is no second
+// wave to hide the LDS latency, so the fragments of the next 16-deep k-step
+// are read while the matrix cores work on the current one (two fragment sets
+// in registers), and the barrier that publishes a stage sits between the two
+// k-steps of the stage before it.
+//
+// Block i of a wave covers rows (i * WM + wm) * 32 .. +32 of the tile (and
+// block j columns (j * WN + wn) * 32 ..): with the waves' blocks interleaved,
+// a fragment's LDS address is a per-lane base plus a constant, so every
+// fragment read is one instruction with an immediate offset (a handful of
+// address registers instead of one per read).
+namespace mf4 {
+constexpr int BM = 256, BN = 256, BK = 32, WM = 2, WN = 2, NT = WM * WN * 64, TM = 4, TN = 4;
+}
+
+template <int OFF>
+__device__ __forceinline__ u32x4_t ds_read16_at(uint32_t addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "LDS immediate offset");
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read8_tr_at(uint32_t addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "LDS immediate offset");
+    u32x2_t v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+// s_waitcnt lgkmcnt(n) (vmcnt and expcnt unconstrained)
+template <int N>
+__device__ __forceinline__ void lds_wait()
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One operand's fragments of one 16-deep k-step: KM ? one 16-byte read per
+// block : two 8-byte transposing reads per block.
+template <bool KM, int T>
+struct Frag4 {
+    u32x4_t k[T];
+    u32x2_t t[T][2];
+    __device__ __forceinline__ void ready()
+    {
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+            if constexpr (KM) {
+                lds_ready(k[i]);
+            } else {
+                lds_ready(t[i][0]);
+                lds_ready(t[i][1]);
+            }
+        }
+    }
+    __device__ __forceinline__ bf16x8_t op(int i) const
+    {
+        if constexpr (KM) {
+            return __builtin_bit_cast(bf16x8_t, k[i]);
+        } else {
+            u32x4_t w = {t[i][0][0], t[i][0][1], t[i][1][0], t[i][1][1]};
+            return __builtin_bit_cast(bf16x8_t, w);
+        }
+    }
+    static constexpr int reads = KM ? T : 2 * T;
+};
+
+// Per-lane LDS bases of one operand's fragment reads (ROWS rows in the tile,
+// W waves along them, wave index w, STAGES stages of ROWS x 32 bf16).
+//  * K-major, stage [row][32 k]: block i of k-step ks reads row
+//    (i W + w) 32 + l%32, 16-byte granule (2 ks + l/32) ^ swz_k(row); the
+//    swizzle depends on row bits 1..3 only, so the base depends on ks alone.
+//  * MN-major, stage [32 k][row]: the swizzle XORs granule bits 2..3 with
+//    k & 3, which for W = 2 mixes in bit 0 of i: two bases (i & 1).
+// Stages at or past 64 KiB take a second base 64 KiB up (the immediate
+// offset of a DS instruction has 16 bits).
+template <bool KM, int ROWS, int W, int STAGES>
+struct FragAddr4 {
+    static constexpr int STAGE_BYTES = ROWS * mf4::BK * 2;
+    static constexpr int NB = KM ? 2 : (W >= 4 ? 1 : 4 / W);
+    uint32_t base[2][NB];   // [stage >= 64 KiB][ks (K-major) or i % NB (MN-major)]
+
+    __device__ __forceinline__ void init(uint32_t lds, int w, int lane)
+    {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            uint32_t a;
+            if constexpr (KM) {
+                const int r = w * 32 + (lane & 31);
+                const int c = ((2 * b + (lane >> 5)) ^ swz_k(r));
+                a = (uint32_t)(r * mf4::BK + c * 8) * 2;
+            } else {
+                const int g = lane >> 4, sl = lane & 15;
+                const int kb = 8 * (g >> 1) + (sl >> 2);
+                const int nb = (b * W + w) * 32 + 16 * (g & 1) + 4 * (sl & 3);
+                a = (uint32_t)(kb * ROWS + (((nb >> 3) ^ swz_n<ROWS>(kb)) << 3) + (nb & 7)) * 2;
+            }
+            base[0][b] = lds + a;
+            base[1][b] = lds + a + 65536;
+        }
+    }
+    // Issue read R of k-step KS of stage G into f (K-major: block R;
+    // MN-major: block R / 2, half R % 2).
+    template <int G, int KS, int R, int T>
+    __device__ __forceinline__ void read_one(Frag4<KM, T> &f) const
+    {
+        constexpr int SOFF = G * STAGE_BYTES, HI = SOFF >= 65536 ? 1 : 0, S0 = SOFF - HI * 65536;
+        if constexpr (KM) {
+            constexpr int off = S0 + R * W * 32 * mf4::BK * 2;
+            f.k[R] = ds_read16_at<off>(base[HI][KS]);
+        } else {
+            constexpr int i = R / 2, h = R % 2, r = i % NB, q = i / NB;
+            constexpr int off = S0 + KS * 16 * ROWS * 2 + q * NB * W * 32 * 2 + h * 4 * ROWS * 2;
+            f.t[i][h] = ds_read8_tr_at<off>(base[HI][r]);
+        }
+    }
+    // Issue the reads of k-step KS of stage G into f.
+    template <int G, int KS, int T>
+    __device__ __forceinline__ void read(Frag4<KM, T> &f) const
+    {
+        constexpr int SOFF = G * STAGE_BYTES, HI = SOFF >= 65536 ? 1 : 0, S0 = SOFF - HI * 65536;
+        sfor<T>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            if constexpr (KM) {
+                constexpr int off = S0 + i * W * 32 * mf4::BK * 2;
+                f.k[i] = ds_read16_at<off>(base[HI][KS]);
+            } else {
+                // block i = q NB + r: r selects the base, q adds 4 W-blocks of
+                // 32 rows' worth of granules (above the swizzled bits)
+                constexpr int r = i % NB, q = i / NB;
+                constexpr int off = S0 + KS * 16 * ROWS * 2 + q * NB * W * 32 * 2;
+                f.t[i][0] = ds_read8_tr_at<off>(base[HI][r]);
+                f.t[i][1] = ds_read8_tr_at<off + 4 * ROWS * 2>(base[HI][r]);
+            }
+        });
+    }
+};
+
+template <bool AKM, bool BKM, typename TO, int STAGES>
+__device__ __forceinline__ void mfma4_body(const GemmView &v, const uint16_t *__restrict__ x,
+                                           const uint16_t *__restrict__ y, TO *__restrict__ z,
+                                           float *__restrict__ ws)
+{
+    using namespace mf4;
+    __shared__ __attribute__((aligned(16))) uint16_t sa[STAGES * BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sb[STAGES * BN * BK];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const uint32_t tiles_n = v.gn.total / BN;
+    const uint32_t nb = (v.gm.total / BM) * tiles_n;
+    uint32_t tm, tn, bidx;
+    mfma_tile_of(nb, tiles_n, v.gb.total, bidx, tm, tn);
+    const uint32_t m0 = tm * BM, n0 = tn * BN;
+    const int32_t bx = p2off<0>(v.gb, bidx), by = p2off<1>(v.gb, bidx), bz = p2off<2>(v.gb, bidx);
+    const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
+    const uint32_t nk = (uint32_t)v.k_per_split / BK;
+
+    DmaPlan<BM, NT, AKM, 0> da;
+    DmaPlan<BN, NT, BKM, 1> db;
+    da.init(v.gm, v.gk, m0, bx, tid);
+    db.init(v.gn, v.gk, n0, by, tid);
+    constexpr int L = DmaPlan<BM, NT, AKM, 0>::N + DmaPlan<BN, NT, BKM, 1>::N;
+
+    FragAddr4<AKM, BM, WM, STAGES> fa;
+    FragAddr4<BKM, BN, WN, STAGES> fb;
+    fa.init(lds_addr(sa), wm, lane);
+    fb.init(lds_addr(sb), wn, lane);
+
+    floatx16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    auto issue = [&](int stg, uint32_t t) {
+        const uint32_t k0 = kbeg + t * BK;
+        da.issue(x, p2off<0>(v.gk, k0), sa + stg * BM * BK, wave);
+        db.issue(y, p2off<1>(v.gk, k0), sb + stg * BN * BK, wave);
+    };
+    auto mma = [&](const Frag4<AKM, TM> &A, const Frag4<BKM, TN> &B) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.op(i), B.op(j), acc[i][j], 0, 0, 0);
+    };
+    // Two fragment sets: F0 holds k-step 0 of a stage, F1 k-step 1.
+    Frag4<AKM, TM> A0, A1;
+    Frag4<BKM, TN> B0, B1;
+    constexpr int NA = Frag4<AKM, TM>::reads;
+
+    // Step of stage G (k-tile t): k-step 0 computes from A0/B0 while k-step 1
+    // is read into A1/B1; then the next stage is published (its copies
+    // waited for, a barrier) and the copy of k-tile t + STAGES - 1 issued into
+    // the stage freed by k-tile t - 1; then k-step 1 computes while k-step 0
+    // of the next stage is read.  Each "wait for the older reads" leaves only
+    // the newest NA reads (the next A fragments) in flight.
+    auto publish = [&](int G, uint32_t t) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 3) * L));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue((G + STAGES - 1) % STAGES, min(t + STAGES - 1, nk - 1));
+    };
+    constexpr int NB_ = Frag4<BKM, TN>::reads;
+    constexpr int LA = DmaPlan<BM, NT, AKM, 0>::N, LB = DmaPlan<BN, NT, BKM, 1>::N;
+    static_assert(NA + NB_ <= TM * TN && LA + LB <= TM * TN, "one read and one copy per product slot");
+    // One k-step of the loop body: the 16 products on (Ac, Bc), one per slot;
+    // in the slots, in this order, the reads of the next k-step (stage GR,
+    // k-step KR) into (An, Bn); when COPY, the copies into stage GC from the
+    // operand offsets (ka, kb); when !COPY, one digit per slot of the offsets
+    // (ka, kb) of k-tile `tc` (scalar work that then runs under the
+    // products instead of delaying the barrier).  The scheduler may not move
+    // anything across a slot boundary, so the reads run under the products
+    // instead of ahead of their wait.  Every read of (Ac, Bc) was issued
+    // during the previous k-step.
+    auto kstep = [&](auto GR, auto KR, auto COPY, auto GC, const Frag4<AKM, TM> &Ac, const Frag4<BKM, TN> &Bc,
+                     Frag4<AKM, TM> &An, Frag4<BKM, TN> &Bn, uint32_t tc, int32_t &ka, int32_t &kb) {
+        constexpr int gr = decltype(GR)::value, kr = decltype(KR)::value, gc = decltype(GC)::value;
+        constexpr bool copy = decltype(COPY)::value;
+        const uint32_t k0 = kbeg + tc * BK;
+        if constexpr (!copy) {
+            ka = 0;
+            kb = 0;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sfor<TM * TN>([&](auto MC) {
+            constexpr int m = decltype(MC)::value, i = m / TN, j = m % TN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac.op(i), Bc.op(j), acc[i][j], 0, 0, 0);
+            if constexpr (m < NA) fa.template read_one<gr, kr, m>(An);
+            else if constexpr (m < NA + NB_) fb.template read_one<gr, kr, m - NA>(Bn);
+            if constexpr (copy && m < LA) da.issue_one(m, x, ka, sa + gc * BM * BK, wave);
+            else if constexpr (copy && m < LA + LB) db.issue_one(m - LA, y, kb, sb + gc * BN * BK, wave);
+            if constexpr (!copy && m < kP2Max) {
+                ka += (int32_t)((k0 >> v.gk.sh[m]) & v.gk.mask[m]) * v.gk.st[0][m];
+                kb += (int32_t)((k0 >> v.gk.sh[m]) & v.gk.mask[m]) * v.gk.st[1][m];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using NoCopy = std::integral_constant<bool, false>;
+    using Copy = std::integral_constant<bool, true>;
+    // Step of stage G (k-tile t) in the loop body: k-step 0 computes from
+    // A0/B0 while k-step 1 is read into A1/B1 (and the operand offsets of
+    // k-tile t + STAGES - 1 are formed); then the next stage is published (its
+    // copies waited for, a barrier); then k-step 1 computes while k-step 0 of
+    // the next stage is read and the copy of k-tile t + STAGES - 1 goes into
+    // the stage freed by k-tile t - 1.
+    auto step = [&](auto GC, uint32_t t) {
+        constexpr int G = decltype(GC)::value;
+        constexpr int GN = (G + 1) % STAGES, GF = (G + STAGES - 1) % STAGES;
+        int32_t ka, kb;
+        lds_wait<0>();
+        A0.ready();
+        B0.ready();
+        kstep(GC, I1{}, NoCopy{}, I0{}, A0, B0, A1, B1, min(t + STAGES - 1, nk - 1), ka, kb);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 3) * L));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        lds_wait<0>();
+        A1.ready();
+        B1.ready();
+        kstep(std::integral_constant<int, GN>{}, I0{}, Copy{}, std::integral_constant<int, GF>{}, A1, B1, A0, B0,
+              0u, ka, kb);
+    };
+    // Step of the tail (fewer than STAGES k-tiles left): the same work, but
+    // every read is waited for within the step, so that no read is in flight
+    // across the branch that skips the steps past the last k-tile.  A0/B0
+    // arrive ready.
+    auto tail_step = [&](auto GC, uint32_t t) {
+        constexpr int G = decltype(GC)::value;
+        fa.template read<G, 1>(A1);
+        fb.template read<G, 1>(B1);
+        mma(A0, B0);
+        lds_wait<0>();
+        A1.ready();
+        B1.ready();
+        publish(G, t);
+        mma(A1, B1);
+        if (t + 1 < nk) {
+            fa.template read<G + 1, 0>(A0);
+            fb.template read<G + 1, 0>(B0);
+            lds_wait<0>();
+            A0.ready();
+            B0.ready();
+        }
+    };
+
+    // prologue: STAGES - 1 k-tiles in flight, the first stage's first k-step read
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue(s, min((uint32_t)s, nk - 1));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * L));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    fa.template read<0, 0>(A0);
+    fb.template read<0, 0>(B0);
+    lds_wait<0>();
+    A0.ready();
+    B0.ready();
+
+    // The loop body runs STAGES k-tiles; every fragment read it issues is
+    // waited for inside it, except those of the next body's first k-step,
+    // which are waited for (and handed on through lds_ready) before the
+    // back-edge, so that no read is in flight at a branch or merge and no
+    // register copy can take one in flight.
+    uint32_t t = 0;
+    for (; t + STAGES <= nk; t += STAGES) {
+        sfor<STAGES>([&](auto GC) { step(GC, t + decltype(GC)::value); });
+        lds_wait<0>();
+        A0.ready();
+        B0.ready();
+    }
+    sfor<STAGES - 1>([&](auto GC) {
+        constexpr int G = decltype(GC)::value;
+        if (t + G < nk) tail_step(GC, t + G);
+    });
+    // nothing may stay in flight past the k-loop
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_wait<0>();
+
+    // Epilogue.  Accumulator element e of lane l holds row
+    // 8*(e/4) + 4*(l/32) + e%4 and column l%32 of its 32x32 block.
     const bool split = v.split > 1;
     float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
     const int32_t zm0 = p2off<1>(v.gm, m0) + bz, zn0 = p2off<1>(v.gn, n0);
@@ -356,35 +803,28 @@ __device__ __forceinline__ void mfma_body(const GemmView &v, const uint16_t *__r
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int32_t hi = zm0 + p2off<1>(v.gm, wm * (BM / WM) + i * 32 + 8 * q);
+            const int32_t hi = zm0 + p2off<1>(v.gm, (i * WM + wm) * 32 + 8 * q);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int32_t on = zn0 + p2off<1>(v.gn, b_col0 + j * 32 + r_lane);
+                const int32_t on = zn0 + p2off<1>(v.gn, (j * WN + wn) * 32 + (lane & 31));
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int32_t o = hi + lo[r] + on;
                     const float val = acc[i][j][4 * q + r];
-                    if constexpr (std::is_void<TC>::value) {
-                        if (split) wsp[o] = val;
-                        else Scalar<TO>::store(z, o, val * v.post_scale);
-                    } else {
-                        // the product as the fp32 output it would be stored as,
-                        // then the two steps exactly as the chained
-                        // elementwise kernel computes them
-                        const int32_t ro = p2off<0>(ce.rb, bidx) + p2off<0>(ce.rm, m0) +
-                                           p2off<0>(ce.rm, wm * (BM / WM) + i * 32 + 8 * q) +
-                                           p2off<0>(ce.rm, 4 * (lane >> 5) + r) +
-                                           p2off<0>(ce.rn, n0 + b_col0 + j * 32 + r_lane);
-                        const float av = val * v.post_scale;
-                        float t = join_any(ce.join_a, av, ((const float *)ce.ya)[ro]) * ce.scale_a;
-                        if constexpr (std::is_same<TC, bf16_t>::value) t = bf16_to_f32(f32_to_bf16(t));
-                        const float xv = (float)Scalar<TC>::load((const TC *)ce.xb, o);
-                        Scalar<TO>::store(z, o, join_any(ce.join_b, xv, t) * ce.scale_b);
-                    }
+                    if (split) wsp[o] = val;
+                    else Scalar<TO>::store(z, o, val * v.post_scale);
                 }
             }
         }
     }
+}
+
+template <bool AKM, bool BKM, typename TO>
+__global__ __launch_bounds__(mf4::NT) void k_mfma4_bf16(GemmView v, const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ y, TO *__restrict__ z,
+                                                        float *__restrict__ ws)
+{
+    mfma4_body<AKM, BKM, TO, TRA_MFMA4_STAGES>(v, x, y, z, ws);
 }
 
 template <int V, bool AKM, bool BKM, typename TO>
@@ -395,11 +835,11 @@ __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_bf
     mfma_body<V, AKM, BKM, TO, void>(v, x, y, z, ws, ChainEpi{});
 }
 
-template <int V, bool AKM, bool BKM, typename TO>
+template <int V, bool AKM, bool BKM, typename TO, int CH>
 __global__ __launch_bounds__(mfma_cfg(V).wm *mfma_cfg(V).wn * 64) void k_mfma_chain(
     GemmView v, const uint16_t *__restrict__ x, const uint16_t *__restrict__ y, TO *__restrict__ z, ChainEpi ce)
 {
-    mfma_body<V, AKM, BKM, TO, TO>(v, x, y, z, nullptr, ce);
+    mfma_body<V, AKM, BKM, TO, TO, CH>(v, x, y, z, nullptr, ce);
 }
 
 // Every (tile, operand layout, output dtype) combination the launcher can
@@ -420,6 +860,18 @@ TRA_MFMA_INST4(2, float)
 TRA_MFMA_INST4(2, bf16_t)
 #undef TRA_MFMA_INST4
 #undef TRA_MFMA_INST
+#define TRA_MFMA4_INST(AKM, BKM, TO)                                                                          \
+    template __global__ void k_mfma4_bf16<AKM, BKM, TO>(GemmView, const uint16_t *, const uint16_t *, TO *, float *);
+TRA_MFMA4_INST(true, true, float)
+TRA_MFMA4_INST(true, false, float)
+TRA_MFMA4_INST(false, true, float)
+TRA_MFMA4_INST(false, false, float)
+TRA_MFMA4_INST(true, true, bf16_t)
+TRA_MFMA4_INST(true, false, bf16_t)
+TRA_MFMA4_INST(false, true, bf16_t)
+TRA_MFMA4_INST(false, false, bf16_t)
+#undef TRA_MFMA4_INST
+
 
 int launch_split_fold(const tra_plan_s &p, const void *ws, void *z, void *stream);
 
@@ -437,15 +889,35 @@ static int launch_v(const tra_plan_s &p, const void *x, const void *y, void *z, 
     return (int)hipGetLastError();
 }
 
+template <bool AKM, bool BKM, typename TO>
+static int launch4(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, hipStream_t s)
+{
+    const GemmView &v = p.gv;
+    dim3 grid((v.gm.total / mf4::BM) * (v.gn.total / mf4::BN), v.gb.total, v.split);
+    void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *) = k_mfma4_bf16<AKM, BKM, TO>;
+    hipLaunchKernelGGL(kern, grid, dim3(mf4::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z,
+                       (float *)ws);
+    return (int)hipGetLastError();
+}
+
 template <int V, typename TO>
 static int launch_layout(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, hipStream_t s)
 {
-    if (p.a_kmajor) {
-        if (p.b_kmajor) return launch_v<V, true, true, TO>(p, x, y, z, ws, s);
-        return launch_v<V, true, false, TO>(p, x, y, z, ws, s);
+    if constexpr (V == 3) {
+        if (p.a_kmajor) {
+            if (p.b_kmajor) return launch4<true, true, TO>(p, x, y, z, ws, s);
+            return launch4<true, false, TO>(p, x, y, z, ws, s);
+        }
+        if (p.b_kmajor) return launch4<false, true, TO>(p, x, y, z, ws, s);
+        return launch4<false, false, TO>(p, x, y, z, ws, s);
+    } else {
+        if (p.a_kmajor) {
+            if (p.b_kmajor) return launch_v<V, true, true, TO>(p, x, y, z, ws, s);
+            return launch_v<V, true, false, TO>(p, x, y, z, ws, s);
+        }
+        if (p.b_kmajor) return launch_v<V, false, true, TO>(p, x, y, z, ws, s);
+        return launch_v<V, false, false, TO>(p, x, y, z, ws, s);
     }
-    if (p.b_kmajor) return launch_v<V, false, true, TO>(p, x, y, z, ws, s);
-    return launch_v<V, false, false, TO>(p, x, y, z, ws, s);
 }
 
 template <typename TO>
@@ -454,6 +926,7 @@ static int launch_tile(const tra_plan_s &p, const void *x, const void *y, void *
     switch (p.tile) {
     case 0: return launch_layout<0, TO>(p, x, y, z, ws, s);
     case 1: return launch_layout<1, TO>(p, x, y, z, ws, s);
+    case 3: return launch_layout<3, TO>(p, x, y, z, ws, s);
     default: return launch_layout<2, TO>(p, x, y, z, ws, s);
     }
 }
@@ -466,8 +939,13 @@ static int launch_chain_v(const tra_plan_s &p, const void *x, const void *y, voi
     const GemmView &v = p.gv;
     dim3 grid((v.gm.total / C.bm) * (v.gn.total / C.bn), v.gb.total, 1);
     void (*k)(GemmView, const uint16_t *, const uint16_t *, TO *, ChainEpi);
-    if (p.a_kmajor) k = p.b_kmajor ? k_mfma_chain<V, true, true, TO> : k_mfma_chain<V, true, false, TO>;
-    else k = p.b_kmajor ? k_mfma_chain<V, false, true, TO> : k_mfma_chain<V, false, false, TO>;
+    if (ce.join_a == J_SUB && ce.join_b == J_MUL) {
+        if (p.a_kmajor) k = p.b_kmajor ? k_mfma_chain<V, true, true, TO, 1> : k_mfma_chain<V, true, false, TO, 1>;
+        else k = p.b_kmajor ? k_mfma_chain<V, false, true, TO, 1> : k_mfma_chain<V, false, false, TO, 1>;
+    } else {
+        if (p.a_kmajor) k = p.b_kmajor ? k_mfma_chain<V, true, true, TO, 0> : k_mfma_chain<V, true, false, TO, 0>;
+        else k = p.b_kmajor ? k_mfma_chain<V, false, true, TO, 0> : k_mfma_chain<V, false, false, TO, 0>;
+    }
     hipLaunchKernelGGL(k, grid, dim3(C.wm * C.wn * 64), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z,
                        ce);
     return (int)hipGetLastError();
@@ -478,7 +956,8 @@ static int launch_chain_t(const tra_plan_s &p, const void *x, const void *y, voi
                           hipStream_t s)
 {
     switch (p.tile) {
-    case 0: return launch_chain_v<0, TO>(p, x, y, z, ce, s);
+    case 0:
+    case 3: return launch_chain_v<0, TO>(p, x, y, z, ce, s);   // the same 256 x 256 tile on eight waves
     case 1: return launch_chain_v<1, TO>(p, x, y, z, ce, s);
     default: return launch_chain_v<2, TO>(p, x, y, z, ce, s);
     }

@@ -19,6 +19,12 @@
 #include "graph.h"
 #include "plan.h"
 
+// Matrix-core tile variants in order of preference: 3 = 256 x 256 on four
+// waves, 0 = 256 x 256 on eight waves, 1 = 128 x 128, 2 = 64 x 64.
+#ifndef TRA_MFMA_ORDER
+#define TRA_MFMA_ORDER 3, 0, 1, 2
+#endif
+
 namespace tra {
 
 static thread_local std::string g_last_error;
@@ -259,8 +265,10 @@ static bool lower_tile(tra_plan_s &p)
     if (contiguous_last(sk, 1, vec)) bk = true;
     else if (contiguous_last(sn, 0, vec)) bk = false;
     else return false;
-    // pick the largest tile variant that divides the problem
-    for (int variant = 0; variant < 4; ++variant) {
+    // pick the first tile variant, in order of preference, that divides the problem
+    static const int kMfmaOrder[] = {TRA_MFMA_ORDER};
+    for (int n = 0; n < 4; ++n) {
+        const int variant = mfma ? kMfmaOrder[n] : n;
         TileShape ts = mfma ? mfma_tile_shape(variant) : valu_tile_shape(variant);
         if (ts.bm == 0) break;
         if (gv.gm.total % ts.bm || gv.gn.total % ts.bn || gv.gk.total % ts.bk) continue;

@@ -254,6 +254,40 @@ def test_graph_plan_uses_the_chooser_and_lays_out_the_workspace():
     assert g.info.n_repartitions == 0
 
 
+def test_graph_node_output_locations():
+    """Where each node leaves its output in the workspace (host only): inside
+    the workspace, the node's output size and dtype, a logsumexp only for the
+    softmax node, and no output for nodes folded into a fused chain."""
+    import ctypes
+    import torch
+    from tensor_relational_algebra_amd import workloads as wl
+    case = wl.MHA_SMALL
+    g = tra.tra_graph_plan(case.graph_desc(), 16)
+    ws = torch.empty(g.info.workspace_bytes, dtype=torch.uint8)
+    sizes = {"Q_proj": 128 * 4 * 32, "K_proj": 128 * 4 * 32, "V_proj": 128 * 4 * 32, "Scores": 4 * 128 * 128,
+             "Attn": 4 * 128 * 128, "O": 128 * 4 * 32, "Output": 128 * 128}
+    dtypes = {"Scores": torch.float32, "Output": torch.float32}
+    for i, name in enumerate(sizes):
+        rel, lse = g.node_output(i, ws)
+        assert rel.numel() == sizes[name] and rel.dtype == dtypes.get(name, torch.bfloat16)
+        assert (lse is not None) == (name == "Attn")
+        if lse is not None:
+            assert lse.numel() == 4 * 128 and lse.dtype == torch.float32
+    gf = tra.tra_graph_plan_ex(case.graph_desc(), 16, None, tra.GRAPH_FUSE_ATTENTION)
+    wf = torch.empty(gf.info.workspace_bytes, dtype=torch.uint8)
+    for i in (3, 4):
+        with pytest.raises(tra.TraError) as e:
+            gf.node_output(i, wf)
+        assert e.value.code == -7
+    assert gf.node_output(5, wf)[0].numel() == sizes["O"]
+    L = tra.lib()
+    o, n, dt, lo, ln = ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int32(), ctypes.c_size_t(), ctypes.c_int64()
+    assert L.tra_graph_node_output(g.handle, 7, ctypes.byref(o), ctypes.byref(n), ctypes.byref(dt),
+                                   ctypes.byref(lo), ctypes.byref(ln)) == -13
+    assert L.tra_graph_node_output(g.handle, 0, None, ctypes.byref(n), ctypes.byref(dt), ctypes.byref(lo),
+                                   ctypes.byref(ln)) == -1
+
+
 def test_graph_plan_errors():
     with pytest.raises(tra.TraError) as e:
         tra.tra_graph_plan("A softmax hst->hst h=2,s=2,t=2 @S in=bf16 out=bf16", 1)

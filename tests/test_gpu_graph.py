@@ -12,7 +12,7 @@ import torch
 import tensor_relational_algebra_amd as tra
 from oracle import mha
 from tensor_relational_algebra_amd import workloads as wl
-from tests.gpu_util import DEV, maxnorm_rel_err
+from tests.gpu_util import DEV, gate, maxnorm_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -66,6 +66,74 @@ def test_full_layer_sampled_rows():
     err = maxnorm_rel_err(out[rows], want)
     assert err <= 2e-2, err
     assert np.isfinite(out).all()
+
+
+def _nodes(case):
+    """(name, output labels, canonical labels, bounds) per node of the graph."""
+    out = []
+    for line in case.graph_desc().splitlines():
+        f = line.split()
+        spec = f[2]
+        bounds = {k: int(v) for k, v in (kv.split("=") for kv in f[3].split(","))}
+        canon = spec.split("->")[1] if f[1] == "softmax" else tra.tra_canonical_labels(spec)
+        out.append((f[0], spec.split("->")[1], canon, bounds))
+    return out
+
+
+def _rows_spread(n, bands, per_band, seed):
+    rng = np.random.default_rng(seed)
+    b = n // bands
+    return np.sort(np.concatenate([k * b + rng.choice(b, per_band, replace=False) for k in range(bands)]))
+
+
+@pytest.mark.parametrize("fuse", [False, True], ids=["unfused", "fused"])
+def test_full_layer_every_node_on_sampled_rows(fuse):
+    """The full layer, chooser-picked d, run node by node: after each node its
+    output relation is read from the workspace, made dense, and compared with
+    the fp64 oracle's tensor on 64 query rows (4 in each 256-row band, every
+    head): Q_proj, Scores, the logsumexp, Attn, O and Output on those rows,
+    K_proj and V_proj whole.  Fused, the scores and softmax nodes write
+    nothing of their own; the fused node's O and the rest are compared."""
+    case = wl.MHA
+    flags = tra.GRAPH_FUSE_ATTENTION if fuse else 0
+    g = tra.tra_graph_plan_ex(case.graph_desc(), 256, None, flags)
+    assert g.info.n_fused == (1 if fuse else 0)
+    host = case.make_inputs()
+    dev = {k: v.to(DEV) for k, v in host.items()}
+    ws = g.workspace(DEV)
+    out = torch.empty(g.info.out_elems, dtype=torch.float32, device=DEV)
+    rows = _rows_spread(case.s, 16, 4, seed=404)
+    want = mha.mha(host, rows=rows)
+    # which axis of each node's output is the query position
+    query_axis = {"Q_proj": 0, "Scores": 1, "Attn": 1, "O": 0, "Output": 0}
+    compared = []
+    for i, (name, olab, canon, bounds) in enumerate(_nodes(case)):
+        root = i == g.info.n_nodes - 1
+        tra.tra_graph_run_node(g, i, dev, out if root else None, ws)
+        torch.cuda.synchronize()
+        if fuse and name in ("Scores", "Attn"):
+            with pytest.raises(tra.TraError):
+                g.node_output(i, ws)
+            continue
+        rel, lse = g.node_output(i, ws)
+        d = dict(zip(canon, g.node_d(i)))
+        dense = tra.from_relation(rel, [bounds[c] for c in olab], [d[c] for c in olab])
+        pairs = [(name, dense)]
+        if lse is not None:
+            pairs.append(("LSE", tra.from_relation(lse, [bounds[c] for c in olab[:-1]], [d[c] for c in olab[:-1]])))
+        for nm, t in pairs:
+            ax = query_axis.get(nm, None if nm != "LSE" else 1)
+            if ax is not None:
+                t = t.index_select(ax, torch.from_numpy(rows).to(DEV))
+            got = t.double().cpu().numpy()
+            assert np.isfinite(got).all(), nm
+            gate(f"attention layer {'fused' if fuse else 'unfused'} {nm} (64 rows)", "graph", got, want[nm], 2e-2)
+            compared.append(nm)
+        if root:
+            # the dense output written by the root node equals its relation
+            assert torch.equal(out.reshape(case.s, case.a), dense)
+    expect = {"Q_proj", "K_proj", "V_proj", "O", "Output"} | (set() if fuse else {"Scores", "Attn", "LSE"})
+    assert set(compared) == expect
 
 
 # --- the attention chain fused into one kernel (online logsumexp over t) ---

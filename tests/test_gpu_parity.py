@@ -16,7 +16,7 @@ import torch
 import tensor_relational_algebra_amd as tra
 from oracle import ref, tra_cpu
 from tensor_relational_algebra_amd import workloads as wl
-from tests.gpu_util import DEV, check, maxnorm_rel_err, run_gpu
+from tests.gpu_util import DEV, check, gate, maxnorm_rel_err, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -97,7 +97,7 @@ def test_nonlinear_joins_small(base, d):
 @pytest.mark.parametrize("d", [wl.matmul_d([16, 1, 1, 16]), wl.matmul_d([8, 1, 1, 32]), wl.matmul_d([16, 2, 2, 16])])
 @pytest.mark.parametrize("base", [wl.SQDIST, wl.MAXPLUS], ids=["sqdist", "maxplus"])
 def test_nonlinear_joins_full_size_sampled(base, d):
-    err, plan = check(base.with_d(d), sample=4096)
+    err, plan = check(base.with_d(d), sample=1 << 17)
     assert plan.kernel == "valu_tile"
 
 
@@ -203,7 +203,7 @@ def test_contract4_small(d):
 @pytest.mark.parametrize("d", [wl.CONTRACT4.d, dict(a=1, b=1, c=1, d=1, e=1, f=1),
                                dict(a=4, b=4, c=4, d=4, e=1, f=1)])
 def test_contract4_full_size_sampled(d):
-    err, plan = check(wl.CONTRACT4.with_d(d), sample=4096, seed=3)
+    err, plan = check(wl.CONTRACT4.with_d(d), sample=1 << 18, seed=3)
     if d == wl.CONTRACT4.d:
         assert plan.kernel == "mfma_bf16"
 
@@ -216,8 +216,23 @@ def test_gemm25d_small(d):
 
 
 def test_gemm25d_full_size_sampled():
-    err, plan = check(wl.GEMM25D, sample=2048, seed=4)
+    err, plan = check(wl.GEMM25D, sample=1 << 16, seed=4)
     assert plan.kernel == "mfma_bf16"
+
+
+def test_gemm25d_full_size_whole_rows():
+    """32 whole rows of Y (two in each of the 16 row blocks, every column, so
+    every output tile column and all four contracted partitions) against the
+    oracle, in the bench's launch configuration."""
+    c = wl.GEMM25D
+    xs = c.make_inputs()
+    z, plan = run_gpu(c, xs)
+    assert plan.kernel == "mfma_bf16" and plan.info.agg_split == 1
+    rng = np.random.default_rng(44)
+    rows = np.sort(np.concatenate([b * 1024 + rng.choice(1024, 2, replace=False) for b in range(16)]))
+    idx = (rows[:, None] * 8192 + np.arange(8192)[None, :]).reshape(-1)
+    want = ref.einsum(c.spec, xs[0], xs[1], c.join, c.agg, out_index=idx)
+    gate("gemm25d 32 whole rows", plan.kernel, z[torch.from_numpy(rows)].double().numpy(), want, 2e-2, 2e-2)
 
 
 def test_gemm_bf16_output_and_post_scale():

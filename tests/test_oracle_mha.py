@@ -71,9 +71,16 @@ def _autograd_reference(t, d_out):
     attn = torch.softmax(sc, dim=2)
     o = torch.einsum("hst,thd->shd", attn, vp)
     out = torch.einsum("shd,ahd->sa", o, leaves["W_O"])
+    # gradients of the intermediates too
+    for x in (qp, o, attn):
+        x.retain_grad()
     g = torch.tensor(mha.ref._as_np(d_out), dtype=torch.float64)
     out.backward(g)
-    return {"d" + n: leaves[n].grad.numpy() for n in leaves}
+    res = {"d" + n: leaves[n].grad.numpy() for n in leaves}
+    res.update({"dQ_proj": qp.grad.numpy(), "dO": o.grad.numpy(), "dAttn": attn.grad.numpy()})
+    # softmax Jacobian applied to dAttn, written out with torch's own softmax backward
+    res["dScores"] = torch.ops.aten._softmax_backward_data(attn.grad, attn, 2, torch.float64).detach().numpy()
+    return res
 
 
 def test_backward_equals_autograd():
@@ -83,6 +90,34 @@ def test_backward_equals_autograd():
     want = _autograd_reference(t, g)
     for name in ("dQ", "dK", "dV", "dW_Q", "dW_K", "dW_V", "dW_O"):
         np.testing.assert_allclose(got[name], want[name], rtol=1e-9, atol=1e-12, err_msg=name)
+
+
+def test_backward_intermediates_equal_autograd():
+    t = _inputs(24, 16, 2, 8, seed=6)
+    g = workloads.draw(4244, (24, 16), "normal", "bf16", std=1.0)
+    got = mha.mha_backward(t, g)
+    want = _autograd_reference(t, g)
+    for name in ("dQ_proj", "dO", "dAttn", "dScores"):
+        np.testing.assert_allclose(got[name], want[name], rtol=1e-9, atol=1e-12, err_msg=name)
+
+
+def test_backward_row_sample_equals_full():
+    """The row-restricted backward (query rows only) equals those rows of the
+    full backward, and of autograd's."""
+    case = workloads.MhaCase(s=32, a=16, h=2, dh=8, wid=96)
+    t = case.make_inputs()
+    g = workloads.draw(9601, (32, 16), "normal", "bf16", std=1.0)
+    full = mha.mha_backward(t, g)
+    auto = _autograd_reference(t, g)
+    rows = np.array([0, 7, 8, 31])
+    part = mha.mha_backward(t, g, rows=rows)
+    assert set(part) == {"dO", "dAttn", "dScores", "dQ_proj", "dQ"}
+    for name in ("dO", "dQ_proj", "dQ"):
+        np.testing.assert_allclose(part[name], full[name][rows], rtol=1e-12, atol=1e-13, err_msg=name)
+        np.testing.assert_allclose(part[name], auto[name][rows], rtol=1e-9, atol=1e-12, err_msg=name)
+    for name in ("dAttn", "dScores"):
+        np.testing.assert_allclose(part[name], full[name][:, rows], rtol=1e-12, atol=1e-13, err_msg=name)
+        np.testing.assert_allclose(part[name], auto[name][:, rows], rtol=1e-9, atol=1e-12, err_msg=name)
 
 
 def test_backward_with_unequal_query_and_key_lengths():
