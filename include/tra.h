@@ -185,6 +185,28 @@ int tra_execute(tra_plan_t plan, const void *x_rel, const void *y_rel, void *z_r
                 void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * tra_execute_static -- tra_execute with no workspace argument, for callers
+ * that cannot allocate device memory (code under stream capture, serving
+ * loops, harnesses that forbid allocation).  The plan's scratch (the partials
+ * of a split aggregation, the range-check flags of the packed max-plus path)
+ * lives in one fixed array per device, tra_static_scratch_bytes() long (16
+ * MiB), which the library holds on every device it runs on until the process
+ * ends; its device address is looked up once per device, with that device
+ * current, on the first call there.  Nothing is allocated or freed.
+ * Every call on a device shares that device's array and its contents are
+ * ignored on entry (every scratch byte a call reads it has written first),
+ * so calls that overlap on one device (two streams, two threads) race and
+ * must be ordered by the caller.  Arguments, layouts and errors as for
+ * tra_execute; a plan whose info.workspace_bytes exceeds the array returns
+ * TRA_E_WORKSPACE (use tra_execute with a workspace), and a failed symbol
+ * lookup TRA_E_HIP.
+ */
+int tra_execute_static(tra_plan_t plan, const void *x_rel, const void *y_rel, void *z_rel, void *hip_stream);
+
+/* Size in bytes of the per-device scratch array of tra_execute_static. */
+size_t tra_static_scratch_bytes(void);
+
+/*
  * tra_execute_chain -- two elementwise EinSums (aggregate NONE, section 2.1's
  * joins) as one pass, the first one's output never written:
  *     t = plan_a(xa, ya)       (rounded to plan_a's output dtype)

@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
             "tra_plan_info": ([P, P], I),
             "tra_plan_destroy": ([P], I),
             "tra_execute": ([P, P, P, P, P, ctypes.c_size_t, P], I),
+            "tra_execute_static": ([P, P, P, P, P], I),
+            "tra_static_scratch_bytes": ([], ctypes.c_size_t),
             "tra_execute_chain": ([P, P, P, P, P, P, P], I),
             "tra_execute_contract_chain": ([P, P, P, P, P, P, P, P, P], I),
             "tra_repartition": ([P, I, P, P, I, P, P, P], I),
@@ -203,6 +205,22 @@ def tra_execute(plan: Plan, x: torch.Tensor, y: Optional[torch.Tensor] = None, z
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().tra_execute(plan.handle, px, py, pz, pw, wb, _stream(stream)))
     return z
+
+
+def tra_execute_static(plan: Plan, x: torch.Tensor, y: Optional[torch.Tensor], z: torch.Tensor,
+                       stream=None) -> torch.Tensor:
+    """tra_execute with the plan's scratch in the library's fixed per-device
+    array (no workspace argument; nothing allocated); z is required."""
+    inf = plan.info
+    px = _dev_ptr(x, "x", inf.x_elems, plan.in_dtype)
+    py = _dev_ptr(y, "y", inf.y_elems, plan.in_dtype) if inf.y_elems else None
+    pz = _dev_ptr(z, "z", inf.z_elems, plan.out_dtype)
+    _check(lib().tra_execute_static(plan.handle, px, py, pz, _stream(stream)))
+    return z
+
+
+def tra_static_scratch_bytes() -> int:
+    return int(lib().tra_static_scratch_bytes())
 
 
 def tra_execute_chain(plan_a: Plan, plan_b: Plan, xa: torch.Tensor, ya: Optional[torch.Tensor],
