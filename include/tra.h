@@ -530,6 +530,16 @@ int tra_graph_execute(tra_graph_t graph, const void *const *leaves, int n_leaves
 /* Free a graph's host memory.  NULL is accepted. */
 int tra_graph_destroy(tra_graph_t graph);
 
+/*
+ * tra_probe_mfma_loop -- measurement aid: `workgroups` workgroups of four
+ * waves each run `iters` rounds of 8 independent bf16 32x32x16 matrix-core
+ * products on register operands (2 * 32 * 32 * 16 * 8 * 4 flop per round and
+ * workgroup), the ceiling the tile kernels are held against beside the
+ * published peak.  out: device buffer of workgroups * 256 floats (written,
+ * values meaningless).  Errors: TRA_E_NULL, TRA_E_OP (counts < 1), TRA_E_HIP.
+ */
+int tra_probe_mfma_loop(int workgroups, int iters, float *out, void *hip_stream);
+
 /* Text of a status code (static storage). */
 const char *tra_status_string(int status);
 

@@ -1,0 +1,52 @@
+// k_probe.hip -- the machine's own ceilings, measured beside the published
+// ones: a loop of bf16 matrix-core products with nothing else in it (no
+// memory traffic besides one store per lane at the end).  The copy ceiling is
+// measured with tra_repartition between identical blockings.
+#include <hip/hip_runtime.h>
+
+#include "tra.h"
+
+namespace tra {
+
+typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
+typedef float floatx16_p __attribute__((ext_vector_type(16)));
+
+// Four waves per workgroup, one per SIMD; each wave runs `iters` rounds of 8
+// independent 32x32x16 products (8 accumulator sets, so no product waits on
+// the one before it), from operands that stay in registers.
+__global__ __launch_bounds__(256) void k_probe_mfma(int iters, float seed, float *__restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    bf16x8_p a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(seed * (float)(lane + e));
+        b[e] = (__bf16)(seed * (float)(lane - e));
+    }
+    floatx16_p acc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[s][e] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[s], 0, 0, 0);
+    }
+    float r = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) r += acc[s][e];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
+}  // namespace tra
+
+extern "C" int tra_probe_mfma_loop(int workgroups, int iters, float *out, void *hip_stream)
+{
+    if (!out) return TRA_E_NULL;
+    if (workgroups < 1 || iters < 1) return TRA_E_OP;
+    hipLaunchKernelGGL(tra::k_probe_mfma, dim3(workgroups), dim3(256), 0, (hipStream_t)hip_stream, iters, 1.0f / 64,
+                       out);
+    return hipGetLastError() == hipSuccess ? TRA_OK : TRA_E_HIP;
+}

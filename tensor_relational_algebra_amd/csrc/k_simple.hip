@@ -56,6 +56,81 @@ __global__ __launch_bounds__(256) void k_generic(GenericDesc g, int join, int ag
     }
 }
 
+// ---------------------------------------------------------------- split reduction
+// Few outputs, each over a long contracted range (a full reduction, a trace,
+// a handful of long dot products).  Output o's range of n_con contracted
+// indices (flattened in ascending key order, the last contracted sub-dim
+// fastest) is cut into `split` chunks of `chunk` consecutive indices, and
+// workgroup (s, o) folds chunk s:
+//  * thread t takes the indices of each contracted row inside the chunk at
+//    t, t + 256, ... (coalesced when the row is contiguous), folding in that
+//    order;
+//  * the 64 lanes of a wave combine by a butterfly, and the four waves'
+//    partials are folded in wave order through LDS (aggregation tier ii);
+//  * with split == 1 that is the output; otherwise partial s goes to
+//    ws[s * n_out + o] (logsumexp as the chunk's own logsumexp) and
+//    k_split_fold folds the chunks in order (tier iii).
+// Every order is fixed, so runs are bitwise reproducible.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void k_reduce_split(GenericDesc g, int join, int agg, int two,
+                                                      const TI *__restrict__ x, const TI *__restrict__ y,
+                                                      TO *__restrict__ z, typename Scalar<TI>::acc *__restrict__ ws)
+{
+    using A = typename Scalar<TI>::acc;
+    const int64_t o = blockIdx.y;
+    const int64_t s = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int64_t xo = 0, yo = 0;
+    radix_offsets(g.out, o, xo, yo);
+    const int last = g.con.n - 1;
+    const int64_t inner = g.con.ext[last];
+    const int64_t sxl = g.con.st[0][last], syl = g.con.st[1][last];
+    const int64_t c0 = s * g.chunk, c1 = min(g.n_con, c0 + g.chunk);
+    Fold<A> f;
+    f.init(agg);
+    for (int64_t r = c0 / inner; r * inner < c1; ++r) {
+        int64_t xr = xo, yr = yo, idx = r;
+        for (int i = last - 1; i >= 0; --i) {
+            const uint32_t e = g.con.ext[i];
+            const int64_t q = idx / e;
+            const int64_t dgt = idx - q * e;
+            idx = q;
+            xr += dgt * g.con.st[0][i];
+            yr += dgt * g.con.st[1][i];
+        }
+        const int64_t lo = max(c0 - r * inner, (int64_t)0), hi = min(inner, c1 - r * inner);
+        for (int64_t e = lo + tid; e < hi; e += 256) {
+            A xv = Scalar<TI>::load(x, xr + e * sxl);
+            A yv = two ? Scalar<TI>::load(y, yr + e * syl) : A(0);
+            f.add(agg, join_any(join, xv, yv));
+        }
+    }
+    __shared__ A wm[4];
+    __shared__ float wsum[4];
+    if constexpr (std::is_same<A, float>::value) {
+        for (int off = 32; off >= 1; off >>= 1) {
+            float om = __shfl_xor(f.m, off, 64);
+            float os = __shfl_xor(f.s, off, 64);
+            f.merge(agg, om, os);
+        }
+        if (lane == 0) wsum[wave] = f.s;
+    } else {
+        for (int off = 32; off >= 1; off >>= 1) f.merge(agg, __shfl_xor(f.m, off, 64), 0);
+    }
+    if (lane == 0) wm[wave] = f.m;
+    __syncthreads();
+    if (tid == 0) {
+        Fold<A> t;
+        t.init(agg);
+        for (int w = 0; w < 4; ++w) {
+            if constexpr (std::is_same<A, float>::value) t.merge(agg, wm[w], wsum[w]);
+            else t.merge(agg, wm[w], 0);
+        }
+        if (g.split == 1) Scalar<TO>::store(z, o, (A)t.result(agg, g.post_scale));
+        else ws[s * g.n_out + o] = agg == A_LSE ? (A)t.result(agg, 1.f) : t.m;
+    }
+}
+
 // ---------------------------------------------------------------- elementwise
 // Aggregate NONE: z = join(x, y) (times post_scale); `vec` consecutive output
 // elements share one digit decomposition.
@@ -406,11 +481,7 @@ __global__ __launch_bounds__(256) void k_split_fold(const A *__restrict__ ws, in
         Fold<A> f;
         f.init(agg);
         for (int s = 0; s < split; ++s) f.merge(agg, ws[(int64_t)s * n + o], A(1));
-        if constexpr (std::is_same<A, float>::value) {
-            Scalar<TO>::store(z, o, f.m * scale);
-        } else {
-            Scalar<TO>::store(z, o, f.m);
-        }
+        Scalar<TO>::store(z, o, (A)f.result(agg, scale));
     }
 }
 
@@ -509,9 +580,29 @@ static int grid_for(int64_t work, int per_block = 256)
         else { using TI = int32_t; using TO = int32_t; CALL; }                              \
     } while (0)
 
-int launch_generic(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream)
+static int launch_fold(int64_t n, int split, int agg, float scale, bool int_acc, int out_dtype, const void *ws,
+                       void *z, hipStream_t s);
+
+// The split reduction (GenericDesc::split > 0) and, with more than one
+// chunk, the in-order fold of its partials.
+static int launch_reduce_split(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws,
+                               hipStream_t s)
+{
+    const GenericDesc &g = p.gen;
+    dim3 grid((unsigned)g.split, (unsigned)g.n_out);
+    TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
+                    hipLaunchKernelGGL((k_reduce_split<TI, TO>), grid, dim3(256), 0, s, g, p.join, p.agg,
+                                       p.n_ops == 2 ? 1 : 0, (const TI *)x, (const TI *)y, (TO *)z,
+                                       (typename Scalar<TI>::acc *)ws));
+    int err = (int)hipGetLastError();
+    if (err || g.split == 1) return err;
+    return launch_fold(g.n_out, g.split, p.agg, p.post_scale, p.in_dtype == D_I32, p.out_dtype, ws, z, s);
+}
+
+int launch_generic(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream)
 {
     hipStream_t s = (hipStream_t)stream;
+    if (p.gen.split > 0) return launch_reduce_split(p, x, y, z, ws, s);
     int grid = grid_for(p.gen.n_out);
     TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
                     hipLaunchKernelGGL((k_generic<TI, TO>), dim3(grid), dim3(256), 0, s, p.gen, p.join, p.agg,
@@ -709,9 +800,10 @@ int launch_elemwise_chain(const tra_plan_s &a, const tra_plan_s &b, const void *
     return launch_chain_t<bf16_t, bf16_t, bf16_t>(a, b, xa, ya, xb, z, s);
 }
 
-int launch_rowreduce(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream)
+int launch_rowreduce(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream)
 {
     hipStream_t s = (hipStream_t)stream;
+    if (p.gen.split > 0) return launch_reduce_split(p, x, y, z, ws, s);
     if (p.row.p2) {
         int grid = grid_for(p.row.n_out * 64);
         TRA_DISPATCH_IO(p.in_dtype, p.out_dtype,
@@ -726,23 +818,27 @@ int launch_rowreduce(const tra_plan_s &p, const void *x, const void *y, void *z,
     return (int)hipGetLastError();
 }
 
-int launch_split_fold(const tra_plan_s &p, const void *ws, void *z, void *stream)
+static int launch_fold(int64_t n, int split, int agg, float scale, bool int_acc, int out_dtype, const void *ws,
+                       void *z, hipStream_t s)
 {
-    hipStream_t s = (hipStream_t)stream;
-    int64_t n = p.info.z_elems;
     int grid = grid_for(n);
-    int split = p.gv.split;
-    if (p.in_dtype == D_I32) {
+    if (int_acc) {
         hipLaunchKernelGGL((k_split_fold<int32_t, int32_t>), dim3(grid), dim3(256), 0, s, (const int32_t *)ws, n,
-                           split, p.agg, 1.0f, (int32_t *)z);
-    } else if (p.out_dtype == D_BF16) {
+                           split, agg, 1.0f, (int32_t *)z);
+    } else if (out_dtype == D_BF16) {
         hipLaunchKernelGGL((k_split_fold<float, bf16_t>), dim3(grid), dim3(256), 0, s, (const float *)ws, n, split,
-                           p.agg, p.post_scale, (bf16_t *)z);
+                           agg, scale, (bf16_t *)z);
     } else {
         hipLaunchKernelGGL((k_split_fold<float, float>), dim3(grid), dim3(256), 0, s, (const float *)ws, n, split,
-                           p.agg, p.post_scale, (float *)z);
+                           agg, scale, (float *)z);
     }
     return (int)hipGetLastError();
+}
+
+int launch_split_fold(const tra_plan_s &p, const void *ws, void *z, void *stream)
+{
+    return launch_fold(p.info.z_elems, p.gv.split, p.agg, p.post_scale, p.in_dtype == D_I32, p.out_dtype, ws, z,
+                       (hipStream_t)stream);
 }
 
 int launch_repartition(const RepartDesc &r, int esz, const void *src, void *dst, void *stream)

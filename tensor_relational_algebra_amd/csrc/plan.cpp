@@ -306,6 +306,11 @@ static bool lower_identity(tra_plan_s &p)
     return true;
 }
 
+// Plans with at most this many outputs and at least this many contracted
+// terms per output take the split reduction (see lower_generic).
+constexpr int64_t kSplitReduceMaxOut = 4096;
+constexpr int64_t kSplitReduceMinTerms = 4096;
+
 static bool lower_generic(tra_plan_s &p)
 {
     const std::string *tz[3] = {&p.xl, p.n_ops == 2 ? &p.yl : nullptr, nullptr};
@@ -344,6 +349,20 @@ static bool lower_generic(tra_plan_s &p)
         }
         p.kernel = TRA_KERNEL_ELEMWISE;
         return true;
+    }
+    // Few outputs and a long contracted range: one thread (or one wavefront)
+    // per output would leave the chip idle.  Cut each output's range into
+    // chunks folded by whole workgroups (four waves, combined in order), and
+    // fold the chunks' partials in order in a second pass: enough chunks for
+    // ~2048 workgroups, each chunk at least 4096 terms.
+    if (p.gen.n_out <= kSplitReduceMaxOut && p.gen.n_con >= kSplitReduceMinTerms && !sc.empty()) {
+        int64_t split = 1;
+        while (split < 1024 && split * 2 * p.gen.n_out <= 2048 && p.gen.n_con / (split * 2) >= kSplitReduceMinTerms)
+            split *= 2;
+        p.gen.split = (int32_t)split;
+        p.gen.chunk = (p.gen.n_con + split - 1) / split;
+        p.info.agg_split = split;
+        p.info.workspace_bytes = split > 1 ? (size_t)split * (size_t)p.gen.n_out * 4 : 0;
     }
     // one wavefront per output row when the last contracted run is contiguous in
     // X and contiguous or broadcast in Y (a Y strided along the run makes every
@@ -593,9 +612,9 @@ int tra_execute(tra_plan_t p, const void *x, const void *y, void *z, void *ws, s
     switch (p->kernel) {
     case TRA_KERNEL_MFMA_BF16: err = launch_mfma_bf16(*p, x, y, z, ws, stream); break;
     case TRA_KERNEL_VALU_TILE: err = launch_valu_tile(*p, x, y, z, ws, stream); break;
-    case TRA_KERNEL_ROWREDUCE: err = launch_rowreduce(*p, x, y, z, stream); break;
+    case TRA_KERNEL_ROWREDUCE: err = launch_rowreduce(*p, x, y, z, ws, stream); break;
     case TRA_KERNEL_ELEMWISE: err = launch_elemwise(*p, x, y, z, stream); break;
-    default: err = launch_generic(*p, x, y, z, stream); break;
+    default: err = launch_generic(*p, x, y, z, ws, stream); break;
     }
     if (err) return fail(TRA_E_HIP, std::string("kernel launch failed: ") + hip_error_text(err));
     return TRA_OK;

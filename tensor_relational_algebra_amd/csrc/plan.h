@@ -29,9 +29,9 @@ struct tra_plan_s {
 namespace tra {
 
 // Launchers (kernels.hip).  Return a hipError_t value (0 = success).
-int launch_generic(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream);
+int launch_generic(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream);
 int launch_elemwise(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream);
-int launch_rowreduce(const tra_plan_s &p, const void *x, const void *y, void *z, void *stream);
+int launch_rowreduce(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream);
 int launch_valu_tile(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream);
 int launch_mfma_bf16(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream);
 int launch_repartition(const RepartDesc &r, int elem_bytes, const void *src, void *dst, void *stream);

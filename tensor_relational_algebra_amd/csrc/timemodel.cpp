@@ -70,10 +70,18 @@ int64_t predict_plan_ns(const tra_plan_s &p)
         rate = p.tile == 1 ? kCal.valu_small_int_terms : kCal.valu_terms;
         bw = kCal.tile_bw;
         break;
-    case TRA_KERNEL_GENERIC: rate = kCal.generic_terms; break;
+    case TRA_KERNEL_GENERIC:
     case TRA_KERNEL_ROWREDUCE:
-        rate = kCal.rowreduce_terms;
-        bw = kCal.rowreduce_bw;
+        if (p.gen.split > 0) {
+            // few outputs, each folded by whole workgroups: bandwidth-bound
+            rate = 1e30;
+            bw = kCal.rowreduce_bw;
+        } else if (p.kernel == TRA_KERNEL_GENERIC) {
+            rate = kCal.generic_terms;
+        } else {
+            rate = kCal.rowreduce_terms;
+            bw = kCal.rowreduce_bw;
+        }
         break;
     default: rate = 1e30; break;   // elementwise: bandwidth-bound
     }

@@ -61,6 +61,12 @@ struct GenericDesc {
     int64_t n_out;
     int64_t n_con;
     float post_scale;
+    // split > 0: few outputs over a long contracted range run as workgroups
+    // of (chunk s, output o), each folding `chunk` consecutive contracted
+    // indices with its four waves; split > 1 adds the in-order fold of the
+    // chunks' partials (workspace [split][n_out])
+    int32_t split;
+    int64_t chunk;
 };
 
 // GEMM view of a two-operand EinSum: output labels only in X form M, only in

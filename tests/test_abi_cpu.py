@@ -166,6 +166,13 @@ def test_cost_matches_hand_worked_values():
         assert tra.tra_cost(c["spec"], c["bounds"], c["d"]) == c["cost"], c["_work"]
 
 
+def test_probe_argument_errors():
+    L = tra.lib()
+    assert L.tra_probe_mfma_loop(0, 1, 0x1000, None) == -7
+    assert L.tra_probe_mfma_loop(1, 0, 0x1000, None) == -7
+    assert L.tra_probe_mfma_loop(1, 1, None, None) == -1
+
+
 def test_softmax_node_cost_matches_hand_worked_values():
     """The library's chooser on one softmax node, at a P that leaves exactly one
     admissible d (every element its own block), returns the hand-worked cost of

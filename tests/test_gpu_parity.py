@@ -464,3 +464,41 @@ def test_execute_contract_chain_matches_three_launches(case):
     got = tra.tra_execute_contract_chain(pc, pa, pb, xc, yc, ya, xb)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+
+
+# ------------------------------------------------------------ few outputs over long contracted ranges
+
+U01 = ("uniform", {"lo": 0.0, "hi": 1.0})
+REDUCE_CASES = [
+    # (name, spec, bounds, d, join, agg, dtype, inputs)
+    ("full_sum", "ij->", {"i": 4096, "j": 4096}, {"i": 1, "j": 1}, "ident", "sum", "f32", (U01,)),
+    ("full_sum_blocked", "ij->", {"i": 4096, "j": 4096}, {"i": 4, "j": 8}, "ident", "sum", "f32", (U01,)),
+    ("trace_of_product", "ij,ji->", {"i": 4096, "j": 4096}, {"i": 1, "j": 1}, "mul", "sum", "f32", (U01, U01)),
+    ("row_max_int", "ij->i", {"i": 16, "j": 1 << 20}, {"i": 1, "j": 1}, "ident", "max", "i32",
+     (("int", {"lo": -1000000, "hi": 1000000}),)),
+    ("sum_int", "ij->", {"i": 2048, "j": 4096}, {"i": 2, "j": 1}, "ident", "sum", "i32",
+     (("int", {"lo": -8, "hi": 8}),)),
+    ("column_min", "ij->j", {"i": 65536, "j": 64}, {"i": 1, "j": 1}, "ident", "min", "f32",
+     (("normal", {"std": 1.0}),)),
+    ("lse_long_rows", "hst->hs", {"h": 4, "s": 16, "t": 65536}, {"h": 2, "s": 4, "t": 2}, "ident", "lse", "f32",
+     (("normal", {"std": 3.0}),)),
+    ("sqdist_bf16", "ij,ij->", {"i": 4096, "j": 4096}, {"i": 4, "j": 8}, "sqdiff", "sum", "bf16",
+     (("normal", {"std": 1.0}),) * 2),
+]
+
+
+@pytest.mark.parametrize("case", REDUCE_CASES, ids=[c[0] for c in REDUCE_CASES])
+def test_few_outputs_long_contracted_range(case):
+    """A reduction to a handful of outputs is cut into chunks folded by whole
+    workgroups (their waves combined in order through LDS), and the chunks'
+    partials are folded in order by a second pass; against the oracle over
+    every output, and bitwise reproducible."""
+    name, spec, bounds, d, join, agg, dt, inputs = case
+    c = wl.EinsumCase(name, 320 + REDUCE_CASES.index(case), spec, bounds, d, join, agg, dt,
+                      "i32" if dt == "i32" else "f32", inputs)
+    err, plan = check(c)
+    assert plan.info.agg_split > 1 and plan.kernel in ("generic", "rowreduce"), plan.info.agg_split
+    xs = c.make_inputs()
+    a, _ = run_gpu(c, xs)
+    b, _ = run_gpu(c, xs)
+    assert torch.equal(a, b)
