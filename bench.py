@@ -518,6 +518,23 @@ def _extra(tra, wl, dev, stream, only):
     if want("sqdist"):
         res.update(_sqdist(tra, wl, dev, stream, scratch))
 
+    if want("ragged"):
+        # the squared distance at 8000 x 256 x 8000 (no tile divides 8000;
+        # relation blocks of 500): masked edge tiles on the same kernel
+        c = wl.SQDIST.scaled({"i": 8000, "j": 256, "k": 8000}, wl.SQDIST.d)
+        x_h, y_h = c.make_inputs()
+        p = tra.tra_plan(c.spec, c.bounds, c.d, c.join, c.agg, c.in_dtype, c.out_dtype)
+        xr = tra.to_relation(x_h.to(dev), [c.d["i"], c.d["j"]])
+        yr = tra.to_relation(y_h.to(dev), [c.d["j"], c.d["k"]])
+        ms, _ = timed_execute(p, xr, yr, reps=10, flush=True)
+        terms = 8000 * 256 * 8000
+        res["sqdist_8000"] = {"ms": round(ms, 4), "TFLOP/s": round(terms * SQDIST_FLOP_PER_TERM / ms / 1e9, 2),
+                              "kernel": p.kernel,
+                              "frac_alu": round(terms * SQDIST_FLOP_PER_TERM / (ms * 1e-3) / VALU_SQDIST_PEAK, 4)}
+        if "sqdist" in res:
+            res["sqdist_8000"]["time_vs_8192"] = round(ms / res["sqdist"]["ms"], 3)
+        del xr, yr
+
     if want("matmul"):
         for base in (wl.MATMUL_F32, wl.MATMUL_I32):
             x, y = (t.to(dev) for t in base.make_inputs())

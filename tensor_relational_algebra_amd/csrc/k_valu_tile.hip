@@ -122,6 +122,19 @@ __device__ __forceinline__ A vinit()
     }
 }
 
+// Offset of row / column idx of a ragged group in tensor slot t (mixed radix,
+// last sub-dimension fastest).
+__device__ __forceinline__ int32_t rad_off(const Radix &r, int t, uint32_t idx)
+{
+    int64_t o = 0;
+    for (int i = r.n - 1; i >= 0; --i) {
+        const uint32_t e = r.ext[i], q = idx / e;
+        o += (int64_t)(idx - q * e) * r.st[t][i];
+        idx = q;
+    }
+    return (int32_t)o;
+}
+
 // ---- int32 max-plus / min-plus on packed 16-bit halves -------------------
 //
 // Every integer of magnitude at most 2048 is exact in IEEE binary16 (11-bit
@@ -197,32 +210,41 @@ __global__ __launch_bounds__(SI_CHECK_THREADS) void k_small_int_check(const int3
 // relation layout, or (split aggregation) to this split's fp32 / int32 slice of
 // the workspace, which the fold kernel combines.
 // Rows ty*4+{0..3}, 64+ty*4+{0..3}; columns tx*4+{0..3}, 64+tx*4+{0..3}.
-template <typename A, typename TO>
+template <typename A, typename TO, bool RAG = false>
 __device__ __forceinline__ void vt_store(const GemmView &v, A (&acc)[8][8], TO *__restrict__ z, A *__restrict__ ws,
-                                         uint32_t m0, uint32_t n0, int32_t bz, int tx, int ty)
+                                         uint32_t m0, uint32_t n0, int32_t bz, int tx, int ty,
+                                         const RaggedMN *rag = nullptr)
 {
     typedef A V4 __attribute__((ext_vector_type(4)));
     const bool split = v.split > 1;
     A *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
-    const int32_t zm0 = p2off<1>(v.gm, m0) + bz, zn0 = p2off<1>(v.gn, n0);
+    const int32_t zm0 = RAG ? bz : p2off<1>(v.gm, m0) + bz, zn0 = RAG ? 0 : p2off<1>(v.gn, n0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t m = i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4);
-        const int32_t om = zm0 + p2off<1>(v.gm, m);
+        // ragged edge: rows past the extent hold values of clamped loads
+        if (RAG && m0 + m >= rag->M) continue;
+        const int32_t om = zm0 + (RAG ? rad_off(rag->m, 1, m0 + m) : p2off<1>(v.gm, m));
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t nbase = h * 64 + tx * 4;
             int32_t on[4];
+            bool ok[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) on[j] = zn0 + p2off<1>(v.gn, nbase + j);
-            const bool vec = on[1] == on[0] + 1 && on[2] == on[0] + 2 && on[3] == on[0] + 3 && ((om + on[0]) & 3) == 0;
+            for (int j = 0; j < 4; ++j) {
+                ok[j] = !RAG || n0 + nbase + j < rag->N;
+                on[j] = RAG ? (ok[j] ? rad_off(rag->n, 1, n0 + nbase + j) : 0) : zn0 + p2off<1>(v.gn, nbase + j);
+            }
+            const bool vec = ok[3] && on[1] == on[0] + 1 && on[2] == on[0] + 2 && on[3] == on[0] + 3 &&
+                             ((om + on[0]) & 3) == 0;
             A r4[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) r4[j] = acc[i][h * 4 + j];
             if (split) {
                 if (vec) *(V4 *)&wsp[om + on[0]] = V4{r4[0], r4[1], r4[2], r4[3]};
                 else
-                    for (int j = 0; j < 4; ++j) wsp[om + on[j]] = r4[j];
+                    for (int j = 0; j < 4; ++j)
+                        if (ok[j]) wsp[om + on[j]] = r4[j];
             } else {
                 if constexpr (std::is_same<A, float>::value) {
 #pragma unroll
@@ -231,9 +253,11 @@ __device__ __forceinline__ void vt_store(const GemmView &v, A (&acc)[8][8], TO *
                 if constexpr (std::is_same<TO, float>::value || std::is_same<TO, int32_t>::value) {
                     if (vec) *(V4 *)&z[om + on[0]] = V4{r4[0], r4[1], r4[2], r4[3]};
                     else
-                        for (int j = 0; j < 4; ++j) z[om + on[j]] = r4[j];
+                        for (int j = 0; j < 4; ++j)
+                            if (ok[j]) z[om + on[j]] = r4[j];
                 } else {
-                    for (int j = 0; j < 4; ++j) Scalar<TO>::store(z, om + on[j], (float)r4[j]);
+                    for (int j = 0; j < 4; ++j)
+                        if (ok[j]) Scalar<TO>::store(z, om + on[j], (float)r4[j]);
                 }
             }
         }
@@ -251,11 +275,16 @@ struct VtLoad {
     int32_t a_off[4], b_off[4];
     int a_row[4], a_col[4], b_row[4], b_col[4];
 
+    // RAG: rows and columns past the extents are clamped to the last valid
+    // one (the last valid vector of 4 for an MN-major operand, whose fastest
+    // extent is a multiple of 4), so every load stays inside the operand; the
+    // store drops what they produce.
+    template <bool RAG = false>
     __device__ __forceinline__ void init(const GemmView &v, uint32_t m0, uint32_t n0, int32_t bx, int32_t by,
-                                         int tid)
+                                         int tid, const RaggedMN *rag = nullptr)
     {
         constexpr int BM = VT_BM, BN = VT_BN, BK = VT_BK;
-        const int32_t am0 = p2off<0>(v.gm, m0) + bx, bn0 = p2off<0>(v.gn, n0) + by;
+        const int32_t am0 = RAG ? bx : p2off<0>(v.gm, m0) + bx, bn0 = RAG ? by : p2off<0>(v.gn, n0) + by;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             int q = tid + VT_THREADS * r;
@@ -266,7 +295,12 @@ struct VtLoad {
                 a_row[r] = (q % (BM / 4)) * 4;  // m
                 a_col[r] = q / (BM / 4);        // k
             }
-            a_off[r] = am0 + p2off<0>(v.gm, a_row[r]) + p2off<0>(v.gk, a_col[r]);
+            if constexpr (RAG) {
+                const uint32_t m = min(m0 + (uint32_t)a_row[r], rag->M - (AK ? 1u : 4u));
+                a_off[r] = am0 + rad_off(rag->m, 0, m) + p2off<0>(v.gk, a_col[r]);
+            } else {
+                a_off[r] = am0 + p2off<0>(v.gm, a_row[r]) + p2off<0>(v.gk, a_col[r]);
+            }
             if constexpr (BKM) {
                 b_col[r] = (q % (BK / 4)) * 4;
                 b_row[r] = q / (BK / 4);
@@ -274,20 +308,27 @@ struct VtLoad {
                 b_row[r] = (q % (BN / 4)) * 4;
                 b_col[r] = q / (BN / 4);
             }
-            b_off[r] = bn0 + p2off<0>(v.gn, b_row[r]) + p2off<1>(v.gk, b_col[r]);
+            if constexpr (RAG) {
+                const uint32_t n = min(n0 + (uint32_t)b_row[r], rag->N - (BKM ? 1u : 4u));
+                b_off[r] = bn0 + rad_off(rag->n, 0, n) + p2off<1>(v.gk, b_col[r]);
+            } else {
+                b_off[r] = bn0 + p2off<0>(v.gn, b_row[r]) + p2off<1>(v.gk, b_col[r]);
+            }
         }
     }
 };
 
-template <int JOIN, int AGG, typename T, typename TO, bool AK, bool BKM>
+template <int JOIN, int AGG, typename T, typename TO, bool AK, bool BKM, bool RAG>
 __global__ __launch_bounds__(VT_THREADS) void k_valu_tile(GemmView v, const T *__restrict__ x,
                                                          const T *__restrict__ y, TO *__restrict__ z,
-                                                         T *__restrict__ ws, const uint32_t *__restrict__ gate)
+                                                         T *__restrict__ ws, const uint32_t *__restrict__ gate,
+                                                         RaggedMN rag)
 {
     using A = T;
     // int32 max-plus / min-plus runs after the packed 16-bit kernel, and only
-    // where the range check found an input it cannot represent
-    if constexpr (small_int_join<JOIN, AGG, T>()) {
+    // where the range check found an input it cannot represent (ragged plans
+    // have no packed path)
+    if constexpr (small_int_join<JOIN, AGG, T>() && !RAG) {
         if (!gate_open(gate, false)) return;
     }
     constexpr int BM = VT_BM, BN = VT_BN, BK = VT_BK;
@@ -307,7 +348,7 @@ __global__ __launch_bounds__(VT_THREADS) void k_valu_tile(GemmView v, const T *_
     const uint32_t kend = kbeg + (uint32_t)v.k_per_split;
 
     VtLoad<AK, BKM> ld;
-    ld.init(v, m0, n0, bx, by, tid);
+    ld.template init<RAG>(v, m0, n0, bx, by, tid, &rag);
     const int32_t *a_off = ld.a_off, *b_off = ld.b_off;
     const int *a_row = ld.a_row, *a_col = ld.a_col, *b_row = ld.b_row, *b_col = ld.b_col;
 
@@ -376,7 +417,7 @@ __global__ __launch_bounds__(VT_THREADS) void k_valu_tile(GemmView v, const T *_
         }
     }
 
-    vt_store<A, TO>(v, acc, z, ws, m0, n0, bz, tx, ty);
+    vt_store<A, TO, RAG>(v, acc, z, ws, m0, n0, bz, tx, ty, &rag);
 }
 
 // Packed 16-bit int32 max-plus / min-plus (see above).  The same 128x128 tile,
@@ -545,26 +586,35 @@ static int launch_vt(const tra_plan_s &p, const void *x, const void *y, void *z,
     dim3 grid((v.gm.total / VT_BM) * (v.gn.total / VT_BN), v.gb.total, v.split);
     const uint32_t *gate = nullptr;
     if constexpr (small_int_join<JOIN, AGG, T>()) {
-        uint32_t *flags = (uint32_t *)((char *)ws + small_int_flags_offset(v.split, p.info.z_elems));
-        hipLaunchKernelGGL(k_small_int_check, dim3(SI_FLAGS), dim3(SI_CHECK_THREADS), 0, s, (const int32_t *)x,
-                           p.info.x_elems, (const int32_t *)y, p.info.y_elems, flags);
+        if (!p.ragged) {
+            uint32_t *flags = (uint32_t *)((char *)ws + small_int_flags_offset(v.split, p.info.z_elems));
+            hipLaunchKernelGGL(k_small_int_check, dim3(SI_FLAGS), dim3(SI_CHECK_THREADS), 0, s, (const int32_t *)x,
+                               p.info.x_elems, (const int32_t *)y, p.info.y_elems, flags);
 #define TRA_H16(AK, BKM)                                                                                 \
     hipLaunchKernelGGL((k_valu_tile_h16<AGG, AK, BKM>), grid, dim3(VT_THREADS), 0, s, v, (const int32_t *)x, \
                        (const int32_t *)y, (int32_t *)z, (int32_t *)ws, (const uint32_t *)flags)
-        if (p.a_kmajor && p.b_kmajor) TRA_H16(true, true);
-        else if (p.a_kmajor) TRA_H16(true, false);
-        else if (p.b_kmajor) TRA_H16(false, true);
-        else TRA_H16(false, false);
+            if (p.a_kmajor && p.b_kmajor) TRA_H16(true, true);
+            else if (p.a_kmajor) TRA_H16(true, false);
+            else if (p.b_kmajor) TRA_H16(false, true);
+            else TRA_H16(false, false);
 #undef TRA_H16
-        gate = flags;
+            gate = flags;
+        }
     }
-#define TRA_VT(AK, BKM)                                                                                  \
-    hipLaunchKernelGGL((k_valu_tile<JOIN, AGG, T, TO, AK, BKM>), grid, dim3(VT_THREADS), 0, s, v,       \
-                       (const T *)x, (const T *)y, (TO *)z, (T *)ws, gate)
-    if (p.a_kmajor && p.b_kmajor) TRA_VT(true, true);
-    else if (p.a_kmajor) TRA_VT(true, false);
-    else if (p.b_kmajor) TRA_VT(false, true);
-    else TRA_VT(false, false);
+#define TRA_VT(AK, BKM, RAG)                                                                             \
+    hipLaunchKernelGGL((k_valu_tile<JOIN, AGG, T, TO, AK, BKM, RAG>), grid, dim3(VT_THREADS), 0, s, v,  \
+                       (const T *)x, (const T *)y, (TO *)z, (T *)ws, gate, p.rag)
+    if (p.ragged) {
+        if (p.a_kmajor && p.b_kmajor) TRA_VT(true, true, true);
+        else if (p.a_kmajor) TRA_VT(true, false, true);
+        else if (p.b_kmajor) TRA_VT(false, true, true);
+        else TRA_VT(false, false, true);
+    } else {
+        if (p.a_kmajor && p.b_kmajor) TRA_VT(true, true, false);
+        else if (p.a_kmajor) TRA_VT(true, false, false);
+        else if (p.b_kmajor) TRA_VT(false, true, false);
+        else TRA_VT(false, false, false);
+    }
 #undef TRA_VT
     int err = (int)hipGetLastError();
     if (err || v.split == 1) return err;

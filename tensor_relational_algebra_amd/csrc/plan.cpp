@@ -226,6 +226,9 @@ static void tile_groups(const tra_plan_s &p, std::string &M, std::string &N, std
     }
 }
 
+// k-tile depth of the vector-ALU tile kernel (masked edge tiles need whole k-tiles)
+constexpr int64_t VT_BK_RAGGED = 32;
+
 static bool lower_tile(tra_plan_s &p)
 {
     if (p.n_ops != 2) return false;
@@ -243,8 +246,8 @@ static bool lower_tile(tra_plan_s &p)
     auto sm = group_subdims(M, p.B, p.d, tm), sn = group_subdims(N, p.B, p.d, tn);
     auto sk = group_subdims(K, p.B, p.d, tk), sb = group_subdims(Bt, p.B, p.d, tb);
     GemmView gv{};
-    if (!to_pow2(sm, gv.gm) || !to_pow2(sn, gv.gn) || !to_pow2(sk, gv.gk) || !to_pow2(sb, gv.gb))
-        return false;
+    const bool pm = to_pow2(sm, gv.gm), pn = to_pow2(sn, gv.gn);
+    if (!to_pow2(sk, gv.gk) || !to_pow2(sb, gv.gb)) return false;
     gv.post_scale = p.post_scale;
     gv.z_elems = p.info.z_elems;
     const bool mfma = p.join == J_MUL && p.agg == A_SUM && p.in_dtype == D_BF16;
@@ -267,7 +270,7 @@ static bool lower_tile(tra_plan_s &p)
     else return false;
     // pick the first tile variant, in order of preference, that divides the problem
     static const int kMfmaOrder[] = {TRA_MFMA_ORDER};
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < 4 && pm && pn; ++n) {
         const int variant = mfma ? kMfmaOrder[n] : n;
         TileShape ts = mfma ? mfma_tile_shape(variant) : valu_tile_shape(variant);
         if (ts.bm == 0) break;
@@ -285,6 +288,34 @@ static bool lower_tile(tra_plan_s &p)
             p.tile = 1;
             p.info.workspace_bytes = small_int_flags_offset(p.gv.split, p.info.z_elems) + SMALL_INT_FLAG_BYTES;
         }
+        return true;
+    }
+    // Masked edge tiles (vector-ALU joins): output rows and columns of any
+    // extent and digit structure, addressed by mixed radix, the last tile row
+    // and column partly out of range; the contracted range keeps whole
+    // power-of-two k-tiles, so every term of every output is a real one.
+    if (!mfma && gv.gk.total % VT_BK_RAGGED == 0) {
+        int64_t M = 1, N = 1;
+        for (auto &d : sm) M *= d.ext;
+        for (auto &d : sn) N *= d.ext;
+        if (M < 4 || N < 4 || M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31)) return false;
+        TileShape ts = valu_tile_shape(0);
+        gv.gm = Pow2Group{};
+        gv.gn = Pow2Group{};
+        gv.gm.total = (uint32_t)((M + ts.bm - 1) / ts.bm * ts.bm);
+        gv.gn.total = (uint32_t)((N + ts.bn - 1) / ts.bn * ts.bn);
+        p.gv = gv;
+        p.tile = 0;
+        p.a_kmajor = ak;
+        p.b_kmajor = bk;
+        p.ragged = true;
+        p.rag.m = to_radix(sm);
+        p.rag.n = to_radix(sn);
+        p.rag.M = (uint32_t)M;
+        p.rag.N = (uint32_t)N;
+        p.kernel = TRA_KERNEL_VALU_TILE;
+        int64_t tiles = (int64_t)(gv.gm.total / ts.bm) * (gv.gn.total / ts.bn) * gv.gb.total;
+        choose_split(p, tiles, gv.gk.total / ts.bk, ts.bk);
         return true;
     }
     return false;

@@ -24,6 +24,8 @@ struct tra_plan_s {
     int tile = 0;              // tile-kernel variant index
     bool a_kmajor = true;      // X contiguous along K (else along M)
     bool b_kmajor = true;      // Y contiguous along K (else along N)
+    bool ragged = false;       // vector-ALU tiles with masked edges (rag below)
+    tra::RaggedMN rag{};
 };
 
 namespace tra {

@@ -80,6 +80,15 @@ struct GemmView {
     float post_scale;
 };
 
+// Output row / column groups of a tile plan whose extents no tile divides or
+// whose sub-dimensions are not all powers of two (vector-ALU tile kernel
+// only): mixed-radix digits with strides {X, Z} for m and {Y, Z} for n, and
+// the true extents; the GemmView's gm / gn then carry only the padded totals.
+struct RaggedMN {
+    Radix m, n;
+    uint32_t M, N;
+};
+
 // Row reduction: one wavefront per output element; `out` as in GenericDesc;
 // `outer` = contracted sub-dims except the last, `inner` = extent and X/Y
 // strides of the last contracted sub-dim (X stride 1).

@@ -502,3 +502,41 @@ def test_few_outputs_long_contracted_range(case):
     a, _ = run_gpu(c, xs)
     b, _ = run_gpu(c, xs)
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ masked edge tiles (ragged extents)
+
+RAGGED_TILE_CASES = [
+    # (name, spec, bounds, d, join, agg, dtype)
+    ("sqdist_300x64x260", "ij,jk->ik", {"i": 300, "j": 64, "k": 260}, {"i": 1, "j": 1, "k": 1}, "sqdiff", "sum", "f32"),
+    ("maxplus_300x64x260", "ij,jk->ik", {"i": 300, "j": 64, "k": 260}, {"i": 1, "j": 1, "k": 1}, "add", "max", "i32"),
+    ("matmul_int_blocked", "ij,jk->ik", {"i": 300, "j": 64, "k": 260}, {"i": 3, "j": 2, "k": 1}, "mul", "sum", "i32"),
+    ("sqdist_mn_major_blocked", "ji,jk->ik", {"i": 644, "j": 128, "k": 1000}, {"i": 7, "j": 4, "k": 5},
+     "sqdiff", "sum", "f32"),
+    ("matmul_k_major_split", "ij,kj->ik", {"i": 1000, "j": 512, "k": 100}, {"i": 5, "j": 2, "k": 1}, "mul", "sum",
+     "f32"),
+    ("minplus_narrow", "ij,kj->ik", {"i": 130, "j": 32, "k": 4}, {"i": 1, "j": 1, "k": 1}, "add", "min", "f32"),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED_TILE_CASES, ids=[c[0] for c in RAGGED_TILE_CASES])
+def test_ragged_extents_on_the_tile_kernel(case):
+    """Output extents no tile divides, and relation blocks that are not powers
+    of two, stay on the vector-ALU tile kernel: the last tile row and column
+    read clamped rows and drop them at the store.  Every output against the
+    oracle (integers exact)."""
+    name, spec, bounds, d, join, agg, dt = case
+    dist = ("int", {"lo": -1000, "hi": 1000}) if dt == "i32" and join == "add" else \
+        (("int", {"lo": -8, "hi": 8}) if dt == "i32" else ("normal", {"std": 1.0}))
+    c = wl.EinsumCase(name, 340 + RAGGED_TILE_CASES.index(case), spec, bounds, d, join, agg, dt, dt, (dist, dist))
+    err, plan = check(c)
+    assert plan.kernel == "valu_tile", plan.kernel
+
+
+@pytest.mark.parametrize("base", [wl.SQDIST, wl.MAXPLUS], ids=["sqdist", "maxplus"])
+def test_ragged_full_size_8000(base):
+    """8000 x 256 x 8000 under d = [16,1,1,16] (relation blocks of 500 rows and
+    columns) on the tile kernel, sampled outputs against the oracle."""
+    c = base.scaled({"i": 8000, "j": 256, "k": 8000}, base.d)
+    err, plan = check(c, sample=1 << 16, seed=8)
+    assert plan.kernel == "valu_tile"
