@@ -392,7 +392,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(BF16_MFMA_PEAK / 1e12, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": "k_mfma_bf16", "launch_ms": round(gemm_ms, 4),
+                     "kernel": "k_mfma4_bf16" if plan.info.tile == 3 else "k_mfma_bf16", "launch_ms": round(gemm_ms, 4),
                      "flop_per_launch": flops,
                      # algorithmic bytes: X and A read once, Y written once
                      "algorithmic_bytes": (B["i"] * B["j"] + B["j"] * B["k"]) * 2 + B["i"] * B["k"] * 4},
@@ -695,6 +695,9 @@ def _mha_backward(tra, wl, dev, stream, fuse=True):
     else:
         # dScores runs chained with dAttn_c: reads dAttn (fp32) and Attn (bf16), writes bf16
         sbytes = {"dScores": 8 * hst}
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
     reps = 5
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
     for r in range(reps):
