@@ -239,14 +239,21 @@ def _events_time_flushed(fn, reps: int, stream, scratch) -> float:
 
 def _measured_roofs(tra, dev, stream) -> dict:
     """The machine's own ceilings beside the published ones: back-to-back bf16
-    matrix-core products on register operands (four waves per SIMD), and a
-    1 GiB same-blocking copy through tra_repartition."""
+    matrix-core products on register operands (one wave per SIMD), once with
+    one operand pair and once with random operands that change from product
+    to product as in a real product, and a 1 GiB same-blocking copy through
+    tra_repartition."""
     import torch
     wg, iters = 1024, 20000
     out = torch.empty(wg * 256, dtype=torch.float32, device=dev)
-    tra.tra_probe_mfma_loop(wg, 100, out)
-    ms = _events_time(lambda: tra.tra_probe_mfma_loop(wg, iters, out), 3, stream)
     fl = 2.0 * 32 * 32 * 16 * 8 * 4 * iters * wg
+    loops = {}
+    for key, distinct in (("mfma_loop", False), ("mfma_loop_random_operands", True)):
+        tra.tra_probe_mfma_loop(wg, 100, out, distinct)
+        ms = _events_time(lambda: tra.tra_probe_mfma_loop(wg, iters, out, distinct), 3, stream)
+        loops[key] = {"TFLOP/s": round(fl / ms / 1e9, 1), "frac_of_published": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4),
+                      "what": f"{wg} workgroups x 4 waves, {iters} rounds of 8 independent 32x32x16 bf16 products"
+                              + (", 8 random operand pairs" if distinct else ", one operand pair")}
     n = 1 << 28
     src = torch.zeros(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -254,8 +261,7 @@ def _measured_roofs(tra, dev, stream) -> dict:
     cp = lambda: tra.tra_repartition(src, shape, [1, 1], [1, 1], dst)
     cp()
     cms = _events_time(cp, 5, stream)
-    return {"mfma_loop": {"TFLOP/s": round(fl / ms / 1e9, 1), "frac_of_published": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4),
-                          "what": f"{wg} workgroups x 4 waves, {iters} rounds of 8 independent 32x32x16 bf16 products"},
+    return {**loops,
             "copy": {"GB/s": round(2.0 * n * 4 / cms / 1e6, 1), "frac_of_published": round(2.0 * n * 4 / (cms * 1e-3) / HBM_PEAK, 4),
                      "what": "1 GiB read + 1 GiB written, tra_repartition between identical blockings"}}
 

@@ -535,10 +535,15 @@ int tra_graph_destroy(tra_graph_t graph);
  * waves each run `iters` rounds of 8 independent bf16 32x32x16 matrix-core
  * products on register operands (2 * 32 * 32 * 16 * 8 * 4 flop per round and
  * workgroup), the ceiling the tile kernels are held against beside the
- * published peak.  out: device buffer of workgroups * 256 floats (written,
- * values meaningless).  Errors: TRA_E_NULL, TRA_E_OP (counts < 1), TRA_E_HIP.
+ * published peak.  distinct_operands = 0: all 8 products take one operand
+ * pair; otherwise each takes its own random values (of the size of the
+ * products' N(0, 0.02) inputs), so the multipliers switch operands from one
+ * product to the next as in a real product, and the chip's power limit sets
+ * the clock as it does there.  out: device buffer of workgroups * 256 floats
+ * (written, values meaningless).  Errors: TRA_E_NULL, TRA_E_OP (counts < 1),
+ * TRA_E_HIP.
  */
-int tra_probe_mfma_loop(int workgroups, int iters, float *out, void *hip_stream);
+int tra_probe_mfma_loop(int workgroups, int iters, int distinct_operands, float *out, void *hip_stream);
 
 /* Text of a status code (static storage). */
 const char *tra_status_string(int status);

@@ -58,7 +58,7 @@ def lib() -> ctypes.CDLL:
             "tra_plan_destroy": ([P], I),
             "tra_execute": ([P, P, P, P, P, ctypes.c_size_t, P], I),
             "tra_execute_static": ([P, P, P, P, P], I),
-            "tra_probe_mfma_loop": ([I, I, P, P], I),
+            "tra_probe_mfma_loop": ([I, I, I, P, P], I),
             "tra_static_scratch_bytes": ([], ctypes.c_size_t),
             "tra_execute_chain": ([P, P, P, P, P, P, P], I),
             "tra_execute_contract_chain": ([P, P, P, P, P, P, P, P, P], I),
@@ -220,10 +220,12 @@ def tra_execute_static(plan: Plan, x: torch.Tensor, y: Optional[torch.Tensor], z
     return z
 
 
-def tra_probe_mfma_loop(workgroups: int, iters: int, out: torch.Tensor, stream=None) -> None:
+def tra_probe_mfma_loop(workgroups: int, iters: int, out: torch.Tensor, distinct_operands: bool = False,
+                        stream=None) -> None:
     """Matrix-core loop for the measured ceiling (see include/tra.h)."""
     _dev_ptr(out, "out", workgroups * 256, DTYPES["f32"])
-    _check(lib().tra_probe_mfma_loop(int(workgroups), int(iters), out.data_ptr(), _stream(stream)))
+    _check(lib().tra_probe_mfma_loop(int(workgroups), int(iters), int(bool(distinct_operands)), out.data_ptr(),
+                                     _stream(stream)))
 
 
 def tra_static_scratch_bytes() -> int:

@@ -17,10 +17,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 // float -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    // both results formed and one selected, so that unrolled callers stay
+    // free of branches
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t nan = (u >> 16) | 0x40u;
+    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? nan : rne);
 }
 
 template <typename T> struct Scalar;

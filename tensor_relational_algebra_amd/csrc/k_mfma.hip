@@ -24,6 +24,7 @@
 // a matmul) runs on the same kernel.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <type_traits>
 #include <utility>
 
@@ -500,6 +501,33 @@ __device__ __forceinline__ void lds_wait()
     asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
 }
 
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read8_at(uint32_t addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "LDS immediate offset");
+    u32x2_t v;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ void ds_write4_at(uint32_t addr, uint32_t val)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "LDS immediate offset");
+    asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(addr), "v"(val), "i"(OFF) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void ds_write2_at(uint32_t addr, uint32_t val)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "LDS immediate offset");
+    asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(addr), "v"(val), "i"(OFF) : "memory");
+}
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // One operand's fragments of one 16-deep k-step: KM ? one 16-byte read per
 // block : two 8-byte transposing reads per block.
 template <bool KM, int T>
@@ -601,14 +629,88 @@ struct FragAddr4 {
     }
 };
 
-template <bool AKM, bool BKM, typename TO, int STAGES>
+// Epilogue of the four-wave tile through LDS, for outputs whose four
+// consecutive columns are one aligned vector: the tile goes out in two halves
+// of 128 rows; each wave writes its accumulators of the half into a row-major
+// staging tile (rows 0-63 of the half in the freed stages of the first
+// operand, rows 64-127 in those of the second), and after a barrier copies 32
+// whole rows of it to memory, one 16-byte (fp32) or 8-byte (bf16) vector per
+// lane, so that every store instruction writes one contiguous row of the
+// tile.  Values and rounding are those of the direct epilogue.
+template <typename T, bool SCALE>
+__device__ __forceinline__ void mfma4_store_staged(const GemmView &v, T *__restrict__ out,
+                                                   const floatx16_t (&acc)[mf4::TM][mf4::TN], uint32_t st_a,
+                                                   uint32_t st_b, uint32_t m0, uint32_t n0, int32_t bz, int wave,
+                                                   int lane)
+{
+    using namespace mf4;
+    constexpr int ES = sizeof(T);
+    constexpr int RB = BN * ES;   // bytes of one staged row
+    const int wm = wave / WN, wn = wave % WN;
+    // Block ii of the half (rows ii*64 .. +63) goes to st_a (ii = 0) or st_b
+    // (ii = 1); within it, the lane's row is wm*32 + 4*(lane/32) + 8q + r and
+    // its column (j*2 + wn)*32 + lane%32.
+    const uint32_t wl = (uint32_t)(((wm * 32 + 4 * (lane >> 5)) * BN + wn * 32 + (lane & 31)) * ES);
+    const uint32_t wb[2] = {st_a + wl, st_b + wl};
+    // read base: rows (wave%2)*32 .. +31 of block wave/2, columns 4*lane .. +3
+    const uint32_t rb = (wave < 2 ? st_a : st_b) + (uint32_t)(((wave & 1) * 32 * BN + 4 * lane) * ES);
+    const int32_t on = p2off<1>(v.gn, n0 + 4 * lane);
+    // lane r < 32 holds the Z offset of row r of a 32-row band
+    const int32_t band_row = p2off<1>(v.gm, lane & 31);
+    const float sc = SCALE ? v.post_scale : 1.f;
+    sfor<2>([&](auto PH) {
+        constexpr int ph = decltype(PH)::value;
+        if constexpr (ph == 1) lds_barrier();   // every wave done reading the first half
+        sfor<2 * TN * 16>([&](auto W) {
+            constexpr int w = decltype(W)::value;
+            constexpr int ii = w / (TN * 16), j = (w / 16) % TN, q = (w / 4) % 4, r = w % 4;
+            constexpr int off = ((8 * q + r) * BN + j * WN * 32) * ES;
+            const float val = acc[2 * ph + ii][j][4 * q + r] * sc;
+            if constexpr (ES == 4) ds_write4_at<off>(wb[ii], __builtin_bit_cast(uint32_t, val));
+            else ds_write2_at<off>(wb[ii], (uint32_t)f32_to_bf16(val));
+        });
+        lds_wait<0>();
+        lds_barrier();
+        // 32 rows of this wave, 8 at a time: reads, one wait, stores
+        const int32_t rowbase = p2off<1>(v.gm, m0 + ph * 128 + wave * 32) + bz;
+        sfor<4>([&](auto G) {
+            constexpr int g = decltype(G)::value;
+            if constexpr (ES == 4) {
+                u32x4_t d[8];
+                sfor<8>([&](auto R) { d[R] = ds_read16_at<(8 * g + decltype(R)::value) * RB>(rb); });
+                lds_wait<0>();
+                sfor<8>([&](auto R) {
+                    constexpr int rr = 8 * g + decltype(R)::value;
+                    lds_ready(d[R]);
+                    const int32_t o = rowbase + __builtin_amdgcn_readlane(band_row, rr) + on;
+                    *(u32x4_t *)(out + o) = d[R];
+                });
+            } else {
+                u32x2_t d[8];
+                sfor<8>([&](auto R) { d[R] = ds_read8_at<(8 * g + decltype(R)::value) * RB>(rb); });
+                lds_wait<0>();
+                sfor<8>([&](auto R) {
+                    constexpr int rr = 8 * g + decltype(R)::value;
+                    lds_ready(d[R]);
+                    const int32_t o = rowbase + __builtin_amdgcn_readlane(band_row, rr) + on;
+                    *(u32x2_t *)(out + o) = d[R];
+                });
+            }
+        });
+    });
+}
+
+template <bool AKM, bool BKM, typename TO, int STAGES, bool VEC>
 __device__ __forceinline__ void mfma4_body(const GemmView &v, const uint16_t *__restrict__ x,
                                            const uint16_t *__restrict__ y, TO *__restrict__ z,
                                            float *__restrict__ ws)
 {
     using namespace mf4;
+    // the operand stages (the epilogue reuses them as a staging tile)
     __shared__ __attribute__((aligned(16))) uint16_t sa[STAGES * BM * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sb[STAGES * BN * BK];
+    static_assert(STAGES * BM * BK * 2 >= 64 * BN * 4 && STAGES * BN * BK * 2 >= 64 * BN * 4,
+                  "each operand's stages hold 64 staged rows");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -795,6 +897,12 @@ __device__ __forceinline__ void mfma4_body(const GemmView &v, const uint16_t *__
     // 8*(e/4) + 4*(l/32) + e%4 and column l%32 of its 32x32 block.
     const bool split = v.split > 1;
     float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
+    if constexpr (VEC) {
+        lds_barrier();   // every wave past its last read of the operand stages
+        if (split) mfma4_store_staged<float, false>(v, wsp, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
+        else mfma4_store_staged<TO, true>(v, z, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
+        return;
+    }
     const int32_t zm0 = p2off<1>(v.gm, m0) + bz, zn0 = p2off<1>(v.gn, n0);
     int32_t lo[4];
 #pragma unroll
@@ -819,12 +927,14 @@ __device__ __forceinline__ void mfma4_body(const GemmView &v, const uint16_t *__
     }
 }
 
-template <bool AKM, bool BKM, typename TO>
+// VEC: the staged epilogue (the output's four consecutive columns form one
+// aligned vector, and z / the workspace are 16-byte aligned)
+template <bool AKM, bool BKM, typename TO, bool VEC>
 __global__ __launch_bounds__(mf4::NT) void k_mfma4_bf16(GemmView v, const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ y, TO *__restrict__ z,
                                                         float *__restrict__ ws)
 {
-    mfma4_body<AKM, BKM, TO, TRA_MFMA4_STAGES>(v, x, y, z, ws);
+    mfma4_body<AKM, BKM, TO, TRA_MFMA4_STAGES, VEC>(v, x, y, z, ws);
 }
 
 template <int V, bool AKM, bool BKM, typename TO>
@@ -861,7 +971,10 @@ TRA_MFMA_INST4(2, bf16_t)
 #undef TRA_MFMA_INST4
 #undef TRA_MFMA_INST
 #define TRA_MFMA4_INST(AKM, BKM, TO)                                                                          \
-    template __global__ void k_mfma4_bf16<AKM, BKM, TO>(GemmView, const uint16_t *, const uint16_t *, TO *, float *);
+    template __global__ void k_mfma4_bf16<AKM, BKM, TO, false>(GemmView, const uint16_t *, const uint16_t *, TO *,  \
+                                                               float *);                                           \
+    template __global__ void k_mfma4_bf16<AKM, BKM, TO, true>(GemmView, const uint16_t *, const uint16_t *, TO *,   \
+                                                              float *);
 TRA_MFMA4_INST(true, true, float)
 TRA_MFMA4_INST(true, false, float)
 TRA_MFMA4_INST(false, true, float)
@@ -889,12 +1002,27 @@ static int launch_v(const tra_plan_s &p, const void *x, const void *y, void *z, 
     return (int)hipGetLastError();
 }
 
+// TRA_MFMA4_VEC_EPILOGUE=0 keeps the direct epilogue everywhere (for A/B runs)
+static bool vec_epilogue_enabled()
+{
+    static const bool on = [] {
+        const char *e = getenv("TRA_MFMA4_VEC_EPILOGUE");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
 template <bool AKM, bool BKM, typename TO>
 static int launch4(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, hipStream_t s)
 {
     const GemmView &v = p.gv;
     dim3 grid((v.gm.total / mf4::BM) * (v.gn.total / mf4::BN), v.gb.total, v.split);
-    void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *) = k_mfma4_bf16<AKM, BKM, TO>;
+    // the staged epilogue when the output's column vectors are aligned in
+    // memory (z for a plain product, the workspace for a split)
+    const void *out = v.split > 1 ? ws : z;
+    const bool vec = v.z_vec4 && ((uintptr_t)out % 16) == 0 && vec_epilogue_enabled();
+    void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *) =
+        vec ? k_mfma4_bf16<AKM, BKM, TO, true> : k_mfma4_bf16<AKM, BKM, TO, false>;
     hipLaunchKernelGGL(kern, grid, dim3(mf4::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z,
                        (float *)ws);
     return (int)hipGetLastError();

@@ -13,16 +13,43 @@ typedef float floatx16_p __attribute__((ext_vector_type(16)));
 
 // Four waves per workgroup, one per SIMD; each wave runs `iters` rounds of 8
 // independent 32x32x16 products (8 accumulator sets, so no product waits on
-// the one before it), from operands that stay in registers.
+// the one before it), from operands that stay in registers.  DISTINCT: each
+// of the 8 products has operands of its own, random bf16 values of the size
+// of N(0, 0.02) inputs, different in every lane, so consecutive products
+// switch operands as they do in a real product (the multipliers toggle, and
+// the clock the chip holds under that load is lower); otherwise all 8 take
+// one operand pair.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x)
+{
+    // a 32-bit integer mixer (multiply / xor-shift rounds)
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+template <bool DISTINCT>
 __global__ __launch_bounds__(256) void k_probe_mfma(int iters, float seed, float *__restrict__ out)
 {
     const int lane = threadIdx.x & 63;
-    bf16x8_p a, b;
+    constexpr int NP = DISTINCT ? 8 : 1;
+    bf16x8_p a[NP], b[NP];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a[e] = (__bf16)(seed * (float)(lane + e));
-        b[e] = (__bf16)(seed * (float)(lane - e));
-    }
+    for (int s = 0; s < NP; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (DISTINCT) {
+                const uint32_t h = probe_hash((uint32_t)(((blockIdx.x * 256 + threadIdx.x) * 8 + s) * 8 + e));
+                // two uniform values in [-0.05, 0.05) per hash
+                a[s][e] = (__bf16)(((float)(h & 0xffffu) / 65536.f - 0.5f) * 0.1f);
+                b[s][e] = (__bf16)(((float)(h >> 16) / 65536.f - 0.5f) * 0.1f);
+            } else {
+                a[s][e] = (__bf16)(seed * (float)(lane + e));
+                b[s][e] = (__bf16)(seed * (float)(lane - e));
+            }
+        }
     floatx16_p acc[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
@@ -30,7 +57,8 @@ __global__ __launch_bounds__(256) void k_probe_mfma(int iters, float seed, float
         for (int e = 0; e < 16; ++e) acc[s][e] = 0.f;
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[s], 0, 0, 0);
+        for (int s = 0; s < 8; ++s)
+            acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s % NP], b[s % NP], acc[s], 0, 0, 0);
     }
     float r = 0.f;
 #pragma unroll
@@ -42,11 +70,15 @@ __global__ __launch_bounds__(256) void k_probe_mfma(int iters, float seed, float
 
 }  // namespace tra
 
-extern "C" int tra_probe_mfma_loop(int workgroups, int iters, float *out, void *hip_stream)
+extern "C" int tra_probe_mfma_loop(int workgroups, int iters, int distinct_operands, float *out, void *hip_stream)
 {
     if (!out) return TRA_E_NULL;
     if (workgroups < 1 || iters < 1) return TRA_E_OP;
-    hipLaunchKernelGGL(tra::k_probe_mfma, dim3(workgroups), dim3(256), 0, (hipStream_t)hip_stream, iters, 1.0f / 64,
-                       out);
+    if (distinct_operands)
+        hipLaunchKernelGGL(tra::k_probe_mfma<true>, dim3(workgroups), dim3(256), 0, (hipStream_t)hip_stream, iters,
+                           1.0f / 64, out);
+    else
+        hipLaunchKernelGGL(tra::k_probe_mfma<false>, dim3(workgroups), dim3(256), 0, (hipStream_t)hip_stream, iters,
+                           1.0f / 64, out);
     return hipGetLastError() == hipSuccess ? TRA_OK : TRA_E_HIP;
 }

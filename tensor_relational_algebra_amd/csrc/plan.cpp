@@ -226,6 +226,29 @@ static void tile_groups(const tra_plan_s &p, std::string &M, std::string &N, std
     }
 }
 
+// Z's four consecutive output columns, from a multiple of 4, are one aligned
+// vector: the column group's lowest digit has Z stride 1 and covers at least
+// two bits, and every other Z stride (rows, the other column digits, the
+// batch) is a multiple of 4 elements.
+static bool z_vec4(const GemmView &gv)
+{
+    bool low = false;
+    for (int i = 0; i < kP2Max; ++i) {
+        if (!gv.gn.mask[i]) continue;
+        if (gv.gn.sh[i] == 0) {
+            if (gv.gn.st[1][i] != 1 || gv.gn.mask[i] < 3) return false;
+            low = true;
+        } else if (gv.gn.st[1][i] % 4) {
+            return false;
+        }
+    }
+    for (int i = 0; i < kP2Max; ++i) {
+        if (gv.gm.mask[i] && gv.gm.st[1][i] % 4) return false;
+        if (gv.gb.mask[i] && gv.gb.st[2][i] % 4) return false;
+    }
+    return low;
+}
+
 // k-tile depth of the vector-ALU tile kernel (masked edge tiles need whole k-tiles)
 constexpr int64_t VT_BK_RAGGED = 32;
 
@@ -276,6 +299,7 @@ static bool lower_tile(tra_plan_s &p)
         if (ts.bm == 0) break;
         if (gv.gm.total % ts.bm || gv.gn.total % ts.bn || gv.gk.total % ts.bk) continue;
         p.gv = gv;
+        p.gv.z_vec4 = z_vec4(gv) ? 1 : 0;
         p.tile = variant;
         p.a_kmajor = ak;
         p.b_kmajor = bk;

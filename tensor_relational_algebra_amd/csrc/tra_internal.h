@@ -78,6 +78,8 @@ struct GemmView {
     int32_t k_per_split;    // K extent each of them folds
     int64_t z_elems;        // for the split workspace stride
     float post_scale;
+    int32_t z_vec4;         // four consecutive columns (from a multiple of 4) are contiguous in Z,
+                            // and every other Z stride is a multiple of 4 elements
 };
 
 // Output row / column groups of a tile plan whose extents no tile divides or

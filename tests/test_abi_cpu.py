@@ -168,9 +168,10 @@ def test_cost_matches_hand_worked_values():
 
 def test_probe_argument_errors():
     L = tra.lib()
-    assert L.tra_probe_mfma_loop(0, 1, 0x1000, None) == -7
-    assert L.tra_probe_mfma_loop(1, 0, 0x1000, None) == -7
-    assert L.tra_probe_mfma_loop(1, 1, None, None) == -1
+    for distinct in (0, 1):
+        assert L.tra_probe_mfma_loop(0, 1, distinct, 0x1000, None) == -7
+        assert L.tra_probe_mfma_loop(1, 0, distinct, 0x1000, None) == -7
+        assert L.tra_probe_mfma_loop(1, 1, distinct, None, None) == -1
 
 
 def test_softmax_node_cost_matches_hand_worked_values():
