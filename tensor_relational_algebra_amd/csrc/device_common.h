@@ -14,16 +14,12 @@ struct bf16_t {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f)
-{
-    // both results formed and one selected, so that unrolled callers stay
-    // free of branches
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t nan = (u >> 16) | 0x40u;
-    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? nan : rne);
-}
+// float -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN
+// (sign and top payload bits kept, quiet bit set).  gfx950 converts in one
+// instruction (v_cvt_pk_bf16_f32, two values at a time); its result equals
+// the integer form (u + 0x7fff + bit 16 of u) >> 16, and (u >> 16) | 0x40 for
+// a NaN, on every 32-bit pattern.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <typename T> struct Scalar;
 template <> struct Scalar<float> {
