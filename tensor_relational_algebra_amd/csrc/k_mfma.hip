@@ -631,20 +631,20 @@ struct FragAddr4 {
 
 // Epilogue of the four-wave tile through LDS, for outputs whose four
 // consecutive columns are one aligned vector: the tile goes out in two halves
-// of 128 rows; each wave writes its accumulators of the half into a row-major
-// staging tile (rows 0-63 of the half in the freed stages of the first
-// operand, rows 64-127 in those of the second), and after a barrier copies 32
-// whole rows of it to memory, one 16-byte (fp32) or 8-byte (bf16) vector per
-// lane, so that every store instruction writes one contiguous row of the
-// tile.  Values and rounding are those of the direct epilogue.
-template <typename T, bool SCALE>
-__device__ __forceinline__ void mfma4_store_staged(const GemmView &v, T *__restrict__ out,
-                                                   const floatx16_t (&acc)[mf4::TM][mf4::TN], uint32_t st_a,
-                                                   uint32_t st_b, uint32_t m0, uint32_t n0, int32_t bz, int wave,
-                                                   int lane)
+// of 128 rows; each wave writes its accumulators of the half (times sc, as S)
+// into a row-major staging tile (rows 0-63 of the half in the freed stages of
+// the first operand, rows 64-127 in those of the second), and after a barrier
+// reads back 32 whole rows of it, four consecutive columns per lane, and hands
+// each row to emit(PH, RR, data): half PH, row RR of the wave's 32, data
+// holding columns 4*lane .. 4*lane + 3 of tile row PH*128 + wave*32 + RR.
+// pre(PH) runs at the start of half PH, before its staging writes (loads a
+// caller issues there are in flight during them).
+template <typename S, typename Pre, typename Emit>
+__device__ __forceinline__ void mfma4_staged(const floatx16_t (&acc)[mf4::TM][mf4::TN], uint32_t st_a, uint32_t st_b,
+                                             float sc, int wave, int lane, Pre &&pre, Emit &&emit)
 {
     using namespace mf4;
-    constexpr int ES = sizeof(T);
+    constexpr int ES = sizeof(S);
     constexpr int RB = BN * ES;   // bytes of one staged row
     const int wm = wave / WN, wn = wave % WN;
     // Block ii of the half (rows ii*64 .. +63) goes to st_a (ii = 0) or st_b
@@ -654,13 +654,11 @@ __device__ __forceinline__ void mfma4_store_staged(const GemmView &v, T *__restr
     const uint32_t wb[2] = {st_a + wl, st_b + wl};
     // read base: rows (wave%2)*32 .. +31 of block wave/2, columns 4*lane .. +3
     const uint32_t rb = (wave < 2 ? st_a : st_b) + (uint32_t)(((wave & 1) * 32 * BN + 4 * lane) * ES);
-    const int32_t on = p2off<1>(v.gn, n0 + 4 * lane);
-    // lane r < 32 holds the Z offset of row r of a 32-row band
-    const int32_t band_row = p2off<1>(v.gm, lane & 31);
-    const float sc = SCALE ? v.post_scale : 1.f;
+    using D = typename std::conditional<ES == 4, u32x4_t, u32x2_t>::type;
     sfor<2>([&](auto PH) {
         constexpr int ph = decltype(PH)::value;
         if constexpr (ph == 1) lds_barrier();   // every wave done reading the first half
+        pre(PH);
         sfor<2 * TN * 16>([&](auto W) {
             constexpr int w = decltype(W)::value;
             constexpr int ii = w / (TN * 16), j = (w / 16) % TN, q = (w / 4) % 4, r = w % 4;
@@ -671,39 +669,135 @@ __device__ __forceinline__ void mfma4_store_staged(const GemmView &v, T *__restr
         });
         lds_wait<0>();
         lds_barrier();
-        // 32 rows of this wave, 8 at a time: reads, one wait, stores
-        const int32_t rowbase = p2off<1>(v.gm, m0 + ph * 128 + wave * 32) + bz;
+        // 32 rows of this wave, 8 at a time: reads, one wait, the rows
         sfor<4>([&](auto G) {
             constexpr int g = decltype(G)::value;
-            if constexpr (ES == 4) {
-                u32x4_t d[8];
-                sfor<8>([&](auto R) { d[R] = ds_read16_at<(8 * g + decltype(R)::value) * RB>(rb); });
-                lds_wait<0>();
-                sfor<8>([&](auto R) {
-                    constexpr int rr = 8 * g + decltype(R)::value;
-                    lds_ready(d[R]);
-                    const int32_t o = rowbase + __builtin_amdgcn_readlane(band_row, rr) + on;
-                    *(u32x4_t *)(out + o) = d[R];
-                });
-            } else {
-                u32x2_t d[8];
-                sfor<8>([&](auto R) { d[R] = ds_read8_at<(8 * g + decltype(R)::value) * RB>(rb); });
-                lds_wait<0>();
-                sfor<8>([&](auto R) {
-                    constexpr int rr = 8 * g + decltype(R)::value;
-                    lds_ready(d[R]);
-                    const int32_t o = rowbase + __builtin_amdgcn_readlane(band_row, rr) + on;
-                    *(u32x2_t *)(out + o) = d[R];
-                });
-            }
+            D d[8];
+            sfor<8>([&](auto R) {
+                constexpr int off = (8 * g + decltype(R)::value) * RB;
+                if constexpr (ES == 4) d[R] = ds_read16_at<off>(rb);
+                else d[R] = ds_read8_at<off>(rb);
+            });
+            lds_wait<0>();
+            sfor<8>([&](auto R) {
+                lds_ready(d[R]);
+                emit(PH, std::integral_constant<int, 8 * g + decltype(R)::value>{}, d[R]);
+            });
         });
     });
 }
 
-template <bool AKM, bool BKM, typename TO, int STAGES, bool VEC>
+// The plain staged epilogue: each row goes out as one 16-byte (fp32) or
+// 8-byte (bf16) vector per lane, so that every store instruction writes one
+// contiguous row of the tile.  Values and rounding are those of the direct
+// epilogue.
+template <typename T, bool SCALE>
+__device__ __forceinline__ void mfma4_store_staged(const GemmView &v, T *__restrict__ out,
+                                                   const floatx16_t (&acc)[mf4::TM][mf4::TN], uint32_t st_a,
+                                                   uint32_t st_b, uint32_t m0, uint32_t n0, int32_t bz, int wave,
+                                                   int lane)
+{
+    const int32_t on = p2off<1>(v.gn, n0 + 4 * lane);
+    // lane r < 32 holds the Z offset of row r of a 32-row band
+    const int32_t band_row = p2off<1>(v.gm, lane & 31);
+    int32_t rowbase[2];
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) rowbase[ph] = p2off<1>(v.gm, m0 + ph * 128 + wave * 32) + bz;
+    mfma4_staged<T>(acc, st_a, st_b, SCALE ? v.post_scale : 1.f, wave, lane, [](auto) {}, [&](auto PH, auto RR, const auto &d) {
+        const int32_t o = rowbase[decltype(PH)::value] + __builtin_amdgcn_readlane(band_row, decltype(RR)::value) + on;
+        *(typename std::remove_const<typename std::remove_reference<decltype(d)>::type>::type *)(out + o) = d;
+    });
+}
+
+// The chained epilogue on the staged rows (the product and the two
+// elementwise steps of a ChainEpi, as the eight-wave chain computes them):
+// the product's fp32 value av (times post_scale), t = join_a(av, ya) times
+// scale_a, rounded to TO when TO is bf16, then join_b(xb, t) times scale_b,
+// stored as TO.  xb and the output share the output's layout, so each lane
+// loads and stores its four columns as one vector; the 32 xb vectors of a
+// half are loaded together, before the half is staged.  YROW: ya does not
+// vary along the output's columns; lane r then loads ya of row r of the
+// wave's 32 once per half, and each row takes it by readlane.
+template <typename TO, int CH, bool YROW>
+__device__ __forceinline__ void mfma4_chain_staged(const GemmView &v, TO *__restrict__ out, const ChainEpi &ce,
+                                                   const floatx16_t (&acc)[mf4::TM][mf4::TN], uint32_t st_a,
+                                                   uint32_t st_b, uint32_t m0, uint32_t n0, uint32_t bidx, int32_t bz,
+                                                   int wave, int lane)
+{
+    const int32_t on = p2off<1>(v.gn, n0 + 4 * lane);
+    const int32_t band_row = p2off<1>(v.gm, lane & 31);
+    const int32_t yband_row = p2off<0>(ce.rm, lane & 31);
+    int32_t rowbase[2], yrowbase[2];
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+        rowbase[ph] = p2off<1>(v.gm, m0 + ph * 128 + wave * 32) + bz;
+        yrowbase[ph] = p2off<0>(ce.rb, bidx) + p2off<0>(ce.rm, m0 + ph * 128 + wave * 32);
+    }
+    int32_t ycol[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ycol[c] = YROW ? 0 : p2off<0>(ce.rn, n0 + 4 * lane + c);
+    const float *__restrict__ ya = (const float *)ce.ya;
+    const TO *__restrict__ xb = (const TO *)ce.xb;
+    using XV = typename std::conditional<sizeof(TO) == 4, u32x4_t, u32x2_t>::type;
+    XV xw[32];
+    float yl = 0.f;
+    auto pre = [&](auto PH) {
+        constexpr int ph = decltype(PH)::value;
+        sfor<32>([&](auto RR) {
+            constexpr int rr = decltype(RR)::value;
+            const int32_t o = rowbase[ph] + __builtin_amdgcn_readlane(band_row, rr) + on;
+            xw[rr] = *(const XV *)(xb + o);
+        });
+        if constexpr (YROW) yl = ya[yrowbase[ph] + yband_row];
+    };
+    mfma4_staged<float>(acc, st_a, st_b, v.post_scale, wave, lane, pre, [&](auto PH, auto RR, const u32x4_t &d) {
+        constexpr int ph = decltype(PH)::value, rr = decltype(RR)::value;
+        const int32_t o = rowbase[ph] + __builtin_amdgcn_readlane(band_row, rr) + on;
+        float xv[4];
+        if constexpr (sizeof(TO) == 4) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xv[c] = __uint_as_float((uint32_t)xw[rr][c]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xv[c] = bf16_to_f32((uint16_t)(xw[rr][c / 2] >> (16 * (c % 2))));
+        }
+        float yrow = 0.f;
+        if constexpr (YROW) yrow = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, yl), rr));
+        const int32_t yo = yrowbase[ph] + __builtin_amdgcn_readlane(yband_row, rr);
+        float res[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // (the element is read into a scalar first: a bit cast taken
+            // directly of a vector element reference read element 0)
+            const float av = __uint_as_float((uint32_t)d[c]);
+            const float yv = YROW ? yrow : ya[yo + ycol[c]];
+            float t;
+            if constexpr (CH == 1) t = (av - yv) * ce.scale_a;
+            else t = join_any(ce.join_a, av, yv) * ce.scale_a;
+            if constexpr (std::is_same<TO, bf16_t>::value) t = bf16_to_f32(f32_to_bf16(t));
+            float o4;
+            if constexpr (CH == 1) o4 = xv[c] * t;
+            else o4 = join_any(ce.join_b, xv[c], t);
+            res[c] = o4 * ce.scale_b;
+        }
+        if constexpr (sizeof(TO) == 4) {
+            u32x4_t w = {__builtin_bit_cast(uint32_t, res[0]), __builtin_bit_cast(uint32_t, res[1]),
+                         __builtin_bit_cast(uint32_t, res[2]), __builtin_bit_cast(uint32_t, res[3])};
+            *(u32x4_t *)(out + o) = w;
+        } else {
+            u32x2_t w = {(uint32_t)f32_to_bf16(res[0]) | ((uint32_t)f32_to_bf16(res[1]) << 16),
+                         (uint32_t)f32_to_bf16(res[2]) | ((uint32_t)f32_to_bf16(res[3]) << 16)};
+            *(u32x2_t *)(out + o) = w;
+        }
+    });
+}
+
+// EPI: 0 the direct epilogue, 1 the staged one, 2 the staged chained one
+// (CH, YROW as for mfma4_chain_staged; ce used only then).
+template <bool AKM, bool BKM, typename TO, int STAGES, int EPI, int CH = 0, bool YROW = false>
 __device__ __forceinline__ void mfma4_body(const GemmView &v, const uint16_t *__restrict__ x,
                                            const uint16_t *__restrict__ y, TO *__restrict__ z,
-                                           float *__restrict__ ws)
+                                           float *__restrict__ ws, const ChainEpi &ce)
 {
     using namespace mf4;
     // the operand stages (the epilogue reuses them as a staging tile)
@@ -897,8 +991,12 @@ __device__ __forceinline__ void mfma4_body(const GemmView &v, const uint16_t *__
     // 8*(e/4) + 4*(l/32) + e%4 and column l%32 of its 32x32 block.
     const bool split = v.split > 1;
     float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
-    if constexpr (VEC) {
+    if constexpr (EPI == 2) {
         lds_barrier();   // every wave past its last read of the operand stages
+        mfma4_chain_staged<TO, CH, YROW>(v, z, ce, acc, lds_addr(sa), lds_addr(sb), m0, n0, bidx, bz, wave, lane);
+        return;
+    } else if constexpr (EPI == 1) {
+        lds_barrier();
         if (split) mfma4_store_staged<float, false>(v, wsp, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
         else mfma4_store_staged<TO, true>(v, z, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
         return;
@@ -934,7 +1032,17 @@ __global__ __launch_bounds__(mf4::NT) void k_mfma4_bf16(GemmView v, const uint16
                                                         const uint16_t *__restrict__ y, TO *__restrict__ z,
                                                         float *__restrict__ ws)
 {
-    mfma4_body<AKM, BKM, TO, TRA_MFMA4_STAGES, VEC>(v, x, y, z, ws);
+    mfma4_body<AKM, BKM, TO, TRA_MFMA4_STAGES, VEC ? 1 : 0>(v, x, y, z, ws, ChainEpi{});
+}
+
+// The product with a chain of two elementwise steps in its staged epilogue
+// (tra_execute_contract_chain on the four-wave tile)
+template <bool AKM, bool BKM, typename TO, int CH, bool YROW>
+__global__ __launch_bounds__(mf4::NT) void k_mfma4_chain(GemmView v, const uint16_t *__restrict__ x,
+                                                         const uint16_t *__restrict__ y, TO *__restrict__ z,
+                                                         ChainEpi ce)
+{
+    mfma4_body<AKM, BKM, TO, TRA_MFMA4_STAGES, 2, CH, YROW>(v, x, y, z, nullptr, ce);
 }
 
 template <int V, bool AKM, bool BKM, typename TO>
@@ -984,6 +1092,22 @@ TRA_MFMA4_INST(true, false, bf16_t)
 TRA_MFMA4_INST(false, true, bf16_t)
 TRA_MFMA4_INST(false, false, bf16_t)
 #undef TRA_MFMA4_INST
+#define TRA_MFMA4C_INST(TO, CH, YROW)                                                                       \
+    template __global__ void k_mfma4_chain<true, true, TO, CH, YROW>(GemmView, const uint16_t *,            \
+                                                                     const uint16_t *, TO *, ChainEpi);       \
+    template __global__ void k_mfma4_chain<true, false, TO, CH, YROW>(GemmView, const uint16_t *,           \
+                                                                      const uint16_t *, TO *, ChainEpi);      \
+    template __global__ void k_mfma4_chain<false, true, TO, CH, YROW>(GemmView, const uint16_t *,           \
+                                                                      const uint16_t *, TO *, ChainEpi);      \
+    template __global__ void k_mfma4_chain<false, false, TO, CH, YROW>(GemmView, const uint16_t *,          \
+                                                                       const uint16_t *, TO *, ChainEpi);
+TRA_MFMA4C_INST(float, 0, false)
+TRA_MFMA4C_INST(float, 1, false)
+TRA_MFMA4C_INST(float, 1, true)
+TRA_MFMA4C_INST(bf16_t, 0, false)
+TRA_MFMA4C_INST(bf16_t, 1, false)
+TRA_MFMA4C_INST(bf16_t, 1, true)
+#undef TRA_MFMA4C_INST
 
 
 int launch_split_fold(const tra_plan_s &p, const void *ws, void *z, void *stream);
@@ -1000,6 +1124,16 @@ static int launch_v(const tra_plan_s &p, const void *x, const void *y, void *z, 
     hipLaunchKernelGGL(kern, grid, dim3(C.wm * C.wn * 64), 0, s, v, (const uint16_t *)x, (const uint16_t *)y,
                        (TO *)z, (float *)ws);
     return (int)hipGetLastError();
+}
+
+// TRA_MFMA4_CHAIN=0 keeps the product chain on the eight-wave tile (for A/B runs)
+static bool chain4_enabled()
+{
+    static const bool on = [] {
+        const char *e = getenv("TRA_MFMA4_CHAIN");
+        return !(e && e[0] == '0');
+    }();
+    return on;
 }
 
 // TRA_MFMA4_VEC_EPILOGUE=0 keeps the direct epilogue everywhere (for A/B runs)
@@ -1079,10 +1213,40 @@ static int launch_chain_v(const tra_plan_s &p, const void *x, const void *y, voi
     return (int)hipGetLastError();
 }
 
+// The four-wave chain: output and xb in the output's layout with aligned
+// four-column vectors; YROW when ya is constant along the output's columns.
+template <typename TO>
+static int launch_chain4(const tra_plan_s &p, const void *x, const void *y, void *z, const ChainEpi &ce,
+                         hipStream_t s)
+{
+    const GemmView &v = p.gv;
+    dim3 grid((v.gm.total / mf4::BM) * (v.gn.total / mf4::BN), v.gb.total, 1);
+    bool yrow = true;
+    for (int i = 0; i < kP2Max; ++i)
+        if (ce.rn.mask[i] && ce.rn.st[0][i]) yrow = false;
+    void (*k)(GemmView, const uint16_t *, const uint16_t *, TO *, ChainEpi);
+    const bool ch = ce.join_a == J_SUB && ce.join_b == J_MUL;
+#define TRA_PICK(AK, BK)                                                                                  \
+    k = !ch ? k_mfma4_chain<AK, BK, TO, 0, false>                                                         \
+            : (yrow ? k_mfma4_chain<AK, BK, TO, 1, true> : k_mfma4_chain<AK, BK, TO, 1, false>)
+    if (p.a_kmajor) {
+        if (p.b_kmajor) TRA_PICK(true, true);
+        else TRA_PICK(true, false);
+    } else {
+        if (p.b_kmajor) TRA_PICK(false, true);
+        else TRA_PICK(false, false);
+    }
+#undef TRA_PICK
+    hipLaunchKernelGGL(k, grid, dim3(mf4::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z, ce);
+    return (int)hipGetLastError();
+}
+
 template <typename TO>
 static int launch_chain_t(const tra_plan_s &p, const void *x, const void *y, void *z, const ChainEpi &ce,
                           hipStream_t s)
 {
+    if (p.tile == 3 && p.gv.z_vec4 && (uintptr_t)z % 16 == 0 && (uintptr_t)ce.xb % 16 == 0 && chain4_enabled())
+        return launch_chain4<TO>(p, x, y, z, ce, s);
     switch (p.tile) {
     case 0:
     case 3: return launch_chain_v<0, TO>(p, x, y, z, ce, s);   // the same 256 x 256 tile on eight waves

@@ -421,8 +421,8 @@ def test_execute_chain_matches_two_launches(case):
 
 
 CONTRACT_CHAIN_CASES = [
-    # (product spec, bounds, d, step a (spec, join), chain dtype, step b join); one
-    # 32-deep k-tile each, so that no plan splits its contracted range
+    # (product spec, bounds, d, step a (spec, join), chain dtype, step b join);
+    # enough output tiles that no plan splits its contracted range
     # the attention backward's softmax Jacobian: Attn * (dO.V^T - Rows), dense
     ("shd,thd->hst", {"s": 512, "t": 512, "h": 2, "d": 32}, {"s": 1, "t": 1, "h": 1, "d": 1},
      ("hst,hs->hst", "sub"), "bf16", "mul"),
@@ -435,10 +435,17 @@ CONTRACT_CHAIN_CASES = [
     # a full operand for the first step, a batched product with a K-major Y
     ("bik,bjk->bij", {"b": 4, "i": 256, "j": 256, "k": 32}, {"b": 2, "i": 1, "j": 1, "k": 1},
      ("bij,bij->bij", "mul"), "bf16", "sub"),
+    # the Jacobian over four k-tiles and 128 output tiles of 256 x 256
+    ("shd,thd->hst", {"s": 1024, "t": 1024, "h": 8, "d": 128}, {"s": 1, "t": 1, "h": 1, "d": 1},
+     ("hst,hs->hst", "sub"), "bf16", "mul"),
+    # the Jacobian with an fp32 chain, blocked rows
+    ("shd,thd->hst", {"s": 1024, "t": 1024, "h": 8, "d": 64}, {"s": 2, "t": 1, "h": 1, "d": 1},
+     ("hst,hs->hst", "sub"), "f32", "mul"),
 ]
 
 
-@pytest.mark.parametrize("case", CONTRACT_CHAIN_CASES, ids=["jacobian", "jacobian-blocked", "colvec-f32", "full-op"])
+@pytest.mark.parametrize("case", CONTRACT_CHAIN_CASES, ids=["jacobian", "jacobian-blocked", "colvec-f32", "full-op",
+                                                          "jacobian-4k-tiles", "jacobian-f32"])
 def test_execute_contract_chain_matches_three_launches(case):
     """A matrix-core product with two elementwise steps in its epilogue is
     bit-identical to the product, then the two steps, each launched alone."""
