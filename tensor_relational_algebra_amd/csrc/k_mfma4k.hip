@@ -1,0 +1,392 @@
+// k_mfma4k.hip -- bf16 x bf16 -> fp32 join + sum aggregation on the four-wave
+// 256 x 256 matrix-core tile with 64-deep stages (tile variant 4), for
+// products whose two operands are both stored contiguously along the
+// contracted labels ("K-major").
+//
+// Page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法",
+// section 2.2: the join of a key-matched pair of sub-tensors is a small
+// matrix product when the join is a product and the aggregate a sum, and the
+// aggregation over the contracted keys is a sum of such products.  As in the
+// 32-deep tiles, one workgroup owns one output tile of one output group and
+// folds every contracted partition into the same fp32 accumulators, the
+// contracted keys in ascending order.
+//
+// Why 64-deep stages.  A K-major operand staged 32 deep is copied in 64-byte
+// pieces of each row: half a cache line per row and stage, which the load
+// path moves at about half the bytes per clock of whole lines.  Here each
+// stage holds 64 k of every row, 128 contiguous bytes, so each copy
+// instruction moves 8 whole lines.  LDS holds two such stages per operand
+// (2 x 2 x 32 KiB): the matrix cores consume one while the next is copied.
+//
+// Per 64-deep k-tile and wave: 4 k-steps of 16 products (32x32x16), 32
+// fragment reads of 16 bytes (no transposing reads: both operands are
+// K-major), 16 direct global -> LDS copies.  Fragments are read two k-steps
+// ahead, so each stage is free after its second k-step and the copies of
+// the k-tile two ahead spread over the last two k-steps (issued in one
+// k-step, 64 KiB per CU backed up the load path and stalled the waves'
+// in-order issue).  Each wave owns a 128 x 128 block
+// of the tile (4 x 4 products of 32 x 32, the 256 accumulators of a lane in
+// the accumulator registers), its 32-row blocks interleaved with the other
+// waves' as in the 32-deep four-wave tile, so the epilogues are shared.
+
+#include "mfma_common.h"
+
+// Cache policy of the direct global -> LDS copies (the aux operand of
+// global_load_lds).
+#ifndef TRA_K4K_CPOL
+#define TRA_K4K_CPOL 0
+#endif
+
+namespace tra {
+
+namespace mf4k {
+constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, NT = WM * WN * 64, TM = 4, TN = 4;
+constexpr int STAGE_ELEMS = 256 * BK;           // one operand's stage (32 KiB)
+constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
+constexpr int COPIES = STAGE_ELEMS / 8 / NT;    // 16-byte copies per thread per operand and stage
+}  // namespace mf4k
+
+// 64-deep K-major stage, [row][64 k]: 8 granules of 16 bytes per row, granule
+// c of row r stored at c ^ swz_k8(r).  The fragment reads of a k-step hit one
+// granule column of 32 consecutive rows; the permutation spreads any 8
+// consecutive rows, and the 8 rows of each parity among 16 consecutive ones,
+// over distinct granule slots, so the reads are free of bank conflicts for
+// 128- and 256-byte bank sets alike.
+__device__ __forceinline__ int swz_k8(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Per-thread plan of one operand's copies into a stage: copy i of thread tid
+// moves LDS granule p = i * NT + tid, i.e. row p / 8, slot p % 8, which holds
+// granule (p % 8) ^ swz_k8(row) of that row.  A wave's 64 copies fill 1 KiB
+// of consecutive LDS (8 rows) from 8 whole 128-byte row segments.  T selects
+// the operand's stride slot of the contracted digits (0 = X, 1 = Y).
+template <int T>
+struct DmaPlan8 {
+    static constexpr int N = mf4k::COPIES;
+    int32_t src[N];   // source offset minus the k-tile term
+
+    __device__ __forceinline__ void init(const Pow2Group &g_rows, const Pow2Group &gk, uint32_t r0, int32_t base,
+                                         int tid)
+    {
+        const int32_t rbase = p2off<0>(g_rows, r0) + base;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int p = i * mf4k::NT + tid;
+            const int row = p >> 3, c = (p & 7) ^ swz_k8(p >> 3);
+            src[i] = rbase + p2off<0>(g_rows, row) + p2off<T>(gk, c * 8);
+        }
+    }
+    // copy i alone (i a compile-time constant at every call)
+    __device__ __forceinline__ void issue_one(int i, const uint16_t *__restrict__ g, int32_t koff, uint16_t *stage,
+                                              int wave)
+    {
+        __builtin_amdgcn_global_load_lds(g + src[i] + koff, (lds_void_t *)(stage + (i * mf4k::NT + wave * 64) * 8), 16,
+                                         0, TRA_K4K_CPOL);
+    }
+};
+
+// Per-lane LDS bases of one operand's fragment reads, one per k-step of a
+// stage: block i of k-step ks reads row (i * 2 + w) * 32 + l % 32, granule
+// 2 ks + l / 32.  The permutation depends only on the lane and the wave (not
+// on i), so block i and stage G add the constant i * 8 KiB + G * 32 KiB.
+struct FragAddr8 {
+    uint32_t base[4];
+
+    __device__ __forceinline__ void init(uint32_t lds, int w, int lane)
+    {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int r = w * 32 + (lane & 31);
+            const int c = (2 * ks + (lane >> 5)) ^ swz_k8(r);
+            base[ks] = lds + (uint32_t)(r * mf4k::BK + c * 8) * 2;
+        }
+    }
+    // issue read R (block R) of k-step KS of stage G into f
+    template <int G, int KS, int R, int T>
+    __device__ __forceinline__ void read_one(Frag4<true, T> &f) const
+    {
+        constexpr int off = G * mf4k::STAGE_BYTES + R * 64 * mf4k::BK * 2;
+        f.k[R] = ds_read16_at<off>(base[KS]);
+    }
+    template <int G, int KS, int T>
+    __device__ __forceinline__ void read(Frag4<true, T> &f) const
+    {
+        sfor<T>([&](auto I) { read_one<G, KS, decltype(I)::value>(f); });
+    }
+};
+
+// EPI: 0 the direct epilogue, 1 the staged one, 2 the staged chained one
+// (CH, YROW as for mfma4_chain_staged; ce used only then).
+template <typename TO, int EPI, int CH = 0, bool YROW = false>
+__device__ __forceinline__ void mfma4k_body(const GemmView &v, const uint16_t *__restrict__ x,
+                                            const uint16_t *__restrict__ y, TO *__restrict__ z,
+                                            float *__restrict__ ws, const ChainEpi &ce)
+{
+    using namespace mf4k;
+    // two stages per operand (the epilogue reuses them as a staging tile)
+    __shared__ __attribute__((aligned(16))) uint16_t sa[2 * STAGE_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t sb[2 * STAGE_ELEMS];
+    static_assert(2 * STAGE_BYTES >= 64 * BN * 4, "each operand's stages hold 64 staged rows");
+    static_assert(BM == mf4::BM && BN == mf4::BN && WM == mf4::WM && WN == mf4::WN && TM == mf4::TM &&
+                      TN == mf4::TN,
+                  "the epilogues assume the 32-deep four-wave tile's wave layout");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const uint32_t tiles_n = v.gn.total / BN;
+    const uint32_t nb = (v.gm.total / BM) * tiles_n;
+    uint32_t tm, tn, bidx;
+    mfma_tile_of(nb, tiles_n, v.gb.total, bidx, tm, tn);
+    const uint32_t m0 = tm * BM, n0 = tn * BN;
+    const int32_t bx = p2off<0>(v.gb, bidx), by = p2off<1>(v.gb, bidx), bz = p2off<2>(v.gb, bidx);
+    const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
+    const uint32_t nk = (uint32_t)v.k_per_split / BK;
+
+    DmaPlan8<0> da;
+    DmaPlan8<1> db;
+    da.init(v.gm, v.gk, m0, bx, tid);
+    db.init(v.gn, v.gk, n0, by, tid);
+    FragAddr8 fa, fb;
+    fa.init(lds_addr(sa), wm, lane);
+    fb.init(lds_addr(sb), wn, lane);
+
+    floatx16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // Four fragment sets, one per k-step of a stage: Fq = (Aq, Bq) holds
+    // k-step q.  Fragments are read two k-steps ahead, so a wave is done
+    // with a stage's LDS after its k-step 1; the stage's copies for two
+    // k-tiles later then spread over its k-steps 2 and 3.
+    Frag4<true, TM> A0, A1, A2, A3;
+    Frag4<true, TN> B0, B1, B2, B3;
+    using FA = Frag4<true, TM>;
+    using FB = Frag4<true, TN>;
+
+    // One 16-deep k-step: the 16 products on (Ac, Bc), one per slot, and in
+    // the slots, in this order:
+    //  * RD: the reads of k-step KR of stage GR into (An, Bn), A in slots 0-3,
+    //    B in slots 4-7;
+    //  * CP: one operand's copies of a k-tile into stage GC (CP = 1: X's from
+    //    offset ka, CP = 2: Y's from offset kb), in slots 4-11;
+    //  * DG: one digit per slot of the operand offsets (ka, kb) of k-tile tc
+    //    (scalar work that runs under the products).
+    // The scheduler may not move anything across a slot boundary, so the
+    // reads and copies run under the products instead of ahead of their wait.
+    auto kstep = [&](auto RD, auto GR, auto KR, auto CP, auto GC, auto DG, const FA &Ac, const FB &Bc, FA &An,
+                     FB &Bn, uint32_t tc, int32_t &ka, int32_t &kb) {
+        constexpr bool rd = decltype(RD)::value, dg = decltype(DG)::value;
+        constexpr int cp = decltype(CP)::value, gr = decltype(GR)::value, kr = decltype(KR)::value,
+                      gc = decltype(GC)::value;
+        const uint32_t k0 = kbeg + tc * BK;
+        if constexpr (dg) {
+            ka = 0;
+            kb = 0;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sfor<TM * TN>([&](auto MC) {
+            constexpr int m = decltype(MC)::value, i = m / TN, j = m % TN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac.op(i), Bc.op(j), acc[i][j], 0, 0, 0);
+            if constexpr (rd && m < TM) fa.template read_one<gr, kr, m>(An);
+            else if constexpr (rd && m < TM + TN) fb.template read_one<gr, kr, m - TM>(Bn);
+            if constexpr (cp == 1 && m >= 4 && m < 4 + COPIES) da.issue_one(m - 4, x, ka, sa + gc * STAGE_ELEMS, wave);
+            if constexpr (cp == 2 && m >= 4 && m < 4 + COPIES) db.issue_one(m - 4, y, kb, sb + gc * STAGE_ELEMS, wave);
+            if constexpr (dg && m < kP2Max) {
+                ka += (int32_t)((k0 >> v.gk.sh[m]) & v.gk.mask[m]) * v.gk.st[0][m];
+                kb += (int32_t)((k0 >> v.gk.sh[m]) & v.gk.mask[m]) * v.gk.st[1][m];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    static_assert(4 + COPIES <= TM * TN && TM + TN <= TM * TN, "one copy and one read per product slot");
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using C0 = std::integral_constant<int, 0>;
+    using CX = std::integral_constant<int, 1>;
+    using CY = std::integral_constant<int, 2>;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    // k-tile t in stage G.  On entry k-steps 0 and 1 are read (F0, F1; the
+    // reads may be in flight).  k-steps 0 and 1 read k-steps 2 and 3; then
+    // the wave has all its fragments of stage G (waited for), and the copies
+    // of k-tile t + 1 into the other stage have landed: a barrier publishes
+    // that stage and frees stage G.  k-steps 2 and 3 read k-steps 0 and 1 of
+    // the other stage and copy k-tile t + 2 into stage G, X's half in k-step
+    // 2 and Y's in k-step 3.  (Near the end that copy re-reads the last
+    // k-tile: every copy stays in bounds, and the count of copies per step
+    // stays fixed.)
+    auto step = [&](auto GC, uint32_t t) {
+        using GO = std::integral_constant<int, 1 - decltype(GC)::value>;
+        int32_t ka = 0, kb = 0;
+        lds_wait<TM + TN>();   // F0 landed (F1 may be in flight)
+        A0.ready();
+        B0.ready();
+        kstep(T_{}, GC, I2{}, C0{}, GC, T_{}, A0, B0, A2, B2, min(t + 2, nk - 1), ka, kb);
+        lds_wait<TM + TN>();   // F1 landed (F2 may be in flight)
+        A1.ready();
+        B1.ready();
+        kstep(T_{}, GC, I3{}, C0{}, GC, F_{}, A1, B1, A3, B3, 0u, ka, kb);
+        lds_wait<0>();   // this wave's reads of stage G are done
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        A2.ready();
+        B2.ready();
+        A3.ready();
+        B3.ready();
+        kstep(T_{}, GO{}, I0{}, CX{}, GC, F_{}, A2, B2, A0, B0, 0u, ka, kb);
+        kstep(T_{}, GO{}, I1{}, CY{}, GC, F_{}, A3, B3, A1, B1, 0u, ka, kb);
+    };
+    // The last k-tile when the count is odd (stage 0): no copies and no reads
+    // past it.
+    auto tail_step = [&](uint32_t) {
+        int32_t ka = 0, kb = 0;
+        lds_wait<TM + TN>();
+        A0.ready();
+        B0.ready();
+        kstep(T_{}, I0{}, I2{}, C0{}, I0{}, F_{}, A0, B0, A2, B2, 0u, ka, kb);
+        lds_wait<TM + TN>();
+        A1.ready();
+        B1.ready();
+        kstep(T_{}, I0{}, I3{}, C0{}, I0{}, F_{}, A1, B1, A3, B3, 0u, ka, kb);
+        lds_wait<TM + TN>();
+        A2.ready();
+        B2.ready();
+        kstep(F_{}, I0{}, I0{}, C0{}, I0{}, F_{}, A2, B2, A0, B0, 0u, ka, kb);
+        lds_wait<0>();
+        A3.ready();
+        B3.ready();
+        kstep(F_{}, I0{}, I0{}, C0{}, I0{}, F_{}, A3, B3, A1, B1, 0u, ka, kb);
+    };
+
+    // prologue: k-tiles 0 and 1 in flight, k-steps 0 and 1 of the first read
+    {
+        const uint32_t k1 = min(1u, nk - 1);
+        const int32_t a0 = p2off<0>(v.gk, kbeg), b0 = p2off<1>(v.gk, kbeg);
+        const int32_t a1 = p2off<0>(v.gk, kbeg + k1 * BK), b1 = p2off<1>(v.gk, kbeg + k1 * BK);
+        sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, a0, sa, wave); });
+        sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, b0, sb, wave); });
+        sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, a1, sa + STAGE_ELEMS, wave); });
+        sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, b1, sb + STAGE_ELEMS, wave); });
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * COPIES));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    fa.template read<0, 0>(A0);
+    fb.template read<0, 0>(B0);
+    fa.template read<0, 1>(A1);
+    fb.template read<0, 1>(B1);
+    lds_wait<0>();
+    A0.ready();
+    B0.ready();
+    A1.ready();
+    B1.ready();
+
+    // The loop body runs two k-tiles (stages 0 and 1); every fragment read it
+    // issues is waited for inside it, except those of the next body's first
+    // two k-steps, which are waited for (and handed on through lds_ready)
+    // before the back-edge, so that no read is in flight at a branch or merge.
+    uint32_t t = 0;
+    for (; t + 2 <= nk; t += 2) {
+        step(I0{}, t);
+        step(I1{}, t + 1);
+        lds_wait<0>();
+        A0.ready();
+        B0.ready();
+        A1.ready();
+        B1.ready();
+    }
+    if (t < nk) tail_step(t);
+    // nothing may stay in flight past the k-loop
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_wait<0>();
+
+    const bool split = v.split > 1;
+    float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
+    if constexpr (EPI == 2) {
+        lds_barrier();   // every wave past its last read of the operand stages
+        mfma4_chain_staged<TO, CH, YROW>(v, z, ce, acc, lds_addr(sa), lds_addr(sb), m0, n0, bidx, bz, wave, lane);
+        return;
+    } else if constexpr (EPI == 1) {
+        lds_barrier();
+        if (split) mfma4_store_staged<float, false>(v, wsp, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
+        else mfma4_store_staged<TO, true>(v, z, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
+        return;
+    }
+    mfma4_store_direct<TO>(v, z, wsp, split, acc, m0, n0, bz, wave);
+}
+
+// VEC: the staged epilogue (the output's four consecutive columns form one
+// aligned vector, and z / the workspace are 16-byte aligned)
+template <typename TO, bool VEC>
+__global__ __launch_bounds__(mf4k::NT) void k_mfma4k_bf16(GemmView v, const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ y, TO *__restrict__ z,
+                                                          float *__restrict__ ws)
+{
+    mfma4k_body<TO, VEC ? 1 : 0>(v, x, y, z, ws, ChainEpi{});
+}
+
+// The product with a chain of two elementwise steps in its staged epilogue
+template <typename TO, int CH, bool YROW>
+__global__ __launch_bounds__(mf4k::NT) void k_mfma4k_chain(GemmView v, const uint16_t *__restrict__ x,
+                                                           const uint16_t *__restrict__ y, TO *__restrict__ z,
+                                                           ChainEpi ce)
+{
+    mfma4k_body<TO, 2, CH, YROW>(v, x, y, z, nullptr, ce);
+}
+
+template <typename TO>
+static int launch4k_t(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, hipStream_t s,
+                      bool vec_ok)
+{
+    const GemmView &v = p.gv;
+    dim3 grid((v.gm.total / mf4k::BM) * (v.gn.total / mf4k::BN), v.gb.total, v.split);
+    const void *out = v.split > 1 ? ws : z;
+    const bool vec = vec_ok && v.z_vec4 && ((uintptr_t)out % 16) == 0;
+    void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *) =
+        vec ? k_mfma4k_bf16<TO, true> : k_mfma4k_bf16<TO, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(mf4k::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z,
+                       (float *)ws);
+    return (int)hipGetLastError();
+}
+
+int launch_mfma4k(const tra_plan_s &p, const void *x, const void *y, void *z, void *ws, void *stream, bool out_f32,
+                  bool vec_ok)
+{
+    hipStream_t s = (hipStream_t)stream;
+    return out_f32 ? launch4k_t<float>(p, x, y, z, ws, s, vec_ok) : launch4k_t<bf16_t>(p, x, y, z, ws, s, vec_ok);
+}
+
+template <typename TO>
+static int launch4k_chain_t(const tra_plan_s &p, const void *x, const void *y, void *z, const ChainEpi &ce,
+                            hipStream_t s)
+{
+    const GemmView &v = p.gv;
+    dim3 grid((v.gm.total / mf4k::BM) * (v.gn.total / mf4k::BN), v.gb.total, 1);
+    bool yrow = true;
+    for (int i = 0; i < kP2Max; ++i)
+        if (ce.rn.mask[i] && ce.rn.st[0][i]) yrow = false;
+    const bool ch = ce.join_a == J_SUB && ce.join_b == J_MUL;
+    void (*k)(GemmView, const uint16_t *, const uint16_t *, TO *, ChainEpi) =
+        !ch ? k_mfma4k_chain<TO, 0, false> : (yrow ? k_mfma4k_chain<TO, 1, true> : k_mfma4k_chain<TO, 1, false>);
+    hipLaunchKernelGGL(k, grid, dim3(mf4k::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z, ce);
+    return (int)hipGetLastError();
+}
+
+int launch_mfma4k_chain(const tra_plan_s &p, const ChainEpi &ce, bool out_f32, const void *x, const void *y, void *z,
+                        void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    return out_f32 ? launch4k_chain_t<float>(p, x, y, z, ce, s) : launch4k_chain_t<bf16_t>(p, x, y, z, ce, s);
+}
+
+}  // namespace tra

@@ -499,7 +499,8 @@ __global__ __launch_bounds__(256) void k_repartition(RepartDesc r, int vec, cons
          u += (int64_t)gridDim.x * blockDim.x) {
         int64_t so = 0, unused = 0;
         radix_offsets(r.dst, u * vec, so, unused);
-        dst[u] = src[so / vec];
+        if (r.scatter) dst[so / vec] = src[u];
+        else dst[u] = src[so / vec];
     }
 }
 
@@ -523,7 +524,9 @@ __device__ __forceinline__ void rep_store(U *p, U v)
     else *p = v;
 }
 
-template <typename U, int UPT, bool NT>
+// SC: scatter form (the source read in order, the destination written at
+// mapped offsets) instead of the gather form.
+template <typename U, int UPT, bool NT, bool SC>
 __global__ __launch_bounds__(256) void k_repartition_p2(Pow2Group g, int lvec, uint32_t n_units,
                                                         const U *__restrict__ src, U *__restrict__ dst)
 {
@@ -531,20 +534,29 @@ __global__ __launch_bounds__(256) void k_repartition_p2(Pow2Group g, int lvec, u
     if (base + 256u * (UPT - 1) < n_units) {
         U v[UPT];
 #pragma unroll
-        for (int i = 0; i < UPT; ++i)
-            v[i] = rep_load<NT>(src + (p2off<0>(g, (base + 256u * i) << lvec) >> lvec));
+        for (int i = 0; i < UPT; ++i) {
+            const uint32_t u = base + 256u * i;
+            v[i] = rep_load<NT>(src + (SC ? u : p2off<0>(g, u << lvec) >> lvec));
+        }
 #pragma unroll
-        for (int i = 0; i < UPT; ++i) rep_store<NT>(dst + base + 256u * i, v[i]);
+        for (int i = 0; i < UPT; ++i) {
+            const uint32_t u = base + 256u * i;
+            rep_store<NT>(dst + (SC ? p2off<0>(g, u << lvec) >> lvec : u), v[i]);
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < UPT; ++i) {
             const uint32_t u = base + 256u * i;
-            if (u < n_units) dst[u] = src[p2off<0>(g, u << lvec) >> lvec];
+            if (u < n_units) {
+                const uint32_t o = p2off<0>(g, u << lvec) >> lvec;
+                if (SC) dst[o] = src[u];
+                else dst[u] = src[o];
+            }
         }
     }
 }
 
-template <typename U>
+template <typename U, bool SC>
 static void launch_rep_p2(const Pow2Group &g, int lvec, int64_t n_units, const void *src, void *dst,
                           hipStream_t s)
 {
@@ -555,7 +567,7 @@ static void launch_rep_p2(const Pow2Group &g, int lvec, int64_t n_units, const v
     const int64_t bytes = n_units * (int64_t)sizeof(U);
     const uint32_t n = (uint32_t)n_units;
 #define TRA_REP_GO(UPT, NT)                                                                               \
-    hipLaunchKernelGGL((k_repartition_p2<U, UPT, NT>), dim3((unsigned)((n_units + 256 * UPT - 1) / (256 * UPT))), \
+    hipLaunchKernelGGL((k_repartition_p2<U, UPT, NT, SC>), dim3((unsigned)((n_units + 256 * UPT - 1) / (256 * UPT))), \
                        dim3(256), 0, s, g, lvec, n, (const U *)src, (U *)dst)
     if (bytes >= (64ll << 20)) TRA_REP_GO(8, true);
     else if (n_units >= 256 * 256 * 4) TRA_REP_GO(4, false);
@@ -863,11 +875,16 @@ int launch_repartition(const RepartDesc &r, int esz, const void *src, void *dst,
     if (p2) {
         int lvec = 0;
         while ((1 << lvec) < r.vec) ++lvec;
+        const bool sc = r.scatter != 0;
         switch (unit) {
-        case 16: launch_rep_p2<u32x4>(g, lvec, n_units, src, dst, s); break;
-        case 8: launch_rep_p2<u32x2>(g, lvec, n_units, src, dst, s); break;
-        case 4: launch_rep_p2<uint32_t>(g, lvec, n_units, src, dst, s); break;
-        default: launch_rep_p2<uint16_t>(g, lvec, n_units, src, dst, s); break;
+        case 16: sc ? launch_rep_p2<u32x4, true>(g, lvec, n_units, src, dst, s)
+                    : launch_rep_p2<u32x4, false>(g, lvec, n_units, src, dst, s); break;
+        case 8: sc ? launch_rep_p2<u32x2, true>(g, lvec, n_units, src, dst, s)
+                   : launch_rep_p2<u32x2, false>(g, lvec, n_units, src, dst, s); break;
+        case 4: sc ? launch_rep_p2<uint32_t, true>(g, lvec, n_units, src, dst, s)
+                   : launch_rep_p2<uint32_t, false>(g, lvec, n_units, src, dst, s); break;
+        default: sc ? launch_rep_p2<uint16_t, true>(g, lvec, n_units, src, dst, s)
+                    : launch_rep_p2<uint16_t, false>(g, lvec, n_units, src, dst, s); break;
         }
         return (int)hipGetLastError();
     }

@@ -126,10 +126,15 @@ struct ElemDesc {
 // Repartition: destination positions enumerated in the destination layout;
 // `dst` has, per destination sub-dimension, the source stride (st[0]).
 // Runs of `vec` consecutive elements are contiguous in both layouts.
+// A re-blocking copy.  Gather form (scatter == 0): unit u of the destination,
+// in its own order, is read from the source offset that `dst` maps u to.
+// Scatter form (scatter == 1): unit u of the source, in its own order, is
+// written to the destination offset that `dst` maps u to.
 struct RepartDesc {
     Radix dst;
     int64_t n_elems;
     int32_t vec;
+    int32_t scatter;
 };
 
 }  // namespace tra

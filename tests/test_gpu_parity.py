@@ -371,6 +371,30 @@ def test_transposed_operands_on_the_matrix_cores(spec, d):
     assert plan.kernel == "mfma_bf16"
 
 
+K64_CASES = [
+    # (spec, bounds, d, out dtype, post_scale): both operands contiguous along
+    # the contracted label over at least 64 elements
+    ("ik,jk->ij", {"i": 4096, "j": 2048, "k": 64}, {"i": 1, "j": 1, "k": 1}, "f32", 1.0),      # one k-tile
+    ("ik,jk->ij", {"i": 4096, "j": 2048, "k": 128}, {"i": 2, "j": 2, "k": 2}, "f32", 1.0),    # blocked k
+    ("ik,jk->ij", {"i": 2048, "j": 2048, "k": 1024}, {"i": 4, "j": 1, "k": 2}, "f32", 1.0),   # split 4 ways
+    ("hsd,htd->hst", {"h": 4, "s": 512, "t": 512, "d": 128}, {"h": 2, "s": 1, "t": 2, "d": 1}, "bf16", 0.125),
+    ("ik,jk->ij", {"i": 1024, "j": 1024, "k": 2048}, {"i": 1, "j": 1, "k": 1}, "bf16", 1.0),  # 32 k-tiles, split
+]
+
+
+@pytest.mark.parametrize("case", K64_CASES, ids=["one-ktile", "blocked-k", "split4", "batched-bf16", "long-k"])
+def test_k_major_products_on_the_64_deep_tile(case):
+    """Products whose operands are both K-major over 64 or more contiguous
+    elements run on the four-wave tile with 64-deep stages (variant 4):
+    parity with the oracle for one k-tile, blocked and split contracted
+    ranges, a batch with bf16 output and a post-scale."""
+    spec, bounds, d, odt, scale = case
+    case = wl.EinsumCase(f"k64_{spec}", 64, spec, bounds, d, "mul", "sum", "bf16", odt, (N002, N002),
+                         post_scale=scale)
+    err, plan = check(case)
+    assert plan.kernel == "mfma_bf16" and plan.info.tile == 4, (plan.kernel, plan.info.tile)
+
+
 @pytest.mark.parametrize("which", ["dX", "dA"])
 def test_blocked_gemm_backward_full_size_sampled(which):
     """The blocked GEMM's backward products at full size: dX = dY A^T

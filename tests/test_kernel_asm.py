@@ -27,7 +27,7 @@ import pytest
 from tensor_relational_algebra_amd import build as tra_build
 
 HIPCC = tra_build.HIPCC
-KERNEL_SOURCES = ["k_mfma.hip", "k_attention.hip"]
+KERNEL_SOURCES = ["k_mfma.hip", "k_mfma4k.hip", "k_attention.hip"]
 
 _LDS_READ = re.compile(r"(ds_read\S*|ds_load\S*)\s+(?:v\[(\d+):(\d+)\]|v(\d+))")
 _WAIT = re.compile(r"s_waitcnt.*lgkmcnt\((\d+)\)")
