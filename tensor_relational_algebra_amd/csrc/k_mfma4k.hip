@@ -31,12 +31,6 @@
 
 #include "mfma_common.h"
 
-// Cache policy of the direct global -> LDS copies (the aux operand of
-// global_load_lds).
-#ifndef TRA_K4K_CPOL
-#define TRA_K4K_CPOL 0
-#endif
-
 namespace tra {
 
 namespace mf4k {
@@ -48,11 +42,13 @@ constexpr int COPIES = STAGE_ELEMS / 8 / NT;    // 16-byte copies per thread per
 
 // 64-deep K-major stage, [row][64 k]: 8 granules of 16 bytes per row, granule
 // c of row r stored at c ^ swz_k8(r).  The fragment reads of a k-step hit one
-// granule column of 32 consecutive rows; the permutation spreads any 8
-// consecutive rows, and the 8 rows of each parity among 16 consecutive ones,
-// over distinct granule slots, so the reads are free of bank conflicts for
-// 128- and 256-byte bank sets alike.
-__device__ __forceinline__ int swz_k8(int r) { return (r ^ (r >> 3)) & 7; }
+// granule column of 16 or 32 consecutive rows from a multiple of 16; the
+// permutation spreads any 8 consecutive rows, and the 8 rows of each parity
+// among 16 consecutive ones, over distinct granule slots, so the reads are
+// free of bank conflicts for 128- and 256-byte bank sets alike.  It depends
+// on row bits 0-3 only, so a fragment read's permutation depends on the
+// lane alone.
+__device__ __forceinline__ int swz_k8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Per-thread plan of one operand's copies into a stage: copy i of thread tid
 // moves LDS granule p = i * NT + tid, i.e. row p / 8, slot p % 8, which holds
@@ -79,8 +75,7 @@ struct DmaPlan8 {
     __device__ __forceinline__ void issue_one(int i, const uint16_t *__restrict__ g, int32_t koff, uint16_t *stage,
                                               int wave)
     {
-        __builtin_amdgcn_global_load_lds(g + src[i] + koff, (lds_void_t *)(stage + (i * mf4k::NT + wave * 64) * 8), 16,
-                                         0, TRA_K4K_CPOL);
+        dma_copy16(g, koff, (uint32_t)src[i], stage + (i * mf4k::NT + wave * 64) * 8);
     }
 };
 
@@ -172,7 +167,9 @@ __device__ __forceinline__ void mfma4k_body(const GemmView &v, const uint16_t *_
     //  * RD: the reads of k-step KR of stage GR into (An, Bn), A in slots 0-3,
     //    B in slots 4-7;
     //  * CP: one operand's copies of a k-tile into stage GC (CP = 1: X's from
-    //    offset ka, CP = 2: Y's from offset kb), in slots 4-11;
+    //    offset ka, CP = 2: Y's from offset kb), in the even slots (spread
+    //    over the k-step: bunched into 8 consecutive slots they cost 6% more
+    //    cycles);
     //  * DG: one digit per slot of the operand offsets (ka, kb) of k-tile tc
     //    (scalar work that runs under the products).
     // The scheduler may not move anything across a slot boundary, so the
@@ -193,8 +190,8 @@ __device__ __forceinline__ void mfma4k_body(const GemmView &v, const uint16_t *_
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac.op(i), Bc.op(j), acc[i][j], 0, 0, 0);
             if constexpr (rd && m < TM) fa.template read_one<gr, kr, m>(An);
             else if constexpr (rd && m < TM + TN) fb.template read_one<gr, kr, m - TM>(Bn);
-            if constexpr (cp == 1 && m >= 4 && m < 4 + COPIES) da.issue_one(m - 4, x, ka, sa + gc * STAGE_ELEMS, wave);
-            if constexpr (cp == 2 && m >= 4 && m < 4 + COPIES) db.issue_one(m - 4, y, kb, sb + gc * STAGE_ELEMS, wave);
+            if constexpr (cp == 1 && m % 2 == 0) da.issue_one(m / 2, x, ka, sa + gc * STAGE_ELEMS, wave);
+            if constexpr (cp == 2 && m % 2 == 0) db.issue_one(m / 2, y, kb, sb + gc * STAGE_ELEMS, wave);
             if constexpr (dg && m < kP2Max) {
                 ka += (int32_t)((k0 >> v.gk.sh[m]) & v.gk.mask[m]) * v.gk.st[0][m];
                 kb += (int32_t)((k0 >> v.gk.sh[m]) & v.gk.mask[m]) * v.gk.st[1][m];
@@ -202,7 +199,7 @@ __device__ __forceinline__ void mfma4k_body(const GemmView &v, const uint16_t *_
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    static_assert(4 + COPIES <= TM * TN && TM + TN <= TM * TN, "one copy and one read per product slot");
+    static_assert(2 * COPIES <= TM * TN && TM + TN <= TM * TN, "one copy and one read per product slot");
     using T_ = std::true_type;
     using F_ = std::false_type;
     using C0 = std::integral_constant<int, 0>;
@@ -325,6 +322,259 @@ __device__ __forceinline__ void mfma4k_body(const GemmView &v, const uint16_t *_
     mfma4_store_direct<TO>(v, z, wsp, split, acc, m0, n0, bz, wave);
 }
 
+// ---------------------------------------------------------------------------
+// The same tile on 16x16x32 products.  Under sustained load the chip is held
+// to its power budget, and a 16x16x32 product moves half the accumulator
+// bytes per flop through the register file of a 32x32x16 one: a loop of
+// products with random operands sustains about 7% more of them at the same
+// budget.  Each wave's 128 x 128 block is 8 x 8 blocks of 16 x 16 (row blocks
+// (2i + wm)*16, column blocks (2j + wn)*16), its 256 accumulators in the
+// accumulator registers.  A k-step is 32 deep (two per stage): 64 products,
+// 16 fragment reads of 16 bytes (lane l: row or column l % 16 of its block,
+// k 8(l/16) .. +7).  Fragments are read one k-step ahead, so a wave is done
+// with a stage after its first k-step; the stage's copies for two k-tiles
+// later spread over its second.
+//
+// The products are issued by inline asm with the accumulators bound to the
+// accumulator registers: with the compiler's own product the 64 four-element
+// accumulators were moved around the register file in every iteration.
+// Being asm, their register hazards are handled here: the accumulators are
+// zeroed and then separated from the first product by wait states, each
+// accumulator is next read by a product 64 products later, fragments come
+// straight from LDS reads (waited for) with no vector-ALU write between, and
+// after the last product wait states precede every read of an accumulator.
+__device__ __forceinline__ void mfma16x16x32(floatx4_t &acc, const u32x4_t &a, const u32x4_t &b)
+{
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Binds every accumulator to the accumulator registers at one point of the
+// instruction stream (an asm that reads and writes each of them).
+__device__ __forceinline__ void acc16_bind(Acc16 &acc)
+{
+#pragma unroll
+    for (int i = 0; i < 2 * mf4::TM; ++i)
+        asm volatile(""
+                     : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                       "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+}
+// Wait states between every write of the accumulators before it and every
+// read after it (the two binds fix the order: volatile asm keeps its order).
+__device__ __forceinline__ void acc16_fence(Acc16 &acc)
+{
+    acc16_bind(acc);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+    acc16_bind(acc);
+}
+
+// One operand's fragments of one 32-deep k-step: 8 blocks of 16 rows.
+struct Frag16 {
+    u32x4_t k[8];
+    __device__ __forceinline__ void ready()
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_ready(k[i]);
+    }
+};
+
+// Per-lane LDS bases of one operand's 16-row fragment reads, one per k-step
+// of a stage: block i of k-step ks reads row (2i + w)*16 + l % 16, granule
+// 4 ks + l / 16; block i and stage G add i * 4 KiB + G * 32 KiB.
+struct FragAddr16 {
+    uint32_t base[2];
+    __device__ __forceinline__ void init(uint32_t lds, int w, int lane)
+    {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int r = w * 16 + (lane & 15);
+            const int c = (4 * ks + (lane >> 4)) ^ swz_k8(r);
+            base[ks] = lds + (uint32_t)(r * mf4k::BK + c * 8) * 2;
+        }
+    }
+    template <int G, int KS, int R>
+    __device__ __forceinline__ void read_one(Frag16 &f) const
+    {
+        constexpr int off = G * mf4k::STAGE_BYTES + R * 32 * mf4k::BK * 2;
+        f.k[R] = ds_read16_at<off>(base[KS]);
+    }
+};
+
+template <typename TO, int EPI, int CH = 0, bool YROW = false>
+__device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t *__restrict__ x,
+                                              const uint16_t *__restrict__ y, TO *__restrict__ z,
+                                              float *__restrict__ ws, const ChainEpi &ce)
+{
+    using namespace mf4k;
+    __shared__ __attribute__((aligned(16))) uint16_t sa[2 * STAGE_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t sb[2 * STAGE_ELEMS];
+    constexpr int NI = 2 * TM, NJ = 2 * TN;   // 16-row and 16-column blocks of a wave
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const uint32_t tiles_n = v.gn.total / BN;
+    const uint32_t nb = (v.gm.total / BM) * tiles_n;
+    uint32_t tm, tn, bidx;
+    mfma_tile_of(nb, tiles_n, v.gb.total, bidx, tm, tn);
+    const uint32_t m0 = tm * BM, n0 = tn * BN;
+    const int32_t bx = p2off<0>(v.gb, bidx), by = p2off<1>(v.gb, bidx), bz = p2off<2>(v.gb, bidx);
+    const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
+    const uint32_t nk = (uint32_t)v.k_per_split / BK;
+
+    DmaPlan8<0> da;
+    DmaPlan8<1> db;
+    da.init(v.gm, v.gk, m0, bx, tid);
+    db.init(v.gn, v.gk, n0, by, tid);
+    FragAddr16 fa, fb;
+    fa.init(lds_addr(sa), wm, lane);
+    fb.init(lds_addr(sb), wn, lane);
+
+    Acc16 acc;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
+    acc16_fence(acc);   // the zeroing lands before the first product reads it
+
+    Frag16 A0, A1, B0, B1;   // k-steps 0 and 1 of a stage
+
+    // One 32-deep k-step: the 64 products on (Ac, Bc), one per slot; in
+    // slots 4r (r < 16) the reads of k-step KR of stage GR into (An, Bn), A
+    // first; in slots 4r + 2 the copies of a k-tile into stage GC (X's from
+    // ka for r < 8, then Y's from kb); in slots 4r + 1 one digit each of the
+    // operand offsets (ka, kb) of k-tile tc.
+    auto kstep = [&](auto RD, auto GR, auto KR, auto CP, auto GC, auto DG, const Frag16 &Ac, const Frag16 &Bc,
+                     Frag16 &An, Frag16 &Bn, uint32_t tc, int32_t &ka, int32_t &kb) {
+        constexpr bool rd = decltype(RD)::value, cp = decltype(CP)::value, dg = decltype(DG)::value;
+        constexpr int gr = decltype(GR)::value, kr = decltype(KR)::value, gc = decltype(GC)::value;
+        const uint32_t k0 = kbeg + tc * BK;
+        if constexpr (dg) {
+            ka = 0;
+            kb = 0;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sfor<NI * NJ>([&](auto MC) {
+            constexpr int m = decltype(MC)::value, i = m / NJ, j = m % NJ, r = m / 4;
+            mfma16x16x32(acc[i][j], Ac.k[i], Bc.k[j]);
+            if constexpr (rd && m % 4 == 0 && r < 8) fa.template read_one<gr, kr, r>(An);
+            if constexpr (rd && m % 4 == 0 && r >= 8) fb.template read_one<gr, kr, r - 8>(Bn);
+            if constexpr (cp && m % 4 == 2 && r < COPIES) da.issue_one(r, x, ka, sa + gc * STAGE_ELEMS, wave);
+            if constexpr (cp && m % 4 == 2 && r >= COPIES) db.issue_one(r - COPIES, y, kb, sb + gc * STAGE_ELEMS, wave);
+            if constexpr (dg && m % 4 == 1 && r < kP2Max) {
+                ka += (int32_t)((k0 >> v.gk.sh[r]) & v.gk.mask[r]) * v.gk.st[0][r];
+                kb += (int32_t)((k0 >> v.gk.sh[r]) & v.gk.mask[r]) * v.gk.st[1][r];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    static_assert(2 * COPIES <= 16 && kP2Max <= 16, "one copy and one digit per four product slots");
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // k-tile t in stage G.  On entry F0 = (A0, B0) holds its k-step 0 (its
+    // reads may be in flight).  k-step 0 reads k-step 1; then the wave has all
+    // its fragments of stage G (waited for) and the copies of k-tile t + 1
+    // into the other stage have landed: a barrier publishes that stage and
+    // frees stage G.  k-step 1 reads k-step 0 of the other stage and copies
+    // k-tile t + 2 into stage G (near the end: the last k-tile again, in
+    // bounds, the count of copies per step fixed).
+    auto step = [&](auto GC, uint32_t t) {
+        using GO = std::integral_constant<int, 1 - decltype(GC)::value>;
+        int32_t ka = 0, kb = 0;
+        lds_wait<0>();
+        A0.ready();
+        B0.ready();
+        kstep(T_{}, GC, I1{}, F_{}, GC, T_{}, A0, B0, A1, B1, min(t + 2, nk - 1), ka, kb);
+        lds_wait<0>();   // this wave's reads of stage G are done
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        A1.ready();
+        B1.ready();
+        kstep(T_{}, GO{}, I0{}, T_{}, GC, F_{}, A1, B1, A0, B0, 0u, ka, kb);
+    };
+    auto tail_step = [&](uint32_t) {
+        int32_t ka = 0, kb = 0;
+        lds_wait<0>();
+        A0.ready();
+        B0.ready();
+        kstep(T_{}, I0{}, I1{}, F_{}, I0{}, F_{}, A0, B0, A1, B1, 0u, ka, kb);
+        lds_wait<0>();
+        A1.ready();
+        B1.ready();
+        kstep(F_{}, I0{}, I0{}, F_{}, I0{}, F_{}, A1, B1, A0, B0, 0u, ka, kb);
+    };
+
+    // prologue: k-tiles 0 and 1 in flight, k-step 0 of the first read
+    {
+        const uint32_t k1 = min(1u, nk - 1);
+        const int32_t a0 = p2off<0>(v.gk, kbeg), b0 = p2off<1>(v.gk, kbeg);
+        const int32_t a1 = p2off<0>(v.gk, kbeg + k1 * BK), b1 = p2off<1>(v.gk, kbeg + k1 * BK);
+        sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, a0, sa, wave); });
+        sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, b0, sb, wave); });
+        sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, a1, sa + STAGE_ELEMS, wave); });
+        sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, b1, sb + STAGE_ELEMS, wave); });
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * COPIES));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    sfor<8>([&](auto I) { fa.template read_one<0, 0, decltype(I)::value>(A0); });
+    sfor<8>([&](auto I) { fb.template read_one<0, 0, decltype(I)::value>(B0); });
+    lds_wait<0>();
+    A0.ready();
+    B0.ready();
+
+    // two k-tiles per loop body; no read in flight at a branch or merge
+    uint32_t t = 0;
+    for (; t + 2 <= nk; t += 2) {
+        step(I0{}, t);
+        step(I1{}, t + 1);
+        lds_wait<0>();
+        A0.ready();
+        B0.ready();
+    }
+    if (t < nk) tail_step(t);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_wait<0>();
+    acc16_fence(acc);   // every product has written its accumulator before any read
+
+    const bool split = v.split > 1;
+    float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
+    if constexpr (EPI == 2) {
+        lds_barrier();
+        mfma4_chain_staged<TO, CH, YROW>(v, z, ce, acc, lds_addr(sa), lds_addr(sb), m0, n0, bidx, bz, wave, lane);
+        return;
+    } else if constexpr (EPI == 1) {
+        lds_barrier();
+        if (split) mfma4_store_staged<float, false>(v, wsp, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
+        else mfma4_store_staged<TO, true>(v, z, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
+        return;
+    }
+    mfma4_store_direct16<TO>(v, z, wsp, split, acc, m0, n0, bz, wave);
+}
+
+// The 64-deep tile's products: 16x16x32 (1) or 32x32x16 (0).
+#ifndef TRA_K4K_M16
+#define TRA_K4K_M16 1
+#endif
+template <typename TO, int EPI, int CH = 0, bool YROW = false>
+__device__ __forceinline__ void mfma4k_run(const GemmView &v, const uint16_t *__restrict__ x,
+                                           const uint16_t *__restrict__ y, TO *__restrict__ z,
+                                           float *__restrict__ ws, const ChainEpi &ce)
+{
+#if TRA_K4K_M16
+    mfma4k16_body<TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
+#else
+    mfma4k_body<TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
+#endif
+}
+
 // VEC: the staged epilogue (the output's four consecutive columns form one
 // aligned vector, and z / the workspace are 16-byte aligned)
 template <typename TO, bool VEC>
@@ -332,7 +582,7 @@ __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_bf16(GemmView v, const uint
                                                           const uint16_t *__restrict__ y, TO *__restrict__ z,
                                                           float *__restrict__ ws)
 {
-    mfma4k_body<TO, VEC ? 1 : 0>(v, x, y, z, ws, ChainEpi{});
+    mfma4k_run<TO, VEC ? 1 : 0>(v, x, y, z, ws, ChainEpi{});
 }
 
 // The product with a chain of two elementwise steps in its staged epilogue
@@ -341,7 +591,7 @@ __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_chain(GemmView v, const uin
                                                            const uint16_t *__restrict__ y, TO *__restrict__ z,
                                                            ChainEpi ce)
 {
-    mfma4k_body<TO, 2, CH, YROW>(v, x, y, z, nullptr, ce);
+    mfma4k_run<TO, 2, CH, YROW>(v, x, y, z, nullptr, ce);
 }
 
 template <typename TO>

@@ -19,6 +19,7 @@ namespace tra {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef short shortx8_t __attribute__((ext_vector_type(8)));
 
 struct MfmaCfg {
@@ -130,6 +131,32 @@ __device__ __forceinline__ void lds_ready(T &v)
     asm volatile("" : "+v"(v));
 }
 
+// One 16-byte direct global -> LDS copy per lane, into the wave's 1 KiB of
+// LDS at `stage`, from g + koff + the lane's offset (elements).
+#ifndef TRA_DMA_BUFFER
+#define TRA_DMA_BUFFER 1
+#endif
+__device__ __forceinline__ void dma_copy16(const uint16_t *__restrict__ g, int32_t koff, uint32_t lane_off,
+                                           uint16_t *stage)
+{
+#if TRA_DMA_BUFFER
+    // buffer form: the operand's base in a buffer descriptor, the k-tile term
+    // as the scalar offset and the lane's byte offset as the vector offset,
+    // so a copy needs no per-lane address arithmetic
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)g, (short)0, -1, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)stage, 16, lane_off * 2u, (uint32_t)koff * 2u, 0, 0);
+#else
+    // (The empty asm keeps the 32-bit offset a 32-bit value at the copy, so the
+    // address stays "scalar base + zero-extended lane offset" and the copy
+    // takes the scalar-base form; a zero extension hoisted out of a loop turns
+    // it into a 64-bit per-lane add per copy.)
+    uint32_t byte_off = lane_off * 2u;
+    asm volatile("" : "+v"(byte_off));
+    __builtin_amdgcn_global_load_lds((const void *)((const char *)(g + koff) + byte_off), (lds_void_t *)stage, 16, 0,
+                                     0);
+#endif
+}
+
 // Per-thread plan of the direct global -> LDS copies of one operand tile
 // (ROWS x 32 k).  Copy r of thread tid moves 16-byte granule p = r*NT + tid of
 // the stage; a wave's 64 copies land on 64 consecutive granules, so the LDS
@@ -158,16 +185,15 @@ struct DmaPlan {
     __device__ __forceinline__ void issue(const uint16_t *__restrict__ g, int32_t koff, uint16_t *stage, int wave)
     {
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-            __builtin_amdgcn_global_load_lds(g + src[i] + koff, (lds_void_t *)(stage + (i * NT + wave * 64) * 8), 16,
-                                             0, 0);
+        for (int i = 0; i < N; ++i) issue_one(i, g, koff, stage, wave);
     }
-    // copy i alone (i a compile-time constant at every call)
+    // copy i alone (i a compile-time constant at every call).  The address is
+    // the wave-uniform k-tile base plus the lane's 32-bit byte offset, so the
+    // copy takes the scalar-base form with no per-lane address arithmetic.
     __device__ __forceinline__ void issue_one(int i, const uint16_t *__restrict__ g, int32_t koff, uint16_t *stage,
                                               int wave)
     {
-        __builtin_amdgcn_global_load_lds(g + src[i] + koff, (lds_void_t *)(stage + (i * NT + wave * 64) * 8), 16, 0,
-                                         0);
+        dma_copy16(g, koff, (uint32_t)src[i], stage + (i * NT + wave * 64) * 8);
     }
 };
 
@@ -353,10 +379,20 @@ struct FragAddr4 {
 // holding columns 4*lane .. 4*lane + 3 of tile row PH*128 + wave*32 + RR.
 // pre(PH) runs at the start of half PH, before its staging writes (loads a
 // caller issues there are in flight during them).
-template <typename S, typename Pre, typename Emit>
-__device__ __forceinline__ void mfma4_staged(const floatx16_t (&acc)[mf4::TM][mf4::TN], uint32_t st_a, uint32_t st_b,
-                                             float sc, int wave, int lane, Pre &&pre, Emit &&emit)
+//
+// Accumulator layouts (the wave's blocks interleaved with the other waves'):
+//  * Acc32 = floatx16_t[4][4] (32x32x16 products): element e of block (i, j)
+//    holds row (2i + wm)*32 + 8(e/4) + 4(l/32) + e%4, column (2j + wn)*32 + l%32;
+//  * Acc16 = floatx4_t[8][8] (16x16x32 products): element e of block (i, j)
+//    holds row (2i + wm)*16 + 4(l/16) + e, column (2j + wn)*16 + l%16.
+using Acc32 = floatx16_t[mf4::TM][mf4::TN];
+using Acc16 = floatx4_t[2 * mf4::TM][2 * mf4::TN];
+
+template <typename S, typename ACC, typename Pre, typename Emit>
+__device__ __forceinline__ void mfma4_staged(const ACC &acc, uint32_t st_a, uint32_t st_b, float sc, int wave,
+                                             int lane, Pre &&pre, Emit &&emit)
 {
+    constexpr bool L16 = std::is_same<ACC, Acc16>::value;
     using namespace mf4;
     constexpr int ES = sizeof(S);
     constexpr int RB = BN * ES;   // bytes of one staged row
@@ -364,7 +400,8 @@ __device__ __forceinline__ void mfma4_staged(const floatx16_t (&acc)[mf4::TM][mf
     // Block ii of the half (rows ii*64 .. +63) goes to st_a (ii = 0) or st_b
     // (ii = 1); within it, the lane's row is wm*32 + 4*(lane/32) + 8q + r and
     // its column (j*2 + wn)*32 + lane%32.
-    const uint32_t wl = (uint32_t)(((wm * 32 + 4 * (lane >> 5)) * BN + wn * 32 + (lane & 31)) * ES);
+    const uint32_t wl = L16 ? (uint32_t)(((wm * 16 + 4 * (lane >> 4)) * BN + wn * 16 + (lane & 15)) * ES)
+                            : (uint32_t)(((wm * 32 + 4 * (lane >> 5)) * BN + wn * 32 + (lane & 31)) * ES);
     const uint32_t wb[2] = {st_a + wl, st_b + wl};
     // read base: rows (wave%2)*32 .. +31 of block wave/2, columns 4*lane .. +3
     const uint32_t rb = (wave < 2 ? st_a : st_b) + (uint32_t)(((wave & 1) * 32 * BN + 4 * lane) * ES);
@@ -373,14 +410,27 @@ __device__ __forceinline__ void mfma4_staged(const floatx16_t (&acc)[mf4::TM][mf
         constexpr int ph = decltype(PH)::value;
         if constexpr (ph == 1) lds_barrier();   // every wave done reading the first half
         pre(PH);
-        sfor<2 * TN * 16>([&](auto W) {
-            constexpr int w = decltype(W)::value;
-            constexpr int ii = w / (TN * 16), j = (w / 16) % TN, q = (w / 4) % 4, r = w % 4;
-            constexpr int off = ((8 * q + r) * BN + j * WN * 32) * ES;
-            const float val = acc[2 * ph + ii][j][4 * q + r] * sc;
-            if constexpr (ES == 4) ds_write4_at<off>(wb[ii], __builtin_bit_cast(uint32_t, val));
-            else ds_write2_at<off>(wb[ii], (uint32_t)f32_to_bf16(val));
-        });
+        if constexpr (L16) {
+            // blocks i = 4 ph .. 4 ph + 3 of the 16-row blocks: block il = i - 4 ph
+            // goes to st_a (il < 2) or st_b, at row (il % 2)*32 + wm*16 + 4(l/16) + e
+            sfor<4 * 2 * TN * 4>([&](auto W) {
+                constexpr int w = decltype(W)::value;
+                constexpr int il = w / (2 * TN * 4), j = (w / 4) % (2 * TN), e = w % 4;
+                constexpr int off = (((il % 2) * 32 + e) * BN + j * WN * 16) * ES;
+                const float val = acc[4 * ph + il][j][e] * sc;
+                if constexpr (ES == 4) ds_write4_at<off>(wb[il / 2], __builtin_bit_cast(uint32_t, val));
+                else ds_write2_at<off>(wb[il / 2], (uint32_t)f32_to_bf16(val));
+            });
+        } else {
+            sfor<2 * TN * 16>([&](auto W) {
+                constexpr int w = decltype(W)::value;
+                constexpr int ii = w / (TN * 16), j = (w / 16) % TN, q = (w / 4) % 4, r = w % 4;
+                constexpr int off = ((8 * q + r) * BN + j * WN * 32) * ES;
+                const float val = acc[2 * ph + ii][j][4 * q + r] * sc;
+                if constexpr (ES == 4) ds_write4_at<off>(wb[ii], __builtin_bit_cast(uint32_t, val));
+                else ds_write2_at<off>(wb[ii], (uint32_t)f32_to_bf16(val));
+            });
+        }
         lds_wait<0>();
         lds_barrier();
         // 32 rows of this wave, 8 at a time: reads, one wait, the rows
@@ -405,9 +455,8 @@ __device__ __forceinline__ void mfma4_staged(const floatx16_t (&acc)[mf4::TM][mf
 // 8-byte (bf16) vector per lane, so that every store instruction writes one
 // contiguous row of the tile.  Values and rounding are those of the direct
 // epilogue.
-template <typename T, bool SCALE>
-__device__ __forceinline__ void mfma4_store_staged(const GemmView &v, T *__restrict__ out,
-                                                   const floatx16_t (&acc)[mf4::TM][mf4::TN], uint32_t st_a,
+template <typename T, bool SCALE, typename ACC>
+__device__ __forceinline__ void mfma4_store_staged(const GemmView &v, T *__restrict__ out, const ACC &acc, uint32_t st_a,
                                                    uint32_t st_b, uint32_t m0, uint32_t n0, int32_t bz, int wave,
                                                    int lane)
 {
@@ -432,9 +481,9 @@ __device__ __forceinline__ void mfma4_store_staged(const GemmView &v, T *__restr
 // half are loaded together, before the half is staged.  YROW: ya does not
 // vary along the output's columns; lane r then loads ya of row r of the
 // wave's 32 once per half, and each row takes it by readlane.
-template <typename TO, int CH, bool YROW>
+template <typename TO, int CH, bool YROW, typename ACC>
 __device__ __forceinline__ void mfma4_chain_staged(const GemmView &v, TO *__restrict__ out, const ChainEpi &ce,
-                                                   const floatx16_t (&acc)[mf4::TM][mf4::TN], uint32_t st_a,
+                                                   const ACC &acc, uint32_t st_a,
                                                    uint32_t st_b, uint32_t m0, uint32_t n0, uint32_t bidx, int32_t bz,
                                                    int wave, int lane)
 {
@@ -536,6 +585,35 @@ __device__ __forceinline__ void mfma4_store_direct(const GemmView &v, TO *__rest
                     if (split) wsp[o] = val;
                     else Scalar<TO>::store(z, o, val * v.post_scale);
                 }
+            }
+        }
+    }
+}
+
+// The direct epilogue for the 16x16 accumulator layout (Acc16).
+template <typename TO>
+__device__ __forceinline__ void mfma4_store_direct16(const GemmView &v, TO *__restrict__ z, float *__restrict__ wsp,
+                                                     bool split, const Acc16 &acc, uint32_t m0, uint32_t n0,
+                                                     int32_t bz, int wave)
+{
+    using namespace mf4;
+    const int lane = threadIdx.x & 63, wm = wave / WN, wn = wave % WN;
+    const int32_t zm0 = p2off<1>(v.gm, m0) + bz, zn0 = p2off<1>(v.gn, n0);
+    int32_t lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lo[e] = p2off<1>(v.gm, 4 * (lane >> 4) + e);
+#pragma unroll
+    for (int i = 0; i < 2 * TM; ++i) {
+        const int32_t hi = zm0 + p2off<1>(v.gm, (i * WM + wm) * 16);
+#pragma unroll
+        for (int j = 0; j < 2 * TN; ++j) {
+            const int32_t on = zn0 + p2off<1>(v.gn, (j * WN + wn) * 16 + (lane & 15));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int32_t o = hi + lo[e] + on;
+                const float val = acc[i][j][e];
+                if (split) wsp[o] = val;
+                else Scalar<TO>::store(z, o, val * v.post_scale);
             }
         }
     }

@@ -87,6 +87,39 @@ def scan_function(body: str) -> list[str]:
     return bad
 
 
+_MFMA = re.compile(r"(v_mfma\S*)\s+(a\[\d+:\d+\]|v\[\d+:\d+\]),\s*(v\[\d+:\d+\]),\s*(v\[\d+:\d+\])")
+
+
+def mfma_operand_hazards(body: str, need: int = 2) -> list[str]:
+    """Matrix-core products whose A or B operand register was written by a
+    vector-ALU instruction fewer than `need` wait states before.  Products
+    issued from inline asm are invisible to the compiler's hazard handling;
+    their operands must come from memory reads (waited for by s_waitcnt), or
+    be separated from a vector-ALU write by wait states."""
+    since: dict[int, int] = {}   # register -> wait states since its last vector-ALU write
+    bad: list[str] = []
+    for raw in body.split("\n"):
+        line = raw.split(";")[0].strip()
+        if not line or line.startswith(".") or line.endswith(":"):
+            continue
+        op = line.split()[0]
+        m = _MFMA.match(line)
+        if m:
+            if any(since.get(r, need) < need for r in _regs(m.group(3)) | _regs(m.group(4))):
+                bad.append(line)
+        elif op.startswith("v_"):
+            parts = line.split(None, 1)
+            dst = parts[1].split(",")[0] if len(parts) > 1 else ""
+            for r in _regs(dst):
+                since[r] = -1
+        n = 1
+        if op == "s_nop":
+            n = int(line.split()[1], 0) + 1
+        for r in since:
+            since[r] += n
+    return bad
+
+
 def scan_assembly(text: str) -> dict[str, list[str]]:
     pieces = re.split(r"\n(_Z\S+):[^\n]*\n", text)
     out = {}
@@ -118,6 +151,20 @@ def test_scanner_flags_a_copy_of_an_in_flight_register():
     assert scan_function(body) == ["ds_write_b32 v2, v90"]
 
 
+def test_operand_hazard_scanner():
+    body = """
+        ds_read_b128 v[10:13], v2
+        s_waitcnt lgkmcnt(0)
+        v_mfma_f32_16x16x32_bf16 a[0:3], v[10:13], v[10:13], a[0:3]
+        v_mov_b32_e32 v11, v5
+        v_mfma_f32_16x16x32_bf16 a[4:7], v[10:13], v[20:23], a[4:7]
+        v_mov_b32_e32 v21, v5
+        s_nop 1
+        v_mfma_f32_16x16x32_bf16 a[8:11], v[12:15], v[20:23], a[8:11]
+    """
+    assert mfma_operand_hazards(body) == ["v_mfma_f32_16x16x32_bf16 a[4:7], v[10:13], v[20:23], a[4:7]"]
+
+
 @pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not installed")
 @pytest.mark.parametrize("source", KERNEL_SOURCES)
 def test_no_register_is_used_before_its_lds_read_lands(source, tmp_path):
@@ -127,7 +174,14 @@ def test_no_register_is_used_before_its_lds_read_lands(source, tmp_path):
         ["--cuda-device-only", "-S", src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
-    found = scan_assembly(out.read_text())
+    text = out.read_text()
+    found = scan_assembly(text)
     assert found, "no kernels found in the assembly"
     offenders = {name: lines[:3] for name, lines in found.items() if lines}
     assert not offenders, offenders
+    # products issued from inline asm: no operand fresh from a vector-ALU write
+    pieces = re.split(r"\n(_Z\S+):[^\n]*\n", text)
+    hazards = {pieces[k]: mfma_operand_hazards(pieces[k + 1].split(".Lfunc_end")[0])[:3]
+               for k in range(1, len(pieces), 2)}
+    hazards = {k: v for k, v in hazards.items() if v}
+    assert not hazards, hazards
