@@ -61,7 +61,8 @@ COMMON_SRCS = ("tensor_relational_algebra_amd/csrc/device_common.h",
                "tensor_relational_algebra_amd/csrc/plan.h")
 TRAFFIC_SRCS = {
     "sqdist": ("tensor_relational_algebra_amd/csrc/k_valu_tile.hip",) + COMMON_SRCS,
-    "gemm": ("tensor_relational_algebra_amd/csrc/k_mfma.hip",) + COMMON_SRCS,
+    "gemm": ("tensor_relational_algebra_amd/csrc/k_mfma4k.hip", "tensor_relational_algebra_amd/csrc/mfma_common.h")
+    + COMMON_SRCS,
     "recut": ("tensor_relational_algebra_amd/csrc/k_simple.hip",) + COMMON_SRCS,
 }
 # squared distance: `bench.py --steps 3 --warmup 1 --no-cpu-baseline --only sqdist`;
@@ -398,7 +399,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(BF16_MFMA_PEAK / 1e12, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": "k_mfma4_bf16" if plan.info.tile == 3 else "k_mfma_bf16", "launch_ms": round(gemm_ms, 4),
+                     "kernel": {4: "k_mfma4k_bf16", 3: "k_mfma4_bf16"}.get(plan.info.tile, "k_mfma_bf16"), "launch_ms": round(gemm_ms, 4),
                      "flop_per_launch": flops,
                      # algorithmic bytes: X and A read once, Y written once
                      "algorithmic_bytes": (B["i"] * B["j"] + B["j"] * B["k"]) * 2 + B["i"] * B["k"] * 4},

@@ -1,7 +1,8 @@
 // k_mfma4k.hip -- bf16 x bf16 -> fp32 join + sum aggregation on the four-wave
 // 256 x 256 matrix-core tile with 64-deep stages (tile variant 4), for
-// products whose two operands are both stored contiguously along the
-// contracted labels ("K-major").
+// products whose first operand is stored contiguously along the contracted
+// labels ("K-major"), the second either K-major or contiguous along its
+// output labels ("MN-major"), each over 64 or more elements.
 //
 // Page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法",
 // section 2.2: the join of a key-matched pair of sub-tensors is a small
@@ -399,7 +400,92 @@ struct FragAddr16 {
     }
 };
 
-template <typename TO, int EPI, int CH = 0, bool YROW = false>
+// 64-deep MN-major stage, [64 k][256 columns]: 32 granules of 16 bytes per
+// k-row, granule c of k-row k stored at c ^ swz_n8(k).  A transposing
+// fragment read of one 16-lane group covers 4 consecutive k-rows x 32 bytes;
+// the permutation moves the 4 rows' 32-byte pieces to distinct offsets
+// within 128 bytes (conflict free), and it depends on k % 4 only, i.e. on
+// the lane.
+__device__ __forceinline__ int swz_n8(int k) { return (k & 3) << 1; }
+
+// Per-thread copies of an MN-major operand into a stage: copy i of thread
+// tid moves LDS granule p = i * NT + tid, k-row p / 32, slot p % 32, which
+// holds granule (p % 32) ^ swz_n8(k) of that k-row (a wave's 64 copies: two
+// whole 512-byte k-rows).
+template <int T>
+struct DmaPlanN8 {
+    static constexpr int N = mf4k::COPIES;
+    int32_t src[N];
+
+    __device__ __forceinline__ void init(const Pow2Group &g_cols, const Pow2Group &gk, uint32_t c0, int32_t base,
+                                         int tid)
+    {
+        const int32_t cbase = p2off<0>(g_cols, c0) + base;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int p = i * mf4k::NT + tid;
+            const int k = p >> 5, gl = (p & 31) ^ swz_n8(p >> 5);
+            src[i] = cbase + p2off<0>(g_cols, gl * 8) + p2off<T>(gk, k);
+        }
+    }
+    __device__ __forceinline__ void issue_one(int i, const uint16_t *__restrict__ g, int32_t koff, uint16_t *stage,
+                                              int wave)
+    {
+        dma_copy16(g, koff, (uint32_t)src[i], stage + (i * mf4k::NT + wave * 64) * 8);
+    }
+};
+
+// One operand's fragments of one 32-deep k-step for an MN-major operand:
+// per 16-column block two transposing 8-byte reads (k 8(l/16) .. +3 and
+// +4 .. +7 of column l % 16).
+struct Frag16N {
+    u32x2_t t[8][2];
+    __device__ __forceinline__ void ready()
+    {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lds_ready(t[j][0]);
+            lds_ready(t[j][1]);
+        }
+    }
+    __device__ __forceinline__ u32x4_t op(int j) const
+    {
+        return u32x4_t{t[j][0][0], t[j][0][1], t[j][1][0], t[j][1][1]};
+    }
+};
+
+// Transposing reads of an MN-major stage (gfx950's ds_read_b64_tr_b16: in each
+// 16-lane group, output lane i element e is element i % 4 of source lane
+// 4e + i / 4).  Lane l = 16 g + s reads 4 columns 4(s % 4) .. +3 of its
+// block at k-row 8g + 4r + s / 4 (read r), so output lane s holds column s,
+// k 8g + 4r .. +3.  Block j = 2 jq + jb covers columns (2j + wn)*16 .. +15;
+// the permutation touches granule bits 1-2 (wn and jb), so there is one base
+// per jb, and jq, the read, the k-step and the stage add constants.
+struct FragAddrN16 {
+    uint32_t base[2];
+    __device__ __forceinline__ void init(uint32_t lds, int w, int lane)
+    {
+        const int g = lane >> 4, sl = lane & 15;
+        const int k = 8 * g + (sl >> 2);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int gran = (4 * jb + 2 * w + ((sl & 3) >> 1)) ^ swz_n8(k);
+            base[jb] = lds + (uint32_t)(k * 256 + gran * 8 + 4 * (sl & 1)) * 2;
+        }
+    }
+    // read R of k-step KS of stage G: block R / 2, half R % 2
+    template <int G, int KS, int R>
+    __device__ __forceinline__ void read_one(Frag16N &f) const
+    {
+        constexpr int j = R / 2, h = R % 2, jb = j % 2, jq = j / 2;
+        constexpr int off = G * mf4k::STAGE_BYTES + (KS * 32 + 4 * h) * 256 * 2 + jq * 8 * 16;
+        f.t[j][h] = ds_read8_tr_at<off>(base[jb]);
+    }
+};
+
+// BKM: the second operand K-major (else MN-major: staged [k][column] and
+// read through the transposing LDS read).
+template <bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false>
 __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t *__restrict__ x,
                                               const uint16_t *__restrict__ y, TO *__restrict__ z,
                                               float *__restrict__ ws, const ChainEpi &ce)
@@ -422,12 +508,15 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
     const uint32_t nk = (uint32_t)v.k_per_split / BK;
 
     DmaPlan8<0> da;
-    DmaPlan8<1> db;
+    typename std::conditional<BKM, DmaPlan8<1>, DmaPlanN8<1>>::type db;
     da.init(v.gm, v.gk, m0, bx, tid);
     db.init(v.gn, v.gk, n0, by, tid);
-    FragAddr16 fa, fb;
+    FragAddr16 fa;
+    typename std::conditional<BKM, FragAddr16, FragAddrN16>::type fb;
     fa.init(lds_addr(sa), wm, lane);
     fb.init(lds_addr(sb), wn, lane);
+    using FB = typename std::conditional<BKM, Frag16, Frag16N>::type;
+    constexpr int NBR = BKM ? 8 : 16;   // fragment reads of the second operand per k-step
 
     Acc16 acc;
 #pragma unroll
@@ -438,15 +527,17 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
             for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
     acc16_fence(acc);   // the zeroing lands before the first product reads it
 
-    Frag16 A0, A1, B0, B1;   // k-steps 0 and 1 of a stage
+    Frag16 A0, A1;   // k-steps 0 and 1 of a stage
+    FB B0, B1;
 
     // One 32-deep k-step: the 64 products on (Ac, Bc), one per slot; in
-    // slots 4r (r < 16) the reads of k-step KR of stage GR into (An, Bn), A
-    // first; in slots 4r + 2 the copies of a k-tile into stage GC (X's from
+    // slots 4r (r < 8) the reads of k-step KR of stage GR into An, and the
+    // reads into Bn in slots 32 + 4r (K-major) or 32 + 2r (MN-major, two per
+    // block); in slots 4r + 2 the copies of a k-tile into stage GC (X's from
     // ka for r < 8, then Y's from kb); in slots 4r + 1 one digit each of the
     // operand offsets (ka, kb) of k-tile tc.
-    auto kstep = [&](auto RD, auto GR, auto KR, auto CP, auto GC, auto DG, const Frag16 &Ac, const Frag16 &Bc,
-                     Frag16 &An, Frag16 &Bn, uint32_t tc, int32_t &ka, int32_t &kb) {
+    auto kstep = [&](auto RD, auto GR, auto KR, auto CP, auto GC, auto DG, const Frag16 &Ac, const FB &Bc,
+                     Frag16 &An, FB &Bn, uint32_t tc, int32_t &ka, int32_t &kb) {
         constexpr bool rd = decltype(RD)::value, cp = decltype(CP)::value, dg = decltype(DG)::value;
         constexpr int gr = decltype(GR)::value, kr = decltype(KR)::value, gc = decltype(GC)::value;
         const uint32_t k0 = kbeg + tc * BK;
@@ -457,9 +548,12 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
         __builtin_amdgcn_sched_barrier(0);
         sfor<NI * NJ>([&](auto MC) {
             constexpr int m = decltype(MC)::value, i = m / NJ, j = m % NJ, r = m / 4;
-            mfma16x16x32(acc[i][j], Ac.k[i], Bc.k[j]);
+            if constexpr (BKM) mfma16x16x32(acc[i][j], Ac.k[i], Bc.k[j]);
+            else mfma16x16x32(acc[i][j], Ac.k[i], Bc.op(j));
             if constexpr (rd && m % 4 == 0 && r < 8) fa.template read_one<gr, kr, r>(An);
-            if constexpr (rd && m % 4 == 0 && r >= 8) fb.template read_one<gr, kr, r - 8>(Bn);
+            constexpr int BS = BKM ? 4 : 2;   // slot spacing of the second operand's reads
+            if constexpr (rd && m >= 32 && (m - 32) % BS == 0 && (m - 32) / BS < NBR)
+                fb.template read_one<gr, kr, (m - 32) / BS>(Bn);
             if constexpr (cp && m % 4 == 2 && r < COPIES) da.issue_one(r, x, ka, sa + gc * STAGE_ELEMS, wave);
             if constexpr (cp && m % 4 == 2 && r >= COPIES) db.issue_one(r - COPIES, y, kb, sb + gc * STAGE_ELEMS, wave);
             if constexpr (dg && m % 4 == 1 && r < kP2Max) {
@@ -525,7 +619,7 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     sfor<8>([&](auto I) { fa.template read_one<0, 0, decltype(I)::value>(A0); });
-    sfor<8>([&](auto I) { fb.template read_one<0, 0, decltype(I)::value>(B0); });
+    sfor<NBR>([&](auto I) { fb.template read_one<0, 0, decltype(I)::value>(B0); });
     lds_wait<0>();
     A0.ready();
     B0.ready();
@@ -563,35 +657,33 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
 #ifndef TRA_K4K_M16
 #define TRA_K4K_M16 1
 #endif
-template <typename TO, int EPI, int CH = 0, bool YROW = false>
+// (The 32x32x16 body takes K-major second operands only.)
+template <bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false>
 __device__ __forceinline__ void mfma4k_run(const GemmView &v, const uint16_t *__restrict__ x,
                                            const uint16_t *__restrict__ y, TO *__restrict__ z,
                                            float *__restrict__ ws, const ChainEpi &ce)
 {
-#if TRA_K4K_M16
-    mfma4k16_body<TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
-#else
-    mfma4k_body<TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
-#endif
+    if constexpr (TRA_K4K_M16 || !BKM) mfma4k16_body<BKM, TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
+    else mfma4k_body<TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
 }
 
 // VEC: the staged epilogue (the output's four consecutive columns form one
 // aligned vector, and z / the workspace are 16-byte aligned)
-template <typename TO, bool VEC>
+template <bool BKM, typename TO, bool VEC>
 __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_bf16(GemmView v, const uint16_t *__restrict__ x,
                                                           const uint16_t *__restrict__ y, TO *__restrict__ z,
                                                           float *__restrict__ ws)
 {
-    mfma4k_run<TO, VEC ? 1 : 0>(v, x, y, z, ws, ChainEpi{});
+    mfma4k_run<BKM, TO, VEC ? 1 : 0>(v, x, y, z, ws, ChainEpi{});
 }
 
 // The product with a chain of two elementwise steps in its staged epilogue
-template <typename TO, int CH, bool YROW>
+template <bool BKM, typename TO, int CH, bool YROW>
 __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_chain(GemmView v, const uint16_t *__restrict__ x,
                                                            const uint16_t *__restrict__ y, TO *__restrict__ z,
                                                            ChainEpi ce)
 {
-    mfma4k_run<TO, 2, CH, YROW>(v, x, y, z, nullptr, ce);
+    mfma4k_run<BKM, TO, 2, CH, YROW>(v, x, y, z, nullptr, ce);
 }
 
 template <typename TO>
@@ -603,7 +695,8 @@ static int launch4k_t(const tra_plan_s &p, const void *x, const void *y, void *z
     const void *out = v.split > 1 ? ws : z;
     const bool vec = vec_ok && v.z_vec4 && ((uintptr_t)out % 16) == 0;
     void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *) =
-        vec ? k_mfma4k_bf16<TO, true> : k_mfma4k_bf16<TO, false>;
+        p.b_kmajor ? (vec ? k_mfma4k_bf16<true, TO, true> : k_mfma4k_bf16<true, TO, false>)
+                   : (vec ? k_mfma4k_bf16<false, TO, true> : k_mfma4k_bf16<false, TO, false>);
     hipLaunchKernelGGL(kern, grid, dim3(mf4k::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z,
                        (float *)ws);
     return (int)hipGetLastError();
@@ -626,8 +719,13 @@ static int launch4k_chain_t(const tra_plan_s &p, const void *x, const void *y, v
     for (int i = 0; i < kP2Max; ++i)
         if (ce.rn.mask[i] && ce.rn.st[0][i]) yrow = false;
     const bool ch = ce.join_a == J_SUB && ce.join_b == J_MUL;
-    void (*k)(GemmView, const uint16_t *, const uint16_t *, TO *, ChainEpi) =
-        !ch ? k_mfma4k_chain<TO, 0, false> : (yrow ? k_mfma4k_chain<TO, 1, true> : k_mfma4k_chain<TO, 1, false>);
+    void (*k)(GemmView, const uint16_t *, const uint16_t *, TO *, ChainEpi);
+    if (p.b_kmajor)
+        k = !ch ? k_mfma4k_chain<true, TO, 0, false>
+                : (yrow ? k_mfma4k_chain<true, TO, 1, true> : k_mfma4k_chain<true, TO, 1, false>);
+    else
+        k = !ch ? k_mfma4k_chain<false, TO, 0, false>
+                : (yrow ? k_mfma4k_chain<false, TO, 1, true> : k_mfma4k_chain<false, TO, 1, false>);
     hipLaunchKernelGGL(k, grid, dim3(mf4k::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z, ce);
     return (int)hipGetLastError();
 }

@@ -20,7 +20,8 @@
 #include "plan.h"
 
 // Matrix-core tile variants in order of preference: 4 = 256 x 256 on four
-// waves with 64-deep stages (both operands K-major, 64 contiguous k), 3 =
+// waves with 64-deep stages (first operand K-major, second K-major or
+// MN-major, 64 contiguous elements each), 3 =
 // 256 x 256 on four waves with 32-deep stages, 0 = 256 x 256 on eight waves,
 // 1 = 128 x 128, 2 = 64 x 64.
 #ifndef TRA_MFMA_ORDER
@@ -296,9 +297,12 @@ static bool lower_tile(tra_plan_s &p)
     // pick the first tile variant, in order of preference, that divides the problem
     static const int kMfmaOrder[] = {TRA_MFMA_ORDER};
     constexpr int kMfmaVariants = sizeof(kMfmaOrder) / sizeof(kMfmaOrder[0]);
-    // the 64-deep stages copy whole 128-byte rows of each operand: both K-major
-    // with 64 contiguous elements along the contracted labels
-    const bool k64 = ak && bk && contiguous_last(sk, 0, 64) && contiguous_last(sk, 1, 64);
+    // the 64-deep stages copy whole 128-byte rows of each operand: the first
+    // K-major with 64 contiguous elements along the contracted labels, the
+    // second likewise or MN-major with 64 contiguous elements along its
+    // output labels
+    const bool k64 = ak && contiguous_last(sk, 0, 64) &&
+                     ((bk && contiguous_last(sk, 1, 64)) || (!bk && contiguous_last(sn, 0, 64)));
     for (int n = 0; n < (mfma ? kMfmaVariants : 4) && pm && pn; ++n) {
         const int variant = mfma ? kMfmaOrder[n] : n;
         if (mfma && variant == 4 && !k64) continue;

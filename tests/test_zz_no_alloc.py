@@ -57,11 +57,12 @@ def test_plan_without_scratch_and_too_large_a_plan():
     p, z, z_ref = _pair("ij,jk->ik", {"i": 2048, "j": 256, "k": 2048}, {"i": 2, "j": 1, "k": 2}, "sqdiff", "sum",
                         "f32", "f32", 8400)
     assert p.info.workspace_bytes == 0 and torch.equal(z, z_ref)
-    big = tra.tra_plan("ij,jk->ik", {"i": 256, "j": 4096, "k": 256}, {"i": 1, "j": 1, "k": 1}, "mul", "sum",
+    # one output tile over a long contracted range: split 128 ways, 32 MiB of partials
+    big = tra.tra_plan("ij,jk->ik", {"i": 256, "j": 8192, "k": 256}, {"i": 1, "j": 1, "k": 1}, "mul", "sum",
                        "bf16", "f32")
     assert big.info.workspace_bytes > tra.tra_static_scratch_bytes()
-    x = torch.zeros(256 * 4096, dtype=torch.bfloat16, device=DEV)
-    y = torch.zeros(4096 * 256, dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros(256 * 8192, dtype=torch.bfloat16, device=DEV)
+    y = torch.zeros(8192 * 256, dtype=torch.bfloat16, device=DEV)
     out = torch.full((256 * 256,), 5.0, dtype=torch.float32, device=DEV)
     with pytest.raises(tra.TraError) as e:
         tra.tra_execute_static(big, x, y, out)
