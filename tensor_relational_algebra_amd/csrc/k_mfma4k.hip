@@ -42,14 +42,19 @@ constexpr int COPIES = STAGE_ELEMS / 8 / NT;    // 16-byte copies per thread per
 }  // namespace mf4k
 
 // 64-deep K-major stage, [row][64 k]: 8 granules of 16 bytes per row, granule
-// c of row r stored at c ^ swz_k8(r).  The fragment reads of a k-step hit one
-// granule column of 16 or 32 consecutive rows from a multiple of 16; the
-// permutation spreads any 8 consecutive rows, and the 8 rows of each parity
-// among 16 consecutive ones, over distinct granule slots, so the reads are
-// free of bank conflicts for 128- and 256-byte bank sets alike.  It depends
-// on row bits 0-3 only, so a fragment read's permutation depends on the
-// lane alone.
-__device__ __forceinline__ int swz_k8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// c of row r stored at c ^ swz_k8(r).  A fragment read takes one granule
+// column of 16 consecutive rows per 16 lanes (16x16x32) or of 32 per 32 lanes
+// (32x32x16).  The permutation, a linear map of row bits 0-4, spreads those
+// rows over distinct banks under each lane grouping the LDS could use for a
+// 16-byte read (8 or 16 consecutive lanes, 8 + 8 lanes 32 apart, 32
+// consecutive lanes).  Bits 0-4 of a fragment's row are the lane's and the
+// wave's, so the permutation depends on them alone.  (The LDS bank-conflict
+// counter reads the same for this map and for a simpler one of bits 0-3:
+// what it counts in the 16x16 kernels is not these reads' permutation.)
+__device__ __forceinline__ int swz_k8(int r)
+{
+    return (((r >> 1) ^ (r >> 4)) & 1) | ((((r) ^ (r >> 1) ^ (r >> 3)) & 1) << 1) | (((r >> 2) & 1) << 2);
+}
 
 // Per-thread plan of one operand's copies into a stage: copy i of thread tid
 // moves LDS granule p = i * NT + tid, i.e. row p / 8, slot p % 8, which holds
@@ -380,7 +385,8 @@ struct Frag16 {
 
 // Per-lane LDS bases of one operand's 16-row fragment reads, one per k-step
 // of a stage: block i of k-step ks reads row (2i + w)*16 + l % 16, granule
-// 4 ks + l / 16; block i and stage G add i * 4 KiB + G * 32 KiB.
+// 4 ks + l / 16 (permuted by row bits 0-4: the lane's and the wave's); block
+// i and stage G add i * 4 KiB + G * 32 KiB.
 struct FragAddr16 {
     uint32_t base[2];
     __device__ __forceinline__ void init(uint32_t lds, int w, int lane)
@@ -402,11 +408,14 @@ struct FragAddr16 {
 
 // 64-deep MN-major stage, [64 k][256 columns]: 32 granules of 16 bytes per
 // k-row, granule c of k-row k stored at c ^ swz_n8(k).  A transposing
-// fragment read of one 16-lane group covers 4 consecutive k-rows x 32 bytes;
-// the permutation moves the 4 rows' 32-byte pieces to distinct offsets
-// within 128 bytes (conflict free), and it depends on k % 4 only, i.e. on
-// the lane.
-__device__ __forceinline__ int swz_n8(int k) { return (k & 3) << 1; }
+// fragment read of one 16-lane group covers 4 consecutive k-rows x 32 bytes,
+// and the next group the same columns 8 k-rows further: k % 4 moves the 4
+// rows' 32-byte pieces to distinct offsets within 128 bytes, and k-row bit 3
+// moves the odd group's to the other 128 bytes, so each 32-lane half of a
+// read covers the 64 banks once.  (With k % 4 alone the two groups collide:
+// the bank-conflict counter of the blocked GEMM halved when bit 3 was added.)
+// It depends on the lane only.
+__device__ __forceinline__ int swz_n8(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
 // Per-thread copies of an MN-major operand into a stage: copy i of thread
 // tid moves LDS granule p = i * NT + tid, k-row p / 32, slot p % 32, which
@@ -458,28 +467,29 @@ struct Frag16N {
 // 16-lane group, output lane i element e is element i % 4 of source lane
 // 4e + i / 4).  Lane l = 16 g + s reads 4 columns 4(s % 4) .. +3 of its
 // block at k-row 8g + 4r + s / 4 (read r), so output lane s holds column s,
-// k 8g + 4r .. +3.  Block j = 2 jq + jb covers columns (2j + wn)*16 .. +15;
-// the permutation touches granule bits 1-2 (wn and jb), so there is one base
-// per jb, and jq, the read, the k-step and the stage add constants.
+// k 8g + 4r .. +3.  Block j covers columns (2j + wn)*16 .. +15, granules
+// 4j + 2wn + (s % 4)/2; the permutation touches granule bits 1-3 (wn and j
+// bits 0-1), so there is one base per j % 4, and j / 4, the read, the k-step
+// and the stage add constants.
 struct FragAddrN16 {
-    uint32_t base[2];
+    uint32_t base[4];
     __device__ __forceinline__ void init(uint32_t lds, int w, int lane)
     {
         const int g = lane >> 4, sl = lane & 15;
         const int k = 8 * g + (sl >> 2);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const int gran = (4 * jb + 2 * w + ((sl & 3) >> 1)) ^ swz_n8(k);
-            base[jb] = lds + (uint32_t)(k * 256 + gran * 8 + 4 * (sl & 1)) * 2;
+        for (int jl = 0; jl < 4; ++jl) {
+            const int gran = (4 * jl + 2 * w + ((sl & 3) >> 1)) ^ swz_n8(k);
+            base[jl] = lds + (uint32_t)(k * 256 + gran * 8 + 4 * (sl & 1)) * 2;
         }
     }
     // read R of k-step KS of stage G: block R / 2, half R % 2
     template <int G, int KS, int R>
     __device__ __forceinline__ void read_one(Frag16N &f) const
     {
-        constexpr int j = R / 2, h = R % 2, jb = j % 2, jq = j / 2;
-        constexpr int off = G * mf4k::STAGE_BYTES + (KS * 32 + 4 * h) * 256 * 2 + jq * 8 * 16;
-        f.t[j][h] = ds_read8_tr_at<off>(base[jb]);
+        constexpr int j = R / 2, h = R % 2, jl = j % 4, jh = j / 4;
+        constexpr int off = G * mf4k::STAGE_BYTES + (KS * 32 + 4 * h) * 256 * 2 + jh * 16 * 16;
+        f.t[j][h] = ds_read8_tr_at<off>(base[jl]);
     }
 };
 
