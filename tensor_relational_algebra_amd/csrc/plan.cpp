@@ -27,6 +27,14 @@
 #ifndef TRA_MFMA_ORDER
 #define TRA_MFMA_ORDER 4, 3, 0, 1, 2
 #endif
+// contiguous elements each operand needs along its staged dimension for the
+// 64-deep tile (one 16-byte copy granule).  With runs of 64 or more every
+// copy moves whole 128-byte lines; shorter runs (the attention projections
+// under the pages' blockings, the four-index contraction) still measured as
+// fast as or faster than the 32-deep tile.
+#ifndef TRA_K64_RUN
+#define TRA_K64_RUN 8
+#endif
 
 namespace tra {
 
@@ -297,12 +305,11 @@ static bool lower_tile(tra_plan_s &p)
     // pick the first tile variant, in order of preference, that divides the problem
     static const int kMfmaOrder[] = {TRA_MFMA_ORDER};
     constexpr int kMfmaVariants = sizeof(kMfmaOrder) / sizeof(kMfmaOrder[0]);
-    // the 64-deep stages copy whole 128-byte rows of each operand: the first
-    // K-major with 64 contiguous elements along the contracted labels, the
-    // second likewise or MN-major with 64 contiguous elements along its
-    // output labels
-    const bool k64 = ak && contiguous_last(sk, 0, 64) &&
-                     ((bk && contiguous_last(sk, 1, 64)) || (!bk && contiguous_last(sn, 0, 64)));
+    // the 64-deep tile: the first operand K-major, the second K-major or
+    // MN-major, each with TRA_K64_RUN contiguous elements along its staged
+    // dimension
+    const bool k64 = ak && contiguous_last(sk, 0, TRA_K64_RUN) &&
+                     ((bk && contiguous_last(sk, 1, TRA_K64_RUN)) || (!bk && contiguous_last(sn, 0, TRA_K64_RUN)));
     for (int n = 0; n < (mfma ? kMfmaVariants : 4) && pm && pn; ++n) {
         const int variant = mfma ? kMfmaOrder[n] : n;
         if (mfma && variant == 4 && !k64) continue;

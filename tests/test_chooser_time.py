@@ -88,7 +88,7 @@ def test_full_attention_layer_keeps_one_blocking():
 def test_time_model_pieces_and_errors():
     p = tra.tra_plan("sa,ahd->shd", {"s": 4096, "a": 4096, "h": 32, "d": 128},
                      {"s": 1, "a": 1, "h": 1, "d": 1}, "mul", "sum", "bf16", "bf16")
-    assert p.kernel == "mfma_bf16" and p.info.tile == 3
+    assert p.kernel == "mfma_bf16" and p.info.tile == 4
     ns = tra.tra_predict_ns(p)
     assert 100_000 < ns < 200_000          # ~2 * 4096^3 * 32 * 128 / 4096 flop at ~0.97 PFLOP/s
     r = tra.tra_predict_repartition_ns([16384, 8192], "f32")
