@@ -1,8 +1,7 @@
 // k_mfma4k.hip -- bf16 x bf16 -> fp32 join + sum aggregation on the four-wave
 // 256 x 256 matrix-core tile with 64-deep stages (tile variant 4), for
-// products whose first operand is stored contiguously along the contracted
-// labels ("K-major"), the second either K-major or contiguous along its
-// output labels ("MN-major"), each over 64 or more elements.
+// products whose operands are each stored contiguously along the contracted
+// labels ("K-major") or along their output labels ("MN-major").
 //
 // Page "EinDecomp：基于爱因斯坦求和与张量关系代数的自动张量并行分解算法",
 // section 2.2: the join of a key-matched pair of sub-tensors is a small
@@ -493,9 +492,9 @@ struct FragAddrN16 {
     }
 };
 
-// BKM: the second operand K-major (else MN-major: staged [k][column] and
-// read through the transposing LDS read).
-template <bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false>
+// AKM / BKM: the first / second operand K-major (else MN-major: staged
+// [k][row or column] and read through the transposing LDS read).
+template <bool AKM, bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false>
 __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t *__restrict__ x,
                                               const uint16_t *__restrict__ y, TO *__restrict__ z,
                                               float *__restrict__ ws, const ChainEpi &ce)
@@ -517,16 +516,17 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
     const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
     const uint32_t nk = (uint32_t)v.k_per_split / BK;
 
-    DmaPlan8<0> da;
+    typename std::conditional<AKM, DmaPlan8<0>, DmaPlanN8<0>>::type da;
     typename std::conditional<BKM, DmaPlan8<1>, DmaPlanN8<1>>::type db;
     da.init(v.gm, v.gk, m0, bx, tid);
     db.init(v.gn, v.gk, n0, by, tid);
-    FragAddr16 fa;
+    typename std::conditional<AKM, FragAddr16, FragAddrN16>::type fa;
     typename std::conditional<BKM, FragAddr16, FragAddrN16>::type fb;
     fa.init(lds_addr(sa), wm, lane);
     fb.init(lds_addr(sb), wn, lane);
+    using FA = typename std::conditional<AKM, Frag16, Frag16N>::type;
     using FB = typename std::conditional<BKM, Frag16, Frag16N>::type;
-    constexpr int NBR = BKM ? 8 : 16;   // fragment reads of the second operand per k-step
+    constexpr int NAR = AKM ? 8 : 16, NBR = BKM ? 8 : 16;   // fragment reads per operand and k-step
 
     Acc16 acc;
 #pragma unroll
@@ -537,17 +537,19 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
             for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
     acc16_fence(acc);   // the zeroing lands before the first product reads it
 
-    Frag16 A0, A1;   // k-steps 0 and 1 of a stage
+    FA A0, A1;   // k-steps 0 and 1 of a stage
     FB B0, B1;
 
-    // One 32-deep k-step: the 64 products on (Ac, Bc), one per slot; in
-    // slots 4r (r < 8) the reads of k-step KR of stage GR into An, and the
-    // reads into Bn in slots 32 + 4r (K-major) or 32 + 2r (MN-major, two per
-    // block); in slots 4r + 2 the copies of a k-tile into stage GC (X's from
+    // One 32-deep k-step: the 64 products on (Ac, Bc), one per slot; the
+    // reads of k-step KR of stage GR into An in slots 4r (K-major) or 2r
+    // (MN-major, two per block) of the first 32, into Bn likewise in the
+    // last 32; in slots 4r + 2 the copies of a k-tile into stage GC (X's from
     // ka for r < 8, then Y's from kb); in slots 4r + 1 one digit each of the
-    // operand offsets (ka, kb) of k-tile tc.
-    auto kstep = [&](auto RD, auto GR, auto KR, auto CP, auto GC, auto DG, const Frag16 &Ac, const FB &Bc,
-                     Frag16 &An, FB &Bn, uint32_t tc, int32_t &ka, int32_t &kb) {
+    // operand offsets (ka, kb) of k-tile tc.  (Reads gathered into the first
+    // slots instead measured 6% slower: one wave per SIMD issues four
+    // instructions per 16-cycle product.)
+    auto kstep = [&](auto RD, auto GR, auto KR, auto CP, auto GC, auto DG, const FA &Ac, const FB &Bc,
+                     FA &An, FB &Bn, uint32_t tc, int32_t &ka, int32_t &kb) {
         constexpr bool rd = decltype(RD)::value, cp = decltype(CP)::value, dg = decltype(DG)::value;
         constexpr int gr = decltype(GR)::value, kr = decltype(KR)::value, gc = decltype(GC)::value;
         const uint32_t k0 = kbeg + tc * BK;
@@ -558,10 +560,12 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
         __builtin_amdgcn_sched_barrier(0);
         sfor<NI * NJ>([&](auto MC) {
             constexpr int m = decltype(MC)::value, i = m / NJ, j = m % NJ, r = m / 4;
-            if constexpr (BKM) mfma16x16x32(acc[i][j], Ac.k[i], Bc.k[j]);
-            else mfma16x16x32(acc[i][j], Ac.k[i], Bc.op(j));
-            if constexpr (rd && m % 4 == 0 && r < 8) fa.template read_one<gr, kr, r>(An);
-            constexpr int BS = BKM ? 4 : 2;   // slot spacing of the second operand's reads
+            if constexpr (AKM && BKM) mfma16x16x32(acc[i][j], Ac.k[i], Bc.k[j]);
+            else if constexpr (AKM) mfma16x16x32(acc[i][j], Ac.k[i], Bc.op(j));
+            else if constexpr (BKM) mfma16x16x32(acc[i][j], Ac.op(i), Bc.k[j]);
+            else mfma16x16x32(acc[i][j], Ac.op(i), Bc.op(j));
+            constexpr int AS = AKM ? 4 : 2, BS = BKM ? 4 : 2;   // slot spacing of the reads
+            if constexpr (rd && m < 32 && m % AS == 0 && m / AS < NAR) fa.template read_one<gr, kr, m / AS>(An);
             if constexpr (rd && m >= 32 && (m - 32) % BS == 0 && (m - 32) / BS < NBR)
                 fb.template read_one<gr, kr, (m - 32) / BS>(Bn);
             if constexpr (cp && m % 4 == 2 && r < COPIES) da.issue_one(r, x, ka, sa + gc * STAGE_ELEMS, wave);
@@ -628,7 +632,7 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    sfor<8>([&](auto I) { fa.template read_one<0, 0, decltype(I)::value>(A0); });
+    sfor<NAR>([&](auto I) { fa.template read_one<0, 0, decltype(I)::value>(A0); });
     sfor<NBR>([&](auto I) { fb.template read_one<0, 0, decltype(I)::value>(B0); });
     lds_wait<0>();
     A0.ready();
@@ -667,33 +671,33 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
 #ifndef TRA_K4K_M16
 #define TRA_K4K_M16 1
 #endif
-// (The 32x32x16 body takes K-major second operands only.)
-template <bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false>
+// (The 32x32x16 body takes two K-major operands only.)
+template <bool AKM, bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false>
 __device__ __forceinline__ void mfma4k_run(const GemmView &v, const uint16_t *__restrict__ x,
                                            const uint16_t *__restrict__ y, TO *__restrict__ z,
                                            float *__restrict__ ws, const ChainEpi &ce)
 {
-    if constexpr (TRA_K4K_M16 || !BKM) mfma4k16_body<BKM, TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
+    if constexpr (TRA_K4K_M16 || !AKM || !BKM) mfma4k16_body<AKM, BKM, TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
     else mfma4k_body<TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
 }
 
 // VEC: the staged epilogue (the output's four consecutive columns form one
 // aligned vector, and z / the workspace are 16-byte aligned)
-template <bool BKM, typename TO, bool VEC>
+template <bool AKM, bool BKM, typename TO, bool VEC>
 __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_bf16(GemmView v, const uint16_t *__restrict__ x,
                                                           const uint16_t *__restrict__ y, TO *__restrict__ z,
                                                           float *__restrict__ ws)
 {
-    mfma4k_run<BKM, TO, VEC ? 1 : 0>(v, x, y, z, ws, ChainEpi{});
+    mfma4k_run<AKM, BKM, TO, VEC ? 1 : 0>(v, x, y, z, ws, ChainEpi{});
 }
 
 // The product with a chain of two elementwise steps in its staged epilogue
-template <bool BKM, typename TO, int CH, bool YROW>
+template <bool AKM, bool BKM, typename TO, int CH, bool YROW>
 __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_chain(GemmView v, const uint16_t *__restrict__ x,
                                                            const uint16_t *__restrict__ y, TO *__restrict__ z,
                                                            ChainEpi ce)
 {
-    mfma4k_run<BKM, TO, 2, CH, YROW>(v, x, y, z, nullptr, ce);
+    mfma4k_run<AKM, BKM, TO, 2, CH, YROW>(v, x, y, z, nullptr, ce);
 }
 
 template <typename TO>
@@ -704,9 +708,16 @@ static int launch4k_t(const tra_plan_s &p, const void *x, const void *y, void *z
     dim3 grid((v.gm.total / mf4k::BM) * (v.gn.total / mf4k::BN), v.gb.total, v.split);
     const void *out = v.split > 1 ? ws : z;
     const bool vec = vec_ok && v.z_vec4 && ((uintptr_t)out % 16) == 0;
-    void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *) =
-        p.b_kmajor ? (vec ? k_mfma4k_bf16<true, TO, true> : k_mfma4k_bf16<true, TO, false>)
-                   : (vec ? k_mfma4k_bf16<false, TO, true> : k_mfma4k_bf16<false, TO, false>);
+    void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *);
+#define TRA_PICK4K(AK, BK) kern = vec ? k_mfma4k_bf16<AK, BK, TO, true> : k_mfma4k_bf16<AK, BK, TO, false>
+    if (p.a_kmajor) {
+        if (p.b_kmajor) TRA_PICK4K(true, true);
+        else TRA_PICK4K(true, false);
+    } else {
+        if (p.b_kmajor) TRA_PICK4K(false, true);
+        else TRA_PICK4K(false, false);
+    }
+#undef TRA_PICK4K
     hipLaunchKernelGGL(kern, grid, dim3(mf4k::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z,
                        (float *)ws);
     return (int)hipGetLastError();
@@ -730,12 +741,17 @@ static int launch4k_chain_t(const tra_plan_s &p, const void *x, const void *y, v
         if (ce.rn.mask[i] && ce.rn.st[0][i]) yrow = false;
     const bool ch = ce.join_a == J_SUB && ce.join_b == J_MUL;
     void (*k)(GemmView, const uint16_t *, const uint16_t *, TO *, ChainEpi);
-    if (p.b_kmajor)
-        k = !ch ? k_mfma4k_chain<true, TO, 0, false>
-                : (yrow ? k_mfma4k_chain<true, TO, 1, true> : k_mfma4k_chain<true, TO, 1, false>);
-    else
-        k = !ch ? k_mfma4k_chain<false, TO, 0, false>
-                : (yrow ? k_mfma4k_chain<false, TO, 1, true> : k_mfma4k_chain<false, TO, 1, false>);
+#define TRA_PICK4KC(AK, BK)                                                                                    \
+    k = !ch ? k_mfma4k_chain<AK, BK, TO, 0, false>                                                             \
+            : (yrow ? k_mfma4k_chain<AK, BK, TO, 1, true> : k_mfma4k_chain<AK, BK, TO, 1, false>)
+    if (p.a_kmajor) {
+        if (p.b_kmajor) TRA_PICK4KC(true, true);
+        else TRA_PICK4KC(true, false);
+    } else {
+        if (p.b_kmajor) TRA_PICK4KC(false, true);
+        else TRA_PICK4KC(false, false);
+    }
+#undef TRA_PICK4KC
     hipLaunchKernelGGL(k, grid, dim3(mf4k::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z, ce);
     return (int)hipGetLastError();
 }

@@ -20,8 +20,8 @@
 #include "plan.h"
 
 // Matrix-core tile variants in order of preference: 4 = 256 x 256 on four
-// waves with 64-deep stages (first operand K-major, second K-major or
-// MN-major, 64 contiguous elements each), 3 =
+// waves with 64-deep stages and 16x16x32 products (runs of TRA_K64_RUN
+// contiguous elements along each operand's staged dimension), 3 =
 // 256 x 256 on four waves with 32-deep stages, 0 = 256 x 256 on eight waves,
 // 1 = 128 x 128, 2 = 64 x 64.
 #ifndef TRA_MFMA_ORDER
@@ -305,10 +305,9 @@ static bool lower_tile(tra_plan_s &p)
     // pick the first tile variant, in order of preference, that divides the problem
     static const int kMfmaOrder[] = {TRA_MFMA_ORDER};
     constexpr int kMfmaVariants = sizeof(kMfmaOrder) / sizeof(kMfmaOrder[0]);
-    // the 64-deep tile: the first operand K-major, the second K-major or
-    // MN-major, each with TRA_K64_RUN contiguous elements along its staged
-    // dimension
-    const bool k64 = ak && contiguous_last(sk, 0, TRA_K64_RUN) &&
+    // the 64-deep tile: each operand K-major or MN-major with TRA_K64_RUN
+    // contiguous elements along its staged dimension
+    const bool k64 = ((ak && contiguous_last(sk, 0, TRA_K64_RUN)) || (!ak && contiguous_last(sm, 0, TRA_K64_RUN))) &&
                      ((bk && contiguous_last(sk, 1, TRA_K64_RUN)) || (!bk && contiguous_last(sn, 0, TRA_K64_RUN)));
     for (int n = 0; n < (mfma ? kMfmaVariants : 4) && pm && pn; ++n) {
         const int variant = mfma ? kMfmaOrder[n] : n;
