@@ -66,21 +66,20 @@ TRAFFIC_SRCS = {
     "recut": ("tensor_relational_algebra_amd/csrc/k_simple.hip",) + COMMON_SRCS,
 }
 # squared distance: `bench.py --steps 3 --warmup 1 --no-cpu-baseline --only sqdist`;
-# FETCH_SIZE read 524,300 KiB and WRITE_SIZE 1,048,576 KiB for the 1,048,576 KiB
-# copy, hence factors 2.0 and 1.0
+# the blocked GEMM and its re-cut: `bench.py --steps 3 --warmup 1 --no-cpu-baseline
+# --no-extra`.  The copy calibration was taken in the same session: FETCH_SIZE read
+# 524,336 KiB and WRITE_SIZE 1,048,619 KiB for the 1,048,576 KiB copy, hence factors
+# 2.0 and 1.0.
 TRAFFIC = {
-    "sqdist": {"src_sha": "439559b799ea0b06", "fetch_kib": 40664.8, "write_kib": 262144.0,
+    "sqdist": {"src_sha": "e60d668d8529fb0d", "fetch_kib": 40698.5, "write_kib": 262144.0,
                "fetch_factor": 2.0, "write_factor": 1.0,
                "profile": "profiles/valu_tile_sqdist_8192x256x8192_hbm_traffic.md"},
-    # the blocked GEMM and its re-cut: `bench.py --steps 3 --warmup 1 --no-cpu-baseline
-    # --no-extra`, the same copy calibration taken in the same session (FETCH_SIZE
-    # 524,330 KiB, WRITE_SIZE 1,048,633 KiB for the 1,048,576 KiB copy)
-    "gemm": {"src_sha": "d560bdf268a78a63", "fetch_kib": 1573336.7, "write_kib": 524288.0,
+    "gemm": {"src_sha": "4979149cd510695b", "fetch_kib": 1580485.2, "write_kib": 526336.0,
              "fetch_factor": 2.0, "write_factor": 1.0,
-             "profile": "profiles/mfma4_gemm25d_16384x8192x8192_hbm_traffic.md"},
-    "recut": {"src_sha": "a7e9ecca8b98b29a", "fetch_kib": 262176.0, "write_kib": 524289.4,
+             "profile": "profiles/mfma4k_gemm25d_16384x8192x8192_hbm_traffic.md"},
+    "recut": {"src_sha": "27b277ed94e55d19", "fetch_kib": 262179.3, "write_kib": 524290.8,
               "fetch_factor": 2.0, "write_factor": 1.0,
-              "profile": "profiles/mfma4_gemm25d_16384x8192x8192_hbm_traffic.md"},
+              "profile": "profiles/mfma4k_gemm25d_16384x8192x8192_hbm_traffic.md"},
 }
 
 
