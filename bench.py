@@ -246,14 +246,17 @@ def _measured_roofs(tra, dev, stream) -> dict:
     import torch
     wg, iters = 1024, 20000
     out = torch.empty(wg * 256, dtype=torch.float32, device=dev)
-    fl = 2.0 * 32 * 32 * 16 * 8 * 4 * iters * wg
     loops = {}
-    for key, distinct in (("mfma_loop", False), ("mfma_loop_random_operands", True)):
-        tra.tra_probe_mfma_loop(wg, 100, out, distinct)
-        ms = _events_time(lambda: tra.tra_probe_mfma_loop(wg, iters, out, distinct), 3, stream)
+    for key, mode in (("mfma_loop", 0), ("mfma_loop_random_operands", 1), ("mfma16_loop_random_operands", 2)):
+        it = iters if mode < 2 else iters // 4
+        fl = (2.0 * 32 * 32 * 16 * 8 if mode < 2 else 2.0 * 16 * 16 * 32 * 64) * 4 * it * wg
+        tra.tra_probe_mfma_loop(wg, 100, out, mode)
+        ms = _events_time(lambda: tra.tra_probe_mfma_loop(wg, it, out, mode), 3, stream)
+        what = (f"{wg} workgroups x 4 waves, {it} rounds of 8 independent 32x32x16 bf16 products"
+                + (", 8 random operand pairs" if mode else ", one operand pair")) if mode < 2 else \
+            f"{wg} workgroups x 4 waves, {it} rounds of 64 independent 16x16x32 bf16 products, 8 random operand pairs"
         loops[key] = {"TFLOP/s": round(fl / ms / 1e9, 1), "frac_of_published": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4),
-                      "what": f"{wg} workgroups x 4 waves, {iters} rounds of 8 independent 32x32x16 bf16 products"
-                              + (", 8 random operand pairs" if distinct else ", one operand pair")}
+                      "what": what}
     n = 1 << 28
     src = torch.zeros(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)

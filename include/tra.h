@@ -541,9 +541,11 @@ int tra_graph_destroy(tra_graph_t graph);
  * pair; otherwise each takes its own random values (of the size of the
  * products' N(0, 0.02) inputs), so the multipliers switch operands from one
  * product to the next as in a real product, and the chip's power limit sets
- * the clock as it does there.  out: device buffer of workgroups * 256 floats
- * (written, values meaningless).  Errors: TRA_E_NULL, TRA_E_OP (counts < 1),
- * TRA_E_HIP.
+ * the clock as it does there.  distinct_operands = 2: rounds of 64 independent
+ * 16x16x32 products (2 * 16 * 16 * 32 * 64 * 4 flop per round and workgroup)
+ * on random operands, the product form of the 64-deep tile.  out: device
+ * buffer of workgroups * 256 floats (written, values meaningless).  Errors:
+ * TRA_E_NULL, TRA_E_OP (counts < 1), TRA_E_HIP.
  */
 int tra_probe_mfma_loop(int workgroups, int iters, int distinct_operands, float *out, void *hip_stream);
 

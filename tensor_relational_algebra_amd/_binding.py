@@ -220,11 +220,12 @@ def tra_execute_static(plan: Plan, x: torch.Tensor, y: Optional[torch.Tensor], z
     return z
 
 
-def tra_probe_mfma_loop(workgroups: int, iters: int, out: torch.Tensor, distinct_operands: bool = False,
+def tra_probe_mfma_loop(workgroups: int, iters: int, out: torch.Tensor, distinct_operands: int = 0,
                         stream=None) -> None:
-    """Matrix-core loop for the measured ceiling (see include/tra.h)."""
+    """Matrix-core loop for the measured ceiling (see include/tra.h): 0 one
+    operand pair, 1 random operands, 2 random operands on 16x16x32 products."""
     _dev_ptr(out, "out", workgroups * 256, DTYPES["f32"])
-    _check(lib().tra_probe_mfma_loop(int(workgroups), int(iters), int(bool(distinct_operands)), out.data_ptr(),
+    _check(lib().tra_probe_mfma_loop(int(workgroups), int(iters), int(distinct_operands), out.data_ptr(),
                                      _stream(stream)))
 
 
