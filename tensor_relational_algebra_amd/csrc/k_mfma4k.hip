@@ -48,8 +48,10 @@ constexpr int COPIES = STAGE_ELEMS / 8 / NT;    // 16-byte copies per thread per
 // 16-byte read (8 or 16 consecutive lanes, 8 + 8 lanes 32 apart, 32
 // consecutive lanes).  Bits 0-4 of a fragment's row are the lane's and the
 // wave's, so the permutation depends on them alone.  (The LDS bank-conflict
-// counter reads the same for this map and for a simpler one of bits 0-3:
-// what it counts in the 16x16 kernels is not these reads' permutation.)
+// counter reads the same for this map and for a simpler one of bits 0-3,
+// about four cycles per read, and near zero with the fragment reads taken
+// out: it counts something in how the LDS serves these 16-byte reads that
+// neither permutation changes, and the kernel's cycles did not move with it.)
 __device__ __forceinline__ int swz_k8(int r)
 {
     return (((r >> 1) ^ (r >> 4)) & 1) | ((((r) ^ (r >> 1) ^ (r >> 3)) & 1) << 1) | (((r >> 2) & 1) << 2);
@@ -403,6 +405,13 @@ struct FragAddr16 {
         constexpr int off = G * mf4k::STAGE_BYTES + R * 32 * mf4k::BK * 2;
         f.k[R] = ds_read16_at<off>(base[KS]);
     }
+    // the same from the stage at byte offset soff (a runtime ring slot)
+    template <int KS, int R>
+    __device__ __forceinline__ void read_rt(Frag16 &f, uint32_t soff) const
+    {
+        constexpr int off = R * 32 * mf4k::BK * 2;
+        f.k[R] = ds_read16_at<off>(base[KS] + soff);
+    }
 };
 
 // 64-deep MN-major stage, [64 k][256 columns]: 32 granules of 16 bytes per
@@ -490,7 +499,35 @@ struct FragAddrN16 {
         constexpr int off = G * mf4k::STAGE_BYTES + (KS * 32 + 4 * h) * 256 * 2 + jh * 16 * 16;
         f.t[j][h] = ds_read8_tr_at<off>(base[jl]);
     }
+    template <int KS, int R>
+    __device__ __forceinline__ void read_rt(Frag16N &f, uint32_t soff) const
+    {
+        constexpr int j = R / 2, h = R % 2, jl = j % 4, jh = j / 4;
+        constexpr int off = (KS * 32 + 4 * h) * 256 * 2 + jh * 16 * 16;
+        f.t[j][h] = ds_read8_tr_at<off>(base[jl] + soff);
+    }
 };
+
+// One piece of digit q of operand T's k-tile offset: PH 0 extracts the
+// digit of k0, PH 1 adds its term to koff.  The empty asm statements pin each
+// piece to its product slot: without them the compiler gathered all digits
+// of a k-step into one run of ~50 scalar instructions between two products,
+// which the wave issues one at a time while the matrix core idles.
+template <int PH, int T>
+__device__ __forceinline__ void digit_piece(uint32_t k0, int q, const Pow2Group &g, uint32_t &dig, int32_t &koff)
+{
+    if constexpr (PH == 0) {
+        uint32_t kk = k0;
+        asm volatile("" : "+s"(kk));
+        dig = (kk >> g.sh[q]) & g.mask[q];
+        asm volatile("" : "+s"(dig));
+    } else {
+        uint32_t dd = dig;
+        asm volatile("" : "+s"(dd));
+        koff += (int32_t)dd * g.st[T][q];
+        asm volatile("" : "+s"(koff));
+    }
+}
 
 // AKM / BKM: the first / second operand K-major (else MN-major: staged
 // [k][row or column] and read through the transposing LDS read).
@@ -500,7 +537,7 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
                                               float *__restrict__ ws, const ChainEpi &ce)
 {
     using namespace mf4k;
-    __shared__ __attribute__((aligned(16))) uint16_t sa[2 * STAGE_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t sa[3 * STAGE_ELEMS];   // 96 + 64 KiB: all of the LDS
     __shared__ __attribute__((aligned(16))) uint16_t sb[2 * STAGE_ELEMS];
     constexpr int NI = 2 * TM, NJ = 2 * TN;   // 16-row and 16-column blocks of a wave
 
@@ -541,84 +578,94 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
     FB B0, B1;
 
     // One 32-deep k-step: the 64 products on (Ac, Bc), one per slot; the
-    // reads of k-step KR of stage GR into An in slots 4r (K-major) or 2r
-    // (MN-major, two per block) of the first 32, into Bn likewise in the
-    // last 32; in slots 4r + 2 the copies of a k-tile into stage GC (X's from
-    // ka for r < 8, then Y's from kb); in slots 4r + 1 one digit each of the
-    // operand offsets (ka, kb) of k-tile tc.  (Reads gathered into the first
-    // slots instead measured 6% slower: one wave per SIMD issues four
-    // instructions per 16-cycle product.)
-    auto kstep = [&](auto RD, auto GR, auto KR, auto CP, auto GC, auto DG, const FA &Ac, const FB &Bc,
-                     FA &An, FB &Bn, uint32_t tc, int32_t &ka, int32_t &kb) {
-        constexpr bool rd = decltype(RD)::value, cp = decltype(CP)::value, dg = decltype(DG)::value;
-        constexpr int gr = decltype(GR)::value, kr = decltype(KR)::value, gc = decltype(GC)::value;
-        const uint32_t k0 = kbeg + tc * BK;
-        if constexpr (dg) {
-            ka = 0;
-            kb = 0;
-        }
+    // reads of k-step KR into An (X's stage at byte offset a_rd) in slots 4r
+    // (K-major) or 2r (MN-major, two per block) of the first 32, into Bn (Y's
+    // stage GBR) likewise in the last 32; in slots 8r + 6 copy r of a k-tile,
+    // X's into the stage at element offset a_wr (XC, from ka) or Y's into
+    // stage GBW (YC, from kb); in odd slots 4q + 1 and 4q + 3 the two pieces
+    // of digit q of ka (DA, of k-tile ta) or kb (DB, of k-tile tb).  (Reads
+    // gathered into the first slots instead measured 6% slower: one wave per
+    // SIMD issues four instructions per 16-cycle product.)
+    auto kstep = [&](auto RD, auto GBR, auto KR, auto XC, auto YC, auto GBW, auto DA, auto DB, const FA &Ac,
+                     const FB &Bc, FA &An, FB &Bn, uint32_t a_rd, uint32_t a_wr, uint32_t ta, uint32_t tb,
+                     int32_t &ka, int32_t &kb) {
+        constexpr bool rd = decltype(RD)::value, xc = decltype(XC)::value, yc = decltype(YC)::value;
+        constexpr bool dga = decltype(DA)::value, dgb = decltype(DB)::value;
+        constexpr int gbr = decltype(GBR)::value, kr = decltype(KR)::value, gbw = decltype(GBW)::value;
+        const uint32_t ka0 = kbeg + ta * BK, kb0 = kbeg + tb * BK;
+        uint32_t dig = 0;
+        if constexpr (dga) ka = 0;
+        if constexpr (dgb) kb = 0;
         __builtin_amdgcn_sched_barrier(0);
         sfor<NI * NJ>([&](auto MC) {
-            constexpr int m = decltype(MC)::value, i = m / NJ, j = m % NJ, r = m / 4;
+            constexpr int m = decltype(MC)::value, i = m / NJ, j = m % NJ, r = m / 8;
             if constexpr (AKM && BKM) mfma16x16x32(acc[i][j], Ac.k[i], Bc.k[j]);
             else if constexpr (AKM) mfma16x16x32(acc[i][j], Ac.k[i], Bc.op(j));
             else if constexpr (BKM) mfma16x16x32(acc[i][j], Ac.op(i), Bc.k[j]);
             else mfma16x16x32(acc[i][j], Ac.op(i), Bc.op(j));
             constexpr int AS = AKM ? 4 : 2, BS = BKM ? 4 : 2;   // slot spacing of the reads
-            if constexpr (rd && m < 32 && m % AS == 0 && m / AS < NAR) fa.template read_one<gr, kr, m / AS>(An);
+            if constexpr (rd && m < 32 && m % AS == 0 && m / AS < NAR) fa.template read_rt<kr, m / AS>(An, a_rd);
             if constexpr (rd && m >= 32 && (m - 32) % BS == 0 && (m - 32) / BS < NBR)
-                fb.template read_one<gr, kr, (m - 32) / BS>(Bn);
-            if constexpr (cp && m % 4 == 2 && r < COPIES) da.issue_one(r, x, ka, sa + gc * STAGE_ELEMS, wave);
-            if constexpr (cp && m % 4 == 2 && r >= COPIES) db.issue_one(r - COPIES, y, kb, sb + gc * STAGE_ELEMS, wave);
-            if constexpr (dg && m % 4 == 1 && r < kP2Max) {
-                ka += (int32_t)((k0 >> v.gk.sh[r]) & v.gk.mask[r]) * v.gk.st[0][r];
-                kb += (int32_t)((k0 >> v.gk.sh[r]) & v.gk.mask[r]) * v.gk.st[1][r];
-            }
+                fb.template read_one<gbr, kr, (m - 32) / BS>(Bn);
+            if constexpr (xc && m % 8 == 6) da.issue_one(r, x, ka, sa + a_wr, wave);
+            if constexpr (yc && m % 8 == 6) db.issue_one(r, y, kb, sb + gbw * STAGE_ELEMS, wave);
+            constexpr int u = (m - 1) / 2;
+            if constexpr (dga && m % 2 == 1 && u / 2 < kP2Max) digit_piece<u % 2, 0>(ka0, u / 2, v.gk, dig, ka);
+            if constexpr (dgb && m % 2 == 1 && u / 2 < kP2Max) digit_piece<u % 2, 1>(kb0, u / 2, v.gk, dig, kb);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    static_assert(2 * COPIES <= 16 && kP2Max <= 16, "one copy and one digit per four product slots");
+    static_assert(COPIES == 8 && 2 * kP2Max <= 32, "a copy per eight product slots, a digit per four");
     using T_ = std::true_type;
     using F_ = std::false_type;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
-    // k-tile t in stage G.  On entry F0 = (A0, B0) holds its k-step 0 (its
-    // reads may be in flight).  k-step 0 reads k-step 1; then the wave has all
-    // its fragments of stage G (waited for) and the copies of k-tile t + 1
-    // into the other stage have landed: a barrier publishes that stage and
-    // frees stage G.  k-step 1 reads k-step 0 of the other stage and copies
-    // k-tile t + 2 into stage G (near the end: the last k-tile again, in
-    // bounds, the count of copies per step fixed).
-    auto step = [&](auto GC, uint32_t t) {
-        using GO = std::integral_constant<int, 1 - decltype(GC)::value>;
-        int32_t ka = 0, kb = 0;
+    // X's stages form a ring of three (k-tile t in slot t % 3), Y's a ring of
+    // two (slot t % 2).  k-tile t: on entry F0 = (A0, B0) holds its k-step 0
+    // (reads may be in flight).  k-step 0 reads k-step 1, copies X's k-tile
+    // t + 2 into X slot (t + 2) % 3 (that of k-tile t - 1, free since the
+    // barrier of k-tile t - 1) and takes the digits of Y's k-tile t + 2.  Then
+    // the wave has read all its fragments of k-tile t and the copies of k-tile
+    // t + 1 have landed (those of X's k-tile t + 2, issued last, may still be
+    // in flight): a barrier publishes k-tile t + 1 and frees Y's slot t % 2.
+    // k-step 1 reads k-step 0 of k-tile t + 1, copies Y's k-tile t + 2 into
+    // slot t % 2 and takes the digits of X's k-tile t + 3.  So every copy has
+    // a whole k-tile of products to land, and the copies of a k-tile spread
+    // over both its k-steps.  Near the end the last k-tile is copied again (in
+    // bounds, the count of copies per k-step fixed).  ia = t % 3.
+    auto step = [&](auto GB, uint32_t t, uint32_t ia, int32_t &ka, int32_t &kb) {
+        using GO = std::integral_constant<int, 1 - decltype(GB)::value>;
+        const uint32_t i1 = ia == 2 ? 0 : ia + 1, i2 = i1 == 2 ? 0 : i1 + 1;
         lds_wait<0>();
         A0.ready();
         B0.ready();
-        kstep(T_{}, GC, I1{}, F_{}, GC, T_{}, A0, B0, A1, B1, min(t + 2, nk - 1), ka, kb);
-        lds_wait<0>();   // this wave's reads of stage G are done
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        kstep(T_{}, GB, I1{}, T_{}, F_{}, GB, F_{}, T_{}, A0, B0, A1, B1, ia * STAGE_BYTES, i2 * STAGE_ELEMS, 0u,
+              min(t + 2, nk - 1), ka, kb);
+        lds_wait<0>();   // this wave's reads of k-tile t are done
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(COPIES));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         A1.ready();
         B1.ready();
-        kstep(T_{}, GO{}, I0{}, T_{}, GC, F_{}, A1, B1, A0, B0, 0u, ka, kb);
+        kstep(T_{}, GO{}, I0{}, F_{}, T_{}, GB, T_{}, F_{}, A1, B1, A0, B0, i1 * STAGE_BYTES, 0u, min(t + 3, nk - 1),
+              0u, ka, kb);
     };
-    auto tail_step = [&](uint32_t) {
-        int32_t ka = 0, kb = 0;
+    auto tail_step = [&](uint32_t ia, int32_t &ka, int32_t &kb) {
         lds_wait<0>();
         A0.ready();
         B0.ready();
-        kstep(T_{}, I0{}, I1{}, F_{}, I0{}, F_{}, A0, B0, A1, B1, 0u, ka, kb);
+        kstep(T_{}, I0{}, I1{}, F_{}, F_{}, I0{}, F_{}, F_{}, A0, B0, A1, B1, ia * STAGE_BYTES, 0u, 0u, 0u, ka, kb);
         lds_wait<0>();
         A1.ready();
         B1.ready();
-        kstep(F_{}, I0{}, I0{}, F_{}, I0{}, F_{}, A1, B1, A0, B0, 0u, ka, kb);
+        kstep(F_{}, I0{}, I0{}, F_{}, F_{}, I0{}, F_{}, F_{}, A1, B1, A0, B0, 0u, 0u, 0u, 0u, ka, kb);
     };
 
-    // prologue: k-tiles 0 and 1 in flight, k-step 0 of the first read
+    // prologue: k-tiles 0 and 1 in flight into slots 0 and 1 of each ring,
+    // X's offset of k-tile 2, k-step 0 of the first read
+    int32_t ka, kb = 0;
     {
         const uint32_t k1 = min(1u, nk - 1);
         const int32_t a0 = p2off<0>(v.gk, kbeg), b0 = p2off<1>(v.gk, kbeg);
@@ -627,27 +674,30 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
         sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, b0, sb, wave); });
         sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, a1, sa + STAGE_ELEMS, wave); });
         sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, b1, sb + STAGE_ELEMS, wave); });
+        ka = p2off<0>(v.gk, kbeg + min(2u, nk - 1) * BK);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * COPIES));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    sfor<NAR>([&](auto I) { fa.template read_one<0, 0, decltype(I)::value>(A0); });
+    sfor<NAR>([&](auto I) { fa.template read_rt<0, decltype(I)::value>(A0, 0u); });
     sfor<NBR>([&](auto I) { fb.template read_one<0, 0, decltype(I)::value>(B0); });
     lds_wait<0>();
     A0.ready();
     B0.ready();
 
     // two k-tiles per loop body; no read in flight at a branch or merge
-    uint32_t t = 0;
+    uint32_t t = 0, ia = 0;
     for (; t + 2 <= nk; t += 2) {
-        step(I0{}, t);
-        step(I1{}, t + 1);
+        step(I0{}, t, ia, ka, kb);
+        ia = ia == 2 ? 0 : ia + 1;
+        step(I1{}, t + 1, ia, ka, kb);
+        ia = ia == 2 ? 0 : ia + 1;
         lds_wait<0>();
         A0.ready();
         B0.ready();
     }
-    if (t < nk) tail_step(t);
+    if (t < nk) tail_step(ia, ka, kb);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_wait<0>();
     acc16_fence(acc);   // every product has written its accumulator before any read
