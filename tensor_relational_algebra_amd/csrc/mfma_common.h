@@ -44,14 +44,16 @@ constexpr int MF_STAGES = 4;    // LDS ring: 3 k-tiles in flight while one is co
 // whose per-group operand is read by every tile of the group, such as the
 // attention weighted sum) the run is taken over all groups, so that a
 // group's tiles share one XCD and its operand is fetched once.
-__device__ __forceinline__ void mfma_tile_of(uint32_t nb, uint32_t tiles_n, uint32_t n_groups, uint32_t &bidx,
-                                             uint32_t &tm, uint32_t &tn)
+// (bx, by): the tile's index within its output group and the group; tile
+// (bx, by) runs on XCD (bx + nb * by) % 8.
+__device__ __forceinline__ void mfma_tile_at(uint32_t bx, uint32_t by, uint32_t nb, uint32_t tiles_n,
+                                             uint32_t n_groups, uint32_t &bidx, uint32_t &tm, uint32_t &tn)
 {
-    uint32_t b = blockIdx.x;
-    bidx = blockIdx.y;
+    uint32_t b = bx;
+    bidx = by;
     const uint32_t n_lin = nb * n_groups;
     if (nb <= 64 && n_groups > 1 && n_lin % 8 == 0) {
-        const uint32_t l = blockIdx.x + nb * blockIdx.y;
+        const uint32_t l = bx + nb * by;
         const uint32_t lin = (l % 8) * (n_lin / 8) + l / 8;
         bidx = lin / nb;
         b = lin % nb;
@@ -66,6 +68,11 @@ __device__ __forceinline__ void mfma_tile_of(uint32_t nb, uint32_t tiles_n, uint
     uint32_t r = b % per;
     tm = first + r % gs;
     tn = r / gs;
+}
+__device__ __forceinline__ void mfma_tile_of(uint32_t nb, uint32_t tiles_n, uint32_t n_groups, uint32_t &bidx,
+                                             uint32_t &tm, uint32_t &tn)
+{
+    mfma_tile_at(blockIdx.x, blockIdx.y, nb, tiles_n, n_groups, bidx, tm, tn);
 }
 
 template <int... Is, typename F>

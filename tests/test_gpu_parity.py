@@ -395,6 +395,31 @@ def test_k_major_products_on_the_64_deep_tile(case):
     assert plan.kernel == "mfma_bf16" and plan.info.tile == 4, (plan.kernel, plan.info.tile)
 
 
+SHORT_CASES = [
+    # (spec, bounds, d, post_scale): one or two 64-deep k-tiles, fp32 output,
+    # more output tiles than compute units (the persistent tile loop)
+    ("ik,jk->ij", {"i": 8192, "j": 4096, "k": 128}, {"i": 1, "j": 1, "k": 1}, 1.0),
+    ("ik,jk->ij", {"i": 8192, "j": 4096, "k": 64}, {"i": 2, "j": 2, "k": 1}, 1.0),
+    ("hsd,htd->hst", {"h": 8, "s": 2048, "t": 2048, "d": 128}, {"h": 2, "s": 2, "t": 1, "d": 1}, 0.088),
+    ("ki,kj->ij", {"i": 4096, "j": 8192, "k": 128}, {"i": 1, "j": 1, "k": 1}, 1.0),
+    ("ik,kj->ij", {"i": 8192, "j": 4096, "k": 128}, {"i": 2, "j": 1, "k": 2}, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SHORT_CASES, ids=["kk-two-ktiles", "kk-one-ktile-blocked", "scores-batched",
+                                                    "mn-mn", "k-mn-blocked"])
+def test_short_products_over_many_tiles(case):
+    """Short contractions (64 or 128 deep) with fp32 output and 512 output
+    tiles: each workgroup walks several tiles, overlapping one tile's stores
+    with the next tile's copies and products.  16384 sampled outputs spread
+    over every tile against the oracle, for all operand layouts."""
+    spec, bounds, d, scale = case
+    c = wl.EinsumCase(f"short_{spec}", 66, spec, bounds, d, "mul", "sum", "bf16", "f32", (N002, N002),
+                      post_scale=scale)
+    err, plan = check(c, sample=16384, seed=11)
+    assert plan.kernel == "mfma_bf16" and plan.info.tile == 4, (plan.kernel, plan.info.tile)
+
+
 @pytest.mark.parametrize("which", ["dX", "dA"])
 def test_blocked_gemm_backward_full_size_sampled(which):
     """The blocked GEMM's backward products at full size: dX = dY A^T
