@@ -475,7 +475,10 @@ __device__ __forceinline__ void mfma4_store_staged(const GemmView &v, T *__restr
     for (int ph = 0; ph < 2; ++ph) rowbase[ph] = p2off<1>(v.gm, m0 + ph * 128 + wave * 32) + bz;
     mfma4_staged<T>(acc, st_a, st_b, SCALE ? v.post_scale : 1.f, wave, lane, [](auto) {}, [&](auto PH, auto RR, const auto &d) {
         const int32_t o = rowbase[decltype(PH)::value] + __builtin_amdgcn_readlane(band_row, decltype(RR)::value) + on;
-        *(typename std::remove_const<typename std::remove_reference<decltype(d)>::type>::type *)(out + o) = d;
+        // streaming stores (1-2% on the blocked GEMM and on the re-cut that
+        // reads its output next)
+        __builtin_nontemporal_store(
+            d, (typename std::remove_const<typename std::remove_reference<decltype(d)>::type>::type *)(out + o));
     });
 }
 
