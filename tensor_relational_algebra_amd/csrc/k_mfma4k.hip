@@ -807,19 +807,18 @@ __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_short(GemmView v, const uin
     da.init(v.gm, v.gk, 0, 0, tid);
     db.init(v.gn, v.gk, 0, 0, tid);
     int32_t ta, tb, tz;   // the tile's offsets in X, Y and Z
-    auto setup = [&](uint32_t l) {
+    auto setup = [&](uint32_t l, int32_t &oa, int32_t &ob, int32_t &oz) {
         uint32_t tm, tn, bidx;
         mfma_tile_at(l % nb, l / nb, nb, tiles_n, v.gb.total, bidx, tm, tn);
         const uint32_t m0 = tm * BM, n0 = tn * BN;
-        ta = p2off<0>(v.gm, m0) + p2off<0>(v.gb, bidx);
-        tb = p2off<0>(v.gn, n0) + p2off<1>(v.gb, bidx);
-        tz = p2off<1>(v.gm, m0) + p2off<1>(v.gn, n0) + p2off<2>(v.gb, bidx);
+        oa = p2off<0>(v.gm, m0) + p2off<0>(v.gb, bidx);
+        ob = p2off<0>(v.gn, n0) + p2off<1>(v.gb, bidx);
+        oz = p2off<1>(v.gm, m0) + p2off<1>(v.gn, n0) + p2off<2>(v.gb, bidx);
     };
-    auto issue = [&]() {
-        sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, ta, sa, wave); });
-        sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, tb, sb, wave); });
-        sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, ta + a1, sa + STAGE_ELEMS, wave); });
-        sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, tb + b1, sb + STAGE_ELEMS, wave); });
+    // k-tile 1's copies (k-tile 0's go out in the product slots)
+    auto issue_k1 = [&](int32_t oa, int32_t ob) {
+        sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, oa + a1, sa + STAGE_ELEMS, wave); });
+        sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, ob + b1, sb + STAGE_ELEMS, wave); });
     };
 
     // staging: per-lane write bases for even and odd 16-column blocks j
@@ -843,9 +842,12 @@ __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_short(GemmView v, const uin
     FB B0, B1;
     // one 32-deep k-step: 64 products, the next k-step's reads in the slots
     // of the main kernel (A's in the first 32, B's in the last 32)
-    auto kstep = [&](auto RD, auto GBR, auto KR, const FA &Ac, const FB &Bc, FA &An, FB &Bn, uint32_t a_rd) {
+    // CP: the next tile's k-tile 0 copies into slot 0 in this k-step, X's
+    // (bit 0, slots 8r + 6) and Y's (bit 1, slots 8r + 2), from offsets oa, ob
+    auto kstep = [&](auto RD, auto GBR, auto KR, auto CP, const FA &Ac, const FB &Bc, FA &An, FB &Bn,
+                     uint32_t a_rd, int32_t oa, int32_t ob) {
         constexpr bool rd = decltype(RD)::value;
-        constexpr int gbr = decltype(GBR)::value, kr = decltype(KR)::value;
+        constexpr int gbr = decltype(GBR)::value, kr = decltype(KR)::value, cp = decltype(CP)::value;
         __builtin_amdgcn_sched_barrier(0);
         sfor<NI * NJ>([&](auto MC) {
             constexpr int m = decltype(MC)::value, i = m / NJ, j = m % NJ;
@@ -857,21 +859,36 @@ __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_short(GemmView v, const uin
             if constexpr (rd && m < 32 && m % AS == 0 && m / AS < NAR) fa.template read_rt<kr, m / AS>(An, a_rd);
             if constexpr (rd && m >= 32 && (m - 32) % BS == 0 && (m - 32) / BS < NBR)
                 fb.template read_one<gbr, kr, (m - 32) / BS>(Bn);
+            if constexpr ((cp & 1) && m % 8 == 6) da.issue_one(m / 8, x, oa, sa, wave);
+            if constexpr ((cp & 2) && m % 8 == 2) db.issue_one(m / 8, y, ob, sb, wave);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
+    static_assert(COPIES == 8, "one copy per eight product slots");
     using T_ = std::true_type;
     using F_ = std::false_type;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
 
-    setup(vid);
-    issue();
+    setup(vid, ta, tb, tz);
+    sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, ta, sa, wave); });
+    sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, tb, sb, wave); });
+    if constexpr (NK == 2) issue_k1(ta, tb);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     for (;;) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        // the next tile (the last tile copies itself again: its slots are
+        // free by then, and the count of copies stays fixed)
+        const uint32_t next = vid + gridDim.x;
+        const bool more = next < n_lin;
+        int32_t nta = ta, ntb = tb, ntz = tz;
+        if (more) setup(next, nta, ntb, ntz);
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -884,31 +901,30 @@ __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_short(GemmView v, const uin
         lds_wait<0>();
         A0.ready();
         B0.ready();
-        kstep(T_{}, I0{}, I1{}, A0, B0, A1, B1, 0u);
+        kstep(T_{}, I0{}, I1{}, C0{}, A0, B0, A1, B1, 0u, 0, 0);
         lds_wait<0>();
         A1.ready();
         B1.ready();
+        lds_barrier();   // every wave is done reading slot 0: the next tile's k-tile 0 may land there
         if constexpr (NK == 2) {
-            kstep(T_{}, I1{}, I0{}, A1, B1, A0, B0, (uint32_t)STAGE_BYTES);
+            kstep(T_{}, I1{}, I0{}, C1{}, A1, B1, A0, B0, (uint32_t)STAGE_BYTES, nta, ntb);
             lds_wait<0>();
             A0.ready();
             B0.ready();
-            kstep(T_{}, I1{}, I1{}, A0, B0, A1, B1, (uint32_t)STAGE_BYTES);
+            kstep(T_{}, I1{}, I1{}, C2{}, A0, B0, A1, B1, (uint32_t)STAGE_BYTES, nta, ntb);
             lds_wait<0>();
             A1.ready();
             B1.ready();
+            kstep(F_{}, I0{}, I0{}, C0{}, A1, B1, A0, B0, 0u, 0, 0);
+        } else {
+            kstep(F_{}, I0{}, I0{}, C3{}, A1, B1, A0, B0, 0u, nta, ntb);
         }
-        kstep(F_{}, I0{}, I0{}, A1, B1, A0, B0, 0u);
         acc16_fence(acc);
         lds_barrier();   // every wave is done with the operand slots
 
         const int32_t ctz = tz + on;
-        const uint32_t next = vid + gridDim.x;
         __builtin_amdgcn_sched_barrier(0);
-        if (next < n_lin) {
-            setup(next);
-            issue();
-        }
+        if constexpr (NK == 2) issue_k1(nta, ntb);
         __builtin_amdgcn_sched_barrier(0);
         sfor<NI>([&](auto P) {
             constexpr int p = decltype(P)::value;
@@ -950,8 +966,16 @@ __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_short(GemmView v, const uin
                 __builtin_nontemporal_store(d[r], (u32x4_t *)(z + o));
             });
         });
-        if (next >= n_lin) break;
+        if (!more) {
+            // the last tile's own copies again: landed before the workgroup
+            // gives up its LDS
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            break;
+        }
         vid = next;
+        ta = nta;
+        tb = ntb;
+        tz = ntz;
         // the next tile's copies, then this tile's 64 stores per lane: the
         // copies have landed once at most 63 operations are outstanding (the
         // barrier at the top of the loop then publishes them; the last
