@@ -420,13 +420,29 @@ __device__ __forceinline__ void mfma4_staged(const ACC &acc, uint32_t st_a, uint
         if constexpr (L16) {
             // blocks i = 4 ph .. 4 ph + 3 of the 16-row blocks: block il = i - 4 ph
             // goes to st_a (il < 2) or st_b, at row (il % 2)*32 + wm*16 + 4(l/16) + e
-            sfor<4 * 2 * TN * 4>([&](auto W) {
-                constexpr int w = decltype(W)::value;
-                constexpr int il = w / (2 * TN * 4), j = (w / 4) % (2 * TN), e = w % 4;
-                constexpr int off = (((il % 2) * 32 + e) * BN + j * WN * 16) * ES;
-                const float val = acc[4 * ph + il][j][e] * sc;
-                if constexpr (ES == 4) ds_write4_at<off>(wb[il / 2], __builtin_bit_cast(uint32_t, val));
-                else ds_write2_at<off>(wb[il / 2], (uint32_t)f32_to_bf16(val));
+            // per block row: its 32 values first, then their writes (one
+            // register per value, so the accumulator reads, products and
+            // writes pipeline instead of chaining through one register)
+            sfor<4>([&](auto IL) {
+                constexpr int il = decltype(IL)::value, i = 4 * ph + il;
+                __builtin_amdgcn_sched_barrier(0);
+                ACC &ma = const_cast<ACC &>(acc);   // the caller's (non-const) accumulators, values unchanged
+                asm volatile("" : "+a"(ma[i][0]), "+a"(ma[i][1]), "+a"(ma[i][2]), "+a"(ma[i][3]), "+a"(ma[i][4]),
+                                  "+a"(ma[i][5]), "+a"(ma[i][6]), "+a"(ma[i][7]));
+                uint32_t val[2 * TN * 4];
+                sfor<2 * TN * 4>([&](auto W) {
+                    constexpr int w = decltype(W)::value, j = w / 4, e = w % 4;
+                    const float f = ma[i][j][e] * sc;
+                    if constexpr (ES == 4) val[w] = __builtin_bit_cast(uint32_t, f);
+                    else val[w] = (uint32_t)f32_to_bf16(f);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+                sfor<2 * TN * 4>([&](auto W) {
+                    constexpr int w = decltype(W)::value, j = w / 4, e = w % 4;
+                    constexpr int off = (((il % 2) * 32 + e) * BN + j * WN * 16) * ES;
+                    if constexpr (ES == 4) ds_write4_at<off>(wb[il / 2], val[w]);
+                    else ds_write2_at<off>(wb[il / 2], val[w]);
+                });
             });
         } else {
             sfor<2 * TN * 16>([&](auto W) {
