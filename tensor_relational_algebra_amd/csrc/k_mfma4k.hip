@@ -1020,7 +1020,7 @@ static int launch4k_t(const tra_plan_s &p, const void *x, const void *y, void *z
     if constexpr (std::is_same<TO, float>::value) {
         const uint32_t n_lin = grid.x * grid.y;
         const int cus = device_cus();
-        if (short_enabled() && vec && v.split == 1 && v.k_per_split <= 2 * mf4k::BK && cus > 0 &&
+        if (short_enabled() && vec && v.split == 1 && v.k_per_split <= 2 * mf4k::BK && cus >= 8 &&
             n_lin > (uint32_t)cus) {
             void (*ks)(GemmView, const uint16_t *, const uint16_t *, float *);
             const bool two = v.k_per_split == 2 * mf4k::BK;
