@@ -117,8 +117,9 @@ typedef struct {
     int32_t n_labels;
     char labels[32];          /* canonical label order, NUL-terminated */
     int32_t tile;             /* tile-kernel variant (mfma: 4 = 256x256 on four waves with 64-deep
-                                 stages, for two operands contiguous along the contracted labels
-                                 over 64 or more elements; 3 = 256x256 on four waves with 32-deep
+                                 stages, for operands with runs of 8 or more elements along the
+                                 dimension they are staged by; 5 = the same stages on a 256x128
+                                 tile, for 128-wide outputs; 3 = 256x256 on four waves with 32-deep
                                  stages, 0 = 256x256 on eight waves, 1 = 128x128, 2 = 64x64;
                                  valu_tile: 1 = int32 max-plus / min-plus with the packed 16-bit
                                  path, see tra_execute, else 0); -1 if none */

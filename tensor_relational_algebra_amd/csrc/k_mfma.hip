@@ -40,6 +40,7 @@ namespace tra {
 TileShape mfma_tile_shape(int variant)
 {
     if (variant == 4) return {256, 256, 64};
+    if (variant == 5) return {256, 128, 64};   // the 64-deep tile, 128 columns
     if (variant == 3) return {256, 256, MF_BK};
     if (variant < 0 || variant > 2) return {0, 0, 0};
     MfmaCfg c = mfma_cfg(variant);
@@ -679,7 +680,8 @@ static int launch_tile(const tra_plan_s &p, const void *x, const void *y, void *
     case 0: return launch_layout<0, TO>(p, x, y, z, ws, s);
     case 1: return launch_layout<1, TO>(p, x, y, z, ws, s);
     case 3: return launch_layout<3, TO>(p, x, y, z, ws, s);
-    case 4: return launch_mfma4k(p, x, y, z, ws, s, std::is_same<TO, float>::value, vec_epilogue_enabled());
+    case 4:
+    case 5: return launch_mfma4k(p, x, y, z, ws, s, std::is_same<TO, float>::value, vec_epilogue_enabled());
     default: return launch_layout<2, TO>(p, x, y, z, ws, s);
     }
 }
@@ -743,7 +745,8 @@ static int launch_chain_t(const tra_plan_s &p, const void *x, const void *y, voi
     case 0:
     case 3:
     case 4: return launch_chain_v<0, TO>(p, x, y, z, ce, s);   // the same 256 x 256 tile on eight waves
-    case 1: return launch_chain_v<1, TO>(p, x, y, z, ce, s);
+    case 1:
+    case 5: return launch_chain_v<1, TO>(p, x, y, z, ce, s);   // 128 x 128 divides the narrow tile's 256 x 128
     default: return launch_chain_v<2, TO>(p, x, y, z, ce, s);
     }
 }

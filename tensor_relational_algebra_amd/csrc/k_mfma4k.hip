@@ -61,10 +61,11 @@ __device__ __forceinline__ int swz_k8(int r)
 // moves LDS granule p = i * NT + tid, i.e. row p / 8, slot p % 8, which holds
 // granule (p % 8) ^ swz_k8(row) of that row.  A wave's 64 copies fill 1 KiB
 // of consecutive LDS (8 rows) from 8 whole 128-byte row segments.  T selects
-// the operand's stride slot of the contracted digits (0 = X, 1 = Y).
-template <int T>
+// the operand's stride slot of the contracted digits (0 = X, 1 = Y); ROWS is
+// the stage's rows (256, or 128 for the narrow tile's second operand).
+template <int T, int ROWS = 256>
 struct DmaPlan8 {
-    static constexpr int N = mf4k::COPIES;
+    static constexpr int N = ROWS * mf4k::BK / 8 / mf4k::NT;
     int32_t src[N];   // source offset minus the k-tile term
 
     __device__ __forceinline__ void init(const Pow2Group &g_rows, const Pow2Group &gk, uint32_t r0, int32_t base,
@@ -357,30 +358,38 @@ __device__ __forceinline__ void mfma16x16x32(floatx4_t &acc, const u32x4_t &a, c
 
 // Binds every accumulator to the accumulator registers at one point of the
 // instruction stream (an asm that reads and writes each of them).
-__device__ __forceinline__ void acc16_bind(Acc16 &acc)
+template <int NJ>
+__device__ __forceinline__ void acc16_bind(floatx4_t (&acc)[2 * mf4::TM][NJ])
 {
 #pragma unroll
-    for (int i = 0; i < 2 * mf4::TM; ++i)
-        asm volatile(""
-                     : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
-                       "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    for (int i = 0; i < 2 * mf4::TM; ++i) {
+        if constexpr (NJ == 8)
+            asm volatile(""
+                         : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                           "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+        else
+            asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]));
+    }
 }
 // Wait states between every write of the accumulators before it and every
 // read after it (the two binds fix the order: volatile asm keeps its order).
-__device__ __forceinline__ void acc16_fence(Acc16 &acc)
+template <int NJ>
+__device__ __forceinline__ void acc16_fence(floatx4_t (&acc)[2 * mf4::TM][NJ])
 {
+    static_assert(NJ == 8 || NJ == 4, "eight or four 16-column blocks per wave");
     acc16_bind(acc);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
     acc16_bind(acc);
 }
 
-// One operand's fragments of one 32-deep k-step: 8 blocks of 16 rows.
+// One operand's fragments of one 32-deep k-step: N blocks of 16 rows.
+template <int N = 8>
 struct Frag16 {
-    u32x4_t k[8];
+    u32x4_t k[N];
     __device__ __forceinline__ void ready()
     {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lds_ready(k[i]);
+        for (int i = 0; i < N; ++i) lds_ready(k[i]);
     }
 };
 
@@ -388,6 +397,7 @@ struct Frag16 {
 // of a stage: block i of k-step ks reads row (2i + w)*16 + l % 16, granule
 // 4 ks + l / 16 (permuted by row bits 0-4: the lane's and the wave's); block
 // i and stage G add i * 4 KiB + G * 32 KiB.
+template <int SB = mf4k::STAGE_BYTES>   // bytes of one stage of the operand
 struct FragAddr16 {
     uint32_t base[2];
     __device__ __forceinline__ void init(uint32_t lds, int w, int lane)
@@ -399,15 +409,15 @@ struct FragAddr16 {
             base[ks] = lds + (uint32_t)(r * mf4k::BK + c * 8) * 2;
         }
     }
-    template <int G, int KS, int R>
-    __device__ __forceinline__ void read_one(Frag16 &f) const
+    template <int G, int KS, int R, typename F>
+    __device__ __forceinline__ void read_one(F &f) const
     {
-        constexpr int off = G * mf4k::STAGE_BYTES + R * 32 * mf4k::BK * 2;
+        constexpr int off = G * SB + R * 32 * mf4k::BK * 2;
         f.k[R] = ds_read16_at<off>(base[KS]);
     }
     // the same from the stage at byte offset soff (a runtime ring slot)
-    template <int KS, int R>
-    __device__ __forceinline__ void read_rt(Frag16 &f, uint32_t soff) const
+    template <int KS, int R, typename F>
+    __device__ __forceinline__ void read_rt(F &f, uint32_t soff) const
     {
         constexpr int off = R * 32 * mf4k::BK * 2;
         f.k[R] = ds_read16_at<off>(base[KS] + soff);
@@ -429,9 +439,10 @@ __device__ __forceinline__ int swz_n8(int k) { return ((k & 3) << 1) | (((k >> 3
 // tid moves LDS granule p = i * NT + tid, k-row p / 32, slot p % 32, which
 // holds granule (p % 32) ^ swz_n8(k) of that k-row (a wave's 64 copies: two
 // whole 512-byte k-rows).
-template <int T>
+template <int T, int COLS = 256>   // COLS: the stage's columns (256, or 128)
 struct DmaPlanN8 {
-    static constexpr int N = mf4k::COPIES;
+    static constexpr int GPR = COLS / 8;   // granules per k-row
+    static constexpr int N = COLS * mf4k::BK / 8 / mf4k::NT;
     int32_t src[N];
 
     __device__ __forceinline__ void init(const Pow2Group &g_cols, const Pow2Group &gk, uint32_t c0, int32_t base,
@@ -441,7 +452,7 @@ struct DmaPlanN8 {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int p = i * mf4k::NT + tid;
-            const int k = p >> 5, gl = (p & 31) ^ swz_n8(p >> 5);
+            const int k = p / GPR, gl = (p % GPR) ^ swz_n8(p / GPR);
             src[i] = cbase + p2off<0>(g_cols, gl * 8) + p2off<T>(gk, k);
         }
     }
@@ -455,12 +466,13 @@ struct DmaPlanN8 {
 // One operand's fragments of one 32-deep k-step for an MN-major operand:
 // per 16-column block two transposing 8-byte reads (k 8(l/16) .. +3 and
 // +4 .. +7 of column l % 16).
+template <int N = 8>
 struct Frag16N {
-    u32x2_t t[8][2];
+    u32x2_t t[N][2];
     __device__ __forceinline__ void ready()
     {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < N; ++j) {
             lds_ready(t[j][0]);
             lds_ready(t[j][1]);
         }
@@ -479,6 +491,7 @@ struct Frag16N {
 // 4j + 2wn + (s % 4)/2; the permutation touches granule bits 1-3 (wn and j
 // bits 0-1), so there is one base per j % 4, and j / 4, the read, the k-step
 // and the stage add constants.
+template <int COLS = 256>   // the stage's columns (256, or 128: then j < 4, one base each)
 struct FragAddrN16 {
     uint32_t base[4];
     __device__ __forceinline__ void init(uint32_t lds, int w, int lane)
@@ -488,22 +501,22 @@ struct FragAddrN16 {
 #pragma unroll
         for (int jl = 0; jl < 4; ++jl) {
             const int gran = (4 * jl + 2 * w + ((sl & 3) >> 1)) ^ swz_n8(k);
-            base[jl] = lds + (uint32_t)(k * 256 + gran * 8 + 4 * (sl & 1)) * 2;
+            base[jl] = lds + (uint32_t)(k * COLS + gran * 8 + 4 * (sl & 1)) * 2;
         }
     }
     // read R of k-step KS of stage G: block R / 2, half R % 2
-    template <int G, int KS, int R>
-    __device__ __forceinline__ void read_one(Frag16N &f) const
+    template <int G, int KS, int R, typename F>
+    __device__ __forceinline__ void read_one(F &f) const
     {
         constexpr int j = R / 2, h = R % 2, jl = j % 4, jh = j / 4;
-        constexpr int off = G * mf4k::STAGE_BYTES + (KS * 32 + 4 * h) * 256 * 2 + jh * 16 * 16;
+        constexpr int off = G * COLS * mf4k::BK * 2 + (KS * 32 + 4 * h) * COLS * 2 + jh * 16 * 16;
         f.t[j][h] = ds_read8_tr_at<off>(base[jl]);
     }
-    template <int KS, int R>
-    __device__ __forceinline__ void read_rt(Frag16N &f, uint32_t soff) const
+    template <int KS, int R, typename F>
+    __device__ __forceinline__ void read_rt(F &f, uint32_t soff) const
     {
         constexpr int j = R / 2, h = R % 2, jl = j % 4, jh = j / 4;
-        constexpr int off = (KS * 32 + 4 * h) * 256 * 2 + jh * 16 * 16;
+        constexpr int off = (KS * 32 + 4 * h) * COLS * 2 + jh * 16 * 16;
         f.t[j][h] = ds_read8_tr_at<off>(base[jl] + soff);
     }
 };
@@ -531,41 +544,47 @@ __device__ __forceinline__ void digit_piece(uint32_t k0, int q, const Pow2Group 
 
 // AKM / BKM: the first / second operand K-major (else MN-major: staged
 // [k][row or column] and read through the transposing LDS read).
-template <bool AKM, bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false>
+template <bool AKM, bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false, int BNW = 256>
 __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t *__restrict__ x,
                                               const uint16_t *__restrict__ y, TO *__restrict__ z,
                                               float *__restrict__ ws, const ChainEpi &ce)
 {
     using namespace mf4k;
-    __shared__ __attribute__((aligned(16))) uint16_t sa[3 * STAGE_ELEMS];   // 96 + 64 KiB: all of the LDS
-    __shared__ __attribute__((aligned(16))) uint16_t sb[2 * STAGE_ELEMS];
-    constexpr int NI = 2 * TM, NJ = 2 * TN;   // 16-row and 16-column blocks of a wave
+    // BNW: the tile's columns, 256 or 128 (each wave then 128 x 64)
+    static_assert(BNW == 256 || BNW == 128, "256 x 256 or 256 x 128 tiles");
+    constexpr int SBE = BNW * BK, SBB = SBE * 2;   // one stage of the second operand
+    __shared__ __attribute__((aligned(16))) uint16_t sa[3 * STAGE_ELEMS];   // 96 + 64 (or 32) KiB
+    __shared__ __attribute__((aligned(16))) uint16_t sb[2 * SBE];
+    constexpr int NI = 2 * TM, NJ = BNW / 32;   // 16-row and 16-column blocks of a wave
+    constexpr int NP = NI * NJ, HALF = NP / 2;   // products per k-step, and half of them
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const uint32_t tiles_n = v.gn.total / BN;
+    const uint32_t tiles_n = v.gn.total / BNW;
     const uint32_t nb = (v.gm.total / BM) * tiles_n;
     uint32_t tm, tn, bidx;
     mfma_tile_of(nb, tiles_n, v.gb.total, bidx, tm, tn);
-    const uint32_t m0 = tm * BM, n0 = tn * BN;
+    const uint32_t m0 = tm * BM, n0 = tn * BNW;
     const int32_t bx = p2off<0>(v.gb, bidx), by = p2off<1>(v.gb, bidx), bz = p2off<2>(v.gb, bidx);
     const uint32_t kbeg = blockIdx.z * (uint32_t)v.k_per_split;
     const uint32_t nk = (uint32_t)v.k_per_split / BK;
 
     typename std::conditional<AKM, DmaPlan8<0>, DmaPlanN8<0>>::type da;
-    typename std::conditional<BKM, DmaPlan8<1>, DmaPlanN8<1>>::type db;
+    using DPB = typename std::conditional<BKM, DmaPlan8<1, BNW>, DmaPlanN8<1, BNW>>::type;
+    DPB db;
     da.init(v.gm, v.gk, m0, bx, tid);
     db.init(v.gn, v.gk, n0, by, tid);
-    typename std::conditional<AKM, FragAddr16, FragAddrN16>::type fa;
-    typename std::conditional<BKM, FragAddr16, FragAddrN16>::type fb;
+    typename std::conditional<AKM, FragAddr16<>, FragAddrN16<>>::type fa;
+    typename std::conditional<BKM, FragAddr16<SBB>, FragAddrN16<BNW>>::type fb;
     fa.init(lds_addr(sa), wm, lane);
     fb.init(lds_addr(sb), wn, lane);
-    using FA = typename std::conditional<AKM, Frag16, Frag16N>::type;
-    using FB = typename std::conditional<BKM, Frag16, Frag16N>::type;
-    constexpr int NAR = AKM ? 8 : 16, NBR = BKM ? 8 : 16;   // fragment reads per operand and k-step
+    using FA = typename std::conditional<AKM, Frag16<>, Frag16N<>>::type;
+    using FB = typename std::conditional<BKM, Frag16<NJ>, Frag16N<NJ>>::type;
+    constexpr int NAR = AKM ? 8 : 16, NBR = BKM ? NJ : 2 * NJ;   // fragment reads per operand and k-step
+    constexpr int CB = DPB::N;                                  // the second operand's copies per k-tile
 
-    Acc16 acc;
+    floatx4_t acc[NI][NJ];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -597,25 +616,27 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
         if constexpr (dga) ka = 0;
         if constexpr (dgb) kb = 0;
         __builtin_amdgcn_sched_barrier(0);
-        sfor<NI * NJ>([&](auto MC) {
-            constexpr int m = decltype(MC)::value, i = m / NJ, j = m % NJ, r = m / 8;
+        sfor<NP>([&](auto MC) {
+            constexpr int m = decltype(MC)::value, i = m / NJ, j = m % NJ;
             if constexpr (AKM && BKM) mfma16x16x32(acc[i][j], Ac.k[i], Bc.k[j]);
             else if constexpr (AKM) mfma16x16x32(acc[i][j], Ac.k[i], Bc.op(j));
             else if constexpr (BKM) mfma16x16x32(acc[i][j], Ac.op(i), Bc.k[j]);
             else mfma16x16x32(acc[i][j], Ac.op(i), Bc.op(j));
-            constexpr int AS = AKM ? 4 : 2, BS = BKM ? 4 : 2;   // slot spacing of the reads
-            if constexpr (rd && m < 32 && m % AS == 0 && m / AS < NAR) fa.template read_rt<kr, m / AS>(An, a_rd);
-            if constexpr (rd && m >= 32 && (m - 32) % BS == 0 && (m - 32) / BS < NBR)
-                fb.template read_one<gbr, kr, (m - 32) / BS>(Bn);
-            if constexpr (xc && m % 8 == 6) da.issue_one(r, x, ka, sa + a_wr, wave);
-            if constexpr (yc && m % 8 == 6) db.issue_one(r, y, kb, sb + gbw * STAGE_ELEMS, wave);
+            constexpr int AS = HALF / NAR, BS = HALF / NBR;   // slot spacing of the reads
+            constexpr int XS = NP / COPIES, YS = NP / CB;     // and of the copies
+            if constexpr (rd && m < HALF && m % AS == 0) fa.template read_rt<kr, m / AS>(An, a_rd);
+            if constexpr (rd && m >= HALF && (m - HALF) % BS == 0)
+                fb.template read_one<gbr, kr, (m - HALF) / BS>(Bn);
+            if constexpr (xc && m % XS == XS - 2) da.issue_one(m / XS, x, ka, sa + a_wr, wave);
+            if constexpr (yc && m % YS == YS - 2) db.issue_one(m / YS, y, kb, sb + gbw * SBE, wave);
             constexpr int u = (m - 1) / 2;
             if constexpr (dga && m % 2 == 1 && u / 2 < kP2Max) digit_piece<u % 2, 0>(ka0, u / 2, v.gk, dig, ka);
             if constexpr (dgb && m % 2 == 1 && u / 2 < kP2Max) digit_piece<u % 2, 1>(kb0, u / 2, v.gk, dig, kb);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    static_assert(COPIES == 8 && 2 * kP2Max <= 32, "a copy per eight product slots, a digit per four");
+    static_assert(NP % COPIES == 0 && NP % CB == 0 && 4 * kP2Max <= NP && HALF % NAR == 0 && HALF % NBR == 0,
+                  "copies and reads spread evenly over a k-step, a digit per four of its slots");
     using T_ = std::true_type;
     using F_ = std::false_type;
     using I0 = std::integral_constant<int, 0>;
@@ -671,12 +692,12 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
         const int32_t a0 = p2off<0>(v.gk, kbeg), b0 = p2off<1>(v.gk, kbeg);
         const int32_t a1 = p2off<0>(v.gk, kbeg + k1 * BK), b1 = p2off<1>(v.gk, kbeg + k1 * BK);
         sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, a0, sa, wave); });
-        sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, b0, sb, wave); });
+        sfor<CB>([&](auto I) { db.issue_one(decltype(I)::value, y, b0, sb, wave); });
         sfor<COPIES>([&](auto I) { da.issue_one(decltype(I)::value, x, a1, sa + STAGE_ELEMS, wave); });
-        sfor<COPIES>([&](auto I) { db.issue_one(decltype(I)::value, y, b1, sb + STAGE_ELEMS, wave); });
+        sfor<CB>([&](auto I) { db.issue_one(decltype(I)::value, y, b1, sb + SBE, wave); });
         ka = p2off<0>(v.gk, kbeg + min(2u, nk - 1) * BK);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * COPIES));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(COPIES + CB));   // k-tile 0 has landed
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -704,7 +725,13 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
 
     const bool split = v.split > 1;
     float *wsp = split ? ws + (int64_t)blockIdx.z * v.z_elems : nullptr;
-    if constexpr (EPI == 2) {
+    if constexpr (BNW != 256) {
+        // the narrow tile stores straight from the accumulators (its outputs
+        // are small next to the operands it streams)
+        static_assert(EPI == 0, "the 256 x 128 tile has the direct epilogue only");
+        mfma4_store_direct16<TO, NJ>(v, z, wsp, split, acc, m0, n0, bz, wave);
+        return;
+    } else if constexpr (EPI == 2) {
         lds_barrier();
         mfma4_chain_staged<TO, CH, YROW>(v, z, ce, acc, lds_addr(sa), lds_addr(sb), m0, n0, bidx, bz, wave, lane);
         return;
@@ -713,8 +740,9 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
         if (split) mfma4_store_staged<float, false>(v, wsp, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
         else mfma4_store_staged<TO, true>(v, z, acc, lds_addr(sa), lds_addr(sb), m0, n0, bz, wave, lane);
         return;
+    } else {
+        mfma4_store_direct16<TO, NJ>(v, z, wsp, split, acc, m0, n0, bz, wave);
     }
-    mfma4_store_direct16<TO>(v, z, wsp, split, acc, m0, n0, bz, wave);
 }
 
 // The 64-deep tile's products: 16x16x32 (1) or 32x32x16 (0).
@@ -722,23 +750,25 @@ __device__ __forceinline__ void mfma4k16_body(const GemmView &v, const uint16_t 
 #define TRA_K4K_M16 1
 #endif
 // (The 32x32x16 body takes two K-major operands only.)
-template <bool AKM, bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false>
+template <bool AKM, bool BKM, typename TO, int EPI, int CH = 0, bool YROW = false, int BNW = 256>
 __device__ __forceinline__ void mfma4k_run(const GemmView &v, const uint16_t *__restrict__ x,
                                            const uint16_t *__restrict__ y, TO *__restrict__ z,
                                            float *__restrict__ ws, const ChainEpi &ce)
 {
-    if constexpr (TRA_K4K_M16 || !AKM || !BKM) mfma4k16_body<AKM, BKM, TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
+    if constexpr (TRA_K4K_M16 || !AKM || !BKM || BNW != 256)
+        mfma4k16_body<AKM, BKM, TO, EPI, CH, YROW, BNW>(v, x, y, z, ws, ce);
     else mfma4k_body<TO, EPI, CH, YROW>(v, x, y, z, ws, ce);
 }
 
 // VEC: the staged epilogue (the output's four consecutive columns form one
-// aligned vector, and z / the workspace are 16-byte aligned)
-template <bool AKM, bool BKM, typename TO, bool VEC>
+// aligned vector, and z / the workspace are 16-byte aligned).  BNW: the
+// tile's columns (256; 128 for the narrow tile, variant 5).
+template <bool AKM, bool BKM, typename TO, bool VEC, int BNW = 256>
 __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_bf16(GemmView v, const uint16_t *__restrict__ x,
                                                           const uint16_t *__restrict__ y, TO *__restrict__ z,
                                                           float *__restrict__ ws)
 {
-    mfma4k_run<AKM, BKM, TO, VEC ? 1 : 0>(v, x, y, z, ws, ChainEpi{});
+    mfma4k_run<AKM, BKM, TO, VEC ? 1 : 0, 0, false, BNW>(v, x, y, z, ws, ChainEpi{});
 }
 
 // The product with a chain of two elementwise steps in its staged epilogue
@@ -790,12 +820,12 @@ __global__ __launch_bounds__(mf4k::NT) void k_mfma4k_short(GemmView v, const uin
 
     typename std::conditional<AKM, DmaPlan8<0>, DmaPlanN8<0>>::type da;
     typename std::conditional<BKM, DmaPlan8<1>, DmaPlanN8<1>>::type db;
-    typename std::conditional<AKM, FragAddr16, FragAddrN16>::type fa;
-    typename std::conditional<BKM, FragAddr16, FragAddrN16>::type fb;
+    typename std::conditional<AKM, FragAddr16<>, FragAddrN16<>>::type fa;
+    typename std::conditional<BKM, FragAddr16<>, FragAddrN16<>>::type fb;
     fa.init(lds_addr(sa), wm, lane);
     fb.init(lds_addr(sb), wn, lane);
-    using FA = typename std::conditional<AKM, Frag16, Frag16N>::type;
-    using FB = typename std::conditional<BKM, Frag16, Frag16N>::type;
+    using FA = typename std::conditional<AKM, Frag16<>, Frag16N<>>::type;
+    using FB = typename std::conditional<BKM, Frag16<>, Frag16N<>>::type;
     constexpr int NAR = AKM ? 8 : 16, NBR = BKM ? 8 : 16;
     constexpr uint32_t k1 = NK - 1;   // k-tile 0 again when there is one
     const int32_t a1 = p2off<0>(v.gk, k1 * BK), b1 = p2off<1>(v.gk, k1 * BK);
@@ -1020,7 +1050,7 @@ static int launch4k_t(const tra_plan_s &p, const void *x, const void *y, void *z
     if constexpr (std::is_same<TO, float>::value) {
         const uint32_t n_lin = grid.x * grid.y;
         const int cus = device_cus();
-        if (short_enabled() && vec && v.split == 1 && v.k_per_split <= 2 * mf4k::BK && cus >= 8 &&
+        if (p.tile == 4 && short_enabled() && vec && v.split == 1 && v.k_per_split <= 2 * mf4k::BK && cus >= 8 &&
             n_lin > (uint32_t)cus) {
             void (*ks)(GemmView, const uint16_t *, const uint16_t *, float *);
             const bool two = v.k_per_split == 2 * mf4k::BK;
@@ -1040,6 +1070,15 @@ static int launch4k_t(const tra_plan_s &p, const void *x, const void *y, void *z
         }
     }
     void (*kern)(GemmView, const uint16_t *, const uint16_t *, TO *, float *);
+    if (p.tile == 5) {
+        // the narrow tile: 256 x 128, direct epilogue
+        grid.x = (v.gm.total / mf4k::BM) * (v.gn.total / 128);
+        if (p.a_kmajor) kern = p.b_kmajor ? k_mfma4k_bf16<true, true, TO, false, 128> : k_mfma4k_bf16<true, false, TO, false, 128>;
+        else kern = p.b_kmajor ? k_mfma4k_bf16<false, true, TO, false, 128> : k_mfma4k_bf16<false, false, TO, false, 128>;
+        hipLaunchKernelGGL(kern, grid, dim3(mf4k::NT), 0, s, v, (const uint16_t *)x, (const uint16_t *)y, (TO *)z,
+                           (float *)ws);
+        return (int)hipGetLastError();
+    }
 #define TRA_PICK4K(AK, BK) kern = vec ? k_mfma4k_bf16<AK, BK, TO, true> : k_mfma4k_bf16<AK, BK, TO, false>
     if (p.a_kmajor) {
         if (p.b_kmajor) TRA_PICK4K(true, true);

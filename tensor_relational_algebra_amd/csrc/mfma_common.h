@@ -617,10 +617,10 @@ __device__ __forceinline__ void mfma4_store_direct(const GemmView &v, TO *__rest
 }
 
 // The direct epilogue for the 16x16 accumulator layout (Acc16).
-template <typename TO>
+template <typename TO, int NJ = 2 * mf4::TN>   // NJ: the wave's 16-column blocks (8, or 4 for 128-wide tiles)
 __device__ __forceinline__ void mfma4_store_direct16(const GemmView &v, TO *__restrict__ z, float *__restrict__ wsp,
-                                                     bool split, const Acc16 &acc, uint32_t m0, uint32_t n0,
-                                                     int32_t bz, int wave)
+                                                     bool split, const floatx4_t (&acc)[2 * mf4::TM][NJ],
+                                                     uint32_t m0, uint32_t n0, int32_t bz, int wave)
 {
     using namespace mf4;
     const int lane = threadIdx.x & 63, wm = wave / WN, wn = wave % WN;
@@ -632,7 +632,7 @@ __device__ __forceinline__ void mfma4_store_direct16(const GemmView &v, TO *__re
     for (int i = 0; i < 2 * TM; ++i) {
         const int32_t hi = zm0 + p2off<1>(v.gm, (i * WM + wm) * 16);
 #pragma unroll
-        for (int j = 0; j < 2 * TN; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int32_t on = zn0 + p2off<1>(v.gn, (j * WN + wn) * 16 + (lane & 15));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {

@@ -25,7 +25,7 @@
 // 256 x 256 on four waves with 32-deep stages, 0 = 256 x 256 on eight waves,
 // 1 = 128 x 128, 2 = 64 x 64.
 #ifndef TRA_MFMA_ORDER
-#define TRA_MFMA_ORDER 4, 3, 0, 1, 2
+#define TRA_MFMA_ORDER 4, 5, 3, 0, 1, 2
 #endif
 // contiguous elements each operand needs along its staged dimension for the
 // 64-deep tile (one 16-byte copy granule).  With runs of 64 or more every
@@ -311,7 +311,7 @@ static bool lower_tile(tra_plan_s &p)
                      ((bk && contiguous_last(sk, 1, TRA_K64_RUN)) || (!bk && contiguous_last(sn, 0, TRA_K64_RUN)));
     for (int n = 0; n < (mfma ? kMfmaVariants : 4) && pm && pn; ++n) {
         const int variant = mfma ? kMfmaOrder[n] : n;
-        if (mfma && variant == 4 && !k64) continue;
+        if (mfma && (variant == 4 || variant == 5) && !k64) continue;
         TileShape ts = mfma ? mfma_tile_shape(variant) : valu_tile_shape(variant);
         if (ts.bm == 0) break;
         if (gv.gm.total % ts.bm || gv.gn.total % ts.bn || gv.gk.total % ts.bk) continue;

@@ -35,8 +35,9 @@ namespace tra {
 // in join terms per nanosecond, bandwidths in bytes per nanosecond.
 struct Calibration {
     double latency_ns = 3700.0;        // per node of back-to-back launches from the library
-    // bf16 matrix cores, tile variants 0/1/2/3/4 (launch latency taken out)
-    double mfma_terms[5] = {487e3, 163e3, 90e3, 518e3, 518e3};
+    // bf16 matrix cores, tile variants 0/1/2/3/4/5 (launch latency taken out;
+    // the narrow 64-deep tile, 5, is priced as the 128 x 128 tile it replaces)
+    double mfma_terms[6] = {487e3, 163e3, 90e3, 518e3, 518e3, 163e3};
     double valu_terms = 22.1e3;        // register-tiled vector-ALU joins (squared distance)
     double valu_small_int_terms = 35.0e3;   // int32 max / min-plus on packed 16-bit halves, range check included
                                             // (inputs within +-1024; outside, the 32-bit path runs at valu_terms)
@@ -63,7 +64,7 @@ int64_t predict_plan_ns(const tra_plan_s &p)
     double bw = kCal.stream_bw;
     switch (p.kernel) {
     case TRA_KERNEL_MFMA_BF16:
-        rate = kCal.mfma_terms[std::min(std::max(p.tile, 0), 4)];
+        rate = kCal.mfma_terms[std::min(std::max(p.tile, 0), 5)];
         bw = kCal.tile_bw;
         break;
     case TRA_KERNEL_VALU_TILE:

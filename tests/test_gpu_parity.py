@@ -395,6 +395,42 @@ def test_k_major_products_on_the_64_deep_tile(case):
     assert plan.kernel == "mfma_bf16" and plan.info.tile == 4, (plan.kernel, plan.info.tile)
 
 
+NARROW_CASES = [
+    # (spec, bounds, d, out dtype): 128-wide outputs on the 64-deep tile's
+    # 256 x 128 form (variant 5), all operand layouts, a blocked relation,
+    # a batch and a split contracted range
+    ("ik,jk->ij", {"i": 1024, "j": 128, "k": 512}, {"i": 1, "j": 1, "k": 1}, "f32"),
+    ("ik,kj->ij", {"i": 2048, "j": 128, "k": 1024}, {"i": 2, "j": 1, "k": 2}, "bf16"),
+    ("ki,kj->ij", {"i": 1024, "j": 128, "k": 256}, {"i": 1, "j": 1, "k": 1}, "f32"),
+    ("ki,jk->ij", {"i": 512, "j": 128, "k": 256}, {"i": 1, "j": 1, "k": 1}, "f32"),
+    ("hst,thd->shd", {"h": 4, "s": 512, "t": 512, "d": 128}, {"h": 2, "s": 1, "t": 2, "d": 1}, "bf16"),
+    ("ik,jk->ij", {"i": 256, "j": 128, "k": 8192}, {"i": 1, "j": 1, "k": 1}, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", NARROW_CASES, ids=["kk", "k-mn-blocked", "mn-mn", "mn-k",
+                                                     "attention-weighted-sum", "split"])
+def test_narrow_products_on_the_64_deep_tile(case):
+    """Products whose output is 128 wide (or whose blocking leaves 128-wide
+    column blocks) run on the 256 x 128 form of the 64-deep tile: parity with
+    the oracle on every element for each operand layout, bf16 and fp32
+    outputs, and a long contracted range split over workgroups."""
+    spec, bounds, d, odt = case
+    c = wl.EinsumCase(f"narrow_{spec}", 67, spec, bounds, d, "mul", "sum", "bf16", odt, (N002, N002))
+    err, plan = check(c)
+    assert plan.kernel == "mfma_bf16" and plan.info.tile == 5, (plan.kernel, plan.info.tile)
+
+
+def test_narrow_tile_weighted_sum_without_split_sampled():
+    """The attention weighted sum at 32 heads x 2048 queries x 1024 keys,
+    head dimension 128: 256 narrow tiles, one per workgroup and no split,
+    on 8192 sampled outputs spread over every tile."""
+    c = wl.EinsumCase("narrow_weighted_sum", 68, "hst,thd->shd", {"h": 32, "s": 2048, "t": 1024, "d": 128},
+                      {"h": 1, "s": 1, "t": 1, "d": 1}, "mul", "sum", "bf16", "bf16", (N002, N002))
+    err, plan = check(c, sample=8192, seed=13)
+    assert plan.kernel == "mfma_bf16" and plan.info.tile == 5 and plan.info.agg_split == 1
+
+
 SHORT_CASES = [
     # (spec, bounds, d, post_scale): one or two 64-deep k-tiles, fp32 output,
     # more output tiles than compute units (the persistent tile loop)
