@@ -74,7 +74,7 @@ TRAFFIC = {
     "sqdist": {"src_sha": "e60d668d8529fb0d", "fetch_kib": 40698.5, "write_kib": 262144.0,
                "fetch_factor": 2.0, "write_factor": 1.0,
                "profile": "profiles/valu_tile_sqdist_8192x256x8192_hbm_traffic.md"},
-    "gemm": {"src_sha": "34842fa09c44dabc", "fetch_kib": 1574096.2, "write_kib": 524307.4,
+    "gemm": {"src_sha": "be99c0e01da4d16d", "fetch_kib": 1573102.0, "write_kib": 524294.8,
              "fetch_factor": 2.0, "write_factor": 1.0,
              "profile": "profiles/mfma4k_gemm25d_16384x8192x8192_hbm_traffic.md"},
     "recut": {"src_sha": "27b277ed94e55d19", "fetch_kib": 262179.3, "write_kib": 524290.8,

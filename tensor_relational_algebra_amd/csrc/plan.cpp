@@ -21,9 +21,9 @@
 
 // Matrix-core tile variants in order of preference: 4 = 256 x 256 on four
 // waves with 64-deep stages and 16x16x32 products (runs of TRA_K64_RUN
-// contiguous elements along each operand's staged dimension), 3 =
-// 256 x 256 on four waves with 32-deep stages, 0 = 256 x 256 on eight waves,
-// 1 = 128 x 128, 2 = 64 x 64.
+// contiguous elements along each operand's staged dimension), 5 = the same
+// on a 256 x 128 tile (128-wide outputs), 3 = 256 x 256 on four waves with
+// 32-deep stages, 0 = 256 x 256 on eight waves, 1 = 128 x 128, 2 = 64 x 64.
 #ifndef TRA_MFMA_ORDER
 #define TRA_MFMA_ORDER 4, 5, 3, 0, 1, 2
 #endif
